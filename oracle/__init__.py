@@ -1,0 +1,32 @@
+"""Test oracle for batched paged decode attention (TEST INFRASTRUCTURE ONLY).
+
+A plain, slow, CPU-only float64 statement of what the GPU library computes,
+written from the pages' description of the method and from the definition of
+softmax attention.  It is used only by ``tests/``, by
+``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py``; the
+library itself never imports, links or calls it, and the two share no code.
+
+Contents and what each part follows:
+
+* ``values``    -- widening of stored bf16 / fp8-e4m3 / fp32 values to float64
+                   (fp8 KV cache: "Track C · Document 10 · Shrinking the
+                   footprint", section on the fp8 cache).
+* ``attention`` -- decode attention over one request's contiguous K/V, the LSE
+                   merge of two partial softmax states, and the cascade
+                   (prefix ++ suffix) check.  The pages state that paging leaves
+                   the attention result unchanged ("Track C · Document 10",
+                   PagedAttention Q&A), so the oracle is the plain definition
+                   over contiguous K/V and never sees pages.
+* ``lowering``  -- page table -> token-flat ``kv_indices``
+                   ("The 25% Page-Size Slowdown That Wasn't", section "Four
+                   meanings of page size" and "When source beats intuition").
+* ``planner``   -- the per-step dispatcher on M_eff = realized batch x GQA
+                   group ("GraniKV: asymmetric KV cache paging for
+                   shared-prefix agents", section 3 "Per-step dispatcher").
+* ``batch``     -- runs the above over a whole synthetic batch.
+
+Parity unpinned: none of the functions here.  The planner's tuning constants
+are inputs; whether their gfx950 values are the right ones is a measurement,
+not an oracle question.
+"""
+from . import values, attention, lowering, planner, batch  # noqa: F401

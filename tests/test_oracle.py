@@ -1,0 +1,433 @@
+"""Pins of the test oracle against facts that do not come from the oracle.
+
+Each check is a function taking the oracle routine under test, so that the
+same check also runs against deliberately broken copies of the oracle (the
+``test_mutant_*`` cases at the bottom): a plausible mistake must fail at
+least one pin.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from oracle import lowering as ol
+from oracle import planner as op
+from oracle import values as ov
+
+RNG = np.random.default_rng(7)
+
+
+# ---------------------------------------------------------------- values ---
+
+def check_fp8_table(decode_one):
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    got = np.array([decode_one(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_fp8_all_codes_match_torch():
+    check_fp8_table(ov.fp8_e4m3_value)
+    assert np.array_equal(ov.FP8_E4M3_TABLE[:0x7F], [ov.fp8_e4m3_value(c) for c in range(0x7F)])
+
+
+def test_bf16_widening_matches_torch():
+    bits = RNG.integers(0, 1 << 16, size=20000, dtype=np.int64).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = ov.bf16_bits_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_fp8_scale_applies_per_head():
+    bits = np.array([[[0x38, 0x40], [0x38, 0x40]]], np.uint8)  # 1.0, 2.0 per head
+    x = ov.stored_to_f64(bits, "fp8", np.array([0.5, 3.0], np.float32))
+    assert np.array_equal(x, [[[0.5, 1.0], [3.0, 6.0]]])
+
+
+# ------------------------------------------------------------- attention ---
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def check_closed_forms(attn):
+    # one token: softmax weight 1 -> o = V_0, lse = s_0
+    q, k, v = _rand(8, 16), _rand(1, 2, 16), _rand(1, 2, 16)
+    o, lse = attn(q, k, v, 0.25)
+    for h in range(8):
+        g = h // 4
+        assert np.allclose(o[h], v[0, g], rtol=0, atol=1e-14)
+        assert np.isclose(lse[h], 0.25 * q[h] @ k[0, g], rtol=0, atol=1e-13)
+    # zero query: uniform weights -> mean of V, lse = ln L
+    L = 37
+    q0, k, v = np.zeros((4, 8)), _rand(L, 1, 8), _rand(L, 1, 8)
+    o, lse = attn(q0, k, v, 1.0)
+    assert np.allclose(o, v[:, 0].mean(0), atol=1e-14)
+    assert np.allclose(lse, math.log(L), atol=1e-14)
+    # two tokens: logistic weights
+    q, k, v = _rand(2, 4), _rand(2, 2, 4), _rand(2, 2, 4)
+    o, lse = attn(q, k, v, 0.5)
+    for h in range(2):
+        s0, s1 = 0.5 * q[h] @ k[0, h], 0.5 * q[h] @ k[1, h]
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert np.allclose(o[h], w0 * v[0, h] + (1 - w0) * v[1, h], atol=1e-14)
+        assert np.isclose(lse[h], math.log(math.exp(s0) + math.exp(s1)), atol=1e-13)
+    # identical keys: uniform weights whatever the query
+    k1 = np.repeat(_rand(1, 1, 8), 9, axis=0)
+    v = _rand(9, 1, 8)
+    o, lse = attn(_rand(2, 8), k1, v, 0.3)
+    assert np.allclose(o, v[:, 0].mean(0), atol=1e-13)
+    # empty: zeros and -inf
+    o, lse = attn(_rand(4, 8), np.zeros((0, 2, 8)), np.zeros((0, 2, 8)), 1.0)
+    assert not o.any() and np.all(lse == -np.inf)
+
+
+def test_attention_closed_forms():
+    check_closed_forms(oa.decode_attention)
+
+
+def check_against_sdpa(attn, cases=12):
+    """torch's scaled_dot_product_attention on CPU in float64, K/V heads
+    repeated so that query head h reads KV head h // G."""
+    for _ in range(cases):
+        H_kv = int(RNG.choice([1, 2, 4]))
+        G = int(RNG.choice([1, 2, 4, 8]))
+        d = int(RNG.choice([1, 4, 64, 128]))
+        L = int(RNG.integers(1, 300))
+        scale = float(RNG.uniform(0.05, 1.0))
+        q, k, v = _rand(H_kv * G, d), _rand(L, H_kv, d), _rand(L, H_kv, d)
+        o, lse = attn(q, k, v, scale)
+        qt = torch.from_numpy(q)[None, :, None, :]                       # 1,H,1,d
+        kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, 0)[None]  # 1,H,L,d
+        vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0]
+        scores = (qt @ kt.transpose(-1, -2))[0, :, 0] * scale
+        lse_ref = torch.logsumexp(scores, dim=-1)
+        assert np.allclose(o, ref.numpy(), rtol=0, atol=1e-12), (H_kv, G, d, L)
+        assert np.allclose(lse, lse_ref.numpy(), rtol=0, atol=1e-11), (H_kv, G, d, L)
+
+
+def test_attention_matches_sdpa_fp64():
+    check_against_sdpa(oa.decode_attention)
+
+
+def _brute(q, k, v, scale):
+    H_q, d = len(q), len(q[0])
+    L, H_kv = len(k), len(k[0]) if len(k) else 1
+    G = H_q // H_kv
+    o, lse = [], []
+    for h in range(H_q):
+        g = h // G
+        s = [scale * sum(q[h][i] * k[j][g][i] for i in range(d)) for j in range(L)]
+        z = sum(math.exp(x) for x in s)
+        o.append([sum(math.exp(s[j]) * v[j][g][i] for j in range(L)) / z for i in range(d)])
+        lse.append(math.log(z))
+    return o, lse
+
+
+def check_against_bruteforce(attn):
+    for _ in range(30):
+        H_kv = int(RNG.integers(1, 3))
+        G = int(RNG.integers(1, 4))
+        d = int(RNG.integers(1, 5))
+        L = int(RNG.integers(1, 9))
+        q, k, v = _rand(H_kv * G, d), _rand(L, H_kv, d), _rand(L, H_kv, d)
+        o, lse = attn(q, k, v, 0.7)
+        ob, lb = _brute(q.tolist(), k.tolist(), v.tolist(), 0.7)
+        assert np.allclose(o, ob, atol=1e-13) and np.allclose(lse, lb, atol=1e-13)
+
+
+def test_attention_matches_bruteforce():
+    check_against_bruteforce(oa.decode_attention)
+
+
+# ----------------------------------------------------------------- merge ---
+
+def check_split_invariance(merge, attn=oa.decode_attention):
+    q, k, v = _rand(8, 16), _rand(23, 2, 16), _rand(23, 2, 16)
+    o_full, lse_full = attn(q, k, v, 0.3)
+    for c in range(0, 24):
+        oa_, la = attn(q, k[:c], v[:c], 0.3)
+        ob, lb = attn(q, k[c:], v[c:], 0.3)
+        o, lse = merge(oa_, la, ob, lb)
+        assert np.allclose(o, o_full, atol=1e-13), c
+        assert np.allclose(lse, lse_full, atol=1e-13), c
+        assert np.allclose(lse, np.logaddexp(la, lb), atol=1e-13)
+
+
+def test_merge_split_at_every_point():
+    check_split_invariance(oa.merge_states)
+
+
+def test_merge_algebra():
+    rows, d = 6, 5
+    sa = (_rand(rows, d), _rand(rows))
+    sb = (_rand(rows, d), _rand(rows))
+    sc = (_rand(rows, d), _rand(rows))
+    ab = oa.merge_states(*sa, *sb)
+    ba = oa.merge_states(*sb, *sa)
+    assert np.allclose(ab[0], ba[0], atol=1e-14) and np.allclose(ab[1], ba[1], atol=1e-14)
+    left = oa.merge_states(*ab, *sc)
+    right = oa.merge_states(*sa, *oa.merge_states(*sb, *sc))
+    assert np.allclose(left[0], right[0], atol=1e-13) and np.allclose(left[1], right[1], atol=1e-13)
+    empty = (np.zeros((rows, d)), np.full(rows, -np.inf))
+    o, lse = oa.merge_states(*sa, *empty)
+    assert np.array_equal(o, sa[0]) and np.array_equal(lse, sa[1])
+    o, lse = oa.merge_states(*empty, *empty)
+    assert not o.any() and np.all(lse == -np.inf) and not np.isnan(o).any()
+
+
+def test_cascade_equals_full():
+    q, kp, vp = _rand(32, 64), _rand(40, 8, 64), _rand(40, 8, 64)
+    ks, vs = _rand(9, 8, 64), _rand(9, 8, 64)
+    o, lse = oa.cascade_attention(q, kp, vp, ks, vs, 0.125)
+    of, lf = oa.decode_attention(q, np.concatenate([kp, ks]), np.concatenate([vp, vs]), 0.125)
+    assert np.allclose(o, of, atol=1e-13) and np.allclose(lse, lf, atol=1e-13)
+    o2, l2 = oa.split_attention(q, np.concatenate([kp, ks]), np.concatenate([vp, vs]), 0.125, [3, 17, 40])
+    assert np.allclose(o2, of, atol=1e-13) and np.allclose(l2, lf, atol=1e-13)
+
+
+# -------------------------------------------------------------- lowering ---
+
+def _random_table(rng, B, p, lmax, pool_extra=5):
+    lens = rng.integers(0, lmax + 1, size=B)
+    npages = [(int(L) + p - 1) // p for L in lens]
+    pool = sum(npages) + pool_extra
+    perm = rng.permutation(pool)
+    indptr = np.concatenate([[0], np.cumsum(npages)])
+    return lens, indptr, perm[: indptr[-1]], pool
+
+
+def check_lowering(lower):
+    rng = np.random.default_rng(3)
+    for p in (1, 2, 3, 16, 128):
+        lens, indptr, pages, pool = _random_table(rng, 7, p, 300)
+        kv_indptr, kv_indices = lower(p, indptr, pages, lens)
+        kv_indptr, kv_indices = np.asarray(kv_indptr), np.asarray(kv_indices)
+        assert kv_indptr[-1] == lens.sum() and len(kv_indices) == lens.sum()
+        # inverse gather: a pool holding each slot's own id, read through the
+        # indices, returns the indices; and every slot sits in its page
+        slot_ids = np.arange(pool * p)
+        assert np.array_equal(slot_ids[kv_indices], kv_indices)
+        for b in range(len(lens)):
+            mine = kv_indices[kv_indptr[b]:kv_indptr[b + 1]]
+            assert len(set(mine.tolist())) == len(mine)
+            own = pages[indptr[b]:indptr[b + 1]]
+            assert set((mine // p).tolist()) <= set(own.tolist())
+            # logical order: token t is at offset t mod p of logical page t // p
+            t = np.arange(len(mine))
+            assert np.array_equal(mine % p, t % p)
+            assert np.array_equal(mine // p, own[t // p])
+
+
+def test_lowering_bruteforce_and_numpy_agree_and_hold_invariants():
+    check_lowering(ol.lower_page_table_bruteforce)
+    check_lowering(ol.lower_page_table)
+    rng = np.random.default_rng(11)
+    for p in (1, 16, 64):
+        lens, indptr, pages, _ = _random_table(rng, 9, p, 200)
+        a = ol.lower_page_table_bruteforce(p, indptr, pages, lens)
+        b = ol.lower_page_table(p, indptr, pages, lens)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_lowering_rejects_wrong_page_counts():
+    with pytest.raises(ol.LoweringError):
+        ol.lower_page_table(16, [0, 2], [3, 4], [16])      # trailing empty page
+    with pytest.raises(ol.LoweringError):
+        ol.lower_page_table(16, [0, 1], [3], [17])         # one page short
+    with pytest.raises(ol.LoweringError):
+        ol.lower_page_table(0, [0, 0], [], [0])
+
+
+def test_index_length_is_batch_times_context(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "index_length.json")))
+    B, L = g["batch"], g["context_tokens"]
+    for p in g["page_sizes"]:
+        n = (L + p - 1) // p
+        indptr = np.arange(B + 1) * n
+        pages = np.random.default_rng(p).permutation(B * n)
+        kv_indptr, kv_indices = ol.lower_page_table(p, indptr, pages, [L] * B)
+        assert len(kv_indices) == g["index_length"] and kv_indptr[-1] == g["index_length"]
+
+
+def test_block_aligned_prefix_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "prefix_block_alignment.json")))
+    assert ol.shared_prefix_pages(g["prefix_tokens"], g["block_size"]) == (g["shared_blocks"], g["unshared_tokens"])
+
+
+def test_worst_case_internal_waste_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "block_internal_waste.json")))
+    p = g["block_size"]
+    waste = [((L + p - 1) // p) * p - L for L in range(1, 10 * p)]
+    assert max(waste) == g["worst_case_unused_slots"]
+
+
+# --------------------------------------------------------------- planner ---
+
+TUNE = dict(t_dense=1024, gate_ratio=1, launch_bytes=0)
+
+
+def _plan(B, G, P, p=16, H_kv=8, d=128, L=None, **kw):
+    args = dict(B=B, H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype="bf16", kv_dtype="bf16",
+                page_size=p, seq_lens=[L if L is not None else P + 100] * B,
+                shared_prefix_len=P, force_path=-1, **TUNE)
+    args.update(kw)
+    return op.plan(**args)
+
+
+def test_dispatcher_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "dispatcher.json")))
+    for c in g["cases"]:
+        r = _plan(c["batch"], c["group"], 4096, t_dense=g["a100_threshold"])
+        assert r["m_eff"] == c["m_eff"] and r["path"] == c["path"], c
+
+
+def test_planner_gate_and_alignment():
+    assert _plan(256, 4, 4096)["path"] == "DENSE"                   # c3 shape
+    assert _plan(512, 4, 512)["path"] == "DENSE"                    # c4 shape
+    r = _plan(256, 4, 2003)
+    assert r["shared_pages"] == 125 and r["prefix_tokens"] == 2000
+    assert _plan(1, 4, 4096)["path"] == "PAGED"                      # nothing to share
+    r = _plan(256, 4, 15)
+    assert r["path"] == "PAGED" and r["shared_pages"] == 0          # no whole page
+    assert _plan(256, 4, 0)["path"] == "PAGED"
+    # the gate: a huge launch cost keeps short prefixes on the paged path
+    # B=4, P=16: saves 3*16*8*128*4 = 196,608 B of prefix reads but adds
+    # 16*128*129 = 264,192 B of partial-state traffic -> stays paged
+    assert _plan(4, 4, 16, launch_bytes=0)["path"] == "PAGED"
+    assert _plan(4, 4, 256, launch_bytes=0)["path"] == "CASCADE"
+    assert _plan(4, 4, 256, launch_bytes=10**12)["path"] == "PAGED"
+    # fp8 K/V has no prefix kernel: paged, and forcing a prefix path is refused
+    assert _plan(256, 4, 4096, kv_dtype="fp8")["path"] == "PAGED"
+    with pytest.raises(op.PlanError) as e:
+        _plan(256, 4, 4096, kv_dtype="fp8", force_path=2)
+    assert e.value.code == "EUNSUPPORTED"
+    with pytest.raises(op.PlanError) as e:
+        _plan(256, 4, 8, force_path=1)
+    assert e.value.code == "EINVAL"
+    r = _plan(256, 4, 4096, force_path=0)
+    assert r["path"] == "PAGED" and r["prefix_tokens"] == 0 and r["shared_pages"] == 256
+
+
+def test_planner_rejects():
+    for kw, code in [(dict(H_q=30), "EINVAL"), (dict(d=96), "EUNSUPPORTED"),
+                     (dict(q_dtype="f32"), "EUNSUPPORTED"), (dict(force_path=3), "EINVAL"),
+                     (dict(L=10), "EINVAL")]:
+        with pytest.raises(op.PlanError) as e:
+            _plan(8, 4, 64, **kw)
+        assert e.value.code == code, kw
+    with pytest.raises(op.PlanError) as e:
+        _plan(8, 16, 64, H_kv=2)                     # G = 16 not built
+    assert e.value.code == "EUNSUPPORTED"
+
+
+# ------------------------------------------------ planted mistakes (CPU) ---
+# Each mutant is a copy of an oracle routine with one plausible mistake.  The
+# pins above must reject every one of them.
+
+def _mut_head_map(q, k, v, s):          # h % H_kv instead of h // G
+    H_q, d = q.shape
+    L, H_kv, _ = k.shape
+    o, lse = np.zeros((H_q, d)), np.full(H_q, -np.inf)
+    for h in range(H_q):
+        g = h % H_kv
+        sc = s * (k[:, g] @ q[h]); m = sc.max(); e = np.exp(sc - m)
+        o[h] = e @ v[:, g] / e.sum(); lse[h] = m + np.log(e.sum())
+    return o, lse
+
+
+def _mut_lse_unscaled(q, k, v, s):      # lse of the raw dot products
+    o, lse = oa.decode_attention(q, k, v, s)
+    if k.shape[0]:
+        o2, l2 = oa.decode_attention(q, k, v, 1.0)
+        lse = l2
+    return o, lse
+
+
+def _mut_no_normalise(q, k, v, s):      # forgets the division by l
+    o, lse = oa.decode_attention(q, k, v, s)
+    if k.shape[0]:
+        H_q = q.shape[0]
+        G = H_q // k.shape[1]
+        for h in range(H_q):
+            sc = s * (k[:, h // G] @ q[h])
+            o[h] *= np.exp(sc - sc.max()).sum()
+    return o, lse
+
+
+def _mut_transposed_pv(q, k, v, s):     # uses K where V belongs
+    return oa.decode_attention(q, k, k, s)
+
+
+def _mut_merge_swapped(o_a, lse_a, o_b, lse_b):   # weights crossed over
+    M = np.maximum(lse_a, lse_b)
+    wa, wb = np.exp(lse_a - M)[:, None], np.exp(lse_b - M)[:, None]
+    return (wb * o_a + wa * o_b) / (wa + wb), M + np.log(wa + wb)[:, 0]
+
+
+def _mut_merge_no_max(o_a, lse_a, o_b, lse_b):    # drops lse_b's weight term
+    o, lse = oa.merge_states(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)
+
+
+def _mut_fp8_bias8(c):
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    sign = -1.0 if s else 1.0
+    return sign * ((m / 8) * 2.0 ** -7 if e == 0 else (1 + m / 8) * 2.0 ** (e - 8))
+
+
+def _mut_lower_swapped(p, indptr, pages, lens):   # offset and page swapped
+    kv_indptr, kv = [0], []
+    for b in range(len(lens)):
+        for t in range(int(lens[b])):
+            kv.append(int(pages[int(indptr[b]) + t % p]) * p + t // p if t % p < indptr[b + 1] - indptr[b] else 0)
+        kv_indptr.append(len(kv))
+    return kv_indptr, kv
+
+
+def _mut_lower_offbyone(p, indptr, pages, lens):  # skips page 0's first slot
+    kv_indptr, kv = ol.lower_page_table(p, indptr, pages, lens)
+    return kv_indptr, kv + (kv % p == 0)
+
+
+@pytest.mark.parametrize("mutant", [_mut_head_map, _mut_transposed_pv])
+def test_mutant_attention_caught_by_sdpa(mutant):
+    with pytest.raises(AssertionError):
+        check_against_sdpa(mutant, cases=8)
+
+
+@pytest.mark.parametrize("mutant", [_mut_lse_unscaled, _mut_no_normalise, _mut_transposed_pv])
+def test_mutant_attention_caught_by_closed_forms(mutant):
+    with pytest.raises(AssertionError):
+        check_closed_forms(mutant)
+
+
+@pytest.mark.parametrize("mutant", [_mut_merge_swapped, _mut_merge_no_max])
+def test_mutant_merge_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_split_invariance(mutant)
+
+
+def test_mutant_fp8_caught():
+    with pytest.raises(AssertionError):
+        check_fp8_table(_mut_fp8_bias8)
+
+
+@pytest.mark.parametrize("mutant", [_mut_lower_swapped, _mut_lower_offbyone])
+def test_mutant_lowering_caught(mutant):
+    with pytest.raises((AssertionError, IndexError)):
+        check_lowering(mutant)

@@ -1,0 +1,13 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This package draws random numbers and lays them out; it computes nothing the
+attention method itself computes.  Both the test oracle and the GPU library
+consume what it produces, and neither side's arithmetic lives here.
+"""
+from .synth import (  # noqa: F401
+    DecodeBatch,
+    CONFIGS,
+    make_config,
+    make_decode_batch,
+    relayout,
+)
