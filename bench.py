@@ -1,0 +1,224 @@
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c1,c2,...]
+
+A step is one whole decode-attention step of one layer as the planner chose
+it (pkv_decode_step: the paged pass, or prefix pass + suffix pass + merge),
+with every input already resident in HBM.  Only kernels are inside the timed
+region: planning, page-table lowering and uploads happen once before it, and
+the same inputs are reused every step (warm caches, no admission ramp).
+
+The headline line is the Llama-3.1-8B-shaped layer (B=32, 32 query / 8 KV
+heads, head_dim 128, 4096 tokens each, bf16, token-flat indices at page size
+1): ``value`` is its algorithmic HBM throughput in GB/s.  The other workloads
+(tiny fp32, shared-prefix cascade, short prefix, long-context fp8) are
+reported under ``extra``.  Prints one JSON line on stdout.
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def algorithmic_bytes(batch, path, prefix_tokens=0):
+    """Bytes the method must move for one step (not re-reads, not split partials)."""
+    B, Hq, Hkv, d = batch.B, batch.H_q, batch.H_kv, batch.d
+    bkv = 2 * BYTES[batch.kv_dtype]
+    bq = BYTES[batch.q_dtype]
+    rows = B * Hq
+    L = [int(x) for x in batch.seq_lens]
+    if path == "PAGED":
+        tot = sum(L)
+        n = tot * Hkv * d * bkv + 4 * tot + 4 * (B + 1) + rows * d * 2 * bq + 4 * rows
+        if batch.kv_dtype == "fp8":
+            n += 8 * Hkv
+        return n
+    P = prefix_tokens
+    S = sum(x - P for x in L)
+    return (P * Hkv * d * bkv + 4 * P + S * Hkv * d * bkv + 4 * S + 2 * rows * d * bq + 4 * rows * (d + 1) * 4
+            + rows * d * bq)
+
+
+def time_steps(fn, steps, warmup):
+    """Warmup, then exactly `steps` calls between two events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def bench_paged_config(name, steps, warmup, **overrides):
+    import torch
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_config
+    b = make_config(name, device="cuda", **overrides)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan()
+    o, lse, ws = db.new_out(), db.new_lse(), db.workspace(plan)
+    ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
+    nbytes = algorithmic_bytes(b, plan.info["path_name"])
+    rec = dict(workload=name, page_size=b.page_size, path=plan.info["path_name"], us_per_step=ms * 1e3,
+               algorithmic_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, num_splits=plan.info["num_splits"],
+               split_tokens=plan.info["split_tokens"], work_items=plan.info["num_work_items"])
+    rec["pct_peak"] = 100.0 * rec["gbs"] / PEAK_HBM_GBS
+    return rec, b, db, plan
+
+
+def bench_prefix_config(name, steps, warmup):
+    """PAGED over unique prefix copies, PAGED over shared pages, and each
+    prefix path, plus the planner's choice."""
+    import torch
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_config, relayout
+    b = make_config(name, device="cuda")
+    P = b.prefix_len
+    out = dict(workload=name, B=b.B, prefix=P)
+    db = DeviceBatch.from_batch(b)
+    o, lse = db.new_out(), db.new_lse()
+    for force, label in ((0, "paged_shared"), (1, "cascade"), (2, "dense"), (-1, "planned")):
+        plan = db.plan(shared_prefix_len=P, force_path=force)
+        ws = db.workspace(plan)
+        ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
+        path = plan.info["path_name"]
+        nbytes = algorithmic_bytes(b, path, plan.info["prefix_tokens"])
+        out[label] = dict(path=path, us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
+                          algorithmic_bytes=nbytes)
+        del ws
+    del db
+    torch.cuda.empty_cache()
+    u = relayout(b, page_size=b.page_size, seed=2000 + int(name[1:]), layout="unique", device="cuda")
+    del b
+    du = DeviceBatch.from_batch(u)
+    plan = du.plan(force_path=0)
+    ws = du.workspace(plan)
+    ms = time_steps(lambda: du.step(plan, o, lse, ws), steps, warmup)
+    nbytes = algorithmic_bytes(u, "PAGED")
+    out["paged_unique"] = dict(path="PAGED", us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
+                               pct_peak=100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, algorithmic_bytes=nbytes)
+    out["speedup_vs_paged_unique"] = out["paged_unique"]["us_per_step"] / out["planned"]["us_per_step"]
+    out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["planned"]["us_per_step"]
+    del du, u, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(batch, reps=3):
+    """The oracle, as it stands, on the same workload on the host cores."""
+    from oracle import batch as ob
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    t = time.perf_counter()
+    n = 0
+    while True:
+        ob.batch_reference(batch)
+        n += 1
+        if n >= reps or time.perf_counter() - t > 20:
+            break
+    dt = (time.perf_counter() - t) / n
+    return dt, threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(the decode step shards by request or KV head with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+    wanted = args.configs.split(",")
+    extra = {}
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    # headline: Llama-3.1-8B layer, page size 1 (token-flat scatter) and 128
+    log("bench c2 p=1")
+    rec1, b1, db1, plan1 = bench_paged_config("c2", args.steps, args.warmup, page_size=1)
+    log(json.dumps(rec1))
+    del db1
+    torch.cuda.empty_cache()
+    log("bench c2 p=128")
+    rec128, b128, db128, _ = bench_paged_config("c2", args.steps, args.warmup)
+    log(json.dumps(rec128))
+    del db128, b128
+    torch.cuda.empty_cache()
+    extra["c2_page128"] = rec128
+    for name in wanted:
+        if name in ("c1", "c5"):
+            log(f"bench {name}")
+            r, _, db, _ = bench_paged_config(name, args.steps, args.warmup)
+            extra[name] = r
+            log(json.dumps(r))
+            del db
+            torch.cuda.empty_cache()
+        elif name in ("c3", "c4"):
+            log(f"bench {name}")
+            extra[name] = bench_prefix_config(name, args.steps, args.warmup)
+            log(json.dumps(extra[name]))
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle) on c2")
+        dt, threads = cpu_baseline(b1)
+        nbytes = rec1["algorithmic_bytes"]
+        cpu = dict(value=nbytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                   sample="whole Llama-layer workload (B=32, 4096 tokens, bf16 widened to fp64), "
+                          f"{dt:.2f} s per step on {platform.processor() or platform.machine()}")
+
+    ms = rec1["us_per_step"] / 1e3
+    line = {
+        "metric": "decode-attn HBM GB/s (algorithmic bytes / step time), Llama-3.1-8B layer, page size 1",
+        "value": rec1["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_step": rec1["us_per_step"],
+        "pct_peak": rec1["pct_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, token-flat indices over a randomly permuted pool)",
+        "config": {"workload": "Llama-3.1-8B decode layer: B=32, 32 q / 8 kv heads, head_dim 128, 4096 tokens "
+                               "per request, bf16, kv_indices of length 131072, page size 1",
+                   "global_batch": 32, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": rec1["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": rec1["gbs"] / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "paged decode step (split kernel + split reduction)"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

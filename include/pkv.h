@@ -1,0 +1,273 @@
+/*
+ * pkv.h -- batched decode attention over a paged KV cache, for AMD gfx950.
+ *
+ * Plain C ABI.  Every pointer is either host memory or device memory, as each
+ * declaration states; no C++ or framework types cross this boundary.  All
+ * device work is enqueued on the caller's HIP stream (passed as void*; NULL
+ * is the default stream) on the caller's current device, and is asynchronous.
+ *
+ * Sources for the operations (the pages this library implements):
+ *   [P1] "The 25% Page-Size Slowdown That Wasn't" -- sections "Four meanings of
+ *        page size" (paged KV cache; lowering a page table into per-token
+ *        indices of length B x L), "When source beats intuition" (the
+ *        host plan() step; contiguous / block / scattered index layouts).
+ *   [P2] "GraniKV: asymmetric KV cache paging for shared-prefix agents" --
+ *        section 2 "Reuse saves prefill, not decode reads" (a shared prefix
+ *        read once per step for all requests instead of once per request) and
+ *        section 3 "Per-step dispatcher" (M_eff = realized batch x GQA group;
+ *        dense at or above a threshold, tiled cascade below it).
+ *   [P3] "Track C · Document 10 · Shrinking the footprint" -- PagedAttention
+ *        Q&A (fixed-size blocks anywhere in memory, results identical to
+ *        unpaged attention), block-size paragraph (block-aligned prefix
+ *        matching), fp8 cache section.
+ *
+ * Conventions used throughout
+ *   - B requests, H_q query heads, H_kv KV heads, G = H_q / H_kv (query head h
+ *     reads KV head h / G), head_dim d.
+ *   - q, o: row-major [B][H_q][d];  lse: [B][H_q], natural log, softmax scale
+ *     included; partial states (o_f32, lse) are fp32.
+ *   - K and V pools: row-major [num_slots][H_kv][d] of the KV dtype, separate
+ *     tensors; num_slots = num_pages * page_size; physical page n holds slots
+ *     n*p .. n*p+p-1.
+ *   - kv_indptr[B+1] and kv_indices[kv_indptr[B]] are int32: request b's
+ *     logical token t lives in slot kv_indices[kv_indptr[b] + t].
+ *   - An empty token set gives o = 0 and lse = -inf.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory; scratch space is the caller's workspace, sized by the plan.  The
+ *     library owns only plan handles (host heap).
+ *   - Every call returns a pkv_status.  Host-detectable errors return before
+ *     anything is enqueued.  Kernels do not bounds-check kv_indices
+ *     (pkv_validate_indices does that on the host); a bad index faults on the
+ *     device and surfaces at the caller's next synchronisation.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_EINVAL = -1,        /* malformed argument: null pointer, bad size, bad indptr */
+    PKV_EUNSUPPORTED = -2,  /* shape / dtype combination not built */
+    PKV_EWORKSPACE = -3,    /* workspace missing or smaller than the plan needs */
+    PKV_ERANGE = -4,        /* an index or length outside what the tables allow */
+    PKV_EHIP = -5,          /* HIP launch error */
+    PKV_ENOMEM = -6         /* host allocation of a plan failed */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_BF16 = 1,
+    PKV_FP8_E4M3 = 2        /* OCP e4m3fn codes; value = code * per-KV-head fp32 scale */
+} pkv_dtype;
+
+typedef enum pkv_path {
+    PKV_PATH_PAGED = 0,     /* every request reads all of its tokens ([P1]) */
+    PKV_PATH_CASCADE = 1,   /* prefix read once with small query tiles, + suffix, + merge ([P2] s.3) */
+    PKV_PATH_DENSE = 2      /* prefix read once with large MFMA query tiles, + suffix, + merge ([P2] s.3) */
+} pkv_path;
+
+/* A caller-owned K/V pool in device memory ([P1] "Four meanings of page
+ * size"; [P3] PagedAttention Q&A).  The library never frees or keeps it. */
+typedef struct pkv_pool {
+    const void* k;          /* device, [num_slots][num_kv_heads][head_dim] of kv_dtype */
+    const void* v;          /* device, same layout as k */
+    const float* k_scale;   /* device, [num_kv_heads]; required iff kv_dtype is FP8 */
+    const float* v_scale;   /* device, [num_kv_heads]; required iff kv_dtype is FP8 */
+    int64_t num_slots;      /* must be a multiple of page_size */
+    int32_t page_size;      /* tokens per page, >= 1 */
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t kv_dtype;       /* pkv_dtype */
+} pkv_pool;
+
+/* One decode step, as the planner sees it (host data only). */
+typedef struct pkv_problem {
+    int32_t batch;              /* B >= 0 */
+    int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+    int32_t num_kv_heads;       /* H_kv >= 1 */
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t q_dtype;            /* pkv_dtype: F32 with F32 K/V, BF16 with BF16 or FP8 K/V */
+    int32_t kv_dtype;           /* pkv_dtype */
+    int32_t page_size;          /* >= 1 */
+    const int32_t* kv_indptr;   /* host, [B+1]: the same values as the device indptr
+                                   later passed to the attention calls */
+    int32_t shared_prefix_len;  /* P: the first P tokens of every request are the same
+                                   tokens, stored in shared pages; 0 = no shared prefix */
+    int32_t force_path;         /* -1: let the planner choose; else a pkv_path */
+} pkv_problem;
+
+/* Constants of the planner.  pkv_tuning_defaults() returns the gfx950 values. */
+typedef struct pkv_tuning {
+    int32_t t_dense;            /* DENSE when M_eff >= t_dense ([P2] s.3 threshold, refitted) */
+    int32_t gate_ratio;         /* PAGED when saved_bytes < gate_ratio * overhead_bytes */
+    int64_t launch_bytes;       /* byte-equivalent of the two extra launches of a cascade */
+    int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU */
+    int32_t min_split_tokens;   /* paged pass: smallest token range per workgroup */
+} pkv_tuning;
+
+typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */
+
+typedef struct pkv_plan_info {
+    int32_t path;               /* pkv_path chosen */
+    int32_t m_eff;              /* B * G ([P2] s.3) */
+    int32_t shared_pages;       /* floor(P / page_size) when a prefix is declared, else 0 */
+    int32_t prefix_tokens;      /* tokens the prefix pass covers (0 on PAGED) */
+    int32_t split_tokens;       /* paged pass: logical tokens per work item */
+    int32_t num_splits;         /* paged pass: work items per (request, head block), max */
+    int32_t heads_per_item;     /* paged pass: KV heads one work item covers */
+    int32_t prefix_splits;      /* prefix pass: ranges the prefix is cut into */
+    int64_t num_work_items;     /* paged pass: workgroups launched */
+    int64_t workspace_bytes;    /* device scratch the plan's calls need (0 allowed) */
+} pkv_plan_info;
+
+/* Human-readable name of a status code (static storage). */
+const char* pkv_status_string(int32_t status);
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+
+/* Fill *out with the gfx950 planner constants. */
+void pkv_tuning_defaults(pkv_tuning* out);
+
+/*
+ * Page table -> token-flat indices (host).  [P1] "Four meanings of page size":
+ * per-page metadata expanded into one index per cached token.  Request b owns
+ * pages page_indices[page_indptr[b] .. page_indptr[b+1]) in logical order and
+ * seq_lens[b] tokens; token t goes to slot page * page_size + t % page_size of
+ * its logical page t / page_size.
+ *   page_indptr   host, [B+1], page_indptr[0] == 0, non-decreasing
+ *   page_indices  host, [page_indptr[B]]
+ *   seq_lens      host, [B]
+ *   kv_indptr_out host, [B+1] written
+ *   kv_indices_out host, [kv_indices_capacity]; sum(seq_lens) entries written
+ * Errors: EINVAL (null pointer, B < 0, page_size < 1, bad indptr, negative
+ * length), ERANGE (a request's page count is not ceil(seq_len / page_size), a
+ * page index is negative or its slots overflow int32, or the output capacity
+ * is too small).  Nothing is written on error.
+ */
+pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size,
+                                const int32_t* page_indptr, const int32_t* page_indices,
+                                const int32_t* seq_lens,
+                                int32_t* kv_indptr_out, int32_t* kv_indices_out,
+                                int64_t kv_indices_capacity);
+
+/*
+ * Check token-flat indices on the host before handing them to a kernel:
+ * kv_indptr[0] == 0, non-decreasing, and 0 <= kv_indices[i] < num_slots.
+ *   kv_indptr host [B+1]; kv_indices host [kv_indptr[B]].
+ * Errors: EINVAL (null pointer, B < 0, bad indptr), ERANGE (an index outside
+ * the pool).
+ */
+pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indices,
+                                int32_t batch, int64_t num_slots);
+
+/*
+ * Plan one decode step (host only, no device work).  [P2] s.3: chooses the
+ * path from M_eff = B * G and the declared shared prefix; [P1] "When source
+ * beats intuition": the host metadata step before the kernels.  Also fixes the
+ * split of each request's tokens into work items (by logical position, so
+ * results do not depend on page size or page placement) and the workspace
+ * size.  tuning may be NULL (gfx950 defaults).  The problem's kv_indptr is
+ * read during the call and not kept.  *out receives a new handle that the
+ * caller frees with pkv_plan_destroy; it can be reused on any stream for any
+ * step with the same problem.
+ * Errors: EINVAL (null pointer, sizes, non-multiple heads, bad indptr, prefix
+ * longer than a request, bad force_path, forced prefix path with no whole
+ * shared page), EUNSUPPORTED (head_dim, dtype pair, or group size not built;
+ * forced prefix path for a dtype pair without a prefix kernel), ENOMEM.
+ */
+pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning* tuning,
+                           pkv_plan** out);
+
+/* Copy a plan's decisions and sizes into *info.  EINVAL on null pointers. */
+pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);
+
+/* Free a plan handle (NULL is allowed). */
+void pkv_plan_destroy(pkv_plan* plan);
+
+/*
+ * Paged decode attention ([P1] "Four meanings of page size"; [P3]
+ * PagedAttention Q&A): each request's query attends over the K/V rows that
+ * kv_indices lists for it.  On a PAGED plan the call covers every token of
+ * each request; on a CASCADE or DENSE plan it covers only tokens
+ * [prefix_tokens, L_b), the suffix that follows the shared prefix, and its
+ * fp32 state is then merged with the prefix pass by pkv_merge_states.
+ *   q           device, [B][H_q][d] of the plan's q dtype
+ *   pool        host struct describing device memory; must match the plan
+ *   kv_indptr   device, [B+1] int32, same values as the plan's host indptr
+ *   kv_indices  device, [kv_indptr[B]] int32 slots
+ *   sm_scale    softmax scale (e.g. 1/sqrt(d))
+ *   o           device, [B][H_q][d] of the q dtype, normalised output; nullable
+ *   o_f32       device, [B][H_q][d] fp32, normalised output; nullable
+ *   lse         device, [B][H_q] fp32; nullable
+ *   workspace   device scratch of >= the plan's workspace_bytes (nullable if 0)
+ * At least one of o, o_f32 must be given.  Writes no other memory.
+ * Errors: EINVAL (null plan/q/indices, no output, pool not matching the plan,
+ * missing fp8 scales), EWORKSPACE, EHIP.
+ */
+pkv_status pkv_paged_decode_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices,
+                                 float sm_scale, void* o, float* o_f32, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Shared-prefix attention, prefix read once for the whole batch ([P2] s.2:
+ * every request needs the whole prefix each step, so it is read once instead
+ * of once per request; s.3: DENSE or tiled CASCADE by M_eff).  For each KV
+ * head, the G query heads of all B requests (M_eff rows) attend over the
+ * prefix_tokens rows listed by prefix_indices.
+ *   q              device, [B][H_q][d] bf16
+ *   prefix_indices device, [prefix_len] int32 slots (typically request 0's
+ *                  first prefix_len entries of kv_indices)
+ *   prefix_len     must equal the plan's prefix_tokens
+ *   o_p            device, [B][H_q][d] fp32, normalised prefix output
+ *   lse_p          device, [B][H_q] fp32
+ * Errors: EINVAL (PAGED plan, null pointers, prefix_len mismatch, pool not
+ * matching), EWORKSPACE, EHIP.
+ */
+pkv_status pkv_cascade_prefix_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                                   const int32_t* prefix_indices, int32_t prefix_len,
+                                   float sm_scale, float* o_p, float* lse_p,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Log-sum-exp combine of two partial softmax states over disjoint token sets
+ * (the step that joins the read-once prefix with each request's suffix, [P2]
+ * s.2-3).  Row by row: M = max(lse_a, lse_b); w = exp(lse - M);
+ * o = (w_a o_a + w_b o_b) / (w_a + w_b); lse = M + ln(w_a + w_b); two empty
+ * states give o = 0, lse = -inf.
+ *   o_a, o_b  device, [rows][d] fp32;  lse_a, lse_b  device, [rows] fp32
+ *   o_out     device, [rows][d] of out_dtype (F32 or BF16)
+ *   lse_out   device, [rows] fp32; nullable
+ * Errors: EINVAL (null pointers, rows < 0, d not in {64,128}),
+ * EUNSUPPORTED (out_dtype), EHIP.
+ */
+pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
+                            const float* o_a, const float* lse_a,
+                            const float* o_b, const float* lse_b,
+                            void* o_out, int32_t out_dtype, float* lse_out, void* stream);
+
+/*
+ * One whole decode step as the plan chose it: PAGED is one paged call; CASCADE
+ * and DENSE run the prefix pass over kv_indices[kv_indptr[0] ..
+ * + prefix_tokens) (request 0's shared pages), the paged pass over each
+ * request's suffix, and the merge, with the partial states kept in the
+ * workspace.  Arguments as in pkv_paged_decode_attn; o is required, lse is
+ * nullable.
+ */
+pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           float sm_scale, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,210 @@
+// C ABI entry points that enqueue device work: argument checks, workspace
+// carving, and kernel launches on the caller's stream.  No allocation, no
+// synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+hipError_t launch_paged_split_f32(const pkv_plan& p, const PagedArgs& a, hipStream_t s);
+hipError_t launch_paged_split_bf16(const pkv_plan& p, const PagedArgs& a, hipStream_t s);
+hipError_t launch_paged_split_fp8(const pkv_plan& p, const PagedArgs& a, hipStream_t s);
+
+hipError_t launch_paged_split(const pkv_plan& p, const PagedArgs& a, hipStream_t s) {
+    switch (p.kv_dtype) {
+        case PKV_F32: return launch_paged_split_f32(p, a, s);
+        case PKV_BF16: return launch_paged_split_bf16(p, a, s);
+        case PKV_FP8_E4M3: return launch_paged_split_fp8(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace pkv
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+pkv_status check_pool(const pkv_plan* pl, const pkv_pool* pool) {
+    if (!pool || !pool->k || !pool->v) return PKV_EINVAL;
+    if (pool->kv_dtype != pl->kv_dtype || pool->num_kv_heads != pl->H_kv ||
+        pool->head_dim != pl->D || pool->page_size != pl->page_size)
+        return PKV_EINVAL;
+    if (pool->num_slots < 0 || pool->num_slots % pool->page_size) return PKV_EINVAL;
+    if (pl->kv_dtype == PKV_FP8_E4M3 && (!pool->k_scale || !pool->v_scale)) return PKV_EINVAL;
+    return PKV_OK;
+}
+
+pkv_status check_workspace(const pkv_plan* pl, const void* ws, size_t ws_bytes) {
+    if (pl->workspace_bytes == 0) return PKV_OK;
+    if (!ws || (int64_t)ws_bytes < pl->workspace_bytes) return PKV_EWORKSPACE;
+    return PKV_OK;
+}
+
+template <typename T>
+T* ws_at(void* ws, int64_t off) {
+    return off < 0 ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EHIP; }
+
+// The paged pass over tokens [plan.prefix_tokens, L_b) of every request.
+pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
+                     void* ws, hipStream_t stream) {
+    pkv::PagedArgs a{};
+    a.q = q;
+    a.k = pool->k;
+    a.v = pool->v;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.kv_indptr = kv_indptr;
+    a.kv_indices = kv_indices;
+    a.H_kv = pl->H_kv;
+    a.token_offset = pl->prefix_tokens;
+    a.split_tokens = pl->split_tokens;
+    a.num_splits = pl->num_splits;
+    a.scale_log2 = sm_scale * kLog2e;
+    if (pl->num_splits == 1) {
+        a.o = o;
+        a.o_f32 = o_f32;
+        a.lse = lse;
+        return hip_status(pkv::launch_paged_split(*pl, a, stream));
+    }
+    a.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
+    a.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
+    hipError_t e = pkv::launch_paged_split(*pl, a, stream);
+    if (e != hipSuccess) return PKV_EHIP;
+    pkv::SplitReduceArgs r{};
+    r.kv_indptr = kv_indptr;
+    r.token_offset = pl->prefix_tokens;
+    r.split_tokens = pl->split_tokens;
+    r.num_splits = pl->num_splits;
+    r.B = pl->B;
+    r.H_q = pl->H_q;
+    r.D = pl->D;
+    r.part_acc = a.part_acc;
+    r.part_ml = a.part_ml;
+    r.o = o;
+    r.out_dtype = pl->q_dtype;
+    r.o_f32 = o_f32;
+    r.lse = lse;
+    return hip_status(pkv::launch_split_reduce(r, stream));
+}
+
+pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* prefix_indices,
+                      float sm_scale, float* o_p, float* lse_p, void* ws, hipStream_t stream) {
+    pkv::PrefixArgs a{};
+    a.q = q;
+    a.k = pool->k;
+    a.v = pool->v;
+    a.prefix_indices = prefix_indices;
+    a.B = pl->B;
+    a.H_kv = pl->H_kv;
+    a.G = pl->G;
+    a.D = pl->D;
+    a.prefix_len = pl->prefix_tokens;
+    a.split_tokens = pl->prefix_split_tokens;
+    a.num_splits = pl->prefix_splits;
+    a.row_tiles = (pl->m_eff + pl->prefix_rows_per_wg - 1) / pl->prefix_rows_per_wg;
+    a.scale_log2 = sm_scale * kLog2e;
+    if (pl->prefix_splits == 1) {
+        a.o = o_p;
+        a.lse = lse_p;
+        return hip_status(pkv::launch_prefix_attn(a, pl->prefix_rows_per_wg, stream));
+    }
+    a.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
+    a.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
+    hipError_t e = pkv::launch_prefix_attn(a, pl->prefix_rows_per_wg, stream);
+    if (e != hipSuccess) return PKV_EHIP;
+    pkv::SplitReduceArgs r{};
+    r.kv_indptr = nullptr;
+    r.split_tokens = pl->prefix_split_tokens;
+    r.num_splits = pl->prefix_splits;
+    r.B = pl->B;
+    r.H_q = pl->H_q;
+    r.D = pl->D;
+    r.part_acc = a.part_acc;
+    r.part_ml = a.part_ml;
+    r.o = nullptr;
+    r.out_dtype = PKV_F32;
+    r.o_f32 = o_p;
+    r.lse = lse_p;
+    return hip_status(pkv::launch_split_reduce(r, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_decode_attn(const pkv_plan* pl, const void* q, const pkv_pool* pool,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
+                                 void* o, float* o_f32, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (!pl) return PKV_EINVAL;
+    if (!o && !o_f32) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    st = check_workspace(pl, ws, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (pl->B == 0) return PKV_OK;
+    if (!q || !kv_indptr || (pl->paged_tokens > 0 && !kv_indices)) return PKV_EINVAL;
+    return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, o_f32, lse, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_cascade_prefix_attn(const pkv_plan* pl, const void* q, const pkv_pool* pool,
+                                   const int32_t* prefix_indices, int32_t prefix_len, float sm_scale,
+                                   float* o_p, float* lse_p, void* ws, size_t ws_bytes, void* stream) {
+    if (!pl) return PKV_EINVAL;
+    if (pl->path == PKV_PATH_PAGED) return PKV_EINVAL;
+    if (prefix_len != pl->prefix_tokens) return PKV_EINVAL;
+    if (!q || !prefix_indices || !o_p || !lse_p) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    st = check_workspace(pl, ws, ws_bytes);
+    if (st != PKV_OK) return st;
+    return run_prefix(pl, q, pool, prefix_indices, sm_scale, o_p, lse_p, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_merge_states(int32_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
+                            const float* o_b, const float* lse_b, void* o_out, int32_t out_dtype,
+                            float* lse_out, void* stream) {
+    if (rows < 0 || (head_dim != 64 && head_dim != 128)) return PKV_EINVAL;
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+    if (rows == 0) return PKV_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return PKV_EINVAL;
+    return hip_status(pkv::launch_merge_states(rows, head_dim, o_a, lse_a, o_b, lse_b, o_out, out_dtype,
+                                               lse_out, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, float sm_scale, void* o, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+    if (!pl || !o) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    st = check_workspace(pl, ws, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (pl->B == 0) return PKV_OK;
+    if (!q || !kv_indptr || !kv_indices) return PKV_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pl->path == PKV_PATH_PAGED)
+        return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, nullptr, lse, ws, s);
+    float* o_p = ws_at<float>(ws, pl->ws_state_o_p);
+    float* lse_p = ws_at<float>(ws, pl->ws_state_lse_p);
+    float* o_s = ws_at<float>(ws, pl->ws_state_o_s);
+    float* lse_s = ws_at<float>(ws, pl->ws_state_lse_s);
+    st = run_prefix(pl, q, pool, kv_indices + pl->indptr0, sm_scale, o_p, lse_p, ws, s);
+    if (st != PKV_OK) return st;
+    st = run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, nullptr, o_s, lse_s, ws, s);
+    if (st != PKV_OK) return st;
+    return hip_status(pkv::launch_merge_states(pl->B * pl->H_q, pl->D, o_p, lse_p, o_s, lse_s, o, pl->q_dtype,
+                                               lse, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,411 @@
+// Paged decode attention for gfx950: gather K/V rows through token-flat
+// indices, split-K online softmax, LDS merge across waves.
+//
+// The operation ("The 25% Page-Size Slowdown That Wasn't", section "Four
+// meanings of page size"; "Track C · Document 10", PagedAttention Q&A): each
+// request's single query token, with G query heads per KV head, attends over
+// the cached K/V rows that kv_indices lists for it, in logical order.
+//
+// Work decomposition.  A workgroup (4 waves) owns one (split, head block,
+// request): split_tokens consecutive logical positions of one request and HB
+// KV heads.  Each wave takes a contiguous quarter of those positions.  The 64
+// lanes of a wave span (KV head, head-dim chunk): LPH lanes read one row, so
+// a wave-wide load reads RS rows -- one token's HB heads when TPI == 1 (the
+// slot is then wave-uniform and the address is scalar), or TPI tokens when
+// the block has fewer heads than a load has rows.
+//
+// Per token a lane forms G partial dot products (one per query head of its
+// KV head), and the row's LPH lanes reduce-scatter them with DPP moves so
+// that each lane ends up owning one query head's score.  The softmax state
+// (running max m, sum l) is then lane-local.  Probabilities are shuffled back
+// along the same DPP pattern for the P.V update; for bf16 and fp8 K/V two
+// consecutive tokens are paired so that P.V runs on v_dot2_f32_bf16.
+//
+// The running max is raised lazily: the accumulator is rescaled only when a
+// score exceeds the current max by more than 2^8 (in the exp2 domain), so
+// probabilities stay <= 256 and the rescale is rare.  The result is the same
+// softmax up to rounding.
+//
+// Everything is ordered by logical token position, so the output does not
+// depend on page size, page placement or timing: runs are bitwise
+// reproducible and page-size invariant.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+template <int KV>
+struct KvTraits;
+template <>
+struct KvTraits<PKV_F32> {
+    static constexpr int BK = 4, EPL = 4, LW = 4;  // bytes/elem, elems/lane, dwords/lane
+};
+template <>
+struct KvTraits<PKV_BF16> {
+    static constexpr int BK = 2, EPL = 8, LW = 4;
+};
+template <>
+struct KvTraits<PKV_FP8_E4M3> {
+    static constexpr int BK = 1, EPL = 8, LW = 2;
+};
+
+template <int LW>
+struct LoadVec;
+template <>
+struct LoadVec<4> {
+    using T = u32x4_t;
+};
+template <>
+struct LoadVec<2> {
+    using T = u32x2_t;
+};
+
+constexpr int kPagedWaves = 4;
+constexpr float kLazyMaxSlack = 8.0f;  // log2 units
+
+template <int KV, int D, int G, int NHL, int TPI>
+struct PagedCfg {
+    using Tr = KvTraits<KV>;
+    static constexpr int BK = Tr::BK, EPL = Tr::EPL, LW = Tr::LW;
+    static constexpr int LPH = D / EPL;
+    static constexpr int RS = 64 / LPH;
+    static constexpr int HB = RS * NHL / TPI;
+    static constexpr int NW = kPagedWaves;
+    static constexpr bool QF32 = (KV == PKV_F32);
+    static constexpr int QW = QF32 ? EPL : EPL / 2;  // q registers per (slot, head)
+    // steps per iteration: 8 KB of K+V in flight per wave per buffer
+    static constexpr int U0 = 32 / (NHL * 2 * LW);
+    static constexpr int U = U0 < 2 ? 2 : U0;
+    static constexpr int TU = U * TPI;  // tokens per wave iteration
+    static constexpr int PARTIALS = NW * TPI;
+    static constexpr int MERGE_FLOATS = PARTIALS * HB * G * D;
+    static constexpr int LDS_FLOATS = MERGE_FLOATS > kMaxSplitTokens ? MERGE_FLOATS : kMaxSplitTokens;
+    static_assert(G <= LPH, "one query head per lane after the row reduction");
+    static_assert(TPI == 1 || NHL == 1, "several tokens per load only with one head slot");
+    static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
+};
+
+template <int KV, int D, int G, int NHL, int TPI>
+__global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const PagedArgs a) {
+    using C = PagedCfg<KV, D, G, NHL, TPI>;
+    constexpr int BK = C::BK, EPL = C::EPL, LW = C::LW, LPH = C::LPH, RS = C::RS, HB = C::HB;
+    constexpr int NW = C::NW, QW = C::QW, U = C::U, TU = C::TU;
+    using LV = typename LoadVec<LW>::T;
+
+    __shared__ float s_buf[C::LDS_FLOATS];
+    __shared__ float s_ml[C::PARTIALS * HB * G * 2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x;
+    const int hblk = blockIdx.y;
+    const int b = blockIdx.z;
+    const int H_kv = a.H_kv;
+    const int H_q = H_kv * G;
+
+    const int seq_beg = a.kv_indptr[b] + a.token_offset;
+    const int len = a.kv_indptr[b + 1] - seq_beg;
+    const int t0 = split * a.split_tokens;
+    if (a.num_splits > 1 && t0 >= len) return;  // empty item: the reduce skips it
+    const int n_tok = max(min(t0 + a.split_tokens, len) - t0, 0);
+
+    // Stage this item's slot indices in LDS.
+    int* s_idx = reinterpret_cast<int*>(s_buf);
+    for (int i = threadIdx.x; i < n_tok; i += NW * 64) s_idx[i] = a.kv_indices[seq_beg + t0 + i];
+    __syncthreads();
+
+    // This wave's contiguous token range [w0, w1) within the item.
+    const int per_wave = ((n_tok + NW - 1) / NW + TU - 1) / TU * TU;
+    const int w0 = min(wave * per_wave, n_tok);
+    const int w1 = min(w0 + per_wave, n_tok);
+    const int niter = (w1 - w0 + TU - 1) / TU;
+
+    const int lrow = lane / LPH;
+    const int lch = lane % LPH;
+    const int tau = TPI > 1 ? lrow / HB : 0;
+    const int fl = head_of_lane<LPH, G>(lch);
+    auto head_local = [&](int i) { return TPI > 1 ? lrow % HB : i * RS + lrow; };
+
+    // Queries, in the lane's XOR-permuted head order: slot u holds head u ^ fl.
+    uint32_t qv[NHL][G][QW];
+    float sc[NHL];
+#pragma unroll
+    for (int i = 0; i < NHL; ++i) {
+        const int kvh = hblk * HB + head_local(i);
+        float s = a.scale_log2;
+        if constexpr (KV == PKV_FP8_E4M3) s *= a.k_scale[kvh];
+        sc[i] = s;
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int qh = kvh * G + (u ^ fl);
+            const char* qp = static_cast<const char*>(a.q) +
+                             ((size_t)b * H_q + qh) * D * (C::QF32 ? 4 : 2) +
+                             (size_t)lch * EPL * (C::QF32 ? 4 : 2);
+            if constexpr (QW == 4) {
+                const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) qv[i][u][w] = x[w];
+            } else {
+#pragma unroll
+                for (int w = 0; w < QW; ++w) qv[i][u][w] = reinterpret_cast<const uint32_t*>(qp)[w];
+            }
+        }
+    }
+
+    float m[NHL], l[NHL];
+    float acc[NHL][G][EPL];
+#pragma unroll
+    for (int i = 0; i < NHL; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[i][u][e] = 0.f;
+    }
+
+    const size_t slot_stride = (size_t)H_kv * D * BK;
+    const char* kbase = static_cast<const char*>(a.k) + (size_t)hblk * HB * D * BK;
+    const char* vbase = static_cast<const char*>(a.v) + (size_t)hblk * HB * D * BK;
+    uint32_t loff[NHL];
+#pragma unroll
+    for (int i = 0; i < NHL; ++i) loff[i] = head_local(i) * D * BK + lch * EPL * BK;
+
+    LV kb[2][U][NHL], vb[2][U][NHL];
+
+    auto issue = [&](int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int tk = min(w0 + it * TU + j * TPI + tau, w1 - 1);
+            int slot = s_idx[tk];
+            if constexpr (TPI == 1) slot = __builtin_amdgcn_readfirstlane(slot);
+            const char* kr = kbase + (size_t)(uint32_t)slot * slot_stride;
+            const char* vr = vbase + (size_t)(uint32_t)slot * slot_stride;
+#pragma unroll
+            for (int i = 0; i < NHL; ++i) {
+                kb[buf][j][i] = *reinterpret_cast<const LV*>(kr + loff[i]);
+                vb[buf][j][i] = *reinterpret_cast<const LV*>(vr + loff[i]);
+            }
+        }
+    };
+
+    auto compute = [&](int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        float s[U][NHL];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool valid = (w0 + it * TU + j * TPI + tau) < w1;
+#pragma unroll
+            for (int i = 0; i < NHL; ++i) {
+                float part[G];
+                if constexpr (KV == PKV_F32) {
+#pragma unroll
+                    for (int u = 0; u < G; ++u) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            t = fmaf(__uint_as_float(qv[i][u][e]), __uint_as_float(kb[buf][j][i][e]), t);
+                        part[u] = t;
+                    }
+                } else if constexpr (KV == PKV_BF16) {
+#pragma unroll
+                    for (int u = 0; u < G; ++u) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kb[buf][j][i][w], t);
+                        part[u] = t;
+                    }
+                } else {
+                    uint32_t kc[4];
+                    kc[0] = fp8x2_to_bf16x2<false>(kb[buf][j][i][0]);
+                    kc[1] = fp8x2_to_bf16x2<true>(kb[buf][j][i][0]);
+                    kc[2] = fp8x2_to_bf16x2<false>(kb[buf][j][i][1]);
+                    kc[3] = fp8x2_to_bf16x2<true>(kb[buf][j][i][1]);
+#pragma unroll
+                    for (int u = 0; u < G; ++u) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kc[w], t);
+                        part[u] = t;
+                    }
+                }
+                const float r = row_reduce_scatter<LPH, G>(part) * sc[i];
+                s[j][i] = valid ? r : -INFINITY;
+            }
+        }
+
+        // Online softmax with a lazily raised maximum.
+        bool need = false;
+        float tmax[NHL];
+#pragma unroll
+        for (int i = 0; i < NHL; ++i) {
+            float t = s[0][i];
+#pragma unroll
+            for (int j = 1; j < U; ++j) t = fmaxf(t, s[j][i]);
+            tmax[i] = t;
+            need |= (t > m[i] + kLazyMaxSlack) || (m[i] == -INFINITY && t != -INFINITY);
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+            for (int i = 0; i < NHL; ++i) {
+                const float mn = fmaxf(m[i], tmax[i]);
+                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[i] - mn);
+                m[i] = mn;
+                l[i] *= alpha;
+                static_for<G>([&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    const float au = xor_shfl<lane_mask_for_head_xor<LPH, G>(u)>(alpha);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[i][u][e] *= au;
+                });
+            }
+        }
+
+        float p[U][NHL];
+#pragma unroll
+        for (int i = 0; i < NHL; ++i) {
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                p[j][i] = (m[i] == -INFINITY) ? 0.f : fast_exp2(s[j][i] - m[i]);
+                sum += p[j][i];
+            }
+            l[i] += sum;
+        }
+
+        // P.V
+        if constexpr (KV == PKV_F32) {
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+#pragma unroll
+                for (int i = 0; i < NHL; ++i)
+                    static_for<G>([&](auto uc) {
+                        constexpr int u = decltype(uc)::value;
+                        const float pu = xor_shfl<lane_mask_for_head_xor<LPH, G>(u)>(p[j][i]);
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            acc[i][u][e] = fmaf(pu, __uint_as_float(vb[buf][j][i][e]), acc[i][u][e]);
+                    });
+        } else {
+#pragma unroll
+            for (int j = 0; j < U; j += 2)
+#pragma unroll
+                for (int i = 0; i < NHL; ++i) {
+                    // value pairs (token j, token j+1) per head-dim element
+                    uint32_t vp[EPL];
+                    if constexpr (KV == PKV_BF16) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            vp[2 * w] = __builtin_amdgcn_perm(vb[buf][j + 1][i][w], vb[buf][j][i][w], 0x05040100u);
+                            vp[2 * w + 1] = __builtin_amdgcn_perm(vb[buf][j + 1][i][w], vb[buf][j][i][w], 0x07060302u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const uint32_t x0 = __builtin_amdgcn_perm(vb[buf][j + 1][i][w], vb[buf][j][i][w], 0x05010400u);
+                            const uint32_t x1 = __builtin_amdgcn_perm(vb[buf][j + 1][i][w], vb[buf][j][i][w], 0x07030602u);
+                            vp[4 * w + 0] = fp8x2_to_bf16x2<false>(x0);
+                            vp[4 * w + 1] = fp8x2_to_bf16x2<true>(x0);
+                            vp[4 * w + 2] = fp8x2_to_bf16x2<false>(x1);
+                            vp[4 * w + 3] = fp8x2_to_bf16x2<true>(x1);
+                        }
+                    }
+                    const uint32_t pp = pack_bf16x2(p[j][i], p[j + 1][i]);
+                    static_for<G>([&](auto uc) {
+                        constexpr int u = decltype(uc)::value;
+                        const uint32_t pu = xor_shfl_u32<lane_mask_for_head_xor<LPH, G>(u)>(pp);
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[i][u][e] = dot2_bf16(vp[e], pu, acc[i][u][e]);
+                    });
+                }
+        }
+    };
+
+    // Two-deep register pipeline: loads of iteration it+1 are in flight
+    // while iteration it is computed.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if (niter > 0) issue(0, B0{});
+    for (int it = 0; it < niter; it += 2) {
+        if (it + 1 < niter) issue(it + 1, B1{});
+        compute(it, B0{});
+        if (it + 1 < niter) {
+            if (it + 2 < niter) issue(it + 2, B0{});
+            compute(it + 1, B1{});
+        }
+    }
+
+    // Merge the NW * TPI partial states of this item in LDS, in a fixed order.
+    __syncthreads();  // every wave is done with s_idx
+    const int pidx = wave * TPI + tau;
+#pragma unroll
+    for (int i = 0; i < NHL; ++i) {
+        const int hl = head_local(i);
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            float* dst = s_buf + ((size_t)(pidx * HB + hl) * G + (u ^ fl)) * D + lch * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4) {
+                f32x4_t x = {acc[i][u][e], acc[i][u][e + 1], acc[i][u][e + 2], acc[i][u][e + 3]};
+                *reinterpret_cast<f32x4_t*>(dst + e) = x;
+            }
+        }
+        float* mlp = s_ml + ((pidx * HB + hl) * G + fl) * 2;
+        mlp[0] = m[i];
+        mlp[1] = l[i];
+    }
+    __syncthreads();
+
+    constexpr int CH = D / 4;  // float4 chunks per head
+    const bool direct = a.num_splits == 1;
+    for (int c = threadIdx.x; c < HB * G * CH; c += NW * 64) {
+        const int qhl = c / CH;
+        const int e4 = c % CH;
+        float M = -INFINITY;
+#pragma unroll
+        for (int pp = 0; pp < C::PARTIALS; ++pp) M = fmaxf(M, s_ml[(pp * HB * G + qhl) * 2]);
+        float L = 0.f;
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int pp = 0; pp < C::PARTIALS; ++pp) {
+                const float mp = s_ml[(pp * HB * G + qhl) * 2];
+                if (mp == -INFINITY) continue;
+                const float w = fast_exp2(mp - M);
+                L += w * s_ml[(pp * HB * G + qhl) * 2 + 1];
+                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(s_buf + ((size_t)pp * HB * G + qhl) * D + e4 * 4);
+                o += w * x;
+            }
+        }
+        const int kvh = hblk * HB + qhl / G;
+        const int qh = kvh * G + qhl % G;
+        if constexpr (KV == PKV_FP8_E4M3) o *= a.v_scale[kvh];
+        const size_t row = (size_t)b * H_q + qh;
+        if (direct) {
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            o *= inv;
+            if (a.o_f32) *reinterpret_cast<f32x4_t*>(a.o_f32 + row * D + e4 * 4) = o;
+            if (a.o) {
+                if constexpr (C::QF32) {
+                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.o) + row * D + e4 * 4) = o;
+                } else {
+                    u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.o) + row * D + e4 * 4) = h;
+                }
+            }
+            if (a.lse && e4 == 0) a.lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+        } else {
+            const size_t prow = ((size_t)b * a.num_splits + split) * H_q + qh;
+            *reinterpret_cast<f32x4_t*>(a.part_acc + prow * D + e4 * 4) = o;
+            if (e4 == 0) {
+                a.part_ml[prow * 2] = M;
+                a.part_ml[prow * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+}  // namespace pkv

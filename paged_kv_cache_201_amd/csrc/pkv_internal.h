@@ -1,0 +1,65 @@
+// Internal declarations shared by the host planner and the HIP launchers.
+// Nothing here is part of the public ABI (include/pkv.h).
+#pragma once
+
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// How one work item of the paged kernel maps its 64 lanes onto K/V rows.
+// A "row" is one (token, KV head) vector of head_dim elements.  Each lane
+// loads EPL consecutive elements; LPH lanes cover a row; one wave-wide load
+// covers RS = 64 / LPH rows.  A work item covers HB KV heads: either NHL
+// loads per token (HB = NHL * RS, one token per load) or TPI tokens per load
+// (HB = RS / TPI).
+struct PagedGeometry {
+    int32_t epl;   // elements per lane per row
+    int32_t lph;   // lanes per row
+    int32_t rs;    // rows per wave-wide load
+    int32_t nhl;   // loads per token (head slots per lane)
+    int32_t tpi;   // tokens per load
+    int32_t hb;    // KV heads per work item
+};
+
+// Lane geometry for a (kv dtype, head_dim, G, H_kv) problem.  Returns false
+// if no kernel is built for it.
+bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t num_kv_heads,
+                    PagedGeometry* out);
+
+// Query rows one prefix-kernel workgroup handles, per path.
+constexpr int32_t kDenseRowsPerWg = 128;
+constexpr int32_t kTiledRowsPerWg = 32;
+// Prefix tokens are split in multiples of this many.
+constexpr int32_t kPrefixTokenQuantum = 64;
+// Paged-pass work items hold a multiple of this many tokens, and at most
+// kMaxSplitTokens (the kernel stages an item's slot indices in LDS).
+constexpr int32_t kSplitQuantum = 64;
+constexpr int32_t kMaxSplitTokens = 2048;
+
+}  // namespace pkv
+
+struct pkv_plan {
+    // problem
+    int32_t B, H_q, H_kv, D, G, q_dtype, kv_dtype, page_size;
+    int32_t indptr0;          // host kv_indptr[0]
+    int32_t prefix_len;       // declared shared prefix (tokens)
+    // decisions
+    int32_t path, m_eff, shared_pages, prefix_tokens;
+    // paged pass
+    pkv::PagedGeometry geo;
+    int32_t head_blocks;
+    int32_t split_tokens, num_splits;
+    int64_t num_work_items;
+    int64_t paged_tokens;     // tokens the paged pass attends (all requests)
+    int32_t paged_max_len;
+    // prefix pass
+    int32_t prefix_rows_per_wg;
+    int32_t prefix_split_tokens, prefix_splits;
+    // workspace layout (byte offsets; -1 = unused)
+    int64_t ws_paged_acc, ws_paged_ml;
+    int64_t ws_prefix_acc, ws_prefix_ml;
+    int64_t ws_state_o_p, ws_state_lse_p, ws_state_o_s, ws_state_lse_s;
+    int64_t workspace_bytes;
+};

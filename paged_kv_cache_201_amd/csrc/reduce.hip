@@ -1,0 +1,122 @@
+// Split-K reduction of the paged pass, and the two-state LSE merge.
+//
+// Both combine partial softmax states over disjoint token sets.  The
+// combination follows from the softmax definition: with state (o, lse) for a
+// token set, the state of the union of two sets is
+//   M = max(lse_a, lse_b),  w = exp(lse - M),
+//   o = (w_a o_a + w_b o_b) / (w_a + w_b),  lse = M + ln(w_a + w_b).
+// It is the step that joins a prefix read once for the whole batch with each
+// request's own suffix ("GraniKV: asymmetric KV cache paging for
+// shared-prefix agents", sections 2 and 3).  Splits are combined in index
+// order, so results are reproducible bit for bit.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+template <int D>
+__global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs a) {
+    constexpr int CH = D / 4;
+    constexpr int RPB = 256 / CH;
+    const int row = blockIdx.x * RPB + threadIdx.x / CH;
+    const int e4 = threadIdx.x % CH;
+    if (row >= a.B * a.H_q) return;
+    const int b = row / a.H_q;
+    const int qh = row % a.H_q;
+    int ns = a.num_splits;
+    if (a.kv_indptr) {
+        const int len = a.kv_indptr[b + 1] - a.kv_indptr[b] - a.token_offset;
+        ns = len > 0 ? (len + a.split_tokens - 1) / a.split_tokens : 0;
+    }
+    const size_t base = (size_t)b * a.num_splits;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.H_q + qh) * 2]);
+    float L = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const size_t prow = (base + s) * a.H_q + qh;
+            const float ms = a.part_ml[prow * 2];
+            if (ms == -INFINITY) continue;
+            const float w = exp2f(ms - M);
+            L += w * a.part_ml[prow * 2 + 1];
+            o += w * *reinterpret_cast<const f32x4_t*>(a.part_acc + prow * D + e4 * 4);
+        }
+    }
+    o *= L > 0.f ? 1.f / L : 0.f;
+    const size_t orow = (size_t)row;
+    if (a.o_f32) *reinterpret_cast<f32x4_t*>(a.o_f32 + orow * D + e4 * 4) = o;
+    if (a.o) {
+        if (a.out_dtype == PKV_F32) {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.o) + orow * D + e4 * 4) = o;
+        } else {
+            u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.o) + orow * D + e4 * 4) = h;
+        }
+    }
+    if (a.lse && e4 == 0) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) merge_states_kernel(int rows, const float* __restrict__ o_a,
+                                                           const float* __restrict__ lse_a,
+                                                           const float* __restrict__ o_b,
+                                                           const float* __restrict__ lse_b,
+                                                           void* __restrict__ o_out, int out_dtype,
+                                                           float* __restrict__ lse_out) {
+    constexpr int CH = D / 4;
+    constexpr int RPB = 256 / CH;
+    const int row = blockIdx.x * RPB + threadIdx.x / CH;
+    const int e4 = threadIdx.x % CH;
+    if (row >= rows) return;
+    const float la = lse_a[row], lb = lse_b[row];
+    const float M = fmaxf(la, lb);
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    float lse = -INFINITY;
+    if (M != -INFINITY) {
+        const float wa = expf(la - M), wb = expf(lb - M);
+        const float inv = 1.f / (wa + wb);
+        const f32x4_t xa = *reinterpret_cast<const f32x4_t*>(o_a + (size_t)row * D + e4 * 4);
+        const f32x4_t xb = *reinterpret_cast<const f32x4_t*>(o_b + (size_t)row * D + e4 * 4);
+        // an empty side has weight 0; never multiply its (possibly stale) values
+        if (wa > 0.f) o += (wa * inv) * xa;
+        if (wb > 0.f) o += (wb * inv) * xb;
+        lse = M + logf(wa + wb);
+    }
+    if (out_dtype == PKV_F32) {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(o_out) + (size_t)row * D + e4 * 4) = o;
+    } else {
+        u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o_out) + (size_t)row * D + e4 * 4) = h;
+    }
+    if (lse_out && e4 == 0) lse_out[row] = lse;
+}
+
+hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t stream) {
+    const int rows = a.B * a.H_q;
+    if (rows == 0) return hipSuccess;
+    if (a.D == 128) {
+        split_reduce_kernel<128><<<(rows + 7) / 8, 256, 0, stream>>>(a);
+    } else {
+        split_reduce_kernel<64><<<(rows + 15) / 16, 256, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_states(int32_t rows, int32_t D, const float* o_a, const float* lse_a,
+                               const float* o_b, const float* lse_b, void* o_out, int32_t out_dtype,
+                               float* lse_out, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    if (D == 128) {
+        merge_states_kernel<128><<<(rows + 7) / 8, 256, 0, stream>>>(rows, o_a, lse_a, o_b, lse_b,
+                                                                      o_out, out_dtype, lse_out);
+    } else {
+        merge_states_kernel<64><<<(rows + 15) / 16, 256, 0, stream>>>(rows, o_a, lse_a, o_b, lse_b,
+                                                                     o_out, out_dtype, lse_out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,309 @@
+"""GPU parity of the HIP path against the float64 oracle (MI355X, gfx950).
+
+Tolerances (fixed before any kernel ran):
+* fp32 K/V: per output row max|o - o_ref| <= 1e-5 * max|o_ref row|, and
+  |lse - lse_ref| <= 1e-5 * max(1, |lse_ref|);
+* bf16 / fp8 K/V: elementwise |o - o_ref| <= 2e-2 and |lse - lse_ref| <= 2e-2.
+Indexing and planning are bit exact (tested on the CPU).  The paged path
+orders its arithmetic by logical token position, so its output must also be
+bitwise identical across page size, page permutation and prefix layout.
+
+Sizes: small cases the oracle finishes in seconds that still span several
+work items and ragged tails; the full workloads at the launch configuration
+the bench times, checked on sampled requests.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _imports():
+    import paged_kv_cache_201_amd as pkv
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from oracle import batch as ob
+    from oracle import attention as oa
+    from workloads import make_config, make_decode_batch, relayout
+    return pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout
+
+
+def check_close(kv_dtype, o, lse, o_ref, lse_ref, what):
+    o = o.detach().float().cpu().double().numpy().reshape(o_ref.shape)
+    lse = lse.detach().float().cpu().double().numpy().reshape(lse_ref.shape)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin), f"{what}: -inf pattern differs"
+    if kv_dtype == "f32":
+        err_o = np.abs(o - o_ref).max(axis=-1)
+        bound = 1e-5 * np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
+        assert (err_o <= bound).all(), f"{what}: o rel err {(err_o / bound).max() * 1e-5:.3g}"
+        err_l = np.abs(lse - lse_ref)[fin]
+        assert (err_l <= 1e-5 * np.maximum(1, np.abs(lse_ref[fin]))).all(), f"{what}: lse err {err_l.max():.3g}"
+    else:
+        err_o = np.abs(o - o_ref).max()
+        err_l = np.abs(lse - lse_ref)[fin].max() if fin.any() else 0.0
+        assert err_o <= 2e-2, f"{what}: o err {err_o:.4g}"
+        assert err_l <= 2e-2, f"{what}: lse err {err_l:.4g}"
+    assert not np.isnan(o).any(), f"{what}: NaN in output"
+
+
+def run_paged(DeviceBatch, batch, tuning=None, want_f32=False):
+    db = DeviceBatch.from_batch(batch)
+    plan = db.plan(force_path=0, tuning=tuning)
+    o, lse = db.paged(plan, want_f32=want_f32)
+    torch.cuda.synchronize()
+    return o, lse, plan
+
+
+def same_bits(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+# ----------------------------------------------------------------- c1 ------
+
+def test_c1_tiny_fp32_page16_and_page1():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b16 = make_config("c1")
+    b1 = relayout(b16, page_size=1, seed=2001, pool_pages=2048)
+    o_ref, lse_ref = ob.batch_reference(b16)
+    say("c1 p=16 paged_decode_attn")
+    o16, l16, plan = run_paged(DeviceBatch, b16)
+    check_close("f32", o16, l16, o_ref, lse_ref, "c1 p=16")
+    say("c1 p=1 paged_decode_attn")
+    o1, l1, _ = run_paged(DeviceBatch, b1)
+    check_close("f32", o1, l1, o_ref, lse_ref, "c1 p=1")
+    assert same_bits(o16, o1) and same_bits(l16, l1), "page size changed the bits"
+    # many small splits: the split-K reduction path at fp32 precision
+    say("c1 p=16 forced splits")
+    os_, ls_, plan_s = run_paged(DeviceBatch, b16, tuning=dict(min_split_tokens=64, target_workgroups=4096))
+    assert plan_s.info["num_splits"] > 1
+    check_close("f32", os_, ls_, o_ref, lse_ref, "c1 split")
+
+
+# ----------------------------------------------------------------- c2 ------
+
+def test_c2_shape_small_all_layouts():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    base = make_config("c2", B=3, own_len=(4096, 4096), page_size=128)
+    o_ref, lse_ref = ob.batch_reference(base)
+    outs = []
+    for p, perm in ((128, "random"), (1, "random"), (1, "identity"), (16, "random")):
+        b = relayout(base, page_size=p, seed=2002, perm=perm)
+        say(f"c2-small p={p} {perm}")
+        o, lse, plan = run_paged(DeviceBatch, b)
+        check_close("bf16", o, lse, o_ref, lse_ref, f"c2 small p={p} {perm}")
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert same_bits(outs[0][0], o) and same_bits(outs[0][1], lse)
+
+
+def test_c2_full_sampled_page1_vs_page128():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b128 = make_config("c2")
+    b1 = relayout(b128, page_size=1, seed=2002)
+    reqs = [0, 13, 31]
+    o_ref, lse_ref = ob.batch_reference(b128, requests=reqs)
+    say("c2 full p=128")
+    o128, l128, plan = run_paged(DeviceBatch, b128)
+    assert plan.info["num_splits"] > 1
+    check_close("bf16", o128[reqs], l128[reqs], o_ref, lse_ref, "c2 p=128")
+    del b128
+    say("c2 full p=1")
+    o1, l1, _ = run_paged(DeviceBatch, b1)
+    assert same_bits(o128, o1) and same_bits(l128, l1), "page 1 vs 128 differ"
+
+
+# ----------------------------------------------------------------- c5 ------
+
+def test_c5_fp8_small():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c5", B=3, own_len=(1000, 3000))
+    o_ref, lse_ref = ob.batch_reference(b)
+    say("c5-small fp8")
+    o, lse, plan = run_paged(DeviceBatch, b)
+    check_close("fp8", o, lse, o_ref, lse_ref, "c5 small")
+    b2 = relayout(b, page_size=1, seed=2005, pool_factor=2)
+    say("c5-small fp8 p=1")
+    o2, l2, _ = run_paged(DeviceBatch, b2)
+    assert same_bits(o, o2) and same_bits(lse, l2)
+
+
+def test_c5_full_sampled():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c5")
+    reqs = [0, 7, 15]
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    say("c5 full fp8")
+    o, lse, plan = run_paged(DeviceBatch, b)
+    check_close("fp8", o[reqs], lse[reqs], o_ref, lse_ref, "c5 full")
+
+
+# --------------------------------------------------------- shared prefix ---
+
+def _cascade_paths(DeviceBatch, batch, ob, reqs=None):
+    db = DeviceBatch.from_batch(batch)
+    P = batch.prefix_len
+    res = {}
+    for force in (0, 1, 2):
+        plan = db.plan(shared_prefix_len=P, force_path=force)
+        say(f"decode_step force={force} B={batch.B} P={P} layout={batch.layout}")
+        o, lse = db.step(plan)
+        torch.cuda.synchronize()
+        res[force] = (o, lse, plan)
+    return db, res
+
+
+def test_cascade_small_all_paths_and_layouts():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    for B, P, own in ((24, 512, (0, 100)), (5, 1000, (1, 3)), (3, 40, (30, 70))):
+        shared = make_decode_batch(seed=31 + B, B=B, H_q=32, H_kv=8, d=128, own_len=own, prefix_len=P,
+                                   page_size=16, layout="shared")
+        o_ref, lse_ref = ob.batch_reference(shared)
+        db, res = _cascade_paths(DeviceBatch, shared, ob)
+        for force, (o, lse, plan) in res.items():
+            check_close("bf16", o, lse, o_ref, lse_ref, f"B={B} P={P} path={force}")
+        # the prefix pass alone, against the oracle over the first tokens
+        plan = res[2][2]
+        n = plan.info["prefix_tokens"]
+        say(f"cascade_prefix_attn B={B} n={n}")
+        o_p, lse_p = db.prefix(plan)
+        torch.cuda.synchronize()
+        op_ref, lp_ref = ob.prefix_reference(shared, n)
+        check_close("bf16", o_p, lse_p, op_ref, lp_ref, f"prefix B={B}")
+        # paged over unique copies of the prefix: same bits as over shared pages
+        unique = relayout(shared, page_size=16, seed=77, layout="unique")
+        say(f"paged unique B={B}")
+        ou, lu, _ = run_paged(DeviceBatch, unique)
+        assert same_bits(ou, res[0][0]) and same_bits(lu, res[0][1]), "layout changed the bits"
+
+
+def _full_prefix_case(name, reqs):
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config(name)
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(shared_prefix_len=b.prefix_len)
+    say(f"{name} full plan={plan.info['path_name']} decode_step")
+    o, lse = db.step(plan)
+    torch.cuda.synchronize()
+    check_close("bf16", o[reqs], lse[reqs], o_ref, lse_ref, f"{name} {plan.info['path_name']}")
+    outs = {plan.info["path"]: (o, lse)}
+    for force in (0, 1, 2):
+        if force in outs:
+            continue
+        p2 = db.plan(shared_prefix_len=b.prefix_len, force_path=force)
+        say(f"{name} full forced {p2.info['path_name']}")
+        o2, l2 = db.step(p2)
+        torch.cuda.synchronize()
+        check_close("bf16", o2[reqs], l2[reqs], o_ref, lse_ref, f"{name} {p2.info['path_name']}")
+        outs[force] = (o2, l2)
+    return plan
+
+
+def test_c3_full_sampled():
+    plan = _full_prefix_case("c3", [0, 100, 255])
+    assert plan.info["m_eff"] == 1024
+
+
+def test_c4_full_sampled():
+    plan = _full_prefix_case("c4", [0, 311, 511])
+    assert plan.info["m_eff"] == 2048
+
+
+# ------------------------------------------------------------ edge cases ---
+
+@pytest.mark.parametrize("case", [
+    dict(B=6, H_q=16, H_kv=2, d=128, own_len=(0, 3), q_dtype="bf16", kv_dtype="bf16", page_size=1),
+    dict(B=4, H_q=3, H_kv=3, d=128, own_len=(1, 900), q_dtype="bf16", kv_dtype="bf16", page_size=7),
+    dict(B=5, H_q=8, H_kv=8, d=64, own_len=(100, 1500), q_dtype="bf16", kv_dtype="bf16", page_size=16),
+    dict(B=3, H_q=16, H_kv=8, d=128, own_len=(2000, 2100), q_dtype="bf16", kv_dtype="bf16", page_size=32),
+    dict(B=2, H_q=64, H_kv=8, d=64, own_len=(300, 700), q_dtype="bf16", kv_dtype="fp8", page_size=16),
+    dict(B=3, H_q=12, H_kv=6, d=128, own_len=(50, 400), q_dtype="bf16", kv_dtype="fp8", page_size=8),
+    dict(B=2, H_q=4, H_kv=1, d=64, own_len=(1, 700), q_dtype="f32", kv_dtype="f32", page_size=3),
+    dict(B=3, H_q=16, H_kv=2, d=128, own_len=(100, 900), q_dtype="f32", kv_dtype="f32", page_size=16),
+    dict(B=1, H_q=32, H_kv=4, d=128, own_len=(1, 1), q_dtype="bf16", kv_dtype="bf16", page_size=16),
+])
+@pytest.mark.parametrize("splits", ["one", "many"])
+def test_edge_shapes(case, splits):
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_decode_batch(seed=sum(case["own_len"]) + case["H_q"], pool_factor=2, **case)
+    tuning = dict(min_split_tokens=64, target_workgroups=100000) if splits == "many" else \
+        dict(min_split_tokens=2048, target_workgroups=1)
+    o_ref, lse_ref = ob.batch_reference(b)
+    say(f"edge {case} splits={splits}")
+    o, lse, plan = run_paged(DeviceBatch, b, tuning=tuning)
+    check_close(case["kv_dtype"], o, lse, o_ref, lse_ref, f"edge {case} {splits}")
+    if case["kv_dtype"] != "f32":
+        of, lf, _ = run_paged(DeviceBatch, b, tuning=tuning, want_f32=True)
+        check_close(case["kv_dtype"], of, lf, o_ref, lse_ref, f"edge f32-out {case}")
+
+
+def test_run_twice_bitwise_identical():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c3", B=40, own_len=(10, 300))
+    db = DeviceBatch.from_batch(b)
+    for force in (0, 1, 2):
+        plan = db.plan(shared_prefix_len=b.prefix_len, force_path=force)
+        say(f"determinism force={force}")
+        o1, l1 = db.step(plan)
+        o2, l2 = db.step(plan)
+        torch.cuda.synchronize()
+        assert same_bits(o1, o2) and same_bits(l1, l2), f"path {force} not reproducible"
+
+
+def test_merge_states_vs_oracle():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    rng = np.random.default_rng(3)
+    for d in (64, 128):
+        rows = 1000
+        o_a, o_b = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+        la, lb = rng.normal(0, 5, rows), rng.normal(0, 5, rows)
+        la[::7] = -np.inf
+        lb[::11] = -np.inf
+        o_ref, l_ref = oa.merge_states(o_a, la, o_b, lb)
+        t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+        lse_out = torch.empty(rows, dtype=torch.float32, device="cuda")
+        say(f"merge_states d={d} f32")
+        o = DeviceBatch.merge(t(o_a), t(la), t(o_b), t(lb), torch.float32, lse_out)
+        torch.cuda.synchronize()
+        check_close("f32", o, lse_out, o_ref, l_ref, f"merge d={d}")
+        say(f"merge_states d={d} bf16")
+        ob16 = DeviceBatch.merge(t(o_a), t(la), t(o_b), t(lb), torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.abs(ob16.float().cpu().numpy() - o_ref).max() <= 2e-2
+
+
+def test_abi_rejects_bad_arguments_without_launching():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c1")
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(tuning=dict(min_split_tokens=64, target_workgroups=4096))
+    assert plan.info["workspace_bytes"] > 0
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_paged_decode_attn(plan, db.q, db.pool, db.kv_indptr, db.kv_indices, 0.125, o=db.new_out(),
+                                  workspace=None)
+    assert e.value.name == "EWORKSPACE"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_paged_decode_attn(plan, db.q, db.pool, db.kv_indptr, db.kv_indices, 0.125,
+                                  workspace=db.workspace(plan))
+    assert e.value.name == "EINVAL"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_cascade_prefix_attn(plan, db.q.bfloat16(), db.pool, db.kv_indices, 0, 0.125,
+                                    db.new_out(torch.float32), db.new_lse())
+    assert e.value.name == "EINVAL"   # a PAGED plan has no prefix pass
+    with pytest.raises(ValueError):
+        pkv.pkv_paged_decode_attn(plan, db.q.cpu(), db.pool, db.kv_indptr, db.kv_indices, 0.125,
+                                  o=db.new_out(), workspace=db.workspace(plan))

@@ -1,0 +1,190 @@
+"""CPU tests of the C library's host half through its C ABI (no GPU calls).
+
+Lowering and planning are compared bit for bit with the oracle's independent
+statements of the same rules; every host-side error path is forced.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_201_amd as pkv
+from oracle import lowering as ol
+from oracle import planner as op
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) == 12, declared
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(pkv.EXPORTS) == declared
+
+
+def test_status_strings_and_version():
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert pkv.pkv_status_string(st) != "unknown status"
+    assert "gfx950" in pkv.pkv_version()
+    d = pkv.pkv_tuning_defaults()
+    assert d["t_dense"] > 0 and d["target_workgroups"] > 0
+
+
+# ---------------------------------------------------------------- lowering --
+
+def _table(rng, B, p, lmax, extra=3):
+    lens = rng.integers(0, lmax + 1, size=B)
+    npg = (lens + p - 1) // p
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    pages = rng.permutation(int(npg.sum()) + extra)[: indptr[-1]].astype(np.int32)
+    return lens.astype(np.int32), indptr, pages
+
+
+@pytest.mark.parametrize("p", [1, 2, 7, 16, 64, 128])
+def test_lowering_matches_oracle_bit_exact(p):
+    rng = np.random.default_rng(p)
+    for B in (0, 1, 5, 33):
+        lens, indptr, pages = _table(rng, B, p, 700)
+        got = pkv.pkv_lower_page_table(p, indptr, pages, lens)
+        ref = ol.lower_page_table(p, indptr, pages, lens)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_lowering_index_length_is_BxL_at_every_page_size():
+    B, L = 32, 4096
+    for p in (1, 128):
+        n = L // p
+        pages = np.random.default_rng(p).permutation(B * n).astype(np.int32)
+        kv_indptr, kv_indices = pkv.pkv_lower_page_table(p, np.arange(B + 1) * n, pages, [L] * B)
+        assert len(kv_indices) == B * L == kv_indptr[-1]
+
+
+def test_lowering_errors():
+    def st(*a):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_lower_page_table(*a)
+        return e.value.name
+    assert st(16, [0, 2], [3, 4], [16]) == "ERANGE"          # trailing empty page
+    assert st(16, [0, 1], [3], [17]) == "ERANGE"             # a page short
+    assert st(0, [0, 0], [], [0]) == "EINVAL"                # page size
+    assert st(16, [1, 2], [3], [5]) == "EINVAL"              # indptr[0] != 0
+    assert st(16, [0, 1], [-3], [5]) == "ERANGE"             # negative page
+    assert st(16, [0, 1], [2**31 // 16], [5]) == "ERANGE"    # slot overflows int32
+    assert st(16, [0, 1], [3], [-1]) == "EINVAL"             # negative length
+
+
+def test_validate_indices():
+    pkv.pkv_validate_indices([0, 2, 3], [5, 0, 9], 10)
+    for args, name in [(([0, 2, 3], [5, 0, 10], 10), "ERANGE"), (([0, 2, 3], [5, -1, 9], 10), "ERANGE"),
+                       (([0, 3, 2], [5, 0, 9], 10), "EINVAL"), (([1, 2, 3], [5, 0, 9], 10), "EINVAL")]:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_validate_indices(*args)
+        assert e.value.name == name
+
+
+# ----------------------------------------------------------------- planner --
+
+TUNE = pkv.pkv_tuning_defaults()
+
+
+def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None):
+    t = dict(TUNE)
+    t.update(tune or {})
+    lens = [int(x) for x in np.atleast_1d(L)] if np.ndim(L) else [int(L)] * B
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ref = err_ref = None
+    try:
+        ref = op.plan(B=B, H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype=q, kv_dtype=kv, page_size=p, seq_lens=lens,
+                      shared_prefix_len=P, force_path=force, t_dense=t["t_dense"], gate_ratio=t["gate_ratio"],
+                      launch_bytes=t["launch_bytes"])
+    except op.PlanError as e:
+        err_ref = e.code
+    got = err_got = None
+    try:
+        got = pkv.pkv_plan_create(batch=B, num_q_heads=H_kv * G, num_kv_heads=H_kv, head_dim=d, q_dtype=q,
+                                  kv_dtype=kv, page_size=p, kv_indptr=indptr, shared_prefix_len=P,
+                                  force_path=force, tuning=t).info
+    except pkv.PkvError as e:
+        err_got = e.name
+    assert err_ref == err_got, (B, G, P, p, err_ref, err_got)
+    if ref is not None:
+        assert got["path_name"] == ref["path"], (B, G, P, p, got, ref)
+        assert got["m_eff"] == ref["m_eff"]
+        assert got["shared_pages"] == ref["shared_pages"]
+        assert got["prefix_tokens"] == ref["prefix_tokens"]
+    return got
+
+
+def test_planner_grid_matches_oracle():
+    for B, G, P, p in itertools.product([0, 1, 2, 3, 8, 64, 255, 256, 512], [1, 2, 4, 8],
+                                        [0, 1, 15, 16, 512, 2003, 4096], [1, 16, 128]):
+        _both(B, G, P, p, L=P + 37)
+
+
+def test_planner_tuning_variants_match_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        tune = dict(t_dense=int(rng.integers(1, 4096)), gate_ratio=int(rng.integers(0, 5)),
+                    launch_bytes=int(rng.integers(0, 10**9)))
+        _both(int(rng.integers(0, 600)), int(rng.choice([1, 2, 4, 8])), int(rng.integers(0, 5000)),
+              int(rng.choice([1, 16, 32, 128])), L=5000 + int(rng.integers(0, 100)), tune=tune)
+
+
+def test_planner_forced_paths_and_errors_match_oracle():
+    for force in (0, 1, 2):
+        for P in (0, 8, 16, 4096):
+            _both(16, 4, P, 16, L=P + 5, force=force)
+    _both(16, 4, 4096, 16, L=5000, kv="fp8", force=2)            # EUNSUPPORTED
+    _both(16, 4, 64, 16, L=5000, q="f32", kv="f32", H_kv=2, d=64)
+    _both(16, 4, 64, 16, L=5000, d=96)                           # EUNSUPPORTED
+    _both(4, 4, 64, 16, L=[100, 100, 20, 100])                   # prefix longer than a request
+    _both(16, 3, 64, 16, L=5000)                                 # G = 3 not built
+    _both(16, 16, 64, 16, L=5000, H_kv=2)                        # G = 16 not built
+
+
+def test_config_shapes_plan_as_documented():
+    c3 = _both(256, 4, 4096, 16, L=4096 + 300)
+    assert c3["m_eff"] == 1024 and c3["shared_pages"] == 256
+    c4 = _both(512, 4, 512, 16, L=512 + 640)
+    assert c4["m_eff"] == 2048
+    c5 = _both(16, 8, 0, 16, L=16384, kv="fp8")
+    assert c5["m_eff"] == 128 and c5["path_name"] == "PAGED"
+
+
+def test_split_partition_covers_every_token_once():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        B = int(rng.integers(1, 64))
+        lens = rng.integers(0, 20000, size=B)
+        P = int(rng.integers(0, lens.min() + 1))
+        t = dict(target_workgroups=int(rng.integers(1, 4096)), min_split_tokens=int(rng.integers(1, 2048)))
+        info = _both(B, 4, P, 16, L=lens, tune=t)
+        if info is None:
+            continue
+        C, S = info["split_tokens"], info["num_splits"]
+        assert C % 64 == 0 and C <= max(2048, 64)
+        for L in lens:
+            n = int(L) - info["prefix_tokens"]
+            covered = sum(max(0, min((s + 1) * C, n) - s * C) for s in range(S))
+            assert covered == n and S * C >= n
+
+
+def test_plan_workspace_and_geometry():
+    info = _both(32, 4, 0, 128, L=4096)
+    assert info["heads_per_item"] == 8 and info["num_splits"] * info["split_tokens"] >= 4096
+    assert info["workspace_bytes"] >= 32 * 32 * info["num_splits"] * 130 * 4 or info["num_splits"] == 1
+    c5 = _both(16, 8, 0, 16, L=16384, kv="fp8")
+    assert c5["heads_per_item"] == 4
+    c1 = _both(4, 4, 0, 16, L=[64, 100, 200, 256], H_kv=2, d=64, q="f32", kv="f32")
+    assert c1["heads_per_item"] == 2 and c1["num_splits"] == 1 and c1["workspace_bytes"] == 0
