@@ -82,6 +82,11 @@ def bench_paged_config(name, steps, warmup, **overrides):
     return rec, b, db, plan
 
 
+def add_ceiling(rec, ceiling):
+    rec["pct_read_ceiling"] = 100.0 * rec["gbs"] / ceiling
+    return rec
+
+
 def bench_prefix_config(name, steps, warmup):
     """PAGED over unique prefix copies, PAGED over shared pages, and each
     prefix path, plus the planner's choice."""
@@ -118,6 +123,25 @@ def bench_prefix_config(name, steps, warmup):
     del du, u, ws
     torch.cuda.empty_cache()
     return out
+
+
+def read_ceiling(steps=20, warmup=5, gib=4):
+    """Streaming-read bandwidth of this GPU (GB/s), through the library's read
+    probe over a buffer far larger than the 256 MB Infinity Cache."""
+    import torch
+    import paged_kv_cache_201_amd as pkv
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    best = None
+    for wgs in (1024, 2048, 4096):
+        out = torch.empty(wgs, dtype=torch.int32, device="cuda")
+        ms = time_steps(lambda: pkv.pkv_stream_read_probe(buf, out, wgs), steps, warmup)
+        gbs = n / (ms * 1e-3) / 1e9
+        best = max(best or 0, gbs)
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def cpu_baseline(batch, reps=3):
@@ -157,15 +181,21 @@ def main():
     wanted = args.configs.split(",")
     extra = {}
     log = lambda m: print(m, file=sys.stderr, flush=True)
+    log("streaming-read ceiling")
+    ceiling = read_ceiling()
+    extra["read_ceiling_gbs"] = ceiling
+    log(f"read ceiling {ceiling:.0f} GB/s")
 
     # headline: Llama-3.1-8B layer, page size 1 (token-flat scatter) and 128
     log("bench c2 p=1")
     rec1, b1, db1, plan1 = bench_paged_config("c2", args.steps, args.warmup, page_size=1)
+    add_ceiling(rec1, ceiling)
     log(json.dumps(rec1))
     del db1
     torch.cuda.empty_cache()
     log("bench c2 p=128")
     rec128, b128, db128, _ = bench_paged_config("c2", args.steps, args.warmup)
+    add_ceiling(rec128, ceiling)
     log(json.dumps(rec128))
     del db128, b128
     torch.cuda.empty_cache()
@@ -174,7 +204,7 @@ def main():
         if name in ("c1", "c5"):
             log(f"bench {name}")
             r, _, db, _ = bench_paged_config(name, args.steps, args.warmup)
-            extra[name] = r
+            extra[name] = add_ceiling(r, ceiling)
             log(json.dumps(r))
             del db
             torch.cuda.empty_cache()
@@ -203,6 +233,7 @@ def main():
         "ms_per_step": ms,
         "us_per_step": rec1["us_per_step"],
         "pct_peak": rec1["pct_peak"],
+        "pct_read_ceiling": rec1["pct_read_ceiling"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -213,7 +244,9 @@ def main():
                    "global_batch": 32, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": rec1["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": rec1["gbs"] / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "paged decode step (split kernel + split reduction)"},
+                     "kernel": "paged decode step: paged_split_kernel + split_reduce_kernel, timed together "
+                               "(events cannot split one library call)",
+                     "read_ceiling_gbs": ceiling},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -109,6 +109,8 @@ typedef struct pkv_tuning {
     int64_t launch_bytes;       /* byte-equivalent of the two extra launches of a cascade */
     int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU */
     int32_t min_split_tokens;   /* paged pass: smallest token range per workgroup */
+    int32_t fuse_split_reduce;  /* 1: the last work item of a request combines its splits
+                                   (one kernel per paged pass); 0: a separate reduce kernel */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */
@@ -124,6 +126,8 @@ typedef struct pkv_plan_info {
     int32_t prefix_splits;      /* prefix pass: ranges the prefix is cut into */
     int64_t num_work_items;     /* paged pass: workgroups launched */
     int64_t workspace_bytes;    /* device scratch the plan's calls need (0 allowed) */
+    int64_t workspace_zero_bytes; /* leading workspace bytes that must be zero before the
+                                     first call on a workspace; every call leaves them zero */
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
@@ -206,7 +210,10 @@ void pkv_plan_destroy(pkv_plan* plan);
  *   o           device, [B][H_q][d] of the q dtype, normalised output; nullable
  *   o_f32       device, [B][H_q][d] fp32, normalised output; nullable
  *   lse         device, [B][H_q] fp32; nullable
- *   workspace   device scratch of >= the plan's workspace_bytes (nullable if 0)
+ *   workspace   device scratch of >= the plan's workspace_bytes (nullable if 0);
+ *               its first workspace_zero_bytes must be zero before the first
+ *               call that uses it (e.g. zero-filled once at allocation); calls
+ *               leave them zero.  Calls that share a workspace must not overlap.
  * At least one of o, o_f32 must be given.  Writes no other memory.
  * Errors: EINVAL (null plan/q/indices, no output, pool not matching the plan,
  * missing fp8 scales), EWORKSPACE, EHIP.
@@ -265,6 +272,20 @@ pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* 
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            float sm_scale, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement aid: read `bytes` of device memory at `buf` once, with 16-byte
+ * loads from num_workgroups workgroups of 256 threads, and write one word per
+ * workgroup to out[num_workgroups] (device).  Its duration gives the
+ * streaming-read bandwidth ceiling of the GPU, against which the attention
+ * kernels' achieved bandwidth is compared ([P1] "When source beats
+ * intuition" and "A backend where pages really do reach the kernel" judge
+ * decode kernels by their fraction of peak DRAM throughput).
+ * Errors: EINVAL (null pointers, bytes not a multiple of 16, misaligned buf,
+ * num_workgroups < 1), EHIP.
+ */
+pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_workgroups,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,7 @@ point it calls, converts torch tensors / numpy arrays to pointers, and raises
 ``PkvError`` when the library returns a non-OK status.  All device work runs
 in the library's HIP kernels; there is no fallback path.  Importing this
 package fails if ``libpkv.so`` has not been built
-(``python -m paged_kv_cache_201_amd.build``).
+(``python paged_kv_cache_201_amd/build.py``).
 
 Device tensors must be contiguous and on a CUDA (HIP) device; this is checked
 before any pointer is passed, so a host pointer never reaches a kernel.
@@ -17,7 +17,7 @@ import numpy as np
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is not built; run `python -m paged_kv_cache_201_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is not built; run `python paged_kv_cache_201_amd/build.py`")
 _lib = ctypes.CDLL(_LIB_PATH)
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ERANGE, PKV_EHIP, PKV_ENOMEM = 0, -1, -2, -3, -4, -5, -6
@@ -54,14 +54,16 @@ class pkv_problem(ctypes.Structure):
 
 class pkv_tuning(ctypes.Structure):
     _fields_ = [("t_dense", ctypes.c_int32), ("gate_ratio", ctypes.c_int32), ("launch_bytes", ctypes.c_int64),
-                ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32)]
+                ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
+                ("fuse_split_reduce", ctypes.c_int32)]
 
 
 class pkv_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("m_eff", ctypes.c_int32), ("shared_pages", ctypes.c_int32),
                 ("prefix_tokens", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
-                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("workspace_zero_bytes", ctypes.c_int64)]
 
 
 _SIGS = {
@@ -83,6 +85,7 @@ _SIGS = {
                                           _vp, _vp]),
     "pkv_decode_step": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]),
+    "pkv_stream_read_probe": (ctypes.c_int32, [_vp, ctypes.c_int64, _vp, ctypes.c_int32, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -180,8 +183,9 @@ class Plan:
 
     def __del__(self):
         h, self.handle = getattr(self, "handle", None), None
-        if h:
-            _lib.pkv_plan_destroy(h)
+        lib = globals().get("_lib")
+        if h and lib is not None:  # the library may already be gone at interpreter exit
+            lib.pkv_plan_destroy(h)
 
 
 def pkv_plan_create(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, page_size, kv_indptr,
@@ -269,6 +273,14 @@ def pkv_decode_step(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None,
                               _dev(kv_indices, "kv_indices", (torch.int32,)), float(sm_scale), _dev(o, "o"),
                               _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
     _check(st, "pkv_decode_step")
+
+
+def pkv_stream_read_probe(buf, out, num_workgroups, stream=None):
+    """Read all of ``buf`` (a CUDA tensor) once; ``out`` holds num_workgroups int32."""
+    import torch
+    _check(_lib.pkv_stream_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                      _dev(out, "out", (torch.int32,)), int(num_workgroups), _stream(stream)),
+           "pkv_stream_read_probe")
 
 
 def workspace_for(plan, device="cuda"):

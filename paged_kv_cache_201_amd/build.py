@@ -1,6 +1,8 @@
 """Build libpkv.so for gfx950 in place (next to this file).
 
-    python -m paged_kv_cache_201_amd.build [-v]
+    python paged_kv_cache_201_amd/build.py [-v]
+
+(run as a file: importing the package loads the library it builds)
 
 Host-only C++ (the planner and page-table lowering) is compiled with g++;
 the HIP sources with hipcc for gfx950.  Objects go to ``_build/`` at the
@@ -19,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "paged_f32.hip", "paged_bf16.hip", "paged_fp8.hip"]
+HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "probe.hip", "paged_f32.hip", "paged_bf16.hip", "paged_fp8.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 ARCH = "gfx950"

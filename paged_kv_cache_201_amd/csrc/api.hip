@@ -52,9 +52,8 @@ T* ws_at(void* ws, int64_t off) {
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EHIP; }
 
 // The paged pass over tokens [plan.prefix_tokens, L_b) of every request.
-pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
-                     const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
-                     void* ws, hipStream_t stream) {
+pkv::PagedArgs paged_args(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, float sm_scale) {
     pkv::PagedArgs a{};
     a.q = q;
     a.k = pool->k;
@@ -68,6 +67,14 @@ pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, co
     a.split_tokens = pl->split_tokens;
     a.num_splits = pl->num_splits;
     a.scale_log2 = sm_scale * kLog2e;
+    a.out_dtype = pl->q_dtype;
+    return a;
+}
+
+pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
+                     void* ws, hipStream_t stream) {
+    pkv::PagedArgs a = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
     if (pl->num_splits == 1) {
         a.o = o;
         a.o_f32 = o_f32;
@@ -76,12 +83,16 @@ pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, co
     }
     a.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
     a.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
+    if (pl->fuse_reduce) {
+        a.counters = ws_at<int32_t>(ws, pl->ws_counters);
+        a.o = o;
+        a.o_f32 = o_f32;
+        a.lse = lse;
+        return hip_status(pkv::launch_paged_split(*pl, a, stream));
+    }
     hipError_t e = pkv::launch_paged_split(*pl, a, stream);
     if (e != hipSuccess) return PKV_EHIP;
     pkv::SplitReduceArgs r{};
-    r.kv_indptr = kv_indptr;
-    r.token_offset = pl->prefix_tokens;
-    r.split_tokens = pl->split_tokens;
     r.num_splits = pl->num_splits;
     r.B = pl->B;
     r.H_q = pl->H_q;
@@ -95,8 +106,8 @@ pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, co
     return hip_status(pkv::launch_split_reduce(r, stream));
 }
 
-pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* prefix_indices,
-                      float sm_scale, float* o_p, float* lse_p, void* ws, hipStream_t stream) {
+pkv::PrefixArgs prefix_args(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* prefix_indices,
+                            float sm_scale) {
     pkv::PrefixArgs a{};
     a.q = q;
     a.k = pool->k;
@@ -111,6 +122,12 @@ pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, c
     a.num_splits = pl->prefix_splits;
     a.row_tiles = (pl->m_eff + pl->prefix_rows_per_wg - 1) / pl->prefix_rows_per_wg;
     a.scale_log2 = sm_scale * kLog2e;
+    return a;
+}
+
+pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* prefix_indices,
+                      float sm_scale, float* o_p, float* lse_p, void* ws, hipStream_t stream) {
+    pkv::PrefixArgs a = prefix_args(pl, q, pool, prefix_indices, sm_scale);
     if (pl->prefix_splits == 1) {
         a.o = o_p;
         a.lse = lse_p;
@@ -121,8 +138,6 @@ pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, c
     hipError_t e = pkv::launch_prefix_attn(a, pl->prefix_rows_per_wg, stream);
     if (e != hipSuccess) return PKV_EHIP;
     pkv::SplitReduceArgs r{};
-    r.kv_indptr = nullptr;
-    r.split_tokens = pl->prefix_split_tokens;
     r.num_splits = pl->prefix_splits;
     r.B = pl->B;
     r.H_q = pl->H_q;
@@ -195,16 +210,33 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pl->path == PKV_PATH_PAGED)
         return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, nullptr, lse, ws, s);
-    float* o_p = ws_at<float>(ws, pl->ws_state_o_p);
-    float* lse_p = ws_at<float>(ws, pl->ws_state_lse_p);
-    float* o_s = ws_at<float>(ws, pl->ws_state_o_s);
-    float* lse_s = ws_at<float>(ws, pl->ws_state_lse_s);
-    st = run_prefix(pl, q, pool, kv_indices + pl->indptr0, sm_scale, o_p, lse_p, ws, s);
-    if (st != PKV_OK) return st;
-    st = run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, nullptr, o_s, lse_s, ws, s);
-    if (st != PKV_OK) return st;
-    return hip_status(pkv::launch_merge_states(pl->B * pl->H_q, pl->D, o_p, lse_p, o_s, lse_s, o, pl->q_dtype,
-                                               lse, s));
+    // Cascade: both passes leave partial states in the workspace, and one
+    // kernel combines the prefix ranges and then the suffix splits of every
+    // row into the output.
+    pkv::PrefixArgs pa = prefix_args(pl, q, pool, kv_indices + pl->indptr0, sm_scale);
+    pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
+    pa.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
+    pa.force_partial = 1;
+    if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
+    pkv::PagedArgs sa = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
+    sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
+    sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
+    sa.force_partial = 1;
+    if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    pkv::SplitReduceArgs r{};
+    r.num_splits = pl->num_splits;
+    r.B = pl->B;
+    r.H_q = pl->H_q;
+    r.D = pl->D;
+    r.part_acc = sa.part_acc;
+    r.part_ml = sa.part_ml;
+    r.pre_acc = pa.part_acc;
+    r.pre_ml = pa.part_ml;
+    r.pre_splits = pl->prefix_splits;
+    r.o = o;
+    r.out_dtype = pl->q_dtype;
+    r.lse = lse;
+    return hip_status(pkv::launch_split_reduce(r, s));
 }
 
 }  // extern "C"

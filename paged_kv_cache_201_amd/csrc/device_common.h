@@ -25,6 +25,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Explicit global-memory (address space 1) pointers, for loads whose base is
+// computed in scalar registers.
+typedef const char __attribute__((address_space(1)))* gbytes_t;
+
+__device__ __forceinline__ gbytes_t as_global(const void* p) { return (gbytes_t)p; }
+
+template <typename T>
+__device__ __forceinline__ T load_global(gbytes_t p) {
+    return *(const T __attribute__((address_space(1)))*)p;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -195,6 +206,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, HI));
+}
+
+// a.lo*b.lo + a.hi*b.hi with a zero accumulator, as the three-operand VOP3P
+// form: the two-operand accumulate form would need the destination zeroed
+// by a separate move first.
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
 
 // sum of a.lo*b.lo + a.hi*b.hi + c, bf16 pairs with fp32 accumulation

@@ -96,6 +96,7 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->launch_bytes = 40LL * 1000 * 1000;   // ~5 us at 8 TB/s for two extra launches
     out->target_workgroups = 1024;
     out->min_split_tokens = 256;
+    out->fuse_split_reduce = 0;  // measured: the device-scope release per item costs more than a launch
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -154,7 +155,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         pkv_tuning_defaults(&tu);
     }
     if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
-        tu.min_split_tokens < 1)
+        tu.min_split_tokens < 1 || tu.fuse_split_reduce < 0 || tu.fuse_split_reduce > 1)
         return PKV_EINVAL;
 
     // Checks, in the same order as the planner's reference statement.
@@ -257,9 +258,10 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->prefix_splits = 0;
     if (path != PKV_PATH_PAGED) {
         const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
-        const int64_t want = std::max<int64_t>(1, ceil_div(tu.target_workgroups, tiles));
+        const int64_t want = std::max<int64_t>(1, ceil_div(pkv::kPrefixTargetWgs, tiles));
         int64_t ps = align_up(ceil_div(prefix_tokens, want), pkv::kPrefixTokenQuantum);
-        ps = std::max<int64_t>(ps, pkv::kPrefixTokenQuantum);
+        ps = std::max<int64_t>(ps, 4 * pkv::kPrefixTokenQuantum);
+        ps = std::min<int64_t>(ps, pkv::kMaxPrefixSplitTokens);
         pl->prefix_split_tokens = (int32_t)ps;
         pl->prefix_splits = (int32_t)ceil_div(prefix_tokens, ps);
     }
@@ -272,22 +274,25 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         off = align_up(off + bytes, kAlign);
         return at;
     };
+    pl->ws_counters = -1;
+    pl->ws_zero_bytes = 0;
+    pl->fuse_reduce = tu.fuse_split_reduce && pl->num_splits > 1 && path == PKV_PATH_PAGED;
+    if (pl->fuse_reduce) {
+        pl->ws_counters = take((int64_t)B * pl->head_blocks * 4);
+        pl->ws_zero_bytes = (int64_t)B * pl->head_blocks * 4;
+    }
     pl->ws_paged_acc = pl->ws_paged_ml = -1;
     pl->ws_prefix_acc = pl->ws_prefix_ml = -1;
-    pl->ws_state_o_p = pl->ws_state_lse_p = pl->ws_state_o_s = pl->ws_state_lse_s = -1;
-    if (pl->num_splits > 1) {
+    // A cascade step keeps both passes as partial states (prefix ranges, then
+    // suffix splits) that one kernel combines; a paged pass with one split
+    // writes its output directly.
+    if (pl->num_splits > 1 || path != PKV_PATH_PAGED) {
         pl->ws_paged_acc = take(rows * pl->num_splits * D * 4);
         pl->ws_paged_ml = take(rows * pl->num_splits * 2 * 4);
     }
     if (path != PKV_PATH_PAGED) {
-        if (pl->prefix_splits > 1) {
-            pl->ws_prefix_acc = take(rows * pl->prefix_splits * D * 4);
-            pl->ws_prefix_ml = take(rows * pl->prefix_splits * 2 * 4);
-        }
-        pl->ws_state_o_p = take(rows * D * 4);
-        pl->ws_state_lse_p = take(rows * 4);
-        pl->ws_state_o_s = take(rows * D * 4);
-        pl->ws_state_lse_s = take(rows * 4);
+        pl->ws_prefix_acc = take(rows * pl->prefix_splits * D * 4);
+        pl->ws_prefix_ml = take(rows * pl->prefix_splits * 2 * 4);
     }
     pl->workspace_bytes = off;
     *out = pl;
@@ -306,6 +311,7 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     info->prefix_splits = pl->prefix_splits;
     info->num_work_items = pl->num_work_items;
     info->workspace_bytes = pl->workspace_bytes;
+    info->workspace_zero_bytes = pl->ws_zero_bytes;
     return PKV_OK;
 }
 

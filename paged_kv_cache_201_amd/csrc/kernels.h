@@ -30,22 +30,28 @@ struct PagedArgs {
     // partial outputs (num_splits > 1)
     float* part_acc;          // [B][num_splits][H_q][D]: sum of 2^(s - M) v
     float* part_ml;           // [B][num_splits][H_q][2]: (M, L), M in log2 units
+    // num_splits > 1 and non-null: [B][head_blocks] arrival counters (zero on
+    // entry, left zero on exit); the last item of a (request, head block) to
+    // finish combines the partials and writes o / o_f32 / lse itself.
+    int32_t* counters;
+    int32_t out_dtype;        // dtype of o (q dtype)
+    int32_t force_partial;    // write partials even with one split (cascade suffix)
 };
 
 // Launch the paged split kernel for the plan's geometry.
 hipError_t launch_paged_split(const pkv_plan& plan, const PagedArgs& a, hipStream_t stream);
 
-// Combine split partials: for each (request, query head) the items
-// 0 .. ceil(len_b / split_tokens) - 1 of that request, or all num_splits items
-// when kv_indptr is null.
+// Combine partial states row by row: the pre_splits partials at pre_acc
+// (the shared-prefix pass of a cascade step; optional) followed by the
+// num_splits partials at part_acc, all in the [B][splits][H_q] layout.
 struct SplitReduceArgs {
-    const int32_t* kv_indptr; // nullable
-    int32_t token_offset;
-    int32_t split_tokens;
     int32_t num_splits;
     int32_t B, H_q, D;
     const float* part_acc;
     const float* part_ml;
+    const float* pre_acc;     // nullable: [B][pre_splits][H_q][D]
+    const float* pre_ml;
+    int32_t pre_splits;
     void* o;                  // nullable; out_dtype
     int32_t out_dtype;
     float* o_f32;             // nullable
@@ -70,6 +76,7 @@ struct PrefixArgs {
     float* lse;               // num_splits == 1: [B][H_q]
     float* part_acc;          // num_splits > 1: [B][num_splits][H_q][D]
     float* part_ml;           // num_splits > 1: [B][num_splits][H_q][2]
+    int32_t force_partial;    // write partials even with one split (cascade step)
 };
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream);
 

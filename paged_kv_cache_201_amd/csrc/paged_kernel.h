@@ -63,6 +63,10 @@ struct LoadVec<2> {
 };
 
 constexpr int kPagedWaves = 4;
+#ifndef PKV_PAGED_PIPE
+#define PKV_PAGED_PIPE 2
+#endif
+constexpr int kPagedPipe = PKV_PAGED_PIPE;  // register buffers of K/V loads (2 or 3)
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units
 
 template <int KV, int D, int G, int NHL, int TPI>
@@ -81,7 +85,9 @@ struct PagedCfg {
     static constexpr int TU = U * TPI;  // tokens per wave iteration
     static constexpr int PARTIALS = NW * TPI;
     static constexpr int MERGE_FLOATS = PARTIALS * HB * G * D;
-    static constexpr int LDS_FLOATS = MERGE_FLOATS > kMaxSplitTokens ? MERGE_FLOATS : kMaxSplitTokens;
+    // slot indices of an item, padded to whole wave iterations
+    static constexpr int IDX_INTS = kMaxSplitTokens + NW * TU;
+    static constexpr int LDS_FLOATS = MERGE_FLOATS > IDX_INTS ? MERGE_FLOATS : IDX_INTS;
     static_assert(G <= LPH, "one query head per lane after the row reduction");
     static_assert(TPI == 1 || NHL == 1, "several tokens per load only with one head slot");
     static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
@@ -98,7 +104,8 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
     __shared__ float s_ml[C::PARTIALS * HB * G * 2];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform, so everything derived from it lives in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x;
     const int hblk = blockIdx.y;
     const int b = blockIdx.z;
@@ -108,19 +115,38 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
     const int seq_beg = a.kv_indptr[b] + a.token_offset;
     const int len = a.kv_indptr[b + 1] - seq_beg;
     const int t0 = split * a.split_tokens;
-    if (a.num_splits > 1 && t0 >= len) return;  // empty item: the reduce skips it
+    // Items past the request's last token only record an empty state
+    // (max -inf, sum 0) for the reduction; item 0 always runs so that an
+    // empty request still gets o = 0, lse = -inf.
+    const int items = max(1, (len + a.split_tokens - 1) / a.split_tokens);
+    if (split >= items) {
+        if (a.counters == nullptr) {
+            for (int qhl = threadIdx.x; qhl < HB * G; qhl += NW * 64) {
+                const int qh = (hblk * HB + qhl / G) * G + qhl % G;
+                const size_t prow = ((size_t)b * a.num_splits + split) * H_q + qh;
+                f32x2_t ml = {-INFINITY, 0.f};
+                *reinterpret_cast<f32x2_t*>(a.part_ml + prow * 2) = ml;
+            }
+        }
+        return;
+    }
     const int n_tok = max(min(t0 + a.split_tokens, len) - t0, 0);
 
-    // Stage this item's slot indices in LDS.
-    int* s_idx = reinterpret_cast<int*>(s_buf);
-    for (int i = threadIdx.x; i < n_tok; i += NW * 64) s_idx[i] = a.kv_indices[seq_beg + t0 + i];
-    __syncthreads();
-
-    // This wave's contiguous token range [w0, w1) within the item.
+    // This wave's contiguous token range [w0, w1) within the item; every
+    // wave range starts on a whole iteration.
     const int per_wave = ((n_tok + NW - 1) / NW + TU - 1) / TU * TU;
     const int w0 = min(wave * per_wave, n_tok);
     const int w1 = min(w0 + per_wave, n_tok);
     const int niter = (w1 - w0 + TU - 1) / TU;
+
+    // Stage this item's slot indices in LDS, padded with the last slot up to
+    // a whole iteration so that the tail needs no clamping (padded tokens are
+    // masked out of the softmax).
+    int* s_idx = reinterpret_cast<int*>(s_buf);
+    const int n_pad = (n_tok + TU - 1) / TU * TU;
+    for (int i = threadIdx.x; i < n_pad; i += NW * 64)
+        s_idx[i] = a.kv_indices[seq_beg + t0 + min(i, n_tok - 1)];
+    __syncthreads();
 
     const int lrow = lane / LPH;
     const int lch = lane % LPH;
@@ -173,21 +199,51 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
 #pragma unroll
     for (int i = 0; i < NHL; ++i) loff[i] = head_local(i) * D * BK + lch * EPL * BK;
 
-    LV kb[2][U][NHL], vb[2][U][NHL];
+    LV kb[kPagedPipe][U][NHL], vb[kPagedPipe][U][NHL];
 
     auto issue = [&](int it, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
+        const int tk0 = w0 + it * TU;
+        int slots[U];
+        if constexpr (TPI == 1) {
+            // one slot per step, the same for the whole wave: vector LDS
+            // reads of consecutive entries, then into scalar registers
+            if constexpr (U % 4 == 0) {
+#pragma unroll
+                for (int j = 0; j < U; j += 4) {
+                    const int4 v = *reinterpret_cast<const int4*>(s_idx + tk0 + j);
+                    slots[j] = __builtin_amdgcn_readfirstlane(v.x);
+                    slots[j + 1] = __builtin_amdgcn_readfirstlane(v.y);
+                    slots[j + 2] = __builtin_amdgcn_readfirstlane(v.z);
+                    slots[j + 3] = __builtin_amdgcn_readfirstlane(v.w);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < U; j += 2) {
+                    const int2 v = *reinterpret_cast<const int2*>(s_idx + tk0 + j);
+                    slots[j] = __builtin_amdgcn_readfirstlane(v.x);
+                    slots[j + 1] = __builtin_amdgcn_readfirstlane(v.y);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < U; ++j) slots[j] = s_idx[tk0 + j * TPI + tau];
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int tk = min(w0 + it * TU + j * TPI + tau, w1 - 1);
-            int slot = s_idx[tk];
-            if constexpr (TPI == 1) slot = __builtin_amdgcn_readfirstlane(slot);
-            const char* kr = kbase + (size_t)(uint32_t)slot * slot_stride;
-            const char* vr = vbase + (size_t)(uint32_t)slot * slot_stride;
+            gbytes_t kr = as_global(kbase) + (size_t)(uint32_t)slots[j] * slot_stride;
+            gbytes_t vr = as_global(vbase) + (size_t)(uint32_t)slots[j] * slot_stride;
+            if constexpr (TPI == 1) {
+                // The row base is wave-uniform: keep it in scalar registers
+                // and opaque, so that each load is (scalar base + 32-bit lane
+                // offset) rather than 64-bit per-lane address arithmetic.
+                asm("" : "+s"(kr));
+                asm("" : "+s"(vr));
+            }
 #pragma unroll
             for (int i = 0; i < NHL; ++i) {
-                kb[buf][j][i] = *reinterpret_cast<const LV*>(kr + loff[i]);
-                vb[buf][j][i] = *reinterpret_cast<const LV*>(vr + loff[i]);
+                kb[buf][j][i] = load_global<LV>(kr + loff[i]);
+                vb[buf][j][i] = load_global<LV>(vr + loff[i]);
             }
         }
     };
@@ -197,7 +253,7 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
         float s[U][NHL];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const bool valid = (w0 + it * TU + j * TPI + tau) < w1;
+            const bool valid = (w0 + it * TU + j * TPI + tau) < w1;  // padded tail tokens
 #pragma unroll
             for (int i = 0; i < NHL; ++i) {
                 float part[G];
@@ -213,9 +269,9 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
                 } else if constexpr (KV == PKV_BF16) {
 #pragma unroll
                     for (int u = 0; u < G; ++u) {
-                        float t = 0.f;
+                        float t = dot2_bf16_first(qv[i][u][0], kb[buf][j][i][0]);
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kb[buf][j][i][w], t);
+                        for (int w = 1; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kb[buf][j][i][w], t);
                         part[u] = t;
                     }
                 } else {
@@ -226,9 +282,9 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
                     kc[3] = fp8x2_to_bf16x2<true>(kb[buf][j][i][1]);
 #pragma unroll
                     for (int u = 0; u < G; ++u) {
-                        float t = 0.f;
+                        float t = dot2_bf16_first(qv[i][u][0], kc[0]);
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kc[w], t);
+                        for (int w = 1; w < 4; ++w) t = dot2_bf16(qv[i][u][w], kc[w], t);
                         part[u] = t;
                     }
                 }
@@ -324,17 +380,35 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
         }
     };
 
-    // Two-deep register pipeline: loads of iteration it+1 are in flight
-    // while iteration it is computed.
+    // Register pipeline kPagedPipe deep: the loads of the next kPagedPipe-1
+    // iterations are in flight while one iteration is computed.
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    if (niter > 0) issue(0, B0{});
-    for (int it = 0; it < niter; it += 2) {
-        if (it + 1 < niter) issue(it + 1, B1{});
-        compute(it, B0{});
-        if (it + 1 < niter) {
-            if (it + 2 < niter) issue(it + 2, B0{});
-            compute(it + 1, B1{});
+    if constexpr (kPagedPipe == 2) {
+        if (niter > 0) issue(0, B0{});
+        for (int it = 0; it < niter; it += 2) {
+            if (it + 1 < niter) issue(it + 1, B1{});
+            compute(it, B0{});
+            if (it + 1 < niter) {
+                if (it + 2 < niter) issue(it + 2, B0{});
+                compute(it + 1, B1{});
+            }
+        }
+    } else {
+        using B2 = std::integral_constant<int, 2>;
+        if (niter > 0) issue(0, B0{});
+        if (niter > 1) issue(1, B1{});
+        for (int it = 0; it < niter; it += 3) {
+            if (it + 2 < niter) issue(it + 2, B2{});
+            compute(it, B0{});
+            if (it + 1 < niter) {
+                if (it + 3 < niter) issue(it + 3, B0{});
+                compute(it + 1, B1{});
+            }
+            if (it + 2 < niter) {
+                if (it + 4 < niter) issue(it + 4, B1{});
+                compute(it + 2, B2{});
+            }
         }
     }
 
@@ -360,7 +434,7 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
     __syncthreads();
 
     constexpr int CH = D / 4;  // float4 chunks per head
-    const bool direct = a.num_splits == 1;
+    const bool direct = a.num_splits == 1 && !a.force_partial;
     for (int c = threadIdx.x; c < HB * G * CH; c += NW * 64) {
         const int qhl = c / CH;
         const int e4 = c % CH;
@@ -405,6 +479,57 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
                 a.part_ml[prow * 2 + 1] = L;
             }
         }
+    }
+    if (direct || a.counters == nullptr) return;
+
+    // Last-arriver combine.  Every item publishes its partial with a device
+    // scope release (fence + counter increment); the item that brings the
+    // counter to the number of items of this request acquires and combines
+    // them in split order, so the result does not depend on which is last.
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        int* ctr = a.counters + (size_t)b * gridDim.y + hblk;
+        const int prev = atomicAdd(ctr, 1);
+        s_last = prev == items - 1;
+        if (s_last) *ctr = 0;  // all ns items have arrived: ready for the next call
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int ns = items;
+    for (int c = threadIdx.x; c < HB * G * CH; c += NW * 64) {
+        const int qhl = c / CH;
+        const int e4 = c % CH;
+        const int kvh = hblk * HB + qhl / G;
+        const int qh = kvh * G + qhl % G;
+        const size_t base = (size_t)b * a.num_splits * H_q + qh;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + (size_t)s * H_q) * 2]);
+        float L = 0.f;
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) {
+            const size_t prow = base + (size_t)s * H_q;
+            const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
+            const float w = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
+            L += w * ml[1];
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.part_acc + prow * D + e4 * 4);
+            if (w > 0.f) o += w * x;
+        }
+        o *= L > 0.f ? 1.f / L : 0.f;
+        const size_t row = (size_t)b * H_q + qh;
+        if (a.o_f32) *reinterpret_cast<f32x4_t*>(a.o_f32 + row * D + e4 * 4) = o;
+        if (a.o) {
+            if constexpr (C::QF32) {
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.o) + row * D + e4 * 4) = o;
+            } else {
+                u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.o) + row * D + e4 * 4) = h;
+            }
+        }
+        if (a.lse && e4 == 0) a.lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
     }
 }
 

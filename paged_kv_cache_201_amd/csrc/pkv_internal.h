@@ -29,10 +29,14 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
                     PagedGeometry* out);
 
 // Query rows one prefix-kernel workgroup handles, per path.
-constexpr int32_t kDenseRowsPerWg = 128;
-constexpr int32_t kTiledRowsPerWg = 32;
-// Prefix tokens are split in multiples of this many.
+constexpr int32_t kDenseRowsPerWg = 256;
+constexpr int32_t kTiledRowsPerWg = 64;
+// Prefix tokens are split in multiples of this many, at most
+// kMaxPrefixSplitTokens per range (the kernel stages a range's indices in LDS).
 constexpr int32_t kPrefixTokenQuantum = 64;
+constexpr int32_t kMaxPrefixSplitTokens = 1024;
+// Prefix-pass workgroups to aim for.
+constexpr int32_t kPrefixTargetWgs = 256;
 // Paged-pass work items hold a multiple of this many tokens, and at most
 // kMaxSplitTokens (the kernel stages an item's slot indices in LDS).
 constexpr int32_t kSplitQuantum = 64;
@@ -52,14 +56,16 @@ struct pkv_plan {
     int32_t head_blocks;
     int32_t split_tokens, num_splits;
     int64_t num_work_items;
+    int32_t fuse_reduce;      // last-arriver combine inside the paged kernel
     int64_t paged_tokens;     // tokens the paged pass attends (all requests)
     int32_t paged_max_len;
     // prefix pass
     int32_t prefix_rows_per_wg;
     int32_t prefix_split_tokens, prefix_splits;
     // workspace layout (byte offsets; -1 = unused)
+    int64_t ws_counters;      // [B][head_blocks] int32 at offset 0, kept zero between calls
+    int64_t ws_zero_bytes;
     int64_t ws_paged_acc, ws_paged_ml;
     int64_t ws_prefix_acc, ws_prefix_ml;
-    int64_t ws_state_o_p, ws_state_lse_p, ws_state_o_s, ws_state_lse_s;
     int64_t workspace_bytes;
 };

@@ -33,25 +33,33 @@ namespace pkv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPrefixTile = 32;  // tokens per K/V tile
 constexpr float kPrefixLazySlack = 8.0f;
 
-template <int D, int NW>
+// NW waves of 32 query rows each share KT-token K/V tiles through a
+// double-buffered LDS ring: while the waves compute tile n from one buffer,
+// tile n+1 (loaded into registers at the top of the iteration) is written
+// into the other, so one barrier per tile suffices.  The range's slot
+// indices are staged in LDS once, so no tile waits on an index load.
+template <int D, int NW, int KT>
 __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArgs a) {
-    constexpr int KT = kPrefixTile;
     constexpr int KROW = D + 8;    // bf16 per LDS row of K (16-byte pad)
-    constexpr int VROW = KT + 8;   // bf16 per LDS row of V^T
+    // bf16 per LDS row of V^T: a multiple of 4 (8-byte reads) whose dword
+    // pitch times 8 (the row step between neighbouring lanes of a transposed
+    // write) is 16 mod 64 banks, so those writes spread over 8 banks.
+    constexpr int VROW = KT + 4;
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
+    constexpr int NTB = KT / 32;   // 32-token blocks per tile
     constexpr int NT = NW * 64;
-    // K tile: KT * D/8 16-byte chunks; V tile: KT/2 token pairs * D/8 chunks
-    constexpr int KITEMS = KT * D / 8;
-    constexpr int VITEMS = (KT / 2) * (D / 8);
+    constexpr int KITEMS = KT * D / 8;          // 16-byte chunks of a K tile
+    constexpr int VITEMS = (KT / 2) * (D / 8);  // token pairs x chunks of a V tile
     constexpr int KCH = (KITEMS + NT - 1) / NT;
     constexpr int VCH = (VITEMS + NT - 1) / NT;
+    constexpr int KBUF = KT * KROW, VBUF = D * VROW;
 
-    __shared__ uint16_t s_k[KT * KROW];
-    __shared__ uint16_t s_vt[D * VROW];
+    __shared__ uint16_t s_k[2][KBUF];
+    __shared__ uint16_t s_vt[2][VBUF];
+    __shared__ int s_idx[kMaxPrefixSplitTokens];
 
     // XCD-aware placement: workgroups are handed to the 8 XCDs round robin,
     // so give each XCD a contiguous run of logical items; row tiles that read
@@ -65,7 +73,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
     const int split = item / (a.row_tiles * a.H_kv);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;        // which half of the wave
     const int lr = lane & 31;
     const int G = a.G;
@@ -73,7 +81,11 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
     const int M = a.B * G;
     const int ts = split * a.split_tokens;
     const int te = min(ts + a.split_tokens, a.prefix_len);
-    const int ntiles = (te - ts + KT - 1) / KT;
+    const int n_tok = te - ts;
+    const int ntiles = (n_tok + KT - 1) / KT;
+
+    // the range's slot indices, padded with the last one to whole tiles
+    for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = a.prefix_indices[ts + min(i, n_tok - 1)];
 
     // This lane's query row.
     const int r = tile * 32 * NW + wave * 32 + lr;
@@ -96,50 +108,58 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
     const size_t slot_stride = (size_t)a.H_kv * D;
     const size_t head_off = (size_t)g * D;
 
-    // Register staging of the next tile.
     u32x4_t kst[KCH];
     u32x4_t vst[VCH][2];
+    // V item id -> (token pair, 16-byte chunk): 16 neighbouring ids cover 8
+    // chunks of 2 token pairs, so a global load still reads whole 128-byte
+    // lines and a transposed LDS write touches 8 different rows.
+    auto v_item = [&](int id, int& tp, int& ch) {
+        constexpr int NCH = D / 8;
+        const int grp = id / 16, sub = id % 16;
+        const int chg = grp % (NCH / 8);          // which group of 8 chunks
+        tp = (grp / (NCH / 8)) * 2 + sub / 8;
+        ch = chg * 8 + sub % 8;
+    };
     auto load_tile = [&](int n) {
-        const int tb = ts + n * KT;
+        const int tb = n * KT;
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int id = c * NT + threadIdx.x;
             if (KITEMS % NT != 0 && id >= KITEMS) break;
             const int t = id / (D / 8), ch = id % (D / 8);
-            const int slot = a.prefix_indices[min(tb + t, te - 1)];
-            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + (size_t)slot * slot_stride + head_off + ch * 8);
+            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + (size_t)s_idx[tb + t] * slot_stride + head_off + ch * 8);
         }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
             const int id = c * NT + threadIdx.x;
             if (VITEMS % NT != 0 && id >= VITEMS) break;
-            const int tp = id / (D / 8), ch = id % (D / 8);
-            const int s0 = a.prefix_indices[min(tb + 2 * tp, te - 1)];
-            const int s1 = a.prefix_indices[min(tb + 2 * tp + 1, te - 1)];
-            vst[c][0] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s0 * slot_stride + head_off + ch * 8);
-            vst[c][1] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s1 * slot_stride + head_off + ch * 8);
+            int tp, ch;
+            v_item(id, tp, ch);
+            vst[c][0] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s_idx[tb + 2 * tp] * slot_stride + head_off + ch * 8);
+            vst[c][1] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s_idx[tb + 2 * tp + 1] * slot_stride + head_off + ch * 8);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
             const int id = c * NT + threadIdx.x;
             if (KITEMS % NT != 0 && id >= KITEMS) break;
             const int t = id / (D / 8), ch = id % (D / 8);
-            *reinterpret_cast<u32x4_t*>(s_k + t * KROW + ch * 8) = kst[c];
+            *reinterpret_cast<u32x4_t*>(&s_k[buf][t * KROW + ch * 8]) = kst[c];
         }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
             const int id = c * NT + threadIdx.x;
             if (VITEMS % NT != 0 && id >= VITEMS) break;
-            const int tp = id / (D / 8), ch = id % (D / 8);
+            int tp, ch;
+            v_item(id, tp, ch);
             // (token 2tp, token 2tp+1) pairs for each of the 8 head-dim elements
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t lo = __builtin_amdgcn_perm(vst[c][1][w], vst[c][0][w], 0x05040100u);
                 const uint32_t hi = __builtin_amdgcn_perm(vst[c][1][w], vst[c][0][w], 0x07060302u);
-                *reinterpret_cast<uint32_t*>(s_vt + (ch * 8 + 2 * w) * VROW + 2 * tp) = lo;
-                *reinterpret_cast<uint32_t*>(s_vt + (ch * 8 + 2 * w + 1) * VROW + 2 * tp) = hi;
+                *reinterpret_cast<uint32_t*>(&s_vt[buf][(ch * 8 + 2 * w) * VROW + 2 * tp]) = lo;
+                *reinterpret_cast<uint32_t*>(&s_vt[buf][(ch * 8 + 2 * w + 1) * VROW + 2 * tp]) = hi;
             }
         }
     };
@@ -149,31 +169,36 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
     float m = -INFINITY, l = 0.f;
 
-    if (ntiles > 0) load_tile(0);
-    for (int n = 0; n < ntiles; ++n) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (n + 1 < ntiles) load_tile(n + 1);
-
-        // S^T = K . Q^T for this wave's 32 rows
-        f32x16_t s = f32x16_t{};
+    auto compute = [&](int n, int buf, auto tailc) {
+        constexpr bool TAIL = decltype(tailc)::value;
+        // S^T = K . Q^T, one 32x32 block per 32 tokens; lane holds row lr and
+        // tokens tb*32 + (i/4)*8 + h*4 + i%4
+        f32x16_t s[NTB];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const bf16x8_t ka = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(s_k + lr * KROW + ks * 16 + h * 8));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s, 0, 0, 0);
+        for (int tb = 0; tb < NTB; ++tb) {
+            s[tb] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8_t ka = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + h * 8]));
+                s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[tb], 0, 0, 0);
+            }
         }
-        // lane holds row lr, tokens (i/4)*8 + h*4 + i%4
-        const int tb = ts + n * KT;
+        if constexpr (TAIL) {
+            const int valid = n_tok - n * KT;
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (tb * 32 + (i / 4) * 8 + h * 4 + (i % 4) >= valid) s[tb][i] = -INFINITY;
+        }
+        // running max over raw scores (the scale is positive)
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = (i / 4) * 8 + h * 4 + (i % 4);
-            s[i] = (tb + t < te) ? s[i] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
         const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float mn = fmaxf(m, mx);
@@ -183,28 +208,30 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
         }
-        float p[16];
+        const float mneg = (m == -INFINITY) ? 0.f : -m;
         float ps = 0.f;
+        bf16x8_t pb[2 * NTB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            p[i] = (m == -INFINITY) ? 0.f : fast_exp2(s[i] - m);
-            ps += p[i];
-        }
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4_t x;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float p0 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w], a.scale_log2, mneg));
+                    const float p1 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w + 1], a.scale_log2, mneg));
+                    ps += p0 + p1;
+                    x[w] = pack_bf16x2(p0, p1);
+                }
+                pb[tb * 2 + c] = __builtin_bit_cast(bf16x8_t, x);
+            }
         l += ps;
-        bf16x8_t pb[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4_t x;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) x[w] = pack_bf16x2(p[c * 8 + 2 * w], p[c * 8 + 2 * w + 1]);
-            pb[c] = __builtin_bit_cast(bf16x8_t, x);
-        }
-        // O^T += V^T . P^T
+        // O^T += V^T . P^T over 16-token chunks
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const uint16_t* vr = s_vt + (db * 32 + lr) * VROW + c * 16 + h * 4;
+            for (int c = 0; c < 2 * NTB; ++c) {
+                const uint16_t* vr = &s_vt[buf][(db * 32 + lr) * VROW + c * 16 + h * 4];
                 const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vr);
                 const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vr + 8);
                 const u32x4_t x = {x0[0], x0[1], x1[0], x1[1]};
@@ -212,12 +239,31 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
                                                                   acc[db], 0, 0, 0);
             }
         }
+    };
+
+    __syncthreads();  // s_idx ready
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    const bool tail = (n_tok % KT) != 0;
+    for (int n = 0; n < ntiles; ++n) {
+        const int buf = n & 1;
+        if (n + 1 < ntiles) load_tile(n + 1);
+        if (tail && n == ntiles - 1) {
+            compute(n, buf, std::integral_constant<bool, true>{});
+        } else {
+            compute(n, buf, std::integral_constant<bool, false>{});
+        }
+        if (n + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
     // Row totals: the two halves of the wave hold disjoint tokens of a row.
     const float L = l + __shfl_xor(l, 32);
     if (!row_ok) return;
-    const bool direct = a.num_splits == 1;
+    const bool direct = a.num_splits == 1 && !a.force_partial;
     float* out;
     float scale;
     if (direct) {
@@ -249,19 +295,17 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream) {
     const int N = a.row_tiles * a.H_kv * a.num_splits;
     if (N == 0) return hipSuccess;
+    if (a.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
     const int grid = (N + 7) / 8 * 8;
-    if (a.D == 128) {
-        if (rows_per_wg == 128) {
-            prefix_attn_kernel<128, 4><<<grid, 256, 0, stream>>>(a);
-        } else {
-            prefix_attn_kernel<128, 1><<<grid, 64, 0, stream>>>(a);
-        }
+    // DENSE: 8 waves x 32 rows share each tile; CASCADE: 2 waves x 32 rows
+    // (small query tiles, more workgroups per CU).  32-token tiles keep the
+    // 8-wave variant within 256 registers per lane (two waves per SIMD).
+    if (rows_per_wg == kDenseRowsPerWg) {
+        if (a.D == 128) prefix_attn_kernel<128, 8, 32><<<grid, 512, 0, stream>>>(a);
+        else prefix_attn_kernel<64, 8, 32><<<grid, 512, 0, stream>>>(a);
     } else {
-        if (rows_per_wg == 128) {
-            prefix_attn_kernel<64, 4><<<grid, 256, 0, stream>>>(a);
-        } else {
-            prefix_attn_kernel<64, 1><<<grid, 64, 0, stream>>>(a);
-        }
+        if (a.D == 128) prefix_attn_kernel<128, 2, 32><<<grid, 128, 0, stream>>>(a);
+        else prefix_attn_kernel<64, 2, 32><<<grid, 128, 0, stream>>>(a);
     }
     return hipGetLastError();
 }

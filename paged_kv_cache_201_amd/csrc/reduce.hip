@@ -16,6 +16,14 @@
 
 namespace pkv {
 
+constexpr int kReduceBatch = 16;  // partials whose loads are issued together
+
+// Thread (row, e4) owns four consecutive outputs of one row.  The row's
+// partials are the pre_splits prefix partials (if any) followed by its
+// num_splits own ones; every one of them holds a valid (max, sum) pair
+// (empty items record -inf, 0).  They are consumed in batches whose loads
+// are all issued before any is used, so a batch costs one memory round
+// trip; batches are combined in order with the usual rescaling.
 template <int D>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs a) {
     constexpr int CH = D / 4;
@@ -25,24 +33,40 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
     if (row >= a.B * a.H_q) return;
     const int b = row / a.H_q;
     const int qh = row % a.H_q;
-    int ns = a.num_splits;
-    if (a.kv_indptr) {
-        const int len = a.kv_indptr[b + 1] - a.kv_indptr[b] - a.token_offset;
-        ns = len > 0 ? (len + a.split_tokens - 1) / a.split_tokens : 0;
-    }
-    const size_t base = (size_t)b * a.num_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[((base + s) * a.H_q + qh) * 2]);
-    float L = 0.f;
+    const int npre = a.pre_acc ? a.pre_splits : 0;
+    const int total = npre + a.num_splits;
+    float L = 0.f, M = -INFINITY;
     f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const size_t prow = (base + s) * a.H_q + qh;
-            const float ms = a.part_ml[prow * 2];
-            if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - M);
-            L += w * a.part_ml[prow * 2 + 1];
-            o += w * *reinterpret_cast<const f32x4_t*>(a.part_acc + prow * D + e4 * 4);
+    for (int k0 = 0; k0 < total; k0 += kReduceBatch) {
+        f32x2_t ml[kReduceBatch];
+        f32x4_t x[kReduceBatch];
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j) {
+            const int k = k0 + j;
+            if (k < total) {
+                const bool pre = k < npre;
+                const size_t prow = pre ? ((size_t)b * a.pre_splits + k) * a.H_q + qh
+                                        : ((size_t)b * a.num_splits + (k - npre)) * a.H_q + qh;
+                ml[j] = *reinterpret_cast<const f32x2_t*>((pre ? a.pre_ml : a.part_ml) + prow * 2);
+                x[j] = *reinterpret_cast<const f32x4_t*>((pre ? a.pre_acc : a.part_acc) + prow * D + e4 * 4);
+            } else {
+                ml[j] = f32x2_t{-INFINITY, 0.f};
+                x[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j) Mc = fmaxf(Mc, ml[j][0]);
+        if (Mc == -INFINITY) continue;
+        const float c = M == -INFINITY ? 0.f : exp2f(M - Mc);  // rescale what is summed so far
+        L *= c;
+        o *= c;
+        M = Mc;
+#pragma unroll
+        for (int j = 0; j < kReduceBatch; ++j) {
+            const float w = ml[j][0] == -INFINITY ? 0.f : exp2f(ml[j][0] - M);
+            L += w * ml[j][1];
+            if (w > 0.f) o += w * x[j];  // an empty item's values are never read into the sum
         }
     }
     o *= L > 0.f ? 1.f / L : 0.f;

@@ -236,12 +236,14 @@ def test_c4_full_sampled():
     dict(B=3, H_q=16, H_kv=2, d=128, own_len=(100, 900), q_dtype="f32", kv_dtype="f32", page_size=16),
     dict(B=1, H_q=32, H_kv=4, d=128, own_len=(1, 1), q_dtype="bf16", kv_dtype="bf16", page_size=16),
 ])
-@pytest.mark.parametrize("splits", ["one", "many"])
+@pytest.mark.parametrize("splits", ["one", "many", "many-separate-reduce"])
 def test_edge_shapes(case, splits):
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_decode_batch(seed=sum(case["own_len"]) + case["H_q"], pool_factor=2, **case)
-    tuning = dict(min_split_tokens=64, target_workgroups=100000) if splits == "many" else \
-        dict(min_split_tokens=2048, target_workgroups=1)
+    tuning = {"one": dict(min_split_tokens=2048, target_workgroups=1),
+              "many": dict(min_split_tokens=64, target_workgroups=100000, fuse_split_reduce=1),
+              "many-separate-reduce": dict(min_split_tokens=64, target_workgroups=100000,
+                                           fuse_split_reduce=0)}[splits]
     o_ref, lse_ref = ob.batch_reference(b)
     say(f"edge {case} splits={splits}")
     o, lse, plan = run_paged(DeviceBatch, b, tuning=tuning)
@@ -249,6 +251,56 @@ def test_edge_shapes(case, splits):
     if case["kv_dtype"] != "f32":
         of, lf, _ = run_paged(DeviceBatch, b, tuning=tuning, want_f32=True)
         check_close(case["kv_dtype"], of, lf, o_ref, lse_ref, f"edge f32-out {case}")
+
+
+@pytest.mark.parametrize("fuse", [0, 1])
+def test_split_combine_variants_agree_and_leave_counters_zero(fuse):
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c2", B=5, own_len=(1, 5000), page_size=16)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(tuning=dict(fuse_split_reduce=fuse, min_split_tokens=256, target_workgroups=4096))
+    assert plan.info["num_splits"] > 4
+    assert (plan.info["workspace_zero_bytes"] > 0) == bool(fuse)
+    ws = db.workspace(plan)
+    say(f"split combine fuse={fuse}")
+    o1, l1 = db.step(plan, ws=ws)
+    o2, l2 = db.step(plan, ws=ws)
+    torch.cuda.synchronize()
+    check_close("bf16", o1, l1, o_ref, lse_ref, f"fuse={fuse}")
+    assert same_bits(o1, o2) and same_bits(l1, l2)
+    nz = plan.info["workspace_zero_bytes"]
+    if nz:
+        assert int(ws[:nz].count_nonzero()) == 0, "arrival counters not reset"
+    other = db.plan(tuning=dict(fuse_split_reduce=1 - fuse, min_split_tokens=256, target_workgroups=4096))
+    o3, l3 = db.step(other)
+    torch.cuda.synchronize()
+    assert same_bits(o1, o3) and same_bits(l1, l3), "fused and separate combine differ"
+
+
+@pytest.mark.parametrize("fuse", [0, 1])
+def test_empty_requests_with_many_splits(fuse):
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    lens = [0, 1500, 0, 63, 64, 65, 0, 1000]
+    b = make_decode_batch(seed=8, B=8, H_q=32, H_kv=8, d=128, own_len=(0, 0), own_lens=lens, page_size=16)
+    o_ref, lse_ref = ob.batch_reference(b)
+    tune = dict(min_split_tokens=64, target_workgroups=100000, fuse_split_reduce=fuse)
+    say(f"empty requests, many splits, fuse={fuse}")
+    o, lse, plan = run_paged(DeviceBatch, b, tuning=tune)
+    assert plan.info["num_splits"] > 1
+    check_close("bf16", o, lse, o_ref, lse_ref, "empty requests")
+    assert torch.isinf(lse[0]).all() and not o[0].float().abs().sum()
+    # a shared prefix whose suffixes are partly empty, on every path
+    c = make_decode_batch(seed=9, B=8, H_q=32, H_kv=8, d=128, own_len=(0, 0), prefix_len=256, own_lens=lens,
+                          page_size=16)
+    o_ref, lse_ref = ob.batch_reference(c)
+    db = DeviceBatch.from_batch(c)
+    for force in (0, 1, 2):
+        plan = db.plan(shared_prefix_len=256, force_path=force, tuning=tune)
+        say(f"empty suffixes force={force} fuse={fuse}")
+        o, lse = db.step(plan)
+        torch.cuda.synchronize()
+        check_close("bf16", o, lse, o_ref, lse_ref, f"empty suffixes path {force}")
 
 
 def test_run_twice_bitwise_identical():

@@ -137,6 +137,7 @@ def make_decode_batch(
     perm: str = "random",
     perm_seed: Optional[int] = None,
     device: Optional[str] = None,
+    own_lens: Optional[list] = None,
 ) -> DecodeBatch:
     """Draw one batch and lay it out in a paged pool.
 
@@ -144,12 +145,16 @@ def make_decode_batch(
     uniformly from the integers ``lo..hi`` inclusive.  ``pool_pages`` fixes the
     pool size in pages; otherwise the pool holds ``pool_factor`` times the live
     pages.  ``perm`` is ``"random"`` or ``"identity"`` (pages in allocation
-    order: the contiguous control).
+    order: the contiguous control).  ``own_lens`` fixes every request's own
+    token count instead (the draw still happens, keeping the stream aligned).
     """
     assert H_q % H_kv == 0 and layout in ("shared", "unique")
     rng = np.random.default_rng(seed)
     lo, hi = own_len
     own = rng.integers(lo, hi + 1, size=B).astype(np.int64)
+    if own_lens is not None:
+        own = np.asarray(own_lens, np.int64)
+        assert own.shape == (B,)
     own_offsets = np.zeros(B + 1, np.int64)
     np.cumsum(own, out=own_offsets[1:])
     seq_lens = (own + prefix_len).astype(np.int32)
