@@ -111,6 +111,9 @@ typedef struct pkv_tuning {
     int32_t min_split_tokens;   /* paged pass: smallest token range per workgroup */
     int32_t fuse_split_reduce;  /* 1: the last work item of a request combines its splits
                                    (one kernel per paged pass); 0: a separate reduce kernel */
+    int32_t concurrent_prefix;  /* 1: pkv_decode_step runs the prefix pass on a library-owned
+                                   side stream (same priority) concurrently with the suffix
+                                   pass, joined by events before the combine; 0: one stream */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */
@@ -264,9 +267,14 @@ pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
  * One whole decode step as the plan chose it: PAGED is one paged call; CASCADE
  * and DENSE run the prefix pass over kv_indices[kv_indptr[0] ..
  * + prefix_tokens) (request 0's shared pages), the paged pass over each
- * request's suffix, and the merge, with the partial states kept in the
- * workspace.  Arguments as in pkv_paged_decode_attn; o is required, lse is
- * nullable.
+ * request's suffix, and one kernel that combines both passes' partial
+ * states (kept in the workspace).  With concurrent_prefix set in the plan's
+ * tuning, the prefix pass is enqueued on a side stream that the library
+ * creates once per device (default priority), forked from and joined back
+ * to `stream` with events, so the MFMA-bound prefix pass and the
+ * bandwidth-bound suffix pass overlap; the call is still ordered on
+ * `stream` as a whole and can be captured into a graph.  Arguments as in
+ * pkv_paged_decode_attn; o is required, lse is nullable.
  */
 pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                            const int32_t* kv_indptr, const int32_t* kv_indices,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
+#include <unordered_map>
 
 #include "kernels.h"
 #include "pkv.h"
@@ -50,6 +52,32 @@ T* ws_at(void* ws, int64_t off) {
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_EHIP; }
+
+// Per-device side stream and fork/join events for running the prefix pass
+// concurrently with the suffix pass.  Created on first use, default
+// priority, kept until the process ends.  The mutex also serialises the
+// record/wait sequence so that two host threads never interleave their use
+// of the shared events.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::unordered_map<int, SideStream> g_side;
+
+hipError_t side_stream_locked(SideStream** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    SideStream& ss = g_side[dev];
+    if (!ss.stream) {
+        if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
 
 // The paged pass over tokens [plan.prefix_tokens, L_b) of every request.
 pkv::PagedArgs paged_args(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
@@ -217,12 +245,26 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
     pa.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
     pa.force_partial = 1;
-    if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
     pkv::PagedArgs sa = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
     sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
     sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
     sa.force_partial = 1;
-    if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    if (pl->concurrent_prefix) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream* ss = nullptr;
+        if (side_stream_locked(&ss) != hipSuccess) return PKV_EHIP;
+        // fork: the side stream starts after everything already on `s`
+        if (hipEventRecord(ss->fork, s) != hipSuccess) return PKV_EHIP;
+        if (hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) return PKV_EHIP;
+        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, ss->stream) != hipSuccess) return PKV_EHIP;
+        if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+        // join: the combine on `s` waits for the prefix pass
+        if (hipEventRecord(ss->join, ss->stream) != hipSuccess) return PKV_EHIP;
+        if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return PKV_EHIP;
+    } else {
+        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
+        if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    }
     pkv::SplitReduceArgs r{};
     r.num_splits = pl->num_splits;
     r.B = pl->B;

@@ -36,6 +36,12 @@ __device__ __forceinline__ T load_global(gbytes_t p) {
     return *(const T __attribute__((address_space(1)))*)p;
 }
 
+// Streaming load: the data is used once, so mark it non-temporal.
+template <typename T>
+__device__ __forceinline__ T load_global_stream(gbytes_t p) {
+    return __builtin_nontemporal_load((const T __attribute__((address_space(1)))*)p);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

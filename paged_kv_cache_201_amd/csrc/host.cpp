@@ -55,8 +55,11 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
     const int32_t rs = 64 / lph;
     // Per-lane registers: q and the output accumulator both hold nhl*G*epl
     // values; 64 keeps two waves per SIMD.
+#ifndef PKV_LANE_VALUES
+#define PKV_LANE_VALUES 64
+#endif
     for (int32_t nhl = 2; nhl >= 1; --nhl) {
-        if (nhl * group * epl <= 64 && num_kv_heads % (rs * nhl) == 0) {
+        if (nhl * group * epl <= PKV_LANE_VALUES && num_kv_heads % (rs * nhl) == 0) {
             *out = PagedGeometry{epl, lph, rs, nhl, 1, rs * nhl};
             return true;
         }
@@ -97,6 +100,7 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->target_workgroups = 1024;
     out->min_split_tokens = 256;
     out->fuse_split_reduce = 0;  // measured: the device-scope release per item costs more than a launch
+    out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -155,7 +159,8 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         pkv_tuning_defaults(&tu);
     }
     if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
-        tu.min_split_tokens < 1 || tu.fuse_split_reduce < 0 || tu.fuse_split_reduce > 1)
+        tu.min_split_tokens < 1 || tu.fuse_split_reduce < 0 || tu.fuse_split_reduce > 1 ||
+        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1)
         return PKV_EINVAL;
 
     // Checks, in the same order as the planner's reference statement.
@@ -231,6 +236,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->prefix_tokens = (int32_t)prefix_tokens;
     pl->geo = geo;
     pl->head_blocks = H_kv / geo.hb;
+    pl->concurrent_prefix = tu.concurrent_prefix;
 
     // Paged pass: cut every request's attended tokens [prefix_tokens, L_b)
     // into work items of split_tokens logical positions.

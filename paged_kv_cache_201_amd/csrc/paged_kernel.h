@@ -62,7 +62,13 @@ struct LoadVec<2> {
     using T = u32x2_t;
 };
 
-constexpr int kPagedWaves = 4;
+#ifndef PKV_PAGED_WAVES
+#define PKV_PAGED_WAVES 4
+#endif
+#ifndef PKV_STREAM_LOADS
+#define PKV_STREAM_LOADS 1  // K/V rows are read once per step: non-temporal loads
+#endif
+constexpr int kPagedWaves = PKV_PAGED_WAVES;
 #ifndef PKV_PAGED_PIPE
 #define PKV_PAGED_PIPE 2
 #endif
@@ -242,8 +248,13 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
             }
 #pragma unroll
             for (int i = 0; i < NHL; ++i) {
-                kb[buf][j][i] = load_global<LV>(kr + loff[i]);
-                vb[buf][j][i] = load_global<LV>(vr + loff[i]);
+                if constexpr (PKV_STREAM_LOADS) {
+                    kb[buf][j][i] = load_global_stream<LV>(kr + loff[i]);
+                    vb[buf][j][i] = load_global_stream<LV>(vr + loff[i]);
+                } else {
+                    kb[buf][j][i] = load_global<LV>(kr + loff[i]);
+                    vb[buf][j][i] = load_global<LV>(vr + loff[i]);
+                }
             }
         }
     };

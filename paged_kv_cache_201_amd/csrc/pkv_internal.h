@@ -29,7 +29,7 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
                     PagedGeometry* out);
 
 // Query rows one prefix-kernel workgroup handles, per path.
-constexpr int32_t kDenseRowsPerWg = 256;
+constexpr int32_t kDenseRowsPerWg = 128;
 constexpr int32_t kTiledRowsPerWg = 64;
 // Prefix tokens are split in multiples of this many, at most
 // kMaxPrefixSplitTokens per range (the kernel stages a range's indices in LDS).
@@ -57,6 +57,7 @@ struct pkv_plan {
     int32_t split_tokens, num_splits;
     int64_t num_work_items;
     int32_t fuse_reduce;      // last-arriver combine inside the paged kernel
+    int32_t concurrent_prefix; // prefix pass on a side stream in decode_step
     int64_t paged_tokens;     // tokens the paged pass attends (all requests)
     int32_t paged_max_len;
     // prefix pass

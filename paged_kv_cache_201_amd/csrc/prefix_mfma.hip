@@ -17,8 +17,12 @@
 // the lane 32 apart.  The exponentiated scores, converted to bf16, are
 // already in the B-operand layout of the second product O^T += V^T . P^T
 // (both operands' k-slots are taken in the same token order), so P never
-// leaves registers.  V is written transposed into LDS so that each lane reads
-// eight consecutive tokens of one head-dim column.
+// leaves registers.  K and V are both kept row-major in LDS; the V^T operand
+// (eight tokens of one head-dim column per lane) is read with gfx950's
+// transposing LDS read, ds_read_b64_tr_b16: within a group of 16 lanes, lane
+// 4c+d receives element d of the 64-bit values read by lanes c, c+4, c+8,
+// c+12, so lanes reading four tokens x four column chunks hand each lane
+// four tokens of one column.
 //
 // Softmax state per row is (m, l) in exp2 units with the same lazily raised
 // maximum as the paged kernel; the partial or final result is written in the
@@ -41,24 +45,20 @@ constexpr float kPrefixLazySlack = 8.0f;
 // into the other, so one barrier per tile suffices.  The range's slot
 // indices are staged in LDS once, so no tile waits on an index load.
 template <int D, int NW, int KT>
-__global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArgs a) {
-    constexpr int KROW = D + 8;    // bf16 per LDS row of K (16-byte pad)
-    // bf16 per LDS row of V^T: a multiple of 4 (8-byte reads) whose dword
-    // pitch times 8 (the row step between neighbouring lanes of a transposed
-    // write) is 16 mod 64 banks, so those writes spread over 8 banks.
-    constexpr int VROW = KT + 4;
+__global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_kernel(const PrefixArgs a) {
+    // bf16 per LDS row of K and of V: a 32-byte pad makes the row pitch 8
+    // banks (mod 64), so the row-gathering operand reads are conflict free
+    constexpr int KROW = D + 16;
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
     constexpr int NTB = KT / 32;   // 32-token blocks per tile
     constexpr int NT = NW * 64;
-    constexpr int KITEMS = KT * D / 8;          // 16-byte chunks of a K tile
-    constexpr int VITEMS = (KT / 2) * (D / 8);  // token pairs x chunks of a V tile
+    constexpr int KITEMS = KT * D / 8;          // 16-byte chunks of a K (or V) tile
     constexpr int KCH = (KITEMS + NT - 1) / NT;
-    constexpr int VCH = (VITEMS + NT - 1) / NT;
-    constexpr int KBUF = KT * KROW, VBUF = D * VROW;
+    constexpr int KBUF = KT * KROW;
 
     __shared__ uint16_t s_k[2][KBUF];
-    __shared__ uint16_t s_vt[2][VBUF];
+    __shared__ uint16_t s_v[2][KBUF];
     __shared__ int s_idx[kMaxPrefixSplitTokens];
 
     // XCD-aware placement: workgroups are handed to the 8 XCDs round robin,
@@ -108,18 +108,7 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
     const size_t slot_stride = (size_t)a.H_kv * D;
     const size_t head_off = (size_t)g * D;
 
-    u32x4_t kst[KCH];
-    u32x4_t vst[VCH][2];
-    // V item id -> (token pair, 16-byte chunk): 16 neighbouring ids cover 8
-    // chunks of 2 token pairs, so a global load still reads whole 128-byte
-    // lines and a transposed LDS write touches 8 different rows.
-    auto v_item = [&](int id, int& tp, int& ch) {
-        constexpr int NCH = D / 8;
-        const int grp = id / 16, sub = id % 16;
-        const int chg = grp % (NCH / 8);          // which group of 8 chunks
-        tp = (grp / (NCH / 8)) * 2 + sub / 8;
-        ch = chg * 8 + sub % 8;
-    };
+    u32x4_t kst[KCH], vst[KCH];
     auto load_tile = [&](int n) {
         const int tb = n * KT;
 #pragma unroll
@@ -127,16 +116,9 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
             const int id = c * NT + threadIdx.x;
             if (KITEMS % NT != 0 && id >= KITEMS) break;
             const int t = id / (D / 8), ch = id % (D / 8);
-            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + (size_t)s_idx[tb + t] * slot_stride + head_off + ch * 8);
-        }
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (VITEMS % NT != 0 && id >= VITEMS) break;
-            int tp, ch;
-            v_item(id, tp, ch);
-            vst[c][0] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s_idx[tb + 2 * tp] * slot_stride + head_off + ch * 8);
-            vst[c][1] = *reinterpret_cast<const u32x4_t*>(vpool + (size_t)s_idx[tb + 2 * tp + 1] * slot_stride + head_off + ch * 8);
+            const size_t off = (size_t)s_idx[tb + t] * slot_stride + head_off + ch * 8;
+            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + off);
+            vst[c] = *reinterpret_cast<const u32x4_t*>(vpool + off);
         }
     };
     auto store_tile = [&](int buf) {
@@ -146,23 +128,16 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
             if (KITEMS % NT != 0 && id >= KITEMS) break;
             const int t = id / (D / 8), ch = id % (D / 8);
             *reinterpret_cast<u32x4_t*>(&s_k[buf][t * KROW + ch * 8]) = kst[c];
-        }
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (VITEMS % NT != 0 && id >= VITEMS) break;
-            int tp, ch;
-            v_item(id, tp, ch);
-            // (token 2tp, token 2tp+1) pairs for each of the 8 head-dim elements
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t lo = __builtin_amdgcn_perm(vst[c][1][w], vst[c][0][w], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(vst[c][1][w], vst[c][0][w], 0x07060302u);
-                *reinterpret_cast<uint32_t*>(&s_vt[buf][(ch * 8 + 2 * w) * VROW + 2 * tp]) = lo;
-                *reinterpret_cast<uint32_t*>(&s_vt[buf][(ch * 8 + 2 * w + 1) * VROW + 2 * tp]) = hi;
-            }
+            *reinterpret_cast<u32x4_t*>(&s_v[buf][t * KROW + ch * 8]) = vst[c];
         }
     };
+    // Transposed-read address of this lane for the V^T operand: lane group
+    // (h, dh) of 16 lanes covers columns db*32 + dh*16 .. +15 and tokens
+    // c*16 + h*4 (+8 for the second read); lane s of the group reads token
+    // s/4 of those four at columns 4*(s%4) .. +3 of the group's sixteen.
+    const int tr_s = lane & 15;
+    const int tr_dh = (lane >> 4) & 1;
+    const int tr_off = (tr_s >> 2) * KROW + tr_dh * 16 + (tr_s & 3) * 4 + h * 4 * KROW;
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -231,10 +206,14 @@ __global__ void __launch_bounds__(NW * 64, 1) prefix_attn_kernel(const PrefixArg
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int c = 0; c < 2 * NTB; ++c) {
-                const uint16_t* vr = &s_vt[buf][(db * 32 + lr) * VROW + c * 16 + h * 4];
-                const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vr);
-                const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vr + 8);
-                const u32x4_t x = {x0[0], x0[1], x1[0], x1[1]};
+                typedef short v4s_t __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+                const uint16_t* vr = &s_v[buf][(c * 16) * KROW + db * 32 + tr_off];
+                const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)vr);
+                const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vr + 8 * KROW));
+                const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0);
+                const u32x2_t y1 = __builtin_bit_cast(u32x2_t, x1);
+                const u32x4_t x = {y0[0], y0[1], y1[0], y1[1]};
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pb[c],
                                                                   acc[db], 0, 0, 0);
             }
@@ -297,12 +276,13 @@ hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t 
     if (N == 0) return hipSuccess;
     if (a.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
     const int grid = (N + 7) / 8 * 8;
-    // DENSE: 8 waves x 32 rows share each tile; CASCADE: 2 waves x 32 rows
-    // (small query tiles, more workgroups per CU).  32-token tiles keep the
-    // 8-wave variant within 256 registers per lane (two waves per SIMD).
+    // DENSE: 4 waves x 32 rows share each tile; CASCADE: 2 waves x 32 rows
+    // (small query tiles, more workgroups per CU).  Both stay within 256
+    // registers per lane, so a prefix workgroup and a paged workgroup can be
+    // resident on one CU together.
     if (rows_per_wg == kDenseRowsPerWg) {
-        if (a.D == 128) prefix_attn_kernel<128, 8, 32><<<grid, 512, 0, stream>>>(a);
-        else prefix_attn_kernel<64, 8, 32><<<grid, 512, 0, stream>>>(a);
+        if (a.D == 128) prefix_attn_kernel<128, 4, 32><<<grid, 256, 0, stream>>>(a);
+        else prefix_attn_kernel<64, 4, 32><<<grid, 256, 0, stream>>>(a);
     } else {
         if (a.D == 128) prefix_attn_kernel<128, 2, 32><<<grid, 128, 0, stream>>>(a);
         else prefix_attn_kernel<64, 2, 32><<<grid, 128, 0, stream>>>(a);

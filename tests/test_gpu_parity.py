@@ -303,6 +303,33 @@ def test_empty_requests_with_many_splits(fuse):
         check_close("bf16", o, lse, o_ref, lse_ref, f"empty suffixes path {force}")
 
 
+def test_concurrent_prefix_pass_matches_single_stream():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_config("c3", B=64, own_len=(0, 300))
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    outs = []
+    for conc in (0, 1):
+        for force in (1, 2):
+            plan = db.plan(shared_prefix_len=b.prefix_len, force_path=force, tuning=dict(concurrent_prefix=conc))
+            say(f"concurrent_prefix={conc} force={force}")
+            o, lse = db.step(plan)
+            torch.cuda.synchronize()
+            check_close("bf16", o, lse, o_ref, lse_ref, f"conc={conc} path={force}")
+            outs.append((o, lse))
+    assert same_bits(outs[0][0], outs[2][0]) and same_bits(outs[1][0], outs[3][0])
+    # on a non-default caller stream, with work queued ahead of the step
+    side = torch.cuda.Stream()
+    plan = db.plan(shared_prefix_len=b.prefix_len, force_path=2, tuning=dict(concurrent_prefix=1))
+    with torch.cuda.stream(side):
+        q_saved = db.q.clone()
+        db.q.mul_(1.0)  # queued work the step must wait for
+        o, lse = db.step(plan, stream=side)
+    torch.cuda.synchronize()
+    assert same_bits(o, outs[3][0]) and same_bits(lse, outs[3][1])
+    assert torch.equal(q_saved, db.q)
+
+
 def test_run_twice_bitwise_identical():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_config("c3", B=40, own_len=(10, 300))
