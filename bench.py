@@ -15,6 +15,7 @@ heads, head_dim 128, 4096 tokens each, bf16, token-flat indices at page size
 reported under ``extra``.  Prints one JSON line on stdout.
 """
 import argparse
+import itertools
 import json
 import math
 import os
@@ -144,6 +145,45 @@ def read_ceiling(steps=20, warmup=5, gib=4):
     return best
 
 
+def host_timing(reps=21):
+    """Median host time (us) of page-table lowering (page sizes 1 and 16) and
+    planning through the C ABI, at 64 .. 2,097,152 tokens over 32 requests."""
+    import ctypes
+    import numpy as np
+    import paged_kv_cache_201_amd as pkv
+    lib = pkv._lib
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    out = {}
+    for n, p in itertools.product((64, 1024, 16384, 262144, 2097152), (1, 16)):
+        B = 32
+        lens = np.full(B, n // B, np.int32)
+        npg = (lens + p - 1) // p
+        page_indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+        pages = np.random.default_rng(n).permutation(int(npg.sum())).astype(np.int32)
+        kv_indptr = np.zeros(B + 1, np.int32)
+        kv_indices = np.zeros(n, np.int32)
+        args = (B, p, page_indptr.ctypes.data_as(i32p), pages.ctypes.data_as(i32p), lens.ctypes.data_as(i32p),
+                kv_indptr.ctypes.data_as(i32p), kv_indices.ctypes.data_as(i32p), ctypes.c_int64(n))
+        tl = []
+        for _ in range(reps):
+            t = time.perf_counter_ns()
+            st = lib.pkv_lower_page_table(*args)
+            tl.append((time.perf_counter_ns() - t) / 1e3)
+            assert st == 0
+        prob = pkv.pkv_problem(B, 32, 8, 128, pkv.DTYPE_CODES["bf16"], pkv.DTYPE_CODES["bf16"], p,
+                               kv_indptr.ctypes.data_as(i32p), 0, -1)
+        tp = []
+        for _ in range(reps):
+            h = ctypes.c_void_p()
+            t = time.perf_counter_ns()
+            st = lib.pkv_plan_create(ctypes.byref(prob), None, ctypes.byref(h))
+            tp.append((time.perf_counter_ns() - t) / 1e3)
+            assert st == 0
+            lib.pkv_plan_destroy(h)
+        out[f"{n}_p{p}"] = dict(lower_us=sorted(tl)[reps // 2], plan_us=sorted(tp)[reps // 2])
+    return out
+
+
 def cpu_baseline(batch, reps=3):
     """The oracle, as it stands, on the same workload on the host cores."""
     from oracle import batch as ob
@@ -212,6 +252,9 @@ def main():
             log(f"bench {name}")
             extra[name] = bench_prefix_config(name, args.steps, args.warmup)
             log(json.dumps(extra[name]))
+
+    extra["host_us"] = host_timing()
+    log(f"host timing {json.dumps(extra['host_us'])}")
 
     cpu = None
     if not args.no_cpu:

@@ -114,6 +114,10 @@ typedef struct pkv_tuning {
     int32_t concurrent_prefix;  /* 1: pkv_decode_step runs the prefix pass on a library-owned
                                    side stream (same priority) concurrently with the suffix
                                    pass, joined by events before the combine; 0: one stream */
+    int32_t prefix_target_workgroups; /* prefix pass: workgroups to aim for (query tiles x
+                                         prefix ranges) */
+    int32_t min_prefix_split_tokens;  /* prefix pass: smallest prefix range per workgroup
+                                         (rounded up to a multiple of 64) */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */

@@ -101,6 +101,8 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->min_split_tokens = 256;
     out->fuse_split_reduce = 0;  // measured: the device-scope release per item costs more than a launch
     out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
+    out->prefix_target_workgroups = 256;
+    out->min_prefix_split_tokens = 256;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -117,10 +119,13 @@ pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t*
         if (n < 0 || L < 0) return PKV_EINVAL;
         if (n != ceil_div(L, page_size)) return PKV_ERANGE;
         if (n > 0 && !page_indices) return PKV_EINVAL;
+        int32_t lo = INT32_MAX, hi = 0;
+        const int32_t* pages = page_indices + page_indptr[b];
         for (int64_t j = 0; j < n; ++j) {
-            const int64_t page = page_indices[page_indptr[b] + j];
-            if (page < 0 || page * page_size + (page_size - 1) > INT32_MAX) return PKV_ERANGE;
+            lo = std::min(lo, pages[j]);
+            hi = std::max(hi, pages[j]);
         }
+        if (n > 0 && (lo < 0 || (int64_t)hi * page_size + (page_size - 1) > INT32_MAX)) return PKV_ERANGE;
         total += L;
     }
     if (total > INT32_MAX || total > kv_indices_capacity) return PKV_ERANGE;
@@ -130,8 +135,20 @@ pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t*
     for (int32_t b = 0; b < batch; ++b) {
         const int32_t* pages = page_indices + page_indptr[b];
         const int32_t L = seq_lens[b];
-        for (int32_t t = 0; t < L; ++t)
-            kv_indices_out[pos++] = pages[t / page_size] * page_size + t % page_size;
+        if (page_size == 1) {  // one token per page: the slots are the pages
+            std::memcpy(kv_indices_out + pos, pages, (size_t)L * sizeof(int32_t));
+            pos += L;
+            kv_indptr_out[b + 1] = (int32_t)pos;
+            continue;
+        }
+        // page by page: slots page*p .. page*p + (tokens on that page) - 1
+        for (int32_t t0 = 0, j = 0; t0 < L; t0 += page_size, ++j) {
+            const int32_t base = pages[j] * page_size;
+            const int32_t cnt = std::min(page_size, L - t0);
+            int32_t* dst = kv_indices_out + pos;
+            for (int32_t i = 0; i < cnt; ++i) dst[i] = base + i;
+            pos += cnt;
+        }
         kv_indptr_out[b + 1] = (int32_t)pos;
     }
     return PKV_OK;
@@ -160,7 +177,8 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     }
     if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
         tu.min_split_tokens < 1 || tu.fuse_split_reduce < 0 || tu.fuse_split_reduce > 1 ||
-        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1)
+        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.prefix_target_workgroups < 1 ||
+        tu.min_prefix_split_tokens < 1)
         return PKV_EINVAL;
 
     // Checks, in the same order as the planner's reference statement.
@@ -264,9 +282,9 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->prefix_splits = 0;
     if (path != PKV_PATH_PAGED) {
         const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
-        const int64_t want = std::max<int64_t>(1, ceil_div(pkv::kPrefixTargetWgs, tiles));
+        const int64_t want = std::max<int64_t>(1, ceil_div(tu.prefix_target_workgroups, tiles));
         int64_t ps = align_up(ceil_div(prefix_tokens, want), pkv::kPrefixTokenQuantum);
-        ps = std::max<int64_t>(ps, 4 * pkv::kPrefixTokenQuantum);
+        ps = std::max<int64_t>(ps, align_up(tu.min_prefix_split_tokens, pkv::kPrefixTokenQuantum));
         ps = std::min<int64_t>(ps, pkv::kMaxPrefixSplitTokens);
         pl->prefix_split_tokens = (int32_t)ps;
         pl->prefix_splits = (int32_t)ceil_div(prefix_tokens, ps);

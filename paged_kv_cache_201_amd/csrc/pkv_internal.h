@@ -35,8 +35,6 @@ constexpr int32_t kTiledRowsPerWg = 64;
 // kMaxPrefixSplitTokens per range (the kernel stages a range's indices in LDS).
 constexpr int32_t kPrefixTokenQuantum = 64;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
-// Prefix-pass workgroups to aim for.
-constexpr int32_t kPrefixTargetWgs = 256;
 // Paged-pass work items hold a multiple of this many tokens, and at most
 // kMaxSplitTokens (the kernel stages an item's slot indices in LDS).
 constexpr int32_t kSplitQuantum = 64;

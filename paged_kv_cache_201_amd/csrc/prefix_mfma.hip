@@ -148,16 +148,22 @@ __global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_kernel
         constexpr bool TAIL = decltype(tailc)::value;
         // S^T = K . Q^T, one 32x32 block per 32 tokens; lane holds row lr and
         // tokens tb*32 + (i/4)*8 + h*4 + i%4
+        // two independent accumulation chains (even and odd k-steps) so that
+        // consecutive MFMAs do not wait on each other's results
         f32x16_t s[NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            s[tb] = f32x16_t{};
+            f32x16_t s_even = f32x16_t{}, s_odd = f32x16_t{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8_t ka = __builtin_bit_cast(
+            for (int ks = 0; ks < NKS; ks += 2) {
+                const bf16x8_t ka0 = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + h * 8]));
-                s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[tb], 0, 0, 0);
+                const bf16x8_t ka1 = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + 16 + h * 8]));
+                s_even = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], s_even, 0, 0, 0);
+                s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], s_odd, 0, 0, 0);
             }
+            s[tb] = s_even + s_odd;
         }
         if constexpr (TAIL) {
             const int valid = n_tok - n * KT;

@@ -241,8 +241,8 @@ def test_edge_shapes(case, splits):
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_decode_batch(seed=sum(case["own_len"]) + case["H_q"], pool_factor=2, **case)
     tuning = {"one": dict(min_split_tokens=2048, target_workgroups=1),
-              "many": dict(min_split_tokens=64, target_workgroups=100000, fuse_split_reduce=1),
-              "many-separate-reduce": dict(min_split_tokens=64, target_workgroups=100000,
+              "many": dict(min_split_tokens=16, target_workgroups=100000, fuse_split_reduce=1),
+              "many-separate-reduce": dict(min_split_tokens=16, target_workgroups=100000,
                                            fuse_split_reduce=0)}[splits]
     o_ref, lse_ref = ob.batch_reference(b)
     say(f"edge {case} splits={splits}")

@@ -173,7 +173,7 @@ def test_split_partition_covers_every_token_once():
         if info is None:
             continue
         C, S = info["split_tokens"], info["num_splits"]
-        assert C % 64 == 0 and C <= max(2048, 64)
+        assert C % 16 == 0 and C <= 2048
         for L in lens:
             n = int(L) - info["prefix_tokens"]
             covered = sum(max(0, min((s + 1) * C, n) - s * C) for s in range(S))
