@@ -145,6 +145,117 @@ def read_ceiling(steps=20, warmup=5, gib=4):
     return best
 
 
+# ------------------------------------------------------------ profiles --
+
+CSRC = os.path.join(ROOT, "paged_kv_cache_201_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_split_kernel.llama_layer_p1.traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 over the library sources and headers: counters taken before a
+    change of any of them no longer describe the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".h", ".hip", ".cpp")):
+                h.update(name.encode())
+                h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def _short(name):
+    name = name.replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(prof_dir):
+    """Markdown table of kernel durations from a rocprofv3 --kernel-trace csv run."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for f in glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    agg = {}
+    for r in rows:
+        n = _short(r["Kernel_Name"])
+        wg = int(r["Workgroup_Size_X"])
+        key = (n, int(r["Grid_Size_X"]) // wg, int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]), wg)
+        agg.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | workgroups (x,y,z) | threads | calls | mean us | median us | min us |",
+           "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{k[0]}` | {k[1]},{k[2]},{k[3]} | {k[4]} | {len(v)} | {statistics.mean(v):.1f} | "
+                   f"{statistics.median(v):.1f} | {min(v):.1f} |")
+    return "\n".join(out), agg
+
+
+def pmc_per_dispatch(prof_dir, counter):
+    """{(kernel, grid size): [counter value per dispatch]} from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(prof_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            out.setdefault(key, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
+    """Turn the rocprofv3 output of the three profiling runs of the headline
+    workload into the committed summaries under profiles/."""
+    table, agg = summarize_trace(trace_dir)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "kernels.llama_layer.trace.md"), "w") as f:
+        f.write("# Kernel durations, Llama-3.1-8B decode layer (B=32, 4096 tokens, bf16), page size 1 and 128\n\n")
+        f.write("Command:\n\n```\n" + commands["trace"] + "\n```\n\n")
+        f.write("Every dispatch of the run, grouped by kernel and grid (the streaming-read probe is the "
+                "read-ceiling measurement; `paged_split_kernel` + `split_reduce_kernel` are one decode step).\n\n")
+        f.write(table + "\n")
+    fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    med = lambda v: sorted(v)[len(v) // 2]
+    # calibration: the read probe reads its 4 GiB buffer once; torch's fill
+    # writes it once
+    probe = [v for (k, _), vs in fetch.items() if "stream_read_kernel" in k for v in vs]
+    fills = [max(vs) for (k, _), vs in write.items() if "FillFunctor" in k]
+    nbytes = 4 << 30
+    fetch_scale = nbytes / (med(probe) * 1024)
+    write_scale = nbytes / (max(fills) * 1024)
+    kernels = {}
+    for (k, grid), vs in fetch.items():
+        if "paged_split_kernel" in k or "split_reduce_kernel" in k:
+            w = write.get((k, grid), [0.0])
+            kernels[f"{k} grid={grid}"] = dict(dispatches=len(vs), fetch_kib_median=med(vs),
+                                               write_kib_median=med(w),
+                                               bytes=med(vs) * 1024 * fetch_scale + med(w) * 1024 * write_scale)
+    rec = dict(workload="Llama-3.1-8B decode layer, B=32, 4096 tokens, bf16, page size 1 and 128 (same plan)",
+               commands=commands, source_sha256=kernel_source_hash(), fetch_scale=fetch_scale,
+               write_scale=write_scale,
+               calibration="FETCH_SIZE of the streaming-read probe over 4 GiB; WRITE_SIZE of torch's fill of "
+                           "the same 4 GiB buffer",
+               kernels=kernels, traffic_bytes_per_step=sum(v["bytes"] for v in kernels.values()))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def measured_traffic():
+    """Scaled HBM bytes per decode step of the headline workload from the
+    committed counter summary, or None when the sources changed since."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_step")
+
+
 def host_timing(reps=21):
     """Median host time (us) of page-table lowering (page sizes 1 and 16) and
     planning through the C ABI, at 64 .. 2,097,152 tokens over 32 requests."""
@@ -210,7 +321,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        t, f, w = args.summarize_profiles
+        prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && "
+        run = "-- python bench.py --configs c2 --steps 20 --warmup 5 --no-cpu"
+        cmds = dict(trace=f"{prof}rocprofv3 --kernel-trace --stats --output-format csv -d {t} -o run {run}",
+                    fetch=f"{prof}timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {f} -o run {run}",
+                    write=f"{prof}timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {w} -o run {run}",
+                    summary=f"python bench.py --summarize-profiles {t} {f} {w}")
+        rec = write_profile_summaries(t, f, w, cmds)
+        print(json.dumps(rec["kernels"], indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(the decode step shards by request or KV head with no exchange).", file=sys.stderr)
@@ -286,7 +410,7 @@ def main():
                                "per request, bf16, kv_indices of length 131072, page size 1",
                    "global_batch": 32, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": rec1["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": rec1["gbs"] / PEAK_HBM_GBS, "traffic": None,
+                     "frac": rec1["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "paged decode step: paged_split_kernel + split_reduce_kernel, timed together "
                                "(events cannot split one library call)",
                      "read_ceiling_gbs": ceiling},

@@ -108,12 +108,14 @@ typedef struct pkv_tuning {
     int32_t gate_ratio;         /* PAGED when saved_bytes < gate_ratio * overhead_bytes */
     int64_t launch_bytes;       /* byte-equivalent of the two extra launches of a cascade */
     int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU */
-    int32_t min_split_tokens;   /* paged pass: smallest token range per workgroup */
-    int32_t fuse_split_reduce;  /* 1: the last work item of a request combines its splits
-                                   (one kernel per paged pass); 0: a separate reduce kernel */
+    int32_t min_split_tokens;   /* paged pass: smallest chunk of positions per workgroup */
     int32_t concurrent_prefix;  /* 1: pkv_decode_step runs the prefix pass on a library-owned
                                    side stream (same priority) concurrently with the suffix
                                    pass, joined by events before the combine; 0: one stream */
+    int32_t fuse_cascade;       /* 1: on a DENSE plan pkv_decode_step runs the prefix items
+                                   and the suffix chunks in one launch, interleaved, so
+                                   that MFMA work and HBM streaming overlap on every CU;
+                                   0: one launch per pass */
     int32_t prefix_target_workgroups; /* prefix pass: workgroups to aim for (query tiles x
                                          prefix ranges) */
     int32_t min_prefix_split_tokens;  /* prefix pass: smallest prefix range per workgroup
@@ -127,14 +129,15 @@ typedef struct pkv_plan_info {
     int32_t m_eff;              /* B * G ([P2] s.3) */
     int32_t shared_pages;       /* floor(P / page_size) when a prefix is declared, else 0 */
     int32_t prefix_tokens;      /* tokens the prefix pass covers (0 on PAGED) */
-    int32_t split_tokens;       /* paged pass: logical tokens per work item */
-    int32_t num_splits;         /* paged pass: work items per (request, head block), max */
+    int32_t split_tokens;       /* paged pass: positions per chunk.  The positions the pass
+                                   attends, request after request, form one flat sequence
+                                   cut into equal chunks, one per workgroup and head block */
+    int32_t num_splits;         /* paged pass: most chunks one request touches (partial
+                                   states per request) */
     int32_t heads_per_item;     /* paged pass: KV heads one work item covers */
     int32_t prefix_splits;      /* prefix pass: ranges the prefix is cut into */
-    int64_t num_work_items;     /* paged pass: workgroups launched */
+    int64_t num_work_items;     /* paged pass: workgroups launched (chunks x head blocks) */
     int64_t workspace_bytes;    /* device scratch the plan's calls need (0 allowed) */
-    int64_t workspace_zero_bytes; /* leading workspace bytes that must be zero before the
-                                     first call on a workspace; every call leaves them zero */
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
@@ -217,10 +220,9 @@ void pkv_plan_destroy(pkv_plan* plan);
  *   o           device, [B][H_q][d] of the q dtype, normalised output; nullable
  *   o_f32       device, [B][H_q][d] fp32, normalised output; nullable
  *   lse         device, [B][H_q] fp32; nullable
- *   workspace   device scratch of >= the plan's workspace_bytes (nullable if 0);
- *               its first workspace_zero_bytes must be zero before the first
- *               call that uses it (e.g. zero-filled once at allocation); calls
- *               leave them zero.  Calls that share a workspace must not overlap.
+ *   workspace   device scratch of >= the plan's workspace_bytes (nullable if 0),
+ *               no initial contents needed.  Calls that share a workspace must
+ *               not overlap.
  * At least one of o, o_f32 must be given.  Writes no other memory.
  * Errors: EINVAL (null plan/q/indices, no output, pool not matching the plan,
  * missing fp8 scales), EWORKSPACE, EHIP.

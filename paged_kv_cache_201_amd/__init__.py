@@ -55,7 +55,7 @@ class pkv_problem(ctypes.Structure):
 class pkv_tuning(ctypes.Structure):
     _fields_ = [("t_dense", ctypes.c_int32), ("gate_ratio", ctypes.c_int32), ("launch_bytes", ctypes.c_int64),
                 ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
-                ("fuse_split_reduce", ctypes.c_int32), ("concurrent_prefix", ctypes.c_int32),
+                ("concurrent_prefix", ctypes.c_int32), ("fuse_cascade", ctypes.c_int32),
                 ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32)]
 
 
@@ -63,8 +63,7 @@ class pkv_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("m_eff", ctypes.c_int32), ("shared_pages", ctypes.c_int32),
                 ("prefix_tokens", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
-                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("workspace_zero_bytes", ctypes.c_int64)]
+                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
 _SIGS = {
@@ -285,7 +284,7 @@ def pkv_stream_read_probe(buf, out, num_workgroups, stream=None):
 
 
 def workspace_for(plan, device="cuda"):
-    """A zero-filled uint8 workspace tensor of the plan's size (None if 0)."""
+    """A uint8 workspace tensor of the plan's size (None if 0)."""
     import torch
     n = plan.info["workspace_bytes"]
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device) if n else None
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device) if n else None

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "probe.hip", "paged_f32.hip", "paged_bf16.hip", "paged_fp8.hip"]
+HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "cascade_fused.hip", "probe.hip", "paged_f32.hip",
+               "paged_bf16.hip", "paged_fp8.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 ARCH = "gfx950"

@@ -90,45 +90,48 @@ pkv::PagedArgs paged_args(const pkv_plan* pl, const void* q, const pkv_pool* poo
     a.v_scale = pool->v_scale;
     a.kv_indptr = kv_indptr;
     a.kv_indices = kv_indices;
+    a.B = pl->B;
     a.H_kv = pl->H_kv;
     a.token_offset = pl->prefix_tokens;
-    a.split_tokens = pl->split_tokens;
-    a.num_splits = pl->num_splits;
+    a.chunk_tokens = pl->split_tokens;
+    a.total_tokens = pl->paged_tokens;
+    a.max_parts = pl->num_splits;
     a.scale_log2 = sm_scale * kLog2e;
     a.out_dtype = pl->q_dtype;
     return a;
+}
+
+// The combine of a paged pass: chunk partials of every request (and, for a
+// cascade step, the prefix ranges before them).
+pkv::SplitReduceArgs chunk_reduce_args(const pkv_plan* pl, const pkv::PagedArgs& a) {
+    pkv::SplitReduceArgs r{};
+    r.B = pl->B;
+    r.H_q = pl->H_q;
+    r.D = pl->D;
+    r.part_acc = a.part_acc;
+    r.part_ml = a.part_ml;
+    r.max_parts = pl->num_splits;
+    r.kv_indptr = a.kv_indptr;
+    r.token_offset = a.token_offset;
+    r.chunk_tokens = a.chunk_tokens;
+    r.out_dtype = pl->q_dtype;
+    return r;
 }
 
 pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
                      const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
                      void* ws, hipStream_t stream) {
     pkv::PagedArgs a = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
-    if (pl->num_splits == 1) {
-        a.o = o;
-        a.o_f32 = o_f32;
-        a.lse = lse;
-        return hip_status(pkv::launch_paged_split(*pl, a, stream));
-    }
+    a.o = o;
+    a.o_f32 = o_f32;
+    a.lse = lse;
     a.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
     a.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
-    if (pl->fuse_reduce) {
-        a.counters = ws_at<int32_t>(ws, pl->ws_counters);
-        a.o = o;
-        a.o_f32 = o_f32;
-        a.lse = lse;
-        return hip_status(pkv::launch_paged_split(*pl, a, stream));
-    }
-    hipError_t e = pkv::launch_paged_split(*pl, a, stream);
-    if (e != hipSuccess) return PKV_EHIP;
-    pkv::SplitReduceArgs r{};
-    r.num_splits = pl->num_splits;
-    r.B = pl->B;
-    r.H_q = pl->H_q;
-    r.D = pl->D;
-    r.part_acc = a.part_acc;
-    r.part_ml = a.part_ml;
+    if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, a, stream) != hipSuccess) return PKV_EHIP;
+    if (!pl->needs_reduce) return PKV_OK;
+    pkv::SplitReduceArgs r = chunk_reduce_args(pl, a);
+    r.skip_whole = 1;
     r.o = o;
-    r.out_dtype = pl->q_dtype;
     r.o_f32 = o_f32;
     r.lse = lse;
     return hip_status(pkv::launch_split_reduce(r, stream));
@@ -166,12 +169,12 @@ pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, c
     hipError_t e = pkv::launch_prefix_attn(a, pl->prefix_rows_per_wg, stream);
     if (e != hipSuccess) return PKV_EHIP;
     pkv::SplitReduceArgs r{};
-    r.num_splits = pl->prefix_splits;
     r.B = pl->B;
     r.H_q = pl->H_q;
     r.D = pl->D;
-    r.part_acc = a.part_acc;
-    r.part_ml = a.part_ml;
+    r.pre_acc = a.part_acc;
+    r.pre_ml = a.part_ml;
+    r.pre_splits = pl->prefix_splits;
     r.o = nullptr;
     r.out_dtype = PKV_F32;
     r.o_f32 = o_p;
@@ -239,7 +242,7 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     if (pl->path == PKV_PATH_PAGED)
         return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, nullptr, lse, ws, s);
     // Cascade: both passes leave partial states in the workspace, and one
-    // kernel combines the prefix ranges and then the suffix splits of every
+    // kernel combines the prefix ranges and then the suffix chunks of every
     // row into the output.
     pkv::PrefixArgs pa = prefix_args(pl, q, pool, kv_indices + pl->indptr0, sm_scale);
     pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
@@ -249,7 +252,9 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
     sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
     sa.force_partial = 1;
-    if (pl->concurrent_prefix) {
+    if (pl->fuse_cascade) {
+        if (pkv::launch_cascade_fused(*pl, pa, sa, s) != hipSuccess) return PKV_EHIP;
+    } else if (pl->concurrent_prefix) {
         std::lock_guard<std::mutex> lock(g_side_mu);
         SideStream* ss = nullptr;
         if (side_stream_locked(&ss) != hipSuccess) return PKV_EHIP;
@@ -257,26 +262,19 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
         if (hipEventRecord(ss->fork, s) != hipSuccess) return PKV_EHIP;
         if (hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) return PKV_EHIP;
         if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, ss->stream) != hipSuccess) return PKV_EHIP;
-        if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
         // join: the combine on `s` waits for the prefix pass
         if (hipEventRecord(ss->join, ss->stream) != hipSuccess) return PKV_EHIP;
         if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return PKV_EHIP;
     } else {
         if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
-        if (pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
     }
-    pkv::SplitReduceArgs r{};
-    r.num_splits = pl->num_splits;
-    r.B = pl->B;
-    r.H_q = pl->H_q;
-    r.D = pl->D;
-    r.part_acc = sa.part_acc;
-    r.part_ml = sa.part_ml;
+    pkv::SplitReduceArgs r = chunk_reduce_args(pl, sa);
     r.pre_acc = pa.part_acc;
     r.pre_ml = pa.part_ml;
     r.pre_splits = pl->prefix_splits;
     r.o = o;
-    r.out_dtype = pl->q_dtype;
     r.lse = lse;
     return hip_status(pkv::launch_split_reduce(r, s));
 }

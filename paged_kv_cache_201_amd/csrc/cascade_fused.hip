@@ -1,0 +1,81 @@
+// One launch for both passes of a DENSE cascade step.
+//
+// The prefix pass is bound by MFMA and LDS work (the prefix is read once for
+// all requests: "GraniKV: asymmetric KV cache paging for shared-prefix
+// agents", sections 2 and 3); the suffix pass of the same step streams each
+// request's own K/V rows from HBM.  Launched one after the other, each kernel
+// leaves the other's resource idle.  Here every workgroup runs either one
+// prefix work item or one suffix chunk, and the two kinds are interleaved in
+// dispatch order (eight prefix workgroups, then eight suffix workgroups, ...)
+// so that each CU holds one of each: while the prefix item waits on MFMA
+// results and LDS, the suffix chunk keeps HBM reads in flight.  Both bodies
+// use 256 threads and at most 256 VGPRs per lane, and they share the LDS
+// allocation.  Results are the same partial states the two separate kernels
+// write.
+#include "paged_dispatch.h"
+#include "prefix_kernel.h"
+
+namespace pkv {
+
+// Role of workgroup i among np prefix workgroups (a multiple of 8) and ns
+// suffix workgroups.  Whole groups of 16 hold eight of each; the remaining
+// workgroups take what is left of the larger kind.  Prefix index p keeps
+// p % 8 == i % 8, the XCD the workgroup runs on, as prefix_item assumes.
+__device__ __forceinline__ void fused_role(const int i, const int np, const int ns, bool& is_prefix, int& idx) {
+    const int groups = min(np, ns) / 8;
+    if (i < 16 * groups) {
+        is_prefix = (i % 16) < 8;
+        idx = (i / 16) * 8 + (i % 8);
+        return;
+    }
+    const int j = i - 16 * groups;
+    const int rest_prefix = np - 8 * groups;
+    is_prefix = j < rest_prefix;
+    idx = 8 * groups + (is_prefix ? j : j - rest_prefix);
+}
+
+template <int D, int G, int NHL, int TPI>
+__global__ void __launch_bounds__(kPagedWaves * 64, 2)
+    cascade_fused_kernel(const PrefixArgs pa, const PagedArgs sa, const int np, const int ns, const int hblks) {
+    using PS = PrefixSmem<D, 32>;
+    using SS = PagedSmem<PKV_BF16, D, G, NHL, TPI>;
+    constexpr size_t kBytes = sizeof(PS) > sizeof(SS) ? sizeof(PS) : sizeof(SS);
+    __shared__ __attribute__((aligned(16))) char smem[kBytes];
+    bool is_prefix;
+    int idx;
+    fused_role(blockIdx.x, np, ns, is_prefix, idx);
+    if (is_prefix)
+        prefix_item<D, kPagedWaves, 32>(pa, *reinterpret_cast<PS*>(smem), idx);
+    else
+        paged_chunk<PKV_BF16, D, G, NHL, TPI>(sa, *reinterpret_cast<SS*>(smem), idx / hblks, idx % hblks);
+}
+
+namespace {
+struct FusedLaunch {
+    const pkv_plan& p;
+    const PrefixArgs& pa;
+    const PagedArgs& sa;
+    hipStream_t s;
+    template <int KV, int D, int G, int NHL, int TPI>
+    hipError_t run() const {
+        if constexpr (KV != PKV_BF16) {
+            return hipErrorInvalidValue;
+        } else {
+            const int np = prefix_blocks(pa.row_tiles * pa.H_kv * pa.num_splits);
+            const int64_t ns = p.num_chunks * p.head_blocks;
+            if (np + ns > INT32_MAX) return hipErrorInvalidValue;
+            if (np + ns == 0) return hipSuccess;
+            cascade_fused_kernel<D, G, NHL, TPI>
+                <<<(uint32_t)(np + ns), kPagedWaves * 64, 0, s>>>(pa, sa, np, (int)ns, p.head_blocks);
+            return hipGetLastError();
+        }
+    }
+};
+}  // namespace
+
+hipError_t launch_cascade_fused(const pkv_plan& p, const PrefixArgs& pa, const PagedArgs& sa, hipStream_t s) {
+    if (pa.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
+    return dispatch_kv<PKV_BF16>(p, FusedLaunch{p, pa, sa, s});
+}
+
+}  // namespace pkv

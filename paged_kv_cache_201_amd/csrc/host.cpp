@@ -97,10 +97,10 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->t_dense = 1024;
     out->gate_ratio = 1;
     out->launch_bytes = 40LL * 1000 * 1000;   // ~5 us at 8 TB/s for two extra launches
-    out->target_workgroups = 1024;
+    out->target_workgroups = 512;   // two workgroups per CU
     out->min_split_tokens = 256;
-    out->fuse_split_reduce = 0;  // measured: the device-scope release per item costs more than a launch
     out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
+    out->fuse_cascade = 1;
     out->prefix_target_workgroups = 256;
     out->min_prefix_split_tokens = 256;
 }
@@ -176,8 +176,9 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         pkv_tuning_defaults(&tu);
     }
     if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
-        tu.min_split_tokens < 1 || tu.fuse_split_reduce < 0 || tu.fuse_split_reduce > 1 ||
-        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.prefix_target_workgroups < 1 ||
+        tu.min_split_tokens < 1 ||
+        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.fuse_cascade < 0 || tu.fuse_cascade > 1 ||
+        tu.prefix_target_workgroups < 1 ||
         tu.min_prefix_split_tokens < 1)
         return PKV_EINVAL;
 
@@ -255,25 +256,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->geo = geo;
     pl->head_blocks = H_kv / geo.hb;
     pl->concurrent_prefix = tu.concurrent_prefix;
-
-    // Paged pass: cut every request's attended tokens [prefix_tokens, L_b)
-    // into work items of split_tokens logical positions.
-    int64_t total = 0, maxl = 0;
-    for (int32_t b = 0; b < B; ++b) {
-        const int64_t L = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
-        total += L;
-        maxl = std::max(maxl, L);
-    }
-    pl->paged_tokens = total;
-    pl->paged_max_len = (int32_t)maxl;
-    const int64_t per_item = ceil_div(total * pl->head_blocks, tu.target_workgroups);
-    int64_t split = std::max<int64_t>(tu.min_split_tokens, per_item);
-    split = align_up(split, pkv::kSplitQuantum);
-    split = std::min<int64_t>(split, align_up(std::max<int64_t>(maxl, 1), pkv::kSplitQuantum));
-    split = std::min<int64_t>(split, pkv::kMaxSplitTokens);
-    pl->split_tokens = (int32_t)split;
-    pl->num_splits = (int32_t)std::max<int64_t>(1, ceil_div(maxl, split));
-    pl->num_work_items = (int64_t)pl->num_splits * pl->head_blocks * B;
+    pl->fuse_cascade = tu.fuse_cascade && path == PKV_PATH_DENSE;
 
     // Prefix pass: M_eff query rows per KV head in tiles, the prefix cut into
     // ranges so that the grid fills the GPU.
@@ -289,6 +272,49 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         pl->prefix_split_tokens = (int32_t)ps;
         pl->prefix_splits = (int32_t)ceil_div(prefix_tokens, ps);
     }
+    // Workgroups of the prefix pass (a multiple of 8 for the XCD placement).
+    const int64_t prefix_wgs =
+        pl->prefix_splits ? align_up((int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg) * pl->prefix_splits, 8)
+                          : 0;
+
+    // Paged pass: the attended positions [prefix_tokens, L_b) of all
+    // requests, request after request, form one flat sequence that is cut
+    // into equal chunks, one workgroup per (chunk, head block).
+    int64_t total = 0;
+    bool any_empty = false;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t n = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
+        total += n;
+        any_empty |= n == 0;
+    }
+    pl->paged_tokens = total;
+    // When one launch runs both passes of a DENSE step, the suffix chunks
+    // fill the workgroup slots the prefix items leave (but at least half).
+    int64_t target = tu.target_workgroups;
+    if (pl->fuse_cascade) target = std::max<int64_t>(target - prefix_wgs, (target + 1) / 2);
+    const int64_t per_item = ceil_div(total * pl->head_blocks, target);
+    int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
+    chunk = align_up(chunk, pkv::kSplitQuantum);
+    chunk = std::min<int64_t>(chunk, pkv::kMaxSplitTokens);
+    pl->split_tokens = (int32_t)chunk;
+    pl->num_chunks = ceil_div(total, chunk);
+    pl->num_work_items = pl->num_chunks * pl->head_blocks;
+    // Partial states per request: the chunks its range touches.
+    int64_t pos = 0, max_parts = 1;
+    bool spans = false;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t n = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
+        if (n > 0) {
+            const int64_t parts = (pos + n - 1) / chunk - pos / chunk + 1;
+            max_parts = std::max(max_parts, parts);
+            spans |= parts > 1;
+        }
+        pos += n;
+    }
+    pl->num_splits = (int32_t)max_parts;
+    // A combine kernel follows the paged pass for a cascade step, when a
+    // request spans chunks, or to write the output of empty requests.
+    pl->needs_reduce = path != PKV_PATH_PAGED || spans || any_empty;
 
     // Workspace layout.
     int64_t off = 0;
@@ -298,19 +324,12 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         off = align_up(off + bytes, kAlign);
         return at;
     };
-    pl->ws_counters = -1;
-    pl->ws_zero_bytes = 0;
-    pl->fuse_reduce = tu.fuse_split_reduce && pl->num_splits > 1 && path == PKV_PATH_PAGED;
-    if (pl->fuse_reduce) {
-        pl->ws_counters = take((int64_t)B * pl->head_blocks * 4);
-        pl->ws_zero_bytes = (int64_t)B * pl->head_blocks * 4;
-    }
     pl->ws_paged_acc = pl->ws_paged_ml = -1;
     pl->ws_prefix_acc = pl->ws_prefix_ml = -1;
     // A cascade step keeps both passes as partial states (prefix ranges, then
-    // suffix splits) that one kernel combines; a paged pass with one split
-    // writes its output directly.
-    if (pl->num_splits > 1 || path != PKV_PATH_PAGED) {
+    // suffix chunks) that one kernel combines; a request inside one chunk of
+    // a paged pass has its output written directly.
+    if (spans || path != PKV_PATH_PAGED) {
         pl->ws_paged_acc = take(rows * pl->num_splits * D * 4);
         pl->ws_paged_ml = take(rows * pl->num_splits * 2 * 4);
     }
@@ -335,7 +354,6 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     info->prefix_splits = pl->prefix_splits;
     info->num_work_items = pl->num_work_items;
     info->workspace_bytes = pl->workspace_bytes;
-    info->workspace_zero_bytes = pl->ws_zero_bytes;
     return PKV_OK;
 }
 

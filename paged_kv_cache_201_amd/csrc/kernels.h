@@ -9,7 +9,11 @@
 
 namespace pkv {
 
-// Arguments of the paged split kernel.  All pointers are device memory.
+// Arguments of the paged kernel.  All pointers are device memory.  The
+// attended positions of all requests (tokens [token_offset, L_b) of each)
+// form one flat sequence of total_tokens positions cut into chunks of
+// chunk_tokens; a request's partial states are numbered by chunk, from the
+// chunk holding its first position.
 struct PagedArgs {
     const void* q;            // [B][H_q][D], q dtype
     const void* k;            // pool [slots][H_kv][D]
@@ -18,40 +22,46 @@ struct PagedArgs {
     const float* v_scale;
     const int32_t* kv_indptr; // [B+1]
     const int32_t* kv_indices;
+    int32_t B;
     int32_t H_kv;
     int32_t token_offset;     // tokens skipped at the start of every request
-    int32_t split_tokens;
-    int32_t num_splits;
+    int32_t chunk_tokens;
+    int64_t total_tokens;
+    int32_t max_parts;        // partial states per request the workspace holds
     float scale_log2;         // sm_scale * log2(e)
-    // direct outputs (num_splits == 1)
+    // outputs of requests that lie inside one chunk (unless force_partial)
     void* o;                  // [B][H_q][D], q dtype, nullable
     float* o_f32;             // nullable
     float* lse;               // [B][H_q], nullable
-    // partial outputs (num_splits > 1)
-    float* part_acc;          // [B][num_splits][H_q][D]: sum of 2^(s - M) v
-    float* part_ml;           // [B][num_splits][H_q][2]: (M, L), M in log2 units
-    // num_splits > 1 and non-null: [B][head_blocks] arrival counters (zero on
-    // entry, left zero on exit); the last item of a (request, head block) to
-    // finish combines the partials and writes o / o_f32 / lse itself.
-    int32_t* counters;
+    // partial outputs
+    float* part_acc;          // [B][max_parts][H_q][D]: sum of 2^(s - M) v
+    float* part_ml;           // [B][max_parts][H_q][2]: (M, L), M in log2 units
     int32_t out_dtype;        // dtype of o (q dtype)
-    int32_t force_partial;    // write partials even with one split (cascade suffix)
+    int32_t force_partial;    // every segment writes a partial (cascade suffix)
 };
 
 // Launch the paged split kernel for the plan's geometry.
 hipError_t launch_paged_split(const pkv_plan& plan, const PagedArgs& a, hipStream_t stream);
 
-// Combine partial states row by row: the pre_splits partials at pre_acc
-// (the shared-prefix pass of a cascade step; optional) followed by the
-// num_splits partials at part_acc, all in the [B][splits][H_q] layout.
+// Combine partial states row by row, in order: first the pre_splits
+// partials of the shared-prefix pass (optional; [B][pre_splits][H_q]), then
+// the chunk partials of the paged pass (optional; [B][max_parts][H_q]), whose
+// count per request follows from kv_indptr and the chunking.  With
+// skip_whole, rows of non-empty requests that lie inside one chunk are left
+// alone (the paged kernel wrote them).  A row with nothing to combine gets
+// o = 0, lse = -inf.
 struct SplitReduceArgs {
-    int32_t num_splits;
     int32_t B, H_q, D;
-    const float* part_acc;
-    const float* part_ml;
-    const float* pre_acc;     // nullable: [B][pre_splits][H_q][D]
+    const float* pre_acc;     // nullable
     const float* pre_ml;
     int32_t pre_splits;
+    const float* part_acc;    // nullable
+    const float* part_ml;
+    int32_t max_parts;
+    const int32_t* kv_indptr; // [B+1]; nullable: no chunk partials, skip nothing
+    int32_t token_offset;
+    int32_t chunk_tokens;
+    int32_t skip_whole;
     void* o;                  // nullable; out_dtype
     int32_t out_dtype;
     float* o_f32;             // nullable
@@ -79,6 +89,12 @@ struct PrefixArgs {
     int32_t force_partial;    // write partials even with one split (cascade step)
 };
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream);
+
+// Both passes of a DENSE cascade step in one launch (bf16): the prefix work
+// items of `pa` (DENSE tiles, partial states) and the chunks of the paged
+// pass `sa` (partial states), interleaved so that they run side by side.
+hipError_t launch_cascade_fused(const pkv_plan& plan, const PrefixArgs& pa, const PagedArgs& sa,
+                                hipStream_t stream);
 
 // Row-wise LSE merge of two fp32 states.
 hipError_t launch_merge_states(int32_t rows, int32_t D, const float* o_a, const float* lse_a,

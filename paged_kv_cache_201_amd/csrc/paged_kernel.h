@@ -6,9 +6,15 @@
 // request's single query token, with G query heads per KV head, attends over
 // the cached K/V rows that kv_indices lists for it, in logical order.
 //
-// Work decomposition.  A workgroup (4 waves) owns one (split, head block,
-// request): split_tokens consecutive logical positions of one request and HB
-// KV heads.  Each wave takes a contiguous quarter of those positions.  The 64
+// Work decomposition.  The tokens the pass attends, request after request,
+// form one flat sequence that is cut into equal chunks of chunk_tokens
+// positions; a workgroup (4 waves) owns one (chunk, head block) pair and
+// walks the requests its chunk touches, one segment per request.  Every
+// workgroup therefore streams the same number of K/V rows whatever the mix of
+// request lengths.  A request that lies inside one chunk gets its output
+// written directly; a request cut by chunk boundaries leaves one partial
+// softmax state per chunk, combined afterwards in chunk order.  Inside a
+// segment each wave takes a contiguous quarter of the positions.  The 64
 // lanes of a wave span (KV head, head-dim chunk): LPH lanes read one row, so
 // a wave-wide load reads RS rows -- one token's HB heads when TPI == 1 (the
 // slot is then wave-uniform and the address is scalar), or TPI tokens when
@@ -99,44 +105,37 @@ struct PagedCfg {
     static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
 };
 
+// LDS of one paged workgroup: slot indices of the current segment, later
+// reused for the per-wave partial accumulators; the per-wave (max, sum).
 template <int KV, int D, int G, int NHL, int TPI>
-__global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const PagedArgs a) {
+struct PagedSmem {
+    using C = PagedCfg<KV, D, G, NHL, TPI>;
+    float buf[C::LDS_FLOATS];
+    float ml[C::PARTIALS * C::HB * G * 2];
+    int first_request;
+};
+
+// One segment: n_tok > 0 consecutive positions of request b, whose slot
+// indices start at kv_indices[idx_beg], for the HB KV heads of head block
+// hblk.  slot < 0: the segment is the whole request and its normalised output
+// goes to o / o_f32 / lse; slot >= 0: its partial state goes to partial
+// index `slot` of request b.  Called by every thread of the workgroup.
+template <int KV, int D, int G, int NHL, int TPI>
+__device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, D, G, NHL, TPI>& sm, const int b,
+                                              const int hblk, const int idx_beg, const int n_tok,
+                                              const int slot) {
     using C = PagedCfg<KV, D, G, NHL, TPI>;
     constexpr int BK = C::BK, EPL = C::EPL, LW = C::LW, LPH = C::LPH, RS = C::RS, HB = C::HB;
     constexpr int NW = C::NW, QW = C::QW, U = C::U, TU = C::TU;
     using LV = typename LoadVec<LW>::T;
-
-    __shared__ float s_buf[C::LDS_FLOATS];
-    __shared__ float s_ml[C::PARTIALS * HB * G * 2];
+    float* const s_buf = sm.buf;
+    float* const s_ml = sm.ml;
 
     const int lane = threadIdx.x & 63;
     // wave-uniform, so everything derived from it lives in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x;
-    const int hblk = blockIdx.y;
-    const int b = blockIdx.z;
     const int H_kv = a.H_kv;
     const int H_q = H_kv * G;
-
-    const int seq_beg = a.kv_indptr[b] + a.token_offset;
-    const int len = a.kv_indptr[b + 1] - seq_beg;
-    const int t0 = split * a.split_tokens;
-    // Items past the request's last token only record an empty state
-    // (max -inf, sum 0) for the reduction; item 0 always runs so that an
-    // empty request still gets o = 0, lse = -inf.
-    const int items = max(1, (len + a.split_tokens - 1) / a.split_tokens);
-    if (split >= items) {
-        if (a.counters == nullptr) {
-            for (int qhl = threadIdx.x; qhl < HB * G; qhl += NW * 64) {
-                const int qh = (hblk * HB + qhl / G) * G + qhl % G;
-                const size_t prow = ((size_t)b * a.num_splits + split) * H_q + qh;
-                f32x2_t ml = {-INFINITY, 0.f};
-                *reinterpret_cast<f32x2_t*>(a.part_ml + prow * 2) = ml;
-            }
-        }
-        return;
-    }
-    const int n_tok = max(min(t0 + a.split_tokens, len) - t0, 0);
 
     // This wave's contiguous token range [w0, w1) within the item; every
     // wave range starts on a whole iteration.
@@ -151,7 +150,7 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
     int* s_idx = reinterpret_cast<int*>(s_buf);
     const int n_pad = (n_tok + TU - 1) / TU * TU;
     for (int i = threadIdx.x; i < n_pad; i += NW * 64)
-        s_idx[i] = a.kv_indices[seq_beg + t0 + min(i, n_tok - 1)];
+        s_idx[i] = a.kv_indices[idx_beg + min(i, n_tok - 1)];
     __syncthreads();
 
     const int lrow = lane / LPH;
@@ -445,7 +444,7 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
     __syncthreads();
 
     constexpr int CH = D / 4;  // float4 chunks per head
-    const bool direct = a.num_splits == 1 && !a.force_partial;
+    const bool direct = slot < 0;
     for (int c = threadIdx.x; c < HB * G * CH; c += NW * 64) {
         const int qhl = c / CH;
         const int e4 = c % CH;
@@ -483,7 +482,7 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
             }
             if (a.lse && e4 == 0) a.lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
         } else {
-            const size_t prow = ((size_t)b * a.num_splits + split) * H_q + qh;
+            const size_t prow = ((size_t)b * a.max_parts + slot) * H_q + qh;
             *reinterpret_cast<f32x4_t*>(a.part_acc + prow * D + e4 * 4) = o;
             if (e4 == 0) {
                 a.part_ml[prow * 2] = M;
@@ -491,57 +490,53 @@ __global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const 
             }
         }
     }
-    if (direct || a.counters == nullptr) return;
+}
 
-    // Last-arriver combine.  Every item publishes its partial with a device
-    // scope release (fence + counter increment); the item that brings the
-    // counter to the number of items of this request acquires and combines
-    // them in split order, so the result does not depend on which is last.
-    __shared__ int s_last;
+// Offset of request i's first attended position in the flat sequence.
+__device__ __forceinline__ int64_t flat_offset(const PagedArgs& a, int i) {
+    return (int64_t)a.kv_indptr[i] - a.kv_indptr[0] - (int64_t)i * a.token_offset;
+}
+
+// One (chunk, head block) work item: positions [w * chunk, (w + 1) * chunk)
+// of the flat sequence, segment by segment.
+template <int KV, int D, int G, int NHL, int TPI>
+__device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D, G, NHL, TPI>& sm, const int w,
+                                            const int hblk) {
+    constexpr int NT = kPagedWaves * 64;
+    const int64_t C = a.chunk_tokens;
+    const int64_t c0 = (int64_t)w * C;
+    const int64_t c1 = c0 + C < a.total_tokens ? c0 + C : a.total_tokens;
+    // The request holding position c0: the one non-empty request whose flat
+    // range contains it.
+    if (threadIdx.x == 0) sm.first_request = -1;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        int* ctr = a.counters + (size_t)b * gridDim.y + hblk;
-        const int prev = atomicAdd(ctr, 1);
-        s_last = prev == items - 1;
-        if (s_last) *ctr = 0;  // all ns items have arrived: ready for the next call
-    }
+    for (int i = threadIdx.x; i < a.B; i += NT)
+        if (flat_offset(a, i) <= c0 && c0 < flat_offset(a, i + 1)) sm.first_request = i;
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int ns = items;
-    for (int c = threadIdx.x; c < HB * G * CH; c += NW * 64) {
-        const int qhl = c / CH;
-        const int e4 = c % CH;
-        const int kvh = hblk * HB + qhl / G;
-        const int qh = kvh * G + qhl % G;
-        const size_t base = (size_t)b * a.num_splits * H_q + qh;
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + (size_t)s * H_q) * 2]);
-        float L = 0.f;
-        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) {
-            const size_t prow = base + (size_t)s * H_q;
-            const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
-            const float w = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
-            L += w * ml[1];
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.part_acc + prow * D + e4 * 4);
-            if (w > 0.f) o += w * x;
-        }
-        o *= L > 0.f ? 1.f / L : 0.f;
-        const size_t row = (size_t)b * H_q + qh;
-        if (a.o_f32) *reinterpret_cast<f32x4_t*>(a.o_f32 + row * D + e4 * 4) = o;
-        if (a.o) {
-            if constexpr (C::QF32) {
-                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.o) + row * D + e4 * 4) = o;
-            } else {
-                u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.o) + row * D + e4 * 4) = h;
-            }
-        }
-        if (a.lse && e4 == 0) a.lse[row] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    int b = __builtin_amdgcn_readfirstlane(sm.first_request);
+    if (b < 0) return;  // kv_indptr does not describe the planned batch
+    bool first = true;
+    for (; b < a.B; ++b) {
+        const int64_t ob = flat_offset(a, b);
+        if (ob >= c1) break;
+        const int64_t on = flat_offset(a, b + 1);
+        const int64_t lo = c0 > ob ? c0 : ob;
+        const int64_t hi = c1 < on ? c1 : on;
+        if (hi <= lo) continue;  // empty request
+        const bool whole = lo == ob && hi == on;
+        const int slot = (whole && !a.force_partial) ? -1 : (int)(w - ob / C);
+        if (slot >= a.max_parts) return;  // kv_indptr does not describe the planned batch
+        if (!first) __syncthreads();  // the previous segment is done with LDS
+        first = false;
+        paged_segment<KV, D, G, NHL, TPI>(a, sm, b, hblk, a.kv_indptr[b] + a.token_offset + (int)(lo - ob),
+                                          (int)(hi - lo), slot);
     }
+}
+
+template <int KV, int D, int G, int NHL, int TPI>
+__global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const PagedArgs a) {
+    __shared__ PagedSmem<KV, D, G, NHL, TPI> sm;
+    paged_chunk<KV, D, G, NHL, TPI>(a, sm, blockIdx.x, blockIdx.y);
 }
 
 }  // namespace pkv

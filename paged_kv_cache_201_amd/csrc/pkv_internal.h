@@ -35,9 +35,9 @@ constexpr int32_t kTiledRowsPerWg = 64;
 // kMaxPrefixSplitTokens per range (the kernel stages a range's indices in LDS).
 constexpr int32_t kPrefixTokenQuantum = 64;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
-// Paged-pass work items hold a multiple of this many tokens, and at most
-// kMaxSplitTokens (the kernel stages an item's slot indices in LDS).
-constexpr int32_t kSplitQuantum = 64;
+// Paged-pass chunks hold a multiple of this many tokens, and at most
+// kMaxSplitTokens (the kernel stages a segment's slot indices in LDS).
+constexpr int32_t kSplitQuantum = 16;
 constexpr int32_t kMaxSplitTokens = 2048;
 
 }  // namespace pkv
@@ -52,18 +52,18 @@ struct pkv_plan {
     // paged pass
     pkv::PagedGeometry geo;
     int32_t head_blocks;
-    int32_t split_tokens, num_splits;
-    int64_t num_work_items;
-    int32_t fuse_reduce;      // last-arriver combine inside the paged kernel
+    int32_t split_tokens;     // positions per chunk of the flat sequence
+    int32_t num_splits;       // partial states per request (chunks one request touches, max)
+    int64_t num_chunks;
+    int64_t num_work_items;   // num_chunks * head_blocks
+    int32_t needs_reduce;     // a combine kernel follows the paged pass
     int32_t concurrent_prefix; // prefix pass on a side stream in decode_step
-    int64_t paged_tokens;     // tokens the paged pass attends (all requests)
-    int32_t paged_max_len;
+    int32_t fuse_cascade;     // decode_step runs both passes in one launch (DENSE)
+    int64_t paged_tokens;     // positions the paged pass attends (all requests)
     // prefix pass
     int32_t prefix_rows_per_wg;
     int32_t prefix_split_tokens, prefix_splits;
     // workspace layout (byte offsets; -1 = unused)
-    int64_t ws_counters;      // [B][head_blocks] int32 at offset 0, kept zero between calls
-    int64_t ws_zero_bytes;
     int64_t ws_paged_acc, ws_paged_ml;
     int64_t ws_prefix_acc, ws_prefix_ml;
     int64_t workspace_bytes;

@@ -1,287 +1,19 @@
-// Shared-prefix attention, prefix read once for the whole batch, on MFMA.
-//
-// "GraniKV: asymmetric KV cache paging for shared-prefix agents", section 2:
-// every decode step each request needs the whole shared prefix, so reading it
-// once for all requests instead of once per request divides the prefix
-// traffic by the batch size; section 3: with M_eff = batch x GQA group query
-// rows per KV head the prefix attention is a real dense contraction, run as
-// large tiles (DENSE) at high M_eff and small tiles (CASCADE) below.
-//
-// For KV head g, the M_eff rows are r = b * G + j (request b, query head
-// g * G + j).  A workgroup owns 32 * NW rows, one KV head and one range of the
-// prefix; its NW waves share each 32-token K/V tile through LDS.
-//
-// Per tile a wave computes S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: with
-// K as the A operand and Q^T as B, a lane of the 32x32 result holds 16 of the
-// 32 tokens of one query row, so the row max and sum need one exchange with
-// the lane 32 apart.  The exponentiated scores, converted to bf16, are
-// already in the B-operand layout of the second product O^T += V^T . P^T
-// (both operands' k-slots are taken in the same token order), so P never
-// leaves registers.  K and V are both kept row-major in LDS; the V^T operand
-// (eight tokens of one head-dim column per lane) is read with gfx950's
-// transposing LDS read, ds_read_b64_tr_b16: within a group of 16 lanes, lane
-// 4c+d receives element d of the 64-bit values read by lanes c, c+4, c+8,
-// c+12, so lanes reading four tokens x four column chunks hand each lane
-// four tokens of one column.
-//
-// Softmax state per row is (m, l) in exp2 units with the same lazily raised
-// maximum as the paged kernel; the partial or final result is written in the
-// same format as the paged pass so the same reduction and merge apply.
-#include <hip/hip_runtime.h>
-
-#include "device_common.h"
-#include "kernels.h"
+// Shared-prefix attention kernels (the body is in prefix_kernel.h).
+#include "prefix_kernel.h"
 
 namespace pkv {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr float kPrefixLazySlack = 8.0f;
-
-// NW waves of 32 query rows each share KT-token K/V tiles through a
-// double-buffered LDS ring: while the waves compute tile n from one buffer,
-// tile n+1 (loaded into registers at the top of the iteration) is written
-// into the other, so one barrier per tile suffices.  The range's slot
-// indices are staged in LDS once, so no tile waits on an index load.
 template <int D, int NW, int KT>
 __global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_kernel(const PrefixArgs a) {
-    // bf16 per LDS row of K and of V: a 32-byte pad makes the row pitch 8
-    // banks (mod 64), so the row-gathering operand reads are conflict free
-    constexpr int KROW = D + 16;
-    constexpr int NKS = D / 16;    // k-steps of the first product
-    constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
-    constexpr int NTB = KT / 32;   // 32-token blocks per tile
-    constexpr int NT = NW * 64;
-    constexpr int KITEMS = KT * D / 8;          // 16-byte chunks of a K (or V) tile
-    constexpr int KCH = (KITEMS + NT - 1) / NT;
-    constexpr int KBUF = KT * KROW;
-
-    __shared__ uint16_t s_k[2][KBUF];
-    __shared__ uint16_t s_v[2][KBUF];
-    __shared__ int s_idx[kMaxPrefixSplitTokens];
-
-    // XCD-aware placement: workgroups are handed to the 8 XCDs round robin,
-    // so give each XCD a contiguous run of logical items; row tiles that read
-    // the same (KV head, prefix range) then share one L2.
-    const int N = a.row_tiles * a.H_kv * a.num_splits;
-    const int per_xcd = (N + 7) / 8;
-    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (item >= N) return;
-    const int tile = item % a.row_tiles;
-    const int g = (item / a.row_tiles) % a.H_kv;
-    const int split = item / (a.row_tiles * a.H_kv);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = lane >> 5;        // which half of the wave
-    const int lr = lane & 31;
-    const int G = a.G;
-    const int H_q = a.H_kv * G;
-    const int M = a.B * G;
-    const int ts = split * a.split_tokens;
-    const int te = min(ts + a.split_tokens, a.prefix_len);
-    const int n_tok = te - ts;
-    const int ntiles = (n_tok + KT - 1) / KT;
-
-    // the range's slot indices, padded with the last one to whole tiles
-    for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = a.prefix_indices[ts + min(i, n_tok - 1)];
-
-    // This lane's query row.
-    const int r = tile * 32 * NW + wave * 32 + lr;
-    const bool row_ok = r < M;
-    const int rb = row_ok ? r / G : 0;
-    const int rq = row_ok ? g * G + r % G : 0;
-    const size_t qrow = (size_t)rb * H_q + rq;
-    bf16x8_t qreg[NKS];
-    {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D + h * 8;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4_t x = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
-            qreg[ks] = __builtin_bit_cast(bf16x8_t, x);
-        }
-    }
-
-    const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
-    const size_t slot_stride = (size_t)a.H_kv * D;
-    const size_t head_off = (size_t)g * D;
-
-    u32x4_t kst[KCH], vst[KCH];
-    auto load_tile = [&](int n) {
-        const int tb = n * KT;
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (KITEMS % NT != 0 && id >= KITEMS) break;
-            const int t = id / (D / 8), ch = id % (D / 8);
-            const size_t off = (size_t)s_idx[tb + t] * slot_stride + head_off + ch * 8;
-            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + off);
-            vst[c] = *reinterpret_cast<const u32x4_t*>(vpool + off);
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (KITEMS % NT != 0 && id >= KITEMS) break;
-            const int t = id / (D / 8), ch = id % (D / 8);
-            *reinterpret_cast<u32x4_t*>(&s_k[buf][t * KROW + ch * 8]) = kst[c];
-            *reinterpret_cast<u32x4_t*>(&s_v[buf][t * KROW + ch * 8]) = vst[c];
-        }
-    };
-    // Transposed-read address of this lane for the V^T operand: lane group
-    // (h, dh) of 16 lanes covers columns db*32 + dh*16 .. +15 and tokens
-    // c*16 + h*4 (+8 for the second read); lane s of the group reads token
-    // s/4 of those four at columns 4*(s%4) .. +3 of the group's sixteen.
-    const int tr_s = lane & 15;
-    const int tr_dh = (lane >> 4) & 1;
-    const int tr_off = (tr_s >> 2) * KROW + tr_dh * 16 + (tr_s & 3) * 4 + h * 4 * KROW;
-
-    f32x16_t acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
-    float m = -INFINITY, l = 0.f;
-
-    auto compute = [&](int n, int buf, auto tailc) {
-        constexpr bool TAIL = decltype(tailc)::value;
-        // S^T = K . Q^T, one 32x32 block per 32 tokens; lane holds row lr and
-        // tokens tb*32 + (i/4)*8 + h*4 + i%4
-        // two independent accumulation chains (even and odd k-steps) so that
-        // consecutive MFMAs do not wait on each other's results
-        f32x16_t s[NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            f32x16_t s_even = f32x16_t{}, s_odd = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ks += 2) {
-                const bf16x8_t ka0 = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + h * 8]));
-                const bf16x8_t ka1 = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + 16 + h * 8]));
-                s_even = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], s_even, 0, 0, 0);
-                s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], s_odd, 0, 0, 0);
-            }
-            s[tb] = s_even + s_odd;
-        }
-        if constexpr (TAIL) {
-            const int valid = n_tok - n * KT;
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (tb * 32 + (i / 4) * 8 + h * 4 + (i % 4) >= valid) s[tb][i] = -INFINITY;
-        }
-        // running max over raw scores (the scale is positive)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-        const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-        }
-        const float mneg = (m == -INFINITY) ? 0.f : -m;
-        float ps = 0.f;
-        bf16x8_t pb[2 * NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4_t x;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float p0 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w], a.scale_log2, mneg));
-                    const float p1 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w + 1], a.scale_log2, mneg));
-                    ps += p0 + p1;
-                    x[w] = pack_bf16x2(p0, p1);
-                }
-                pb[tb * 2 + c] = __builtin_bit_cast(bf16x8_t, x);
-            }
-        l += ps;
-        // O^T += V^T . P^T over 16-token chunks
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int c = 0; c < 2 * NTB; ++c) {
-                typedef short v4s_t __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
-                const uint16_t* vr = &s_v[buf][(c * 16) * KROW + db * 32 + tr_off];
-                const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)vr);
-                const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vr + 8 * KROW));
-                const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0);
-                const u32x2_t y1 = __builtin_bit_cast(u32x2_t, x1);
-                const u32x4_t x = {y0[0], y0[1], y1[0], y1[1]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pb[c],
-                                                                  acc[db], 0, 0, 0);
-            }
-        }
-    };
-
-    __syncthreads();  // s_idx ready
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-    const bool tail = (n_tok % KT) != 0;
-    for (int n = 0; n < ntiles; ++n) {
-        const int buf = n & 1;
-        if (n + 1 < ntiles) load_tile(n + 1);
-        if (tail && n == ntiles - 1) {
-            compute(n, buf, std::integral_constant<bool, true>{});
-        } else {
-            compute(n, buf, std::integral_constant<bool, false>{});
-        }
-        if (n + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
-    }
-
-    // Row totals: the two halves of the wave hold disjoint tokens of a row.
-    const float L = l + __shfl_xor(l, 32);
-    if (!row_ok) return;
-    const bool direct = a.num_splits == 1 && !a.force_partial;
-    float* out;
-    float scale;
-    if (direct) {
-        out = a.o + qrow * D;
-        scale = L > 0.f ? 1.f / L : 0.f;
-    } else {
-        out = a.part_acc + (((size_t)rb * a.num_splits + split) * H_q + rq) * D;
-        scale = 1.f;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t x = {acc[db][q4 * 4] * scale, acc[db][q4 * 4 + 1] * scale, acc[db][q4 * 4 + 2] * scale,
-                               acc[db][q4 * 4 + 3] * scale};
-            *reinterpret_cast<f32x4_t*>(out + db * 32 + q4 * 8 + h * 4) = x;
-        }
-    if (h == 0) {
-        if (direct) {
-            a.lse[qrow] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
-        } else {
-            float* ml = a.part_ml + (((size_t)rb * a.num_splits + split) * H_q + rq) * 2;
-            ml[0] = m;
-            ml[1] = L;
-        }
-    }
+    __shared__ PrefixSmem<D, KT> sm;
+    prefix_item<D, NW, KT>(a, sm, blockIdx.x);
 }
 
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream) {
     const int N = a.row_tiles * a.H_kv * a.num_splits;
     if (N == 0) return hipSuccess;
     if (a.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
-    const int grid = (N + 7) / 8 * 8;
+    const int grid = prefix_blocks(N);
     // DENSE: 4 waves x 32 rows share each tile; CASCADE: 2 waves x 32 rows
     // (small query tiles, more workgroups per CU).  Both stay within 256
     // registers per lane, so a prefix workgroup and a paged workgroup can be

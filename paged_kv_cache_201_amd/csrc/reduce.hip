@@ -19,11 +19,11 @@ namespace pkv {
 constexpr int kReduceBatch = 16;  // partials whose loads are issued together
 
 // Thread (row, e4) owns four consecutive outputs of one row.  The row's
-// partials are the pre_splits prefix partials (if any) followed by its
-// num_splits own ones; every one of them holds a valid (max, sum) pair
-// (empty items record -inf, 0).  They are consumed in batches whose loads
-// are all issued before any is used, so a batch costs one memory round
-// trip; batches are combined in order with the usual rescaling.
+// partials are the pre_splits prefix partials (if any) followed by the chunk
+// partials of its request (if any); each holds a (max, sum) pair, max = -inf
+// for an empty state.  They are consumed in batches whose loads are all
+// issued before any is used, so a batch costs one memory round trip;
+// batches are combined in order with the usual rescaling.
 template <int D>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs a) {
     constexpr int CH = D / 4;
@@ -34,7 +34,19 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
     const int b = row / a.H_q;
     const int qh = row % a.H_q;
     const int npre = a.pre_acc ? a.pre_splits : 0;
-    const int total = npre + a.num_splits;
+    int nparts = 0;
+    if (a.kv_indptr) {
+        // the chunks that request b's positions [ob, on) of the flat sequence touch
+        const int64_t base = (int64_t)a.kv_indptr[0];
+        const int64_t ob = a.kv_indptr[b] - base - (int64_t)b * a.token_offset;
+        const int64_t on = a.kv_indptr[b + 1] - base - (int64_t)(b + 1) * a.token_offset;
+        if (on > ob) {
+            nparts = (int)((on - 1) / a.chunk_tokens - ob / a.chunk_tokens + 1);
+            if (a.skip_whole && nparts == 1) return;  // written by the paged kernel
+            nparts = a.part_acc ? min(nparts, a.max_parts) : 0;
+        }
+    }
+    const int total = npre + nparts;
     float L = 0.f, M = -INFINITY;
     f32x4_t o = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < total; k0 += kReduceBatch) {
@@ -46,7 +58,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
             if (k < total) {
                 const bool pre = k < npre;
                 const size_t prow = pre ? ((size_t)b * a.pre_splits + k) * a.H_q + qh
-                                        : ((size_t)b * a.num_splits + (k - npre)) * a.H_q + qh;
+                                        : ((size_t)b * a.max_parts + (k - npre)) * a.H_q + qh;
                 ml[j] = *reinterpret_cast<const f32x2_t*>((pre ? a.pre_ml : a.part_ml) + prow * 2);
                 x[j] = *reinterpret_cast<const f32x4_t*>((pre ? a.pre_acc : a.part_acc) + prow * D + e4 * 4);
             } else {

@@ -236,14 +236,13 @@ def test_c4_full_sampled():
     dict(B=3, H_q=16, H_kv=2, d=128, own_len=(100, 900), q_dtype="f32", kv_dtype="f32", page_size=16),
     dict(B=1, H_q=32, H_kv=4, d=128, own_len=(1, 1), q_dtype="bf16", kv_dtype="bf16", page_size=16),
 ])
-@pytest.mark.parametrize("splits", ["one", "many", "many-separate-reduce"])
+@pytest.mark.parametrize("splits", ["one", "many", "balanced"])
 def test_edge_shapes(case, splits):
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_decode_batch(seed=sum(case["own_len"]) + case["H_q"], pool_factor=2, **case)
     tuning = {"one": dict(min_split_tokens=2048, target_workgroups=1),
-              "many": dict(min_split_tokens=16, target_workgroups=100000, fuse_split_reduce=1),
-              "many-separate-reduce": dict(min_split_tokens=16, target_workgroups=100000,
-                                           fuse_split_reduce=0)}[splits]
+              "many": dict(min_split_tokens=16, target_workgroups=100000),
+              "balanced": dict(min_split_tokens=16, target_workgroups=7)}[splits]
     o_ref, lse_ref = ob.batch_reference(b)
     say(f"edge {case} splits={splits}")
     o, lse, plan = run_paged(DeviceBatch, b, tuning=tuning)
@@ -253,54 +252,82 @@ def test_edge_shapes(case, splits):
         check_close(case["kv_dtype"], of, lf, o_ref, lse_ref, f"edge f32-out {case}")
 
 
-@pytest.mark.parametrize("fuse", [0, 1])
-def test_split_combine_variants_agree_and_leave_counters_zero(fuse):
+@pytest.mark.parametrize("chunk", [16, 256, 2048])
+def test_chunkings_agree_with_oracle_and_repeat_bitwise(chunk):
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_config("c2", B=5, own_len=(1, 5000), page_size=16)
     o_ref, lse_ref = ob.batch_reference(b)
     db = DeviceBatch.from_batch(b)
-    plan = db.plan(tuning=dict(fuse_split_reduce=fuse, min_split_tokens=256, target_workgroups=4096))
-    assert plan.info["num_splits"] > 4
-    assert (plan.info["workspace_zero_bytes"] > 0) == bool(fuse)
+    plan = db.plan(tuning=dict(min_split_tokens=chunk, target_workgroups=10**8))
+    assert plan.info["split_tokens"] == chunk
     ws = db.workspace(plan)
-    say(f"split combine fuse={fuse}")
+    if ws is not None:
+        ws.fill_(0xFF)  # the workspace needs no initial contents (0xFFFFFFFF is a NaN)
+    say(f"chunk={chunk}")
     o1, l1 = db.step(plan, ws=ws)
     o2, l2 = db.step(plan, ws=ws)
     torch.cuda.synchronize()
-    check_close("bf16", o1, l1, o_ref, lse_ref, f"fuse={fuse}")
+    check_close("bf16", o1, l1, o_ref, lse_ref, f"chunk={chunk}")
     assert same_bits(o1, o2) and same_bits(l1, l2)
-    nz = plan.info["workspace_zero_bytes"]
-    if nz:
-        assert int(ws[:nz].count_nonzero()) == 0, "arrival counters not reset"
-    other = db.plan(tuning=dict(fuse_split_reduce=1 - fuse, min_split_tokens=256, target_workgroups=4096))
-    o3, l3 = db.step(other)
-    torch.cuda.synchronize()
-    assert same_bits(o1, o3) and same_bits(l1, l3), "fused and separate combine differ"
 
 
-@pytest.mark.parametrize("fuse", [0, 1])
-def test_empty_requests_with_many_splits(fuse):
+def test_empty_and_tiny_requests_across_chunks():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     lens = [0, 1500, 0, 63, 64, 65, 0, 1000]
     b = make_decode_batch(seed=8, B=8, H_q=32, H_kv=8, d=128, own_len=(0, 0), own_lens=lens, page_size=16)
     o_ref, lse_ref = ob.batch_reference(b)
-    tune = dict(min_split_tokens=64, target_workgroups=100000, fuse_split_reduce=fuse)
-    say(f"empty requests, many splits, fuse={fuse}")
-    o, lse, plan = run_paged(DeviceBatch, b, tuning=tune)
-    assert plan.info["num_splits"] > 1
-    check_close("bf16", o, lse, o_ref, lse_ref, "empty requests")
-    assert torch.isinf(lse[0]).all() and not o[0].float().abs().sum()
+    for tune in (dict(min_split_tokens=64, target_workgroups=100000), dict(min_split_tokens=2048)):
+        say(f"empty requests {tune}")
+        o, lse, plan = run_paged(DeviceBatch, b, tuning=tune)
+        check_close("bf16", o, lse, o_ref, lse_ref, f"empty requests {tune}")
+        assert torch.isinf(lse[0]).all() and not o[0].float().abs().sum()
+    # many one-to-three-token requests share each chunk, empty ones between
+    lens = [int(x) for x in np.random.default_rng(3).integers(0, 4, size=300)]
+    t = make_decode_batch(seed=10, B=300, H_q=16, H_kv=4, d=64, own_len=(0, 0), own_lens=lens, q_dtype="f32",
+                          kv_dtype="f32", page_size=1)
+    o_ref, lse_ref = ob.batch_reference(t)
+    for tune in (dict(min_split_tokens=16, target_workgroups=100000), dict(min_split_tokens=2048)):
+        say(f"tiny requests {tune}")
+        o, lse, plan = run_paged(DeviceBatch, t, tuning=tune)
+        check_close("f32", o, lse, o_ref, lse_ref, f"tiny requests {tune}")
     # a shared prefix whose suffixes are partly empty, on every path
+    lens = [0, 1500, 0, 63, 64, 65, 0, 1000]
     c = make_decode_batch(seed=9, B=8, H_q=32, H_kv=8, d=128, own_len=(0, 0), prefix_len=256, own_lens=lens,
                           page_size=16)
     o_ref, lse_ref = ob.batch_reference(c)
     db = DeviceBatch.from_batch(c)
     for force in (0, 1, 2):
-        plan = db.plan(shared_prefix_len=256, force_path=force, tuning=tune)
-        say(f"empty suffixes force={force} fuse={fuse}")
+        plan = db.plan(shared_prefix_len=256, force_path=force, tuning=dict(min_split_tokens=64,
+                                                                            target_workgroups=100000))
+        say(f"empty suffixes force={force}")
         o, lse = db.step(plan)
         torch.cuda.synchronize()
         check_close("bf16", o, lse, o_ref, lse_ref, f"empty suffixes path {force}")
+
+
+def test_fused_cascade_launch_matches_separate_launches():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    cases = [make_config("c3", B=64, own_len=(0, 300)),
+             make_decode_batch(seed=12, B=37, H_q=16, H_kv=2, d=64, own_len=(0, 700), prefix_len=320,
+                               page_size=16),
+             make_decode_batch(seed=13, B=5, H_q=64, H_kv=8, d=128, own_len=(1, 3000), prefix_len=2048,
+                               page_size=16)]
+    for b in cases:
+        o_ref, lse_ref = ob.batch_reference(b)
+        db = DeviceBatch.from_batch(b)
+        outs = []
+        for fuse in (0, 1):
+            for tune in (dict(), dict(min_split_tokens=16, target_workgroups=100000, prefix_target_workgroups=4096,
+                                      min_prefix_split_tokens=64)):
+                t = dict(tune, fuse_cascade=fuse)
+                plan = db.plan(shared_prefix_len=b.prefix_len, force_path=2, tuning=t)
+                say(f"fused cascade B={b.B} G={b.H_q // b.H_kv} d={b.d} {t}")
+                o, lse = db.step(plan)
+                torch.cuda.synchronize()
+                check_close("bf16", o, lse, o_ref, lse_ref, f"fuse={fuse} {tune}")
+                outs.append((o, lse))
+        assert same_bits(outs[0][0], outs[2][0]) and same_bits(outs[0][1], outs[2][1])
+        assert same_bits(outs[1][0], outs[3][0]) and same_bits(outs[1][1], outs[3][1])
 
 
 def test_concurrent_prefix_pass_matches_single_stream():
@@ -311,7 +338,8 @@ def test_concurrent_prefix_pass_matches_single_stream():
     outs = []
     for conc in (0, 1):
         for force in (1, 2):
-            plan = db.plan(shared_prefix_len=b.prefix_len, force_path=force, tuning=dict(concurrent_prefix=conc))
+            plan = db.plan(shared_prefix_len=b.prefix_len, force_path=force,
+                           tuning=dict(concurrent_prefix=conc, fuse_cascade=0))
             say(f"concurrent_prefix={conc} force={force}")
             o, lse = db.step(plan)
             torch.cuda.synchronize()
@@ -320,7 +348,7 @@ def test_concurrent_prefix_pass_matches_single_stream():
     assert same_bits(outs[0][0], outs[2][0]) and same_bits(outs[1][0], outs[3][0])
     # on a non-default caller stream, with work queued ahead of the step
     side = torch.cuda.Stream()
-    plan = db.plan(shared_prefix_len=b.prefix_len, force_path=2, tuning=dict(concurrent_prefix=1))
+    plan = db.plan(shared_prefix_len=b.prefix_len, force_path=2, tuning=dict(concurrent_prefix=1, fuse_cascade=0))
     with torch.cuda.stream(side):
         q_saved = db.q.clone()
         db.q.mul_(1.0)  # queued work the step must wait for

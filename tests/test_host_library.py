@@ -38,7 +38,12 @@ def test_status_strings_and_version():
         assert pkv.pkv_status_string(st) != "unknown status"
     assert "gfx950" in pkv.pkv_version()
     d = pkv.pkv_tuning_defaults()
-    assert d["t_dense"] > 0 and d["target_workgroups"] > 0
+    # every field lands where the C struct has it (a shifted field shows up here)
+    assert d["t_dense"] >= 1 and d["gate_ratio"] >= 0 and d["launch_bytes"] >= 0
+    assert d["target_workgroups"] >= 1 and 1 <= d["min_split_tokens"] <= 2048
+    assert d["concurrent_prefix"] in (0, 1) and d["fuse_cascade"] in (0, 1)
+    assert d["prefix_target_workgroups"] >= 1 and 1 <= d["min_prefix_split_tokens"] <= 1024
+    assert len(d) == 9
 
 
 # ---------------------------------------------------------------- lowering --
@@ -162,29 +167,53 @@ def test_config_shapes_plan_as_documented():
     assert c5["m_eff"] == 128 and c5["path_name"] == "PAGED"
 
 
-def test_split_partition_covers_every_token_once():
+def _chunking(lens, prefix_tokens, C):
+    """Chunks of the flat sequence of attended positions, and the most chunks
+    any one request touches (its partial states)."""
+    total, parts, pos = 0, 1, 0
+    for L in lens:
+        n = int(L) - prefix_tokens
+        if n > 0:
+            parts = max(parts, (pos + n - 1) // C - pos // C + 1)
+        pos += n
+    return -(-pos // C), parts
+
+
+def test_chunk_partition_is_balanced_and_counted():
     rng = np.random.default_rng(5)
     for _ in range(200):
         B = int(rng.integers(1, 64))
         lens = rng.integers(0, 20000, size=B)
+        if rng.random() < 0.3:
+            lens[rng.integers(0, B, size=B // 2)] = 0
         P = int(rng.integers(0, lens.min() + 1))
         t = dict(target_workgroups=int(rng.integers(1, 4096)), min_split_tokens=int(rng.integers(1, 2048)))
         info = _both(B, 4, P, 16, L=lens, tune=t)
         if info is None:
             continue
-        C, S = info["split_tokens"], info["num_splits"]
-        assert C % 16 == 0 and C <= 2048
-        for L in lens:
-            n = int(L) - info["prefix_tokens"]
-            covered = sum(max(0, min((s + 1) * C, n) - s * C) for s in range(S))
-            assert covered == n and S * C >= n
+        C = info["split_tokens"]
+        assert C % 16 == 0 and 16 <= C <= 2048
+        assert C >= min(2048, t["min_split_tokens"])
+        chunks, parts = _chunking(lens, info["prefix_tokens"], C)
+        head_blocks = 8 // info["heads_per_item"]
+        assert info["num_work_items"] == chunks * head_blocks
+        assert info["num_splits"] == parts
+        # every chunk but the last holds exactly C positions: equal work per workgroup
+        total = int(sum(int(L) - info["prefix_tokens"] for L in lens))
+        assert chunks == 0 or (chunks - 1) * C < total <= chunks * C
 
 
 def test_plan_workspace_and_geometry():
     info = _both(32, 4, 0, 128, L=4096)
-    assert info["heads_per_item"] == 8 and info["num_splits"] * info["split_tokens"] >= 4096
-    assert info["workspace_bytes"] >= 32 * 32 * info["num_splits"] * 130 * 4 or info["num_splits"] == 1
+    assert info["heads_per_item"] == 8 and info["num_work_items"] * info["split_tokens"] >= 32 * 4096
+    rows = 32 * 32
+    if info["num_splits"] > 1:
+        assert info["workspace_bytes"] >= rows * info["num_splits"] * 130 * 4
     c5 = _both(16, 8, 0, 16, L=16384, kv="fp8")
     assert c5["heads_per_item"] == 4
-    c1 = _both(4, 4, 0, 16, L=[64, 100, 200, 256], H_kv=2, d=64, q="f32", kv="f32")
+    # one chunk holds every request whole: outputs written directly, no workspace
+    c1 = _both(4, 4, 0, 16, L=[64, 100, 200, 256], H_kv=2, d=64, q="f32", kv="f32", tune=dict(min_split_tokens=2048))
     assert c1["heads_per_item"] == 2 and c1["num_splits"] == 1 and c1["workspace_bytes"] == 0
+    # a cascade step keeps partial states for both passes
+    c3 = _both(256, 4, 4096, 16, L=4096 + 300)
+    assert c3["workspace_bytes"] >= 256 * 32 * (c3["prefix_splits"] + c3["num_splits"]) * 130 * 4
