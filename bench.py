@@ -88,9 +88,14 @@ def add_ceiling(rec, ceiling):
     return rec
 
 
-def bench_prefix_config(name, steps, warmup):
-    """PAGED over unique prefix copies, PAGED over shared pages, and each
-    prefix path, plus the planner's choice."""
+# legs of a shared-prefix workload: label, forced path, tuning
+PREFIX_LEGS = (("paged_shared", 0, None), ("cascade", 1, None), ("dense", 2, None),
+               ("dense_separate", 2, dict(fuse_cascade=0)), ("planned", -1, None))
+
+
+def bench_prefix_config(name, steps, warmup, legs=None):
+    """PAGED over unique prefix copies, PAGED over shared pages, each prefix
+    path (DENSE also as two launches), and the planner's choice."""
     import torch
     from paged_kv_cache_201_amd.step import DeviceBatch
     from workloads import make_config, relayout
@@ -99,8 +104,10 @@ def bench_prefix_config(name, steps, warmup):
     out = dict(workload=name, B=b.B, prefix=P)
     db = DeviceBatch.from_batch(b)
     o, lse = db.new_out(), db.new_lse()
-    for force, label in ((0, "paged_shared"), (1, "cascade"), (2, "dense"), (-1, "planned")):
-        plan = db.plan(shared_prefix_len=P, force_path=force)
+    for label, force, tune in PREFIX_LEGS:
+        if legs and label not in legs:
+            continue
+        plan = db.plan(shared_prefix_len=P, force_path=force, tuning=tune)
         ws = db.workspace(plan)
         ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
         path = plan.info["path_name"]
@@ -110,19 +117,23 @@ def bench_prefix_config(name, steps, warmup):
         del ws
     del db
     torch.cuda.empty_cache()
-    u = relayout(b, page_size=b.page_size, seed=2000 + int(name[1:]), layout="unique", device="cuda")
+    if not legs or "paged_unique" in legs:
+        u = relayout(b, page_size=b.page_size, seed=2000 + int(name[1:]), layout="unique", device="cuda")
+        du = DeviceBatch.from_batch(u)
+        plan = du.plan(force_path=0)
+        ws = du.workspace(plan)
+        ms = time_steps(lambda: du.step(plan, o, lse, ws), steps, warmup)
+        nbytes = algorithmic_bytes(u, "PAGED")
+        out["paged_unique"] = dict(path="PAGED", us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
+                                   pct_peak=100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                   algorithmic_bytes=nbytes)
+        del du, u, ws
     del b
-    du = DeviceBatch.from_batch(u)
-    plan = du.plan(force_path=0)
-    ws = du.workspace(plan)
-    ms = time_steps(lambda: du.step(plan, o, lse, ws), steps, warmup)
-    nbytes = algorithmic_bytes(u, "PAGED")
-    out["paged_unique"] = dict(path="PAGED", us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
-                               pct_peak=100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, algorithmic_bytes=nbytes)
-    out["speedup_vs_paged_unique"] = out["paged_unique"]["us_per_step"] / out["planned"]["us_per_step"]
-    out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["planned"]["us_per_step"]
-    del du, u, ws
     torch.cuda.empty_cache()
+    if "planned" in out and "paged_unique" in out:
+        out["speedup_vs_paged_unique"] = out["paged_unique"]["us_per_step"] / out["planned"]["us_per_step"]
+    if "planned" in out and "paged_shared" in out:
+        out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["planned"]["us_per_step"]
     return out
 
 
@@ -135,7 +146,7 @@ def read_ceiling(steps=20, warmup=5, gib=4):
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     best = None
-    for wgs in (1024, 2048, 4096):
+    for wgs in (512, 1024, 2048):
         out = torch.empty(wgs, dtype=torch.int32, device="cuda")
         ms = time_steps(lambda: pkv.pkv_stream_read_probe(buf, out, wgs), steps, warmup)
         gbs = n / (ms * 1e-3) / 1e9
@@ -244,6 +255,42 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
     return rec
 
 
+def write_prefix_traffic(name, unique_dir, separate_dir, commands):
+    """Prefix-traffic reduction of a shared-prefix workload from two FETCH_SIZE
+    runs: PAGED over per-request prefix copies, and the cascade step run as
+    separate launches (so that the prefix pass has its own dispatches)."""
+    import statistics
+    from workloads import make_config
+    b = make_config(name)
+    P, B = b.prefix_len, b.B
+    prefix_bytes = P * b.H_kv * b.d * 2 * BYTES[b.kv_dtype]
+    res = {}
+    for label, d in (("paged_unique", unique_dir), ("cascade_separate", separate_dir)):
+        fetch = pmc_per_dispatch(d, "FETCH_SIZE")
+        probe = [v for (k, _), vs in fetch.items() if "stream_read_kernel" in k for v in vs]
+        scale = (4 << 30) / (statistics.median(probe) * 1024)
+        per = {}
+        for (k, grid), vs in fetch.items():
+            if k.startswith("pkv::") and "stream_read" not in k:
+                per[f"{k} grid={grid}"] = statistics.median(vs) * 1024 * scale
+        res[label] = dict(fetch_scale=scale, bytes_per_dispatch=per)
+    pre = [v for k, v in res["cascade_separate"]["bytes_per_dispatch"].items() if "prefix_attn_kernel" in k]
+    uniq = sum(v for k, v in res["paged_unique"]["bytes_per_dispatch"].items() if "paged_split_kernel" in k)
+    casc = sum(res["cascade_separate"]["bytes_per_dispatch"].values())
+    rec = dict(workload=f"{name}: B={B} requests sharing a {P}-token prefix, {b.H_q}/{b.H_kv} heads, d={b.d}, "
+                        f"{b.kv_dtype}, page size {b.page_size}",
+               commands=commands, source_sha256=kernel_source_hash(), prefix_bytes=prefix_bytes,
+               per_request_prefix_bytes_total=B * prefix_bytes,
+               prefix_pass_fetch_bytes=sum(pre),
+               reduction_vs_per_request_reads=B * prefix_bytes / sum(pre) if pre else None,
+               paged_unique_fetch_bytes=uniq, cascade_step_fetch_bytes=casc,
+               saved_over_prefix_bytes=(uniq - casc) / prefix_bytes, runs=res)
+    path = os.path.join(ROOT, "profiles", f"prefix_attn_kernel.{name}_shared_prefix.traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def measured_traffic():
     """Scaled HBM bytes per decode step of the headline workload from the
     committed counter summary, or None when the sources changed since."""
@@ -317,13 +364,29 @@ def cpu_baseline(batch, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", metavar="CONFIG:LEG[,LEG]",
+                    help="time only these legs of one shared-prefix workload (e.g. c3:paged_unique) and exit; "
+                         "for profiling one leg at a time")
+    ap.add_argument("--summarize-prefix-traffic", nargs=3, metavar=("CONFIG", "UNIQUE_DIR", "SEPARATE_DIR"),
+                    help="write the prefix-traffic summary from two FETCH_SIZE runs (see --only) and exit")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
     args = ap.parse_args()
+    if args.summarize_prefix_traffic:
+        name, u, c = args.summarize_prefix_traffic
+        prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE"
+        cmds = dict(paged_unique=f"{prof} --output-format csv -d {u} -o run -- python bench.py --only {name}:paged_unique "
+                                 "--steps 10 --warmup 2",
+                    cascade_separate=f"{prof} --output-format csv -d {c} -o run -- python bench.py --only "
+                                     f"{name}:dense_separate --steps 10 --warmup 2",
+                    summary=f"python bench.py --summarize-prefix-traffic {name} {u} {c}")
+        rec = write_prefix_traffic(name, u, c, cmds)
+        print(json.dumps({k: v for k, v in rec.items() if k != "runs"}, indent=1))
+        return
     if args.summarize_profiles:
         t, f, w = args.summarize_profiles
         prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && "
@@ -342,6 +405,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.only:
+        name, legs = args.only.split(":")
+        read_ceiling(steps=1, warmup=0)  # a known 4 GiB read, to scale FETCH_SIZE by
+        print(json.dumps(bench_prefix_config(name, args.steps, args.warmup, legs=legs.split(","))), flush=True)
+        return
     wanted = args.configs.split(",")
     extra = {}
     log = lambda m: print(m, file=sys.stderr, flush=True)

@@ -112,10 +112,12 @@ typedef struct pkv_tuning {
     int32_t concurrent_prefix;  /* 1: pkv_decode_step runs the prefix pass on a library-owned
                                    side stream (same priority) concurrently with the suffix
                                    pass, joined by events before the combine; 0: one stream */
-    int32_t fuse_cascade;       /* 1: on a DENSE plan pkv_decode_step runs the prefix items
-                                   and the suffix chunks in one launch, interleaved, so
-                                   that MFMA work and HBM streaming overlap on every CU;
-                                   0: one launch per pass */
+    int32_t fuse_cascade;       /* k > 0: on a DENSE plan, pkv_decode_step runs the prefix
+                                   items and the suffix chunks in one launch, interleaved so
+                                   that MFMA work and HBM streaming overlap on every CU, when
+                                   the prefix pass has at least k MFMA flops per byte of
+                                   suffix K/V and its items fill at most half of
+                                   target_workgroups; 0: always one launch per pass */
     int32_t prefix_target_workgroups; /* prefix pass: workgroups to aim for (query tiles x
                                          prefix ranges) */
     int32_t min_prefix_split_tokens;  /* prefix pass: smallest prefix range per workgroup
@@ -288,9 +290,10 @@ pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Measurement aid: read `bytes` of device memory at `buf` once, with 16-byte
- * loads from num_workgroups workgroups of 256 threads, and write one word per
- * workgroup to out[num_workgroups] (device).  Its duration gives the
+ * Measurement aid: read `bytes` of device memory at `buf` once (each of
+ * num_workgroups workgroups of 256 threads streams one contiguous block with
+ * 16-byte non-temporal loads) and write one word per workgroup to
+ * out[num_workgroups] (device).  Its duration gives the
  * streaming-read bandwidth ceiling of the GPU, against which the attention
  * kernels' achieved bandwidth is compared ([P1] "When source beats
  * intuition" and "A backend where pages really do reach the kernel" judge

@@ -98,11 +98,11 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->gate_ratio = 1;
     out->launch_bytes = 40LL * 1000 * 1000;   // ~5 us at 8 TB/s for two extra launches
     out->target_workgroups = 512;   // two workgroups per CU
-    out->min_split_tokens = 256;
+    out->min_split_tokens = 64;
     out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
-    out->fuse_cascade = 1;
+    out->fuse_cascade = 12;  // MFMA flops per suffix byte: fused on c3 (57), separate on c4 (3)
     out->prefix_target_workgroups = 256;
-    out->min_prefix_split_tokens = 256;
+    out->min_prefix_split_tokens = 64;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -177,7 +177,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     }
     if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
         tu.min_split_tokens < 1 ||
-        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.fuse_cascade < 0 || tu.fuse_cascade > 1 ||
+        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.fuse_cascade < 0 ||
         tu.prefix_target_workgroups < 1 ||
         tu.min_prefix_split_tokens < 1)
         return PKV_EINVAL;
@@ -288,10 +288,17 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         any_empty |= n == 0;
     }
     pl->paged_tokens = total;
-    // When one launch runs both passes of a DENSE step, the suffix chunks
-    // fill the workgroup slots the prefix items leave (but at least half).
+    // One launch runs both passes of a DENSE step when the prefix pass is
+    // heavy enough to hide suffix streaming under it and its items take at
+    // most half of the workgroup slots; the suffix chunks then fill the rest.
+    if (pl->fuse_cascade) {
+        const int64_t prefix_flops = 4 * m_eff * prefix_tokens * D * H_kv;
+        const int64_t suffix_bytes = total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+        if (2 * prefix_wgs > tu.target_workgroups || prefix_flops < (int64_t)tu.fuse_cascade * suffix_bytes)
+            pl->fuse_cascade = 0;
+    }
     int64_t target = tu.target_workgroups;
-    if (pl->fuse_cascade) target = std::max<int64_t>(target - prefix_wgs, (target + 1) / 2);
+    if (pl->fuse_cascade) target -= prefix_wgs;
     const int64_t per_item = ceil_div(total * pl->head_blocks, target);
     int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
     chunk = align_up(chunk, pkv::kSplitQuantum);

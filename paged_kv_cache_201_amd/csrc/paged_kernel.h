@@ -79,6 +79,14 @@ constexpr int kPagedWaves = PKV_PAGED_WAVES;
 #define PKV_PAGED_PIPE 2
 #endif
 constexpr int kPagedPipe = PKV_PAGED_PIPE;  // register buffers of K/V loads (2 or 3)
+// fp8 K/V: tokens per iteration and pipeline depth (the fp8 kernel is bound
+// by vector ALU work, so its loads need to run further ahead)
+#ifndef PKV_FP8_PIPE
+#define PKV_FP8_PIPE 2
+#endif
+#ifndef PKV_FP8_U
+#define PKV_FP8_U 0
+#endif
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units
 
 template <int KV, int D, int G, int NHL, int TPI>
@@ -92,25 +100,26 @@ struct PagedCfg {
     static constexpr bool QF32 = (KV == PKV_F32);
     static constexpr int QW = QF32 ? EPL : EPL / 2;  // q registers per (slot, head)
     // steps per iteration: 8 KB of K+V in flight per wave per buffer
-    static constexpr int U0 = 32 / (NHL * 2 * LW);
+    static constexpr int U0 = (KV == PKV_FP8_E4M3 && PKV_FP8_U > 0) ? PKV_FP8_U : 32 / (NHL * 2 * LW);
     static constexpr int U = U0 < 2 ? 2 : U0;
+    static constexpr int PIPE = KV == PKV_FP8_E4M3 ? PKV_FP8_PIPE : kPagedPipe;
     static constexpr int TU = U * TPI;  // tokens per wave iteration
     static constexpr int PARTIALS = NW * TPI;
     static constexpr int MERGE_FLOATS = PARTIALS * HB * G * D;
-    // slot indices of an item, padded to whole wave iterations
+    // slot indices of a chunk, padded by whole wave iterations
     static constexpr int IDX_INTS = kMaxSplitTokens + NW * TU;
-    static constexpr int LDS_FLOATS = MERGE_FLOATS > IDX_INTS ? MERGE_FLOATS : IDX_INTS;
     static_assert(G <= LPH, "one query head per lane after the row reduction");
     static_assert(TPI == 1 || NHL == 1, "several tokens per load only with one head slot");
     static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
 };
 
-// LDS of one paged workgroup: slot indices of the current segment, later
-// reused for the per-wave partial accumulators; the per-wave (max, sum).
+// LDS of one paged workgroup: the per-wave partial accumulators and (max,
+// sum) pairs of a segment, and the slot indices of the current segment.
 template <int KV, int D, int G, int NHL, int TPI>
 struct PagedSmem {
     using C = PagedCfg<KV, D, G, NHL, TPI>;
-    float buf[C::LDS_FLOATS];
+    float buf[C::MERGE_FLOATS];
+    int idx[C::IDX_INTS];
     float ml[C::PARTIALS * C::HB * G * 2];
     int first_request;
 };
@@ -119,11 +128,13 @@ struct PagedSmem {
 // indices start at kv_indices[idx_beg], for the HB KV heads of head block
 // hblk.  slot < 0: the segment is the whole request and its normalised output
 // goes to o / o_f32 / lse; slot >= 0: its partial state goes to partial
-// index `slot` of request b.  Called by every thread of the workgroup.
+// index `slot` of request b.  staged: sm.idx already holds the segment's slot
+// indices (and at least a whole iteration past its end).  Called by every
+// thread of the workgroup.
 template <int KV, int D, int G, int NHL, int TPI>
 __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, D, G, NHL, TPI>& sm, const int b,
                                               const int hblk, const int idx_beg, const int n_tok,
-                                              const int slot) {
+                                              const int slot, const bool staged) {
     using C = PagedCfg<KV, D, G, NHL, TPI>;
     constexpr int BK = C::BK, EPL = C::EPL, LW = C::LW, LPH = C::LPH, RS = C::RS, HB = C::HB;
     constexpr int NW = C::NW, QW = C::QW, U = C::U, TU = C::TU;
@@ -144,14 +155,15 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
     const int w1 = min(w0 + per_wave, n_tok);
     const int niter = (w1 - w0 + TU - 1) / TU;
 
-    // Stage this item's slot indices in LDS, padded with the last slot up to
-    // a whole iteration so that the tail needs no clamping (padded tokens are
-    // masked out of the softmax).
-    int* s_idx = reinterpret_cast<int*>(s_buf);
-    const int n_pad = (n_tok + TU - 1) / TU * TU;
-    for (int i = threadIdx.x; i < n_pad; i += NW * 64)
-        s_idx[i] = a.kv_indices[idx_beg + min(i, n_tok - 1)];
-    __syncthreads();
+    // Stage this segment's slot indices in LDS, padded with the last slot up
+    // to a whole iteration so that the tail needs no clamping (padded tokens
+    // are masked out of the softmax).
+    int* const s_idx = sm.idx;
+    if (!staged) {
+        const int n_pad = (n_tok + TU - 1) / TU * TU;
+        for (int i = threadIdx.x; i < n_pad; i += NW * 64) s_idx[i] = a.kv_indices[idx_beg + min(i, n_tok - 1)];
+        __syncthreads();
+    }
 
     const int lrow = lane / LPH;
     const int lch = lane % LPH;
@@ -204,7 +216,7 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
 #pragma unroll
     for (int i = 0; i < NHL; ++i) loff[i] = head_local(i) * D * BK + lch * EPL * BK;
 
-    LV kb[kPagedPipe][U][NHL], vb[kPagedPipe][U][NHL];
+    LV kb[C::PIPE][U][NHL], vb[C::PIPE][U][NHL];
 
     auto issue = [&](int it, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
@@ -390,11 +402,11 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         }
     };
 
-    // Register pipeline kPagedPipe deep: the loads of the next kPagedPipe-1
+    // Register pipeline C::PIPE deep: the loads of the next C::PIPE - 1
     // iterations are in flight while one iteration is computed.
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    if constexpr (kPagedPipe == 2) {
+    if constexpr (C::PIPE == 2) {
         if (niter > 0) issue(0, B0{});
         for (int it = 0; it < niter; it += 2) {
             if (it + 1 < niter) issue(it + 1, B1{});
@@ -506,8 +518,17 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
     const int64_t C = a.chunk_tokens;
     const int64_t c0 = (int64_t)w * C;
     const int64_t c1 = c0 + C < a.total_tokens ? c0 + C : a.total_tokens;
-    // The request holding position c0: the one non-empty request whose flat
-    // range contains it.
+    // Without a skipped prefix the flat sequence is kv_indices itself, so
+    // the chunk's slot indices are staged at once, while the request holding
+    // position c0 (the one non-empty request whose flat range contains it)
+    // is looked up.
+    const bool flat = a.token_offset == 0;
+    if (flat) {
+        constexpr int TU = PagedCfg<KV, D, G, NHL, TPI>::TU;
+        const int n = (int)(c1 - c0);
+        const int64_t beg = (int64_t)a.kv_indptr[0] + c0;
+        for (int i = threadIdx.x; i < n + TU; i += NT) sm.idx[i] = a.kv_indices[beg + min(i, n - 1)];
+    }
     if (threadIdx.x == 0) sm.first_request = -1;
     __syncthreads();
     for (int i = threadIdx.x; i < a.B; i += NT)
@@ -528,8 +549,9 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
         if (slot >= a.max_parts) return;  // kv_indptr does not describe the planned batch
         if (!first) __syncthreads();  // the previous segment is done with LDS
         first = false;
+        // the first segment starts at c0: its indices are staged already
         paged_segment<KV, D, G, NHL, TPI>(a, sm, b, hblk, a.kv_indptr[b] + a.token_offset + (int)(lo - ob),
-                                          (int)(hi - lo), slot);
+                                          (int)(hi - lo), slot, flat && lo == c0);
     }
 }
 
