@@ -244,8 +244,13 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
             kernels[f"{k} grid={grid}"] = dict(dispatches=len(vs), fetch_kib_median=med(vs),
                                                write_kib_median=med(w),
                                                bytes=med(vs) * 1024 * fetch_scale + med(w) * 1024 * write_scale)
+    # the sources the profiled run was built from (its bench line), else these
+    try:
+        sha = json.loads(open(trace_dir.rstrip("/") + ".json").read().strip().splitlines()[-1])["source_sha256"]
+    except (OSError, ValueError, KeyError, IndexError):
+        sha = kernel_source_hash()
     rec = dict(workload="Llama-3.1-8B decode layer, B=32, 4096 tokens, bf16, page size 1 and 128 (same plan)",
-               commands=commands, source_sha256=kernel_source_hash(), fetch_scale=fetch_scale,
+               commands=commands, source_sha256=sha, fetch_scale=fetch_scale,
                write_scale=write_scale,
                calibration="FETCH_SIZE of the streaming-read probe over 4 GiB; WRITE_SIZE of torch's fill of "
                            "the same 4 GiB buffer",
@@ -277,9 +282,13 @@ def write_prefix_traffic(name, unique_dir, separate_dir, commands):
     pre = [v for k, v in res["cascade_separate"]["bytes_per_dispatch"].items() if "prefix_attn_kernel" in k]
     uniq = sum(v for k, v in res["paged_unique"]["bytes_per_dispatch"].items() if "paged_split_kernel" in k)
     casc = sum(res["cascade_separate"]["bytes_per_dispatch"].values())
+    try:
+        sha = json.loads(open(separate_dir.rstrip("/") + ".json").read().strip().splitlines()[-1])["source_sha256"]
+    except (OSError, ValueError, KeyError, IndexError):
+        sha = kernel_source_hash()
     rec = dict(workload=f"{name}: B={B} requests sharing a {P}-token prefix, {b.H_q}/{b.H_kv} heads, d={b.d}, "
                         f"{b.kv_dtype}, page size {b.page_size}",
-               commands=commands, source_sha256=kernel_source_hash(), prefix_bytes=prefix_bytes,
+               commands=commands, source_sha256=sha, prefix_bytes=prefix_bytes,
                per_request_prefix_bytes_total=B * prefix_bytes,
                prefix_pass_fetch_bytes=sum(pre),
                reduction_vs_per_request_reads=B * prefix_bytes / sum(pre) if pre else None,
@@ -408,7 +417,9 @@ def main():
     if args.only:
         name, legs = args.only.split(":")
         read_ceiling(steps=1, warmup=0)  # a known 4 GiB read, to scale FETCH_SIZE by
-        print(json.dumps(bench_prefix_config(name, args.steps, args.warmup, legs=legs.split(","))), flush=True)
+        rec = bench_prefix_config(name, args.steps, args.warmup, legs=legs.split(","))
+        rec["source_sha256"] = kernel_source_hash()
+        print(json.dumps(rec), flush=True)
         return
     wanted = args.configs.split(",")
     extra = {}
@@ -483,6 +494,7 @@ def main():
                                "(events cannot split one library call)",
                      "read_ceiling_gbs": ceiling},
         "cpu_baseline": cpu,
+        "source_sha256": kernel_source_hash(),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

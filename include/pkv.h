@@ -122,6 +122,8 @@ typedef struct pkv_tuning {
                                          prefix ranges) */
     int32_t min_prefix_split_tokens;  /* prefix pass: smallest prefix range per workgroup
                                          (rounded up to a multiple of 64) */
+    int32_t max_heads_per_item; /* paged pass: at most this many KV heads per work item
+                                   (0: as many as one wave-wide load covers) */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */

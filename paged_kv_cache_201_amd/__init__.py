@@ -56,7 +56,8 @@ class pkv_tuning(ctypes.Structure):
     _fields_ = [("t_dense", ctypes.c_int32), ("gate_ratio", ctypes.c_int32), ("launch_bytes", ctypes.c_int64),
                 ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
                 ("concurrent_prefix", ctypes.c_int32), ("fuse_cascade", ctypes.c_int32),
-                ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32)]
+                ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32),
+                ("max_heads_per_item", ctypes.c_int32)]
 
 
 class pkv_plan_info(ctypes.Structure):

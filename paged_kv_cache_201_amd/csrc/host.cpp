@@ -40,7 +40,7 @@ bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 namespace pkv {
 
-bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t num_kv_heads,
+bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t num_kv_heads, int32_t max_heads,
                     PagedGeometry* out) {
     if (head_dim != 64 && head_dim != 128) return false;
     if (!group_supported(group) || num_kv_heads < 1) return false;
@@ -58,14 +58,15 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
 #ifndef PKV_LANE_VALUES
 #define PKV_LANE_VALUES 64
 #endif
+    const auto allowed = [&](int32_t hb) { return max_heads <= 0 || hb <= max_heads; };
     for (int32_t nhl = 2; nhl >= 1; --nhl) {
-        if (nhl * group * epl <= PKV_LANE_VALUES && num_kv_heads % (rs * nhl) == 0) {
+        if (nhl * group * epl <= PKV_LANE_VALUES && num_kv_heads % (rs * nhl) == 0 && allowed(rs * nhl)) {
             *out = PagedGeometry{epl, lph, rs, nhl, 1, rs * nhl};
             return true;
         }
     }
     for (int32_t hb = rs / 2; hb >= 1; hb /= 2) {
-        if (num_kv_heads % hb == 0) {
+        if (num_kv_heads % hb == 0 && allowed(hb)) {
             *out = PagedGeometry{epl, lph, rs, 1, rs / hb, hb};
             return true;
         }
@@ -94,15 +95,22 @@ const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
 void pkv_tuning_defaults(pkv_tuning* out) {
     if (!out) return;
-    out->t_dense = 1024;
-    out->gate_ratio = 1;
-    out->launch_bytes = 40LL * 1000 * 1000;   // ~5 us at 8 TB/s for two extra launches
+    // Dispatcher constants refitted on MI355X from a forced-path sweep over
+    // B in {1..512}, G in {1,2,4,8}, P in {256..8192}, suffixes U{64..512}:
+    // DENSE (with its fused launch) was never slower than the tiled path by
+    // more than noise at any M_eff, so every cascade step goes DENSE; the
+    // PAGED gate with R = 3 and a 10 MB launch term picks a path within 15 %
+    // of the fastest in every cell (0.6 % on average).
+    out->t_dense = 1;
+    out->gate_ratio = 3;
+    out->launch_bytes = 10LL * 1000 * 1000;
     out->target_workgroups = 512;   // two workgroups per CU
     out->min_split_tokens = 64;
     out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
     out->fuse_cascade = 12;  // MFMA flops per suffix byte: fused on c3 (57), separate on c4 (3)
     out->prefix_target_workgroups = 256;
     out->min_prefix_split_tokens = 64;
+    out->max_heads_per_item = 0;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -179,7 +187,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         tu.min_split_tokens < 1 ||
         tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.fuse_cascade < 0 ||
         tu.prefix_target_workgroups < 1 ||
-        tu.min_prefix_split_tokens < 1)
+        tu.min_prefix_split_tokens < 1 || tu.max_heads_per_item < 0)
         return PKV_EINVAL;
 
     // Checks, in the same order as the planner's reference statement.
@@ -204,7 +212,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         !group_supported(G))
         return PKV_EUNSUPPORTED;
     pkv::PagedGeometry geo;
-    if (!pkv::paged_geometry(pr->kv_dtype, D, G, H_kv, &geo)) return PKV_EUNSUPPORTED;
+    if (!pkv::paged_geometry(pr->kv_dtype, D, G, H_kv, tu.max_heads_per_item, &geo)) return PKV_EUNSUPPORTED;
 
     // Path choice.
     const int64_t n_shared = P > 0 ? B : 0;
@@ -302,7 +310,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     const int64_t per_item = ceil_div(total * pl->head_blocks, target);
     int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
     chunk = align_up(chunk, pkv::kSplitQuantum);
-    chunk = std::min<int64_t>(chunk, pkv::kMaxSplitTokens);
+    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(geo.rs, geo.nhl, G, D));
     pl->split_tokens = (int32_t)chunk;
     pl->num_chunks = ceil_div(total, chunk);
     pl->num_work_items = pl->num_chunks * pl->head_blocks;

@@ -107,7 +107,7 @@ struct PagedCfg {
     static constexpr int PARTIALS = NW * TPI;
     static constexpr int MERGE_FLOATS = PARTIALS * HB * G * D;
     // slot indices of a chunk, padded by whole wave iterations
-    static constexpr int IDX_INTS = kMaxSplitTokens + NW * TU;
+    static constexpr int IDX_INTS = max_chunk_tokens(RS, NHL, G, D) + NW * TU;
     static_assert(G <= LPH, "one query head per lane after the row reduction");
     static_assert(TPI == 1 || NHL == 1, "several tokens per load only with one head slot");
     static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");

@@ -25,7 +25,8 @@ struct PagedGeometry {
 
 // Lane geometry for a (kv dtype, head_dim, G, H_kv) problem.  Returns false
 // if no kernel is built for it.
-bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t num_kv_heads,
+// max_heads > 0 limits the KV heads per work item.
+bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t num_kv_heads, int32_t max_heads,
                     PagedGeometry* out);
 
 // Query rows one prefix-kernel workgroup handles, per path.
@@ -36,9 +37,14 @@ constexpr int32_t kTiledRowsPerWg = 64;
 constexpr int32_t kPrefixTokenQuantum = 64;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // Paged-pass chunks hold a multiple of this many tokens, and at most
-// kMaxSplitTokens (the kernel stages a segment's slot indices in LDS).
+// max_chunk_tokens(...) (the kernel stages a chunk's slot indices in LDS next
+// to the per-wave merge buffer of 16 * rows_per_load * nhl * G * d bytes; the
+// index stage is sized so that two workgroups still fit in a CU's 160 KB).
 constexpr int32_t kSplitQuantum = 16;
-constexpr int32_t kMaxSplitTokens = 2048;
+constexpr int32_t kMaxSplitTokens = 4096;
+constexpr int32_t max_chunk_tokens(int32_t rs, int32_t nhl, int32_t group, int32_t head_dim) {
+    return 16 * rs * nhl * group * head_dim > 40 * 1024 ? 2048 : kMaxSplitTokens;
+}
 
 }  // namespace pkv
 
