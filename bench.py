@@ -374,7 +374,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", metavar="CONFIG:LEG[,LEG]",

@@ -53,17 +53,13 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
     }
     const int32_t lph = head_dim / epl;
     const int32_t rs = 64 / lph;
-    // Per-lane registers: q and the output accumulator both hold nhl*G*epl
-    // values; 64 keeps two waves per SIMD.
-#ifndef PKV_LANE_VALUES
-#define PKV_LANE_VALUES 64
-#endif
+    // One head slot per lane (measured faster than two on every workload):
+    // a wave-wide load covers RS rows, one token's RS heads, or TPI tokens of
+    // fewer heads when the head count or max_heads calls for it.
     const auto allowed = [&](int32_t hb) { return max_heads <= 0 || hb <= max_heads; };
-    for (int32_t nhl = 2; nhl >= 1; --nhl) {
-        if (nhl * group * epl <= PKV_LANE_VALUES && num_kv_heads % (rs * nhl) == 0 && allowed(rs * nhl)) {
-            *out = PagedGeometry{epl, lph, rs, nhl, 1, rs * nhl};
-            return true;
-        }
+    if (num_kv_heads % rs == 0 && allowed(rs)) {
+        *out = PagedGeometry{epl, lph, rs, 1, 1, rs};
+        return true;
     }
     for (int32_t hb = rs / 2; hb >= 1; hb /= 2) {
         if (num_kv_heads % hb == 0 && allowed(hb)) {

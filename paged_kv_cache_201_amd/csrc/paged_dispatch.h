@@ -11,10 +11,7 @@ template <int KV, int D, int G, class L>
 hipError_t dispatch_layout(const pkv_plan& p, const L& l) {
     using C1 = PagedCfg<KV, D, G, 1, 1>;
     constexpr int RS = C1::RS;
-    if (p.geo.nhl == 2) {
-        if constexpr (2 * G * C1::EPL <= 64) return l.template run<KV, D, G, 2, 1>();
-        return hipErrorInvalidValue;
-    }
+    if (p.geo.nhl != 1) return hipErrorInvalidValue;
     switch (p.geo.tpi) {
         case 1: return l.template run<KV, D, G, 1, 1>();
         case 2:

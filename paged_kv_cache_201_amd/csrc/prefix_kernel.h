@@ -46,17 +46,27 @@ constexpr float kPrefixLazySlack = 8.0f;
 // tile n+1 (loaded into registers at the top of the iteration) is written
 // into the other, so one barrier per tile suffices.  The range's slot
 // indices are staged in LDS once, so no tile waits on an index load.
-// LDS of one prefix workgroup.
+// LDS of one prefix workgroup: a ring of STAGES K and V tiles and the slot
+// indices of the workgroup's prefix range.  Tile rows are D bf16 with no
+// padding; the 16-byte chunks of row t are stored XOR-swizzled (chunk c at
+// position c ^ (t mod D/8)) so that the operand reads of 16 or 32 rows hit
+// distinct banks.
 template <int D, int KT>
 struct PrefixSmem {
-    // bf16 per LDS row of K and of V: a 32-byte pad makes the row pitch 8
-    // banks (mod 64), so the row-gathering operand reads are conflict free
-    static constexpr int KROW = D + 16;
-    static constexpr int KBUF = KT * KROW;
-    uint16_t k[2][KBUF];
-    uint16_t v[2][KBUF];
+    static constexpr int STAGES = 4;
+    uint16_t k[STAGES][KT * D];
+    uint16_t v[STAGES][KT * D];
     int idx[kMaxPrefixSplitTokens];
 };
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // Number of prefix blocks to launch for N work items (a multiple of 8, see
 // prefix_item).
@@ -66,13 +76,15 @@ __host__ __device__ inline int prefix_blocks(int n_items) { return (n_items + 7)
 // workgroup's index among the prefix workgroups of the launch.
 template <int D, int NW, int KT>
 __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, KT>& sm, const int p) {
-    constexpr int KROW = PrefixSmem<D, KT>::KROW;
+    constexpr int CPR = D / 8;                  // 16-byte chunks per tile row
+    constexpr int S = PrefixSmem<D, KT>::STAGES;
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
     constexpr int NTB = KT / 32;   // 32-token blocks per tile
     constexpr int NT = NW * 64;
-    constexpr int KITEMS = KT * D / 8;          // 16-byte chunks of a K (or V) tile
-    constexpr int KCH = (KITEMS + NT - 1) / NT;
+    constexpr int BLOCKS = KT * D * 2 / 1024;   // 1 KB wave-wide LDS copies per K (or V) tile
+    static_assert(BLOCKS % NW == 0, "each wave copies whole 1 KB blocks of a tile");
+    constexpr int PER_WAVE = BLOCKS / NW;
     auto& s_k = sm.k;
     auto& s_v = sm.v;
     int* const s_idx = sm.idx;
@@ -124,36 +136,52 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     const size_t slot_stride = (size_t)a.H_kv * D;
     const size_t head_off = (size_t)g * D;
 
-    u32x4_t kst[KCH], vst[KCH];
-    auto load_tile = [&](int n) {
-        const int tb = n * KT;
+    // Tile n goes to ring stage n % S straight from global memory with
+    // gfx950's global_load_lds_dwordx4: lane l of a wave-wide copy fetches one
+    // 16-byte chunk and the hardware stores it at LDS block base + 16 l, so
+    // no registers hold tiles in flight and S - 1 tiles can be outstanding.
+    // Each lane picks the global chunk that belongs at its LDS position
+    // (row t, swizzled chunk q holds chunk q ^ (t mod CPR)).
+    // The copies are issued as inline assembly: the waits for them are the
+    // explicit vmcnt waits of the tile loop (the compiler, which cannot tell
+    // the ring stages apart, would otherwise drain every copy before each LDS
+    // read).  Each statement sets M0 itself; nothing else in these kernels
+    // uses M0.
+    typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+    // LDS byte addresses of the two rings (M0 takes a 32-bit LDS address)
+    const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_k[0][0]);
+    const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_v[0][0]);
+    auto lds_copy16 = [](const uint16_t* src, uint32_t m0) {
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+    };
+    auto issue_tile = [&](int n) {
+        const int stage = n % S;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (KITEMS % NT != 0 && id >= KITEMS) break;
-            const int t = id / (D / 8), ch = id % (D / 8);
-            const size_t off = (size_t)s_idx[tb + t] * slot_stride + head_off + ch * 8;
-            kst[c] = *reinterpret_cast<const u32x4_t*>(kpool + off);
-            vst[c] = *reinterpret_cast<const u32x4_t*>(vpool + off);
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int blk = wave * PER_WAVE + j;
+            const int p = blk * 64 + lane;
+            const int t = p / CPR;
+            const int c = (p % CPR) ^ (t & (CPR - 1));
+            const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + c * 8;
+            const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
+            lds_copy16(kpool + off, k_lds + dst);
+            lds_copy16(vpool + off, v_lds + dst);
         }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int id = c * NT + threadIdx.x;
-            if (KITEMS % NT != 0 && id >= KITEMS) break;
-            const int t = id / (D / 8), ch = id % (D / 8);
-            *reinterpret_cast<u32x4_t*>(&s_k[buf][t * KROW + ch * 8]) = kst[c];
-            *reinterpret_cast<u32x4_t*>(&s_v[buf][t * KROW + ch * 8]) = vst[c];
-        }
-    };
-    // Transposed-read address of this lane for the V^T operand: lane group
+    // Transposed-read addresses of this lane for the V^T operand: lane group
     // (h, dh) of 16 lanes covers columns db*32 + dh*16 .. +15 and tokens
     // c*16 + h*4 (+8 for the second read); lane s of the group reads token
     // s/4 of those four at columns 4*(s%4) .. +3 of the group's sixteen.
+    // Rows c*16 + r keep the swizzle of row r (16 is a multiple of CPR).
     const int tr_s = lane & 15;
     const int tr_dh = (lane >> 4) & 1;
-    const int tr_off = (tr_s >> 2) * KROW + tr_dh * 16 + (tr_s & 3) * 4 + h * 4 * KROW;
+    const int tr_row = (tr_s >> 2) + h * 4;
+    const int tr_chunk = tr_dh * 2 + ((tr_s & 3) >> 1);  // chunk within a 32-column block
+    const int tr_elem = (tr_s & 1) * 4;
+    auto tr_off = [&](int row, int db) {
+        return row * D + (((db * 4 + tr_chunk) ^ (row & (CPR - 1))) << 3) + tr_elem;
+    };
+    const int kr_swz = lr & (CPR - 1);  // swizzle of the K rows this lane reads
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -173,9 +201,11 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
 #pragma unroll
             for (int ks = 0; ks < NKS; ks += 2) {
                 const bf16x8_t ka0 = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + h * 8]));
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                  &s_k[buf][(tb * 32 + lr) * D + (((ks * 2 + h) ^ kr_swz) << 3)]));
                 const bf16x8_t ka1 = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s_k[buf][(tb * 32 + lr) * KROW + ks * 16 + 16 + h * 8]));
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                  &s_k[buf][(tb * 32 + lr) * D + (((ks * 2 + 2 + h) ^ kr_swz) << 3)]));
                 s_even = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], s_even, 0, 0, 0);
                 s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], s_odd, 0, 0, 0);
             }
@@ -230,9 +260,10 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
             for (int c = 0; c < 2 * NTB; ++c) {
                 typedef short v4s_t __attribute__((ext_vector_type(4)));
                 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
-                const uint16_t* vr = &s_v[buf][(c * 16) * KROW + db * 32 + tr_off];
-                const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)vr);
-                const v4s_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vr + 8 * KROW));
+                const uint16_t* vb = &s_v[buf][c * 16 * D];
+                const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vb + tr_off(tr_row, db)));
+                const v4s_t x1 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vb + tr_off(tr_row + 8, db)));
                 const u32x2_t y0 = __builtin_bit_cast(u32x2_t, x0);
                 const u32x2_t y1 = __builtin_bit_cast(u32x2_t, x1);
                 const u32x4_t x = {y0[0], y0[1], y1[0], y1[1]};
@@ -242,23 +273,29 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
         }
     };
 
+    // The query loads above must not be left in flight: the tile loop's
+    // vmcnt waits count only the copies.
+    wait_vmcnt<0>();
     __syncthreads();  // s_idx ready
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
+    for (int n = 0; n < S - 1 && n < ntiles; ++n) issue_tile(n);
     const bool tail = (n_tok % KT) != 0;
     for (int n = 0; n < ntiles; ++n) {
-        const int buf = n & 1;
-        if (n + 1 < ntiles) load_tile(n + 1);
+        // this wave's copies of tile n have landed once at most the copies of
+        // the tiles issued after it are in flight; the barrier then makes
+        // every wave's part visible and retires the stage read at n - 1
+        const int younger = min(ntiles - 1, n + S - 2) - n;
+        static_assert(S == 4, "wait counts below assume four stages");
+        if (younger >= 2) wait_vmcnt<4 * PER_WAVE>();
+        else if (younger == 1) wait_vmcnt<2 * PER_WAVE>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (n + S - 1 < ntiles) issue_tile(n + S - 1);
+        const int buf = n % S;
         if (tail && n == ntiles - 1) {
             compute(n, buf, std::integral_constant<bool, true>{});
         } else {
             compute(n, buf, std::integral_constant<bool, false>{});
         }
-        if (n + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
     }
 
     // Row totals: the two halves of the wave hold disjoint tokens of a row.

@@ -206,7 +206,8 @@ def test_chunk_partition_is_balanced_and_counted():
 
 def test_plan_workspace_and_geometry():
     info = _both(32, 4, 0, 128, L=4096)
-    assert info["heads_per_item"] == 8 and info["num_work_items"] * info["split_tokens"] >= 32 * 4096
+    # one wave-wide load covers 4 rows of 128 bf16: 4 KV heads per item, 2 head blocks
+    assert info["heads_per_item"] == 4 and info["num_work_items"] * info["split_tokens"] >= 2 * 32 * 4096
     rows = 32 * 32
     if info["num_splits"] > 1:
         assert info["workspace_bytes"] >= rows * info["num_splits"] * 130 * 4
@@ -215,6 +216,9 @@ def test_plan_workspace_and_geometry():
     # one chunk holds every request whole: outputs written directly, no workspace
     c1 = _both(4, 4, 0, 16, L=[64, 100, 200, 256], H_kv=2, d=64, q="f32", kv="f32", tune=dict(min_split_tokens=2048))
     assert c1["heads_per_item"] == 2 and c1["num_splits"] == 1 and c1["workspace_bytes"] == 0
+    # max_heads_per_item narrows the work items
+    one = _both(32, 4, 0, 128, L=4096, tune=dict(max_heads_per_item=1))
+    assert one["heads_per_item"] == 1
     # a cascade step keeps partial states for both passes
     c3 = _both(256, 4, 4096, 16, L=4096 + 300)
     assert c3["workspace_bytes"] >= 256 * 32 * (c3["prefix_splits"] + c3["num_splits"]) * 130 * 4
