@@ -188,13 +188,11 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
     float m = -INFINITY, l = 0.f;
 
-    auto compute = [&](int n, int buf, auto tailc) {
-        constexpr bool TAIL = decltype(tailc)::value;
-        // S^T = K . Q^T, one 32x32 block per 32 tokens; lane holds row lr and
-        // tokens tb*32 + (i/4)*8 + h*4 + i%4
-        // two independent accumulation chains (even and odd k-steps) so that
-        // consecutive MFMAs do not wait on each other's results
-        f32x16_t s[NTB];
+    // S^T = K . Q^T for tile n (one 32x32 block per 32 tokens; lane holds row
+    // lr and tokens tb*32 + (i/4)*8 + h*4 + i%4), in two independent
+    // accumulation chains (even and odd k-steps) so that consecutive MFMAs
+    // do not wait on each other's results.  Padded tail tokens get -inf.
+    auto qk = [&](int n, int buf, f32x16_t (&s)[NTB]) {
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             f32x16_t s_even = f32x16_t{}, s_odd = f32x16_t{};
@@ -211,14 +209,18 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
             }
             s[tb] = s_even + s_odd;
         }
-        if constexpr (TAIL) {
-            const int valid = n_tok - n * KT;
+        const int valid = n_tok - n * KT;
+        if (valid < KT) {
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (tb * 32 + (i / 4) * 8 + h * 4 + (i % 4) >= valid) s[tb][i] = -INFINITY;
         }
+    };
+
+    // Online softmax of one tile's scores and O^T += V^T . P^T.
+    auto softmax_pv = [&](const f32x16_t (&s)[NTB], int buf) {
         // running max over raw scores (the scale is positive)
         float mx = -INFINITY;
 #pragma unroll
@@ -278,24 +280,35 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     wait_vmcnt<0>();
     __syncthreads();  // s_idx ready
     for (int n = 0; n < S - 1 && n < ntiles; ++n) issue_tile(n);
-    const bool tail = (n_tok % KT) != 0;
-    for (int n = 0; n < ntiles; ++n) {
-        // this wave's copies of tile n have landed once at most the copies of
-        // the tiles issued after it are in flight; the barrier then makes
-        // every wave's part visible and retires the stage read at n - 1
-        const int younger = min(ntiles - 1, n + S - 2) - n;
-        static_assert(S == 4, "wait counts below assume four stages");
+    static_assert(S == 4, "wait counts below assume four stages");
+    // Wait until this wave's copies of tile n have landed: at most the copies
+    // of the tiles issued after it (up to tile `last`) may still be in flight.
+    auto wait_tile = [&](int n, int last) {
+        const int younger = min(ntiles - 1, last) - n;
         if (younger >= 2) wait_vmcnt<4 * PER_WAVE>();
         else if (younger == 1) wait_vmcnt<2 * PER_WAVE>();
         else wait_vmcnt<0>();
+    };
+    // Software pipeline: while the softmax and P.V of tile n run, the scores
+    // of tile n + 1 are already on the matrix cores and tiles n + 2, n + 3
+    // are on their way into the ring.
+    f32x16_t s_cur[NTB], s_next[NTB];
+    if (ntiles > 0) {
+        wait_tile(0, S - 2);
         __syncthreads();
-        if (n + S - 1 < ntiles) issue_tile(n + S - 1);
-        const int buf = n % S;
-        if (tail && n == ntiles - 1) {
-            compute(n, buf, std::integral_constant<bool, true>{});
-        } else {
-            compute(n, buf, std::integral_constant<bool, false>{});
+        qk(0, 0, s_cur);
+    }
+    for (int n = 0; n < ntiles; ++n) {
+        if (n + 1 < ntiles) {
+            // tiles 0 .. n + S - 2 have been issued
+            wait_tile(n + 1, n + S - 2);
+            __syncthreads();  // tile n + 1 visible; every wave is done with tile n - 1
+            if (n + S - 1 < ntiles) issue_tile(n + S - 1);  // into the stage of tile n - 1
+            qk(n + 1, (n + 1) % S, s_next);
         }
+        softmax_pv(s_cur, n % S);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) s_cur[tb] = s_next[tb];
     }
 
     // Row totals: the two halves of the wave hold disjoint tokens of a row.
