@@ -202,6 +202,16 @@ def summarize_trace(prof_dir):
     return "\n".join(out), agg
 
 
+def write_trace_summary(trace_dir, name, title, command):
+    """profiles/kernels.<name>.trace.md from one rocprofv3 --kernel-trace run."""
+    table, _ = summarize_trace(trace_dir)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"kernels.{name}.trace.md")
+    with open(path, "w") as f:
+        f.write(f"# Kernel durations, {title}\n\nCommand:\n\n```\n{command}\n```\n\n{table}\n")
+    return path
+
+
 def pmc_per_dispatch(prof_dir, counter):
     """{(kernel, grid size): [counter value per dispatch]} from a rocprofv3 --pmc csv run."""
     import csv
@@ -382,6 +392,8 @@ def main():
                          "for profiling one leg at a time")
     ap.add_argument("--summarize-prefix-traffic", nargs=3, metavar=("CONFIG", "UNIQUE_DIR", "SEPARATE_DIR"),
                     help="write the prefix-traffic summary from two FETCH_SIZE runs (see --only) and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CONFIGS"),
+                    help="write profiles/kernels.<configs>.trace.md from a kernel-trace run of --configs CONFIGS")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
     args = ap.parse_args()
@@ -395,6 +407,14 @@ def main():
                     summary=f"python bench.py --summarize-prefix-traffic {name} {u} {c}")
         rec = write_prefix_traffic(name, u, c, cmds)
         print(json.dumps({k: v for k, v in rec.items() if k != "runs"}, indent=1))
+        return
+    if args.summarize_trace:
+        d, configs = args.summarize_trace
+        cmd = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --kernel-trace --stats "
+               f"--output-format csv -d {d} -o run -- python bench.py --configs {configs} --steps 20 --warmup 20 --no-cpu")
+        title = (f"workloads {configs} (each leg of the shared-prefix workloads, then the long fp8 workload; "
+                 "the Llama layer at page size 1 and 128 runs first in every bench run)")
+        print(write_trace_summary(d, configs.replace(",", "_"), title, cmd))
         return
     if args.summarize_profiles:
         t, f, w = args.summarize_profiles
@@ -437,9 +457,17 @@ def main():
     del db1
     torch.cuda.empty_cache()
     log("bench c2 p=128")
-    rec128, b128, db128, _ = bench_paged_config("c2", args.steps, args.warmup)
+    rec128, b128, db128, plan128 = bench_paged_config("c2", args.steps, args.warmup)
     add_ceiling(rec128, ceiling)
     log(json.dumps(rec128))
+    # the same step with the kernel reading the page table (1,024 page entries
+    # instead of 131,072 token indices)
+    o, lse, ws = db128.new_out(), db128.new_lse(), db128.workspace(plan128)
+    ms = time_steps(lambda: db128.paged_pages(plan128, o=o, lse=lse, ws=ws), args.steps, args.warmup)
+    nb = rec128["algorithmic_bytes"] - 4 * 32 * 4096 + 4 * 32 * (4096 // 128)
+    extra["c2_page128_page_table"] = dict(us_per_step=ms * 1e3, gbs=nb / (ms * 1e-3) / 1e9, algorithmic_bytes=nb)
+    log(json.dumps(extra["c2_page128_page_table"]))
+    del o, lse, ws
     del db128, b128
     torch.cuda.empty_cache()
     extra["c2_page128"] = rec128

@@ -237,6 +237,29 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* plan, const void* q, const pkv_
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same operation reading the page table instead of token-flat indices
+ * ([P1] "A backend where pages really do reach the kernel": per-page
+ * metadata consumed by the kernel itself; "Four meanings of page size").
+ * Logical position t of request b is slot
+ * page_indices[page_indptr[b] + t / page_size] * page_size + t % page_size,
+ * with page_size from the plan.  Output is bit for bit that of
+ * pkv_paged_decode_attn over the lowered indices (same plan, same kernels).
+ *   kv_indptr     device, [B+1] int32 token offsets: kv_indptr[b+1] - kv_indptr[b]
+ *                 = L_b, the same values as the plan's host indptr
+ *   page_indptr   device, [B+1] int32; request b owns ceil(L_b / page_size) pages
+ *   page_indices  device, [page_indptr[B]] int32 physical page numbers
+ * Other arguments as pkv_paged_decode_attn.  The kernels do not bounds-check
+ * the page table (pkv_lower_page_table does on the host).
+ * Errors: EINVAL (null plan/q/indptr/page table, no output, pool not matching
+ * the plan, missing fp8 scales), EWORKSPACE, EHIP.
+ */
+pkv_status pkv_paged_decode_attn_pages(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                                       const int32_t* kv_indptr, const int32_t* page_indptr,
+                                       const int32_t* page_indices, float sm_scale, void* o,
+                                       float* o_f32, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Shared-prefix attention, prefix read once for the whole batch ([P2] s.2:
  * every request needs the whole prefix each step, so it is read once instead
  * of once per request; s.3: DENSE or tiled CASCADE by M_eff).  For each KV

@@ -80,6 +80,8 @@ _SIGS = {
     "pkv_plan_destroy": (None, [_vp]),
     "pkv_paged_decode_attn": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp,
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attn_pages": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, _vp,
+                                                     ctypes.c_float, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "pkv_cascade_prefix_attn": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, ctypes.c_int32,
                                                  ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "pkv_merge_states": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
@@ -242,6 +244,19 @@ def pkv_paged_decode_attn(plan, q, pool, kv_indptr, kv_indices, sm_scale, o=None
                                     _dev(o, "o", allow_none=True), _dev(o_f32, "o_f32", (torch.float32,), True),
                                     _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
     _check(st, "pkv_paged_decode_attn")
+
+
+def pkv_paged_decode_attn_pages(plan, q, pool, kv_indptr, page_indptr, page_indices, sm_scale, o=None, o_f32=None,
+                                lse=None, workspace=None, stream=None):
+    import torch
+    ws, wsb = _ws(workspace, plan)
+    i32 = (torch.int32,)
+    st = _lib.pkv_paged_decode_attn_pages(plan.handle, _dev(q, "q"), ctypes.byref(pool),
+                                          _dev(kv_indptr, "kv_indptr", i32), _dev(page_indptr, "page_indptr", i32),
+                                          _dev(page_indices, "page_indices", i32), float(sm_scale),
+                                          _dev(o, "o", allow_none=True), _dev(o_f32, "o_f32", (torch.float32,), True),
+                                          _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
+    _check(st, "pkv_paged_decode_attn_pages")
 
 
 def pkv_cascade_prefix_attn(plan, q, pool, prefix_indices, prefix_len, sm_scale, o_p, lse_p, workspace=None,

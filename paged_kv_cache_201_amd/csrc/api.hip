@@ -118,10 +118,8 @@ pkv::SplitReduceArgs chunk_reduce_args(const pkv_plan* pl, const pkv::PagedArgs&
     return r;
 }
 
-pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
-                     const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
-                     void* ws, hipStream_t stream) {
-    pkv::PagedArgs a = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
+pkv_status run_paged_args(const pkv_plan* pl, pkv::PagedArgs a, void* o, float* o_f32, float* lse, void* ws,
+                          hipStream_t stream) {
     a.o = o;
     a.o_f32 = o_f32;
     a.lse = lse;
@@ -135,6 +133,12 @@ pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, co
     r.o_f32 = o_f32;
     r.lse = lse;
     return hip_status(pkv::launch_split_reduce(r, stream));
+}
+
+pkv_status run_paged(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, float sm_scale, void* o, float* o_f32, float* lse,
+                     void* ws, hipStream_t stream) {
+    return run_paged_args(pl, paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale), o, o_f32, lse, ws, stream);
 }
 
 pkv::PrefixArgs prefix_args(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* prefix_indices,
@@ -200,6 +204,25 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* pl, const void* q, const pkv_po
     if (!q || !kv_indptr || (pl->paged_tokens > 0 && !kv_indices)) return PKV_EINVAL;
     return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, o_f32, lse, ws,
                      static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_paged_decode_attn_pages(const pkv_plan* pl, const void* q, const pkv_pool* pool,
+                                       const int32_t* kv_indptr, const int32_t* page_indptr,
+                                       const int32_t* page_indices, float sm_scale, void* o, float* o_f32,
+                                       float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!pl) return PKV_EINVAL;
+    if (!o && !o_f32) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    st = check_workspace(pl, ws, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (pl->B == 0) return PKV_OK;
+    if (!q || !kv_indptr || !page_indptr || (pl->paged_tokens > 0 && !page_indices)) return PKV_EINVAL;
+    pkv::PagedArgs a = paged_args(pl, q, pool, kv_indptr, nullptr, sm_scale);
+    a.page_indptr = page_indptr;
+    a.page_indices = page_indices;
+    a.page_size = pl->page_size;
+    return run_paged_args(pl, a, o, o_f32, lse, ws, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_cascade_prefix_attn(const pkv_plan* pl, const void* q, const pkv_pool* pool,

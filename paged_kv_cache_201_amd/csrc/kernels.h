@@ -21,7 +21,10 @@ struct PagedArgs {
     const float* k_scale;     // [H_kv] (fp8)
     const float* v_scale;
     const int32_t* kv_indptr; // [B+1]
-    const int32_t* kv_indices;
+    const int32_t* kv_indices;   // token-flat slots; null when the page table is read instead
+    const int32_t* page_indptr;  // [B+1], with page_indices: pages of request b
+    const int32_t* page_indices;
+    int32_t page_size;
     int32_t B;
     int32_t H_kv;
     int32_t token_offset;     // tokens skipped at the start of every request

@@ -125,7 +125,8 @@ struct PagedSmem {
 };
 
 // One segment: n_tok > 0 consecutive positions of request b, whose slot
-// indices start at kv_indices[idx_beg], for the HB KV heads of head block
+// indices start at kv_indices[idx_beg] (with a page table instead: logical
+// positions from idx_beg - kv_indptr[b] on), for the HB KV heads of head block
 // hblk.  slot < 0: the segment is the whole request and its normalised output
 // goes to o / o_f32 / lse; slot >= 0: its partial state goes to partial
 // index `slot` of request b.  staged: sm.idx already holds the segment's slot
@@ -161,7 +162,19 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
     int* const s_idx = sm.idx;
     if (!staged) {
         const int n_pad = (n_tok + TU - 1) / TU * TU;
-        for (int i = threadIdx.x; i < n_pad; i += NW * 64) s_idx[i] = a.kv_indices[idx_beg + min(i, n_tok - 1)];
+        if (a.page_indices) {
+            // from the page table: logical position t of request b lives in
+            // slot page_indices[page_indptr[b] + t / p] * p + t % p
+            const int t0 = idx_beg - a.kv_indptr[b];
+            const int32_t* pages = a.page_indices + a.page_indptr[b];
+            const int p = a.page_size;
+            for (int i = threadIdx.x; i < n_pad; i += NW * 64) {
+                const int t = t0 + min(i, n_tok - 1);
+                s_idx[i] = pages[t / p] * p + t % p;
+            }
+        } else {
+            for (int i = threadIdx.x; i < n_pad; i += NW * 64) s_idx[i] = a.kv_indices[idx_beg + min(i, n_tok - 1)];
+        }
         __syncthreads();
     }
 
@@ -522,7 +535,7 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
     // the chunk's slot indices are staged at once, while the request holding
     // position c0 (the one non-empty request whose flat range contains it)
     // is looked up.
-    const bool flat = a.token_offset == 0;
+    const bool flat = a.token_offset == 0 && a.page_indices == nullptr;
     if (flat) {
         constexpr int TU = PagedCfg<KV, D, G, NHL, TPI>::TU;
         const int n = (int)(c1 - c0);

@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 from . import (Plan, make_pool, pkv_cascade_prefix_attn, pkv_decode_step, pkv_lower_page_table,
-               pkv_merge_states, pkv_paged_decode_attn, pkv_plan_create, workspace_for)
+               pkv_merge_states, pkv_paged_decode_attn, pkv_paged_decode_attn_pages, pkv_plan_create,
+               workspace_for)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 _NAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
@@ -37,6 +38,9 @@ class DeviceBatch:
         self.kv_indices_host = kv_indices_host
         self.kv_indptr = torch.from_numpy(self.kv_indptr_host).to(dev)
         self.kv_indices = torch.from_numpy(kv_indices_host if len(kv_indices_host) else np.zeros(1, np.int32)).to(dev)
+        self.page_indptr = torch.from_numpy(np.asarray(page_indptr, np.int32)).to(dev)
+        pages = np.asarray(page_indices, np.int32)
+        self.page_indices = torch.from_numpy(pages if len(pages) else np.zeros(1, np.int32)).to(dev)
         self.pool = make_pool(self.k_pool, self.v_pool, self.page_size, self.k_scale, self.v_scale)
         self.sm_scale = 1.0 / math.sqrt(self.d)
 
@@ -79,6 +83,19 @@ class DeviceBatch:
         pkv_paged_decode_attn(plan, self.q, self.pool, self.kv_indptr, self.kv_indices,
                               self.sm_scale if sm_scale is None else sm_scale, o, o_f32, lse,
                               self.workspace(plan) if ws is None else ws, stream)
+        return (o if o is not None else o_f32), lse
+
+    def paged_pages(self, plan, o=None, o_f32=None, lse=None, ws=None, sm_scale=None, stream=None, want_f32=False):
+        """As paged(), with the kernel reading the page table instead of kv_indices."""
+        if o is None and o_f32 is None:
+            if want_f32:
+                o_f32 = self.new_out(torch.float32)
+            else:
+                o = self.new_out()
+        lse = self.new_lse() if lse is None else lse
+        pkv_paged_decode_attn_pages(plan, self.q, self.pool, self.kv_indptr, self.page_indptr, self.page_indices,
+                                    self.sm_scale if sm_scale is None else sm_scale, o, o_f32, lse,
+                                    self.workspace(plan) if ws is None else ws, stream)
         return (o if o is not None else o_f32), lse
 
     def prefix_indices(self, plan):

@@ -271,6 +271,56 @@ def test_chunkings_agree_with_oracle_and_repeat_bitwise(chunk):
     assert same_bits(o1, o2) and same_bits(l1, l2)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_narrow_head_blocks_and_long_chunks(kv):
+    """Work items of 1 and 2 KV heads (several tokens per wave-wide load) and
+    whole-request chunks of 4096 positions with no combine step."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_decode_batch(seed=21, B=6, H_q=32, H_kv=8, d=128, own_len=(1, 4096), q_dtype="bf16", kv_dtype=kv,
+                          page_size=16)
+    o_ref, lse_ref = ob.batch_reference(b)
+    for tune in (dict(max_heads_per_item=1), dict(max_heads_per_item=2, min_split_tokens=16, target_workgroups=4096),
+                 dict(max_heads_per_item=1, min_split_tokens=4096, target_workgroups=1)):
+        say(f"narrow heads {kv} {tune}")
+        o, lse, plan = run_paged(DeviceBatch, b, tuning=tune)
+        assert plan.info["heads_per_item"] == tune["max_heads_per_item"]
+        check_close(kv, o, lse, o_ref, lse_ref, f"{kv} {tune}")
+        if tune.get("min_split_tokens") == 4096:
+            assert plan.info["split_tokens"] == 4096 and plan.info["num_splits"] <= 2
+
+
+def test_page_table_reads_match_token_flat_bitwise():
+    """pkv_paged_decode_attn_pages (the kernel reads the page table) against
+    pkv_paged_decode_attn over the lowered indices: same bits, and the oracle."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    c1 = make_config("c1")
+    c2 = make_config("c2", B=3, own_len=(1, 3000))
+    cases = [("c1 p16", c1), ("c1 p1", relayout(c1, page_size=1, seed=2001, pool_pages=2048)),
+             ("c2 p128", c2), ("c2 p7", relayout(c2, page_size=7, seed=2002)),
+             ("c5 p16", make_config("c5", B=2, own_len=(1, 3000))),
+             ("empty", make_decode_batch(seed=8, B=6, H_q=32, H_kv=8, d=128, own_len=(0, 0),
+                                         own_lens=[0, 700, 0, 1, 17, 0], page_size=16))]
+    for name, b in cases:
+        o_ref, lse_ref = ob.batch_reference(b)
+        db = DeviceBatch.from_batch(b)
+        for tune in (None, dict(min_split_tokens=16, target_workgroups=100000), dict(max_heads_per_item=1)):
+            plan = db.plan(force_path=0, tuning=tune)
+            say(f"page table {name} {tune}")
+            o1, l1 = db.paged(plan)
+            o2, l2 = db.paged_pages(plan)
+            torch.cuda.synchronize()
+            assert same_bits(o1, o2) and same_bits(l1, l2), f"{name} {tune}: page-table read differs"
+            check_close(b.kv_dtype, o2, l2, o_ref, lse_ref, f"page table {name}")
+    # the suffix pass of a cascade plan, fp32 state out
+    c = make_config("c3", B=16, own_len=(0, 200))
+    dc = DeviceBatch.from_batch(c)
+    plan = dc.plan(shared_prefix_len=c.prefix_len, force_path=2)
+    o1, l1 = dc.paged(plan, want_f32=True)
+    o2, l2 = dc.paged_pages(plan, want_f32=True)
+    torch.cuda.synchronize()
+    assert same_bits(o1, o2) and same_bits(l1, l2)
+
+
 def test_empty_and_tiny_requests_across_chunks():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     lens = [0, 1500, 0, 63, 64, 65, 0, 1000]
@@ -418,6 +468,13 @@ def test_abi_rejects_bad_arguments_without_launching():
         pkv.pkv_cascade_prefix_attn(plan, db.q.bfloat16(), db.pool, db.kv_indices, 0, 0.125,
                                     db.new_out(torch.float32), db.new_lse())
     assert e.value.name == "EINVAL"   # a PAGED plan has no prefix pass
+    with pytest.raises(pkv.PkvError) as e:   # page-table form: missing page table
+        pkv._check(pkv._lib.pkv_paged_decode_attn_pages(plan.handle, db.q.data_ptr(), pkv.ctypes.byref(db.pool),
+                                                        db.kv_indptr.data_ptr(), None, None, 0.125,
+                                                        db.new_out().data_ptr(), None, None,
+                                                        db.workspace(plan).data_ptr(), plan.info["workspace_bytes"],
+                                                        None), "pages")
+    assert e.value.name == "EINVAL"
     with pytest.raises(ValueError):
         pkv.pkv_paged_decode_attn(plan, db.q.cpu(), db.pool, db.kv_indptr, db.kv_indices, 0.125,
                                   o=db.new_out(), workspace=db.workspace(plan))
