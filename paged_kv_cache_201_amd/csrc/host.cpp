@@ -306,7 +306,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     const int64_t per_item = ceil_div(total * pl->head_blocks, target);
     int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
     chunk = align_up(chunk, pkv::kSplitQuantum);
-    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(geo.rs, geo.nhl, G, D));
+    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(geo.rs, geo.nhl, geo.tpi, G, D));
     pl->split_tokens = (int32_t)chunk;
     pl->num_chunks = ceil_div(total, chunk);
     pl->num_work_items = pl->num_chunks * pl->head_blocks;

@@ -87,6 +87,9 @@ constexpr int kPagedPipe = PKV_PAGED_PIPE;  // register buffers of K/V loads (2 
 #ifndef PKV_FP8_U
 #define PKV_FP8_U 0
 #endif
+#ifndef PKV_BF16_U
+#define PKV_BF16_U 0
+#endif
 constexpr float kLazyMaxSlack = 8.0f;  // log2 units
 
 template <int KV, int D, int G, int NHL, int TPI>
@@ -100,14 +103,22 @@ struct PagedCfg {
     static constexpr bool QF32 = (KV == PKV_F32);
     static constexpr int QW = QF32 ? EPL : EPL / 2;  // q registers per (slot, head)
     // steps per iteration: 8 KB of K+V in flight per wave per buffer
-    static constexpr int U0 = (KV == PKV_FP8_E4M3 && PKV_FP8_U > 0) ? PKV_FP8_U : 32 / (NHL * 2 * LW);
+    static constexpr int U0 = (KV == PKV_FP8_E4M3 && PKV_FP8_U > 0)  ? PKV_FP8_U
+                              : (KV == PKV_BF16 && PKV_BF16_U > 0)    ? PKV_BF16_U
+                                                                      : 32 / (NHL * 2 * LW);
     static constexpr int U = U0 < 2 ? 2 : U0;
     static constexpr int PIPE = KV == PKV_FP8_E4M3 ? PKV_FP8_PIPE : kPagedPipe;
     static constexpr int TU = U * TPI;  // tokens per wave iteration
     static constexpr int PARTIALS = NW * TPI;
-    static constexpr int MERGE_FLOATS = PARTIALS * HB * G * D;
+    // With one token per load the four waves merge pairwise (waves 2, 3 into
+    // 0, 1, then 1 into 0) through two LDS slots; otherwise every partial
+    // gets a slot and the output loop combines them all.
+    static constexpr bool TREE = TPI == 1 && NW == 4;
+    static constexpr int MERGE_SLOTS = TREE ? 2 : PARTIALS;
+    static constexpr int OUT_PARTIALS = TREE ? 1 : PARTIALS;
+    static constexpr int MERGE_FLOATS = MERGE_SLOTS * HB * G * D;
     // slot indices of a chunk, padded by whole wave iterations
-    static constexpr int IDX_INTS = max_chunk_tokens(RS, NHL, G, D) + NW * TU;
+    static constexpr int IDX_INTS = max_chunk_tokens(RS, NHL, TPI, G, D) + NW * TU;
     static_assert(G <= LPH, "one query head per lane after the row reduction");
     static_assert(TPI == 1 || NHL == 1, "several tokens per load only with one head slot");
     static_assert(U % 2 == 0, "tokens are paired for the P.V dot products");
@@ -120,7 +131,7 @@ struct PagedSmem {
     using C = PagedCfg<KV, D, G, NHL, TPI>;
     float buf[C::MERGE_FLOATS];
     int idx[C::IDX_INTS];
-    float ml[C::PARTIALS * C::HB * G * 2];
+    float ml[C::MERGE_SLOTS * C::HB * G * 2];
     int first_request;
 };
 
@@ -447,24 +458,67 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         }
     }
 
-    // Merge the NW * TPI partial states of this item in LDS, in a fixed order.
+    // Merge the NW * TPI partial states of this segment in a fixed order.
     __syncthreads();  // every wave is done with s_idx
-    const int pidx = wave * TPI + tau;
+    // A partial state in LDS slot `sl`: acc rows of G query heads and the
+    // (max, sum) pair of this lane's head, at the positions this lane owns.
+    auto publish = [&](int sl) {
 #pragma unroll
-    for (int i = 0; i < NHL; ++i) {
-        const int hl = head_local(i);
+        for (int i = 0; i < NHL; ++i) {
+            const int hl = head_local(i);
 #pragma unroll
-        for (int u = 0; u < G; ++u) {
-            float* dst = s_buf + ((size_t)(pidx * HB + hl) * G + (u ^ fl)) * D + lch * EPL;
+            for (int u = 0; u < G; ++u) {
+                float* dst = s_buf + ((size_t)(sl * HB + hl) * G + (u ^ fl)) * D + lch * EPL;
 #pragma unroll
-            for (int e = 0; e < EPL; e += 4) {
-                f32x4_t x = {acc[i][u][e], acc[i][u][e + 1], acc[i][u][e + 2], acc[i][u][e + 3]};
-                *reinterpret_cast<f32x4_t*>(dst + e) = x;
+                for (int e = 0; e < EPL; e += 4) {
+                    f32x4_t x = {acc[i][u][e], acc[i][u][e + 1], acc[i][u][e + 2], acc[i][u][e + 3]};
+                    *reinterpret_cast<f32x4_t*>(dst + e) = x;
+                }
             }
+            float* mlp = s_ml + ((sl * HB + hl) * G + fl) * 2;
+            mlp[0] = m[i];
+            mlp[1] = l[i];
         }
-        float* mlp = s_ml + ((pidx * HB + hl) * G + fl) * 2;
-        mlp[0] = m[i];
-        mlp[1] = l[i];
+    };
+    if constexpr (C::TREE) {
+        // Combine the state in slot `sl` into this wave's registers.
+        auto absorb = [&](int sl) {
+#pragma unroll
+            for (int i = 0; i < NHL; ++i) {
+                const int hl = head_local(i);
+                const float* mlp = s_ml + ((sl * HB + hl) * G + fl) * 2;
+                const float m2 = mlp[0], l2 = mlp[1];
+                const float mn = fmaxf(m[i], m2);
+                const float wa = (m[i] == -INFINITY) ? 0.f : fast_exp2(m[i] - mn);
+                const float wb = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mn);
+                m[i] = mn;
+                l[i] = l[i] * wa + l2 * wb;
+                static_for<G>([&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    const float au = xor_shfl<lane_mask_for_head_xor<LPH, G>(u)>(wa);
+                    const float bu = xor_shfl<lane_mask_for_head_xor<LPH, G>(u)>(wb);
+                    const float* src = s_buf + ((size_t)(sl * HB + hl) * G + (u ^ fl)) * D + lch * EPL;
+#pragma unroll
+                    for (int e = 0; e < EPL; e += 4) {
+                        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + e);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) acc[i][u][e + k] = acc[i][u][e + k] * au + x[k] * bu;
+                    }
+                });
+            }
+        };
+        if (wave >= 2) publish(wave - 2);
+        __syncthreads();
+        if (wave < 2) absorb(wave);
+        __syncthreads();
+        if (wave == 1) publish(0);
+        __syncthreads();
+        if (wave == 0) {
+            absorb(0);
+            publish(0);
+        }
+    } else {
+        publish(wave * TPI + tau);
     }
     __syncthreads();
 
@@ -475,12 +529,12 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         const int e4 = c % CH;
         float M = -INFINITY;
 #pragma unroll
-        for (int pp = 0; pp < C::PARTIALS; ++pp) M = fmaxf(M, s_ml[(pp * HB * G + qhl) * 2]);
+        for (int pp = 0; pp < C::OUT_PARTIALS; ++pp) M = fmaxf(M, s_ml[(pp * HB * G + qhl) * 2]);
         float L = 0.f;
         f32x4_t o = {0.f, 0.f, 0.f, 0.f};
         if (M != -INFINITY) {
 #pragma unroll
-            for (int pp = 0; pp < C::PARTIALS; ++pp) {
+            for (int pp = 0; pp < C::OUT_PARTIALS; ++pp) {
                 const float mp = s_ml[(pp * HB * G + qhl) * 2];
                 if (mp == -INFINITY) continue;
                 const float w = fast_exp2(mp - M);
@@ -568,8 +622,12 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
     }
 }
 
+#ifndef PKV_PAGED_OCC
+#define PKV_PAGED_OCC 2
+#endif
 template <int KV, int D, int G, int NHL, int TPI>
-__global__ void __launch_bounds__(kPagedWaves * 64, 2) paged_split_kernel(const PagedArgs a) {
+__global__ void __launch_bounds__(kPagedWaves * 64) __attribute__((amdgpu_waves_per_eu(PKV_PAGED_OCC)))
+paged_split_kernel(const PagedArgs a) {
     __shared__ PagedSmem<KV, D, G, NHL, TPI> sm;
     paged_chunk<KV, D, G, NHL, TPI>(a, sm, blockIdx.x, blockIdx.y);
 }

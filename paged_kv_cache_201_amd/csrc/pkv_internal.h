@@ -37,13 +37,15 @@ constexpr int32_t kTiledRowsPerWg = 64;
 constexpr int32_t kPrefixTokenQuantum = 64;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // Paged-pass chunks hold a multiple of this many tokens, and at most
-// max_chunk_tokens(...) (the kernel stages a chunk's slot indices in LDS next
-// to the per-wave merge buffer of 16 * rows_per_load * nhl * G * d bytes; the
-// index stage is sized so that two workgroups still fit in a CU's 160 KB).
+// max_chunk_tokens(...): the kernel stages a chunk's slot indices in LDS next
+// to its merge buffer (two wave states with one token per load, else one per
+// wave and token lane group: 4 bytes x slots x heads per item x G x d), and
+// the index stage is sized so that two workgroups still fit in a CU's 160 KB.
 constexpr int32_t kSplitQuantum = 16;
 constexpr int32_t kMaxSplitTokens = 4096;
-constexpr int32_t max_chunk_tokens(int32_t rs, int32_t nhl, int32_t group, int32_t head_dim) {
-    return 16 * rs * nhl * group * head_dim > 40 * 1024 ? 2048 : kMaxSplitTokens;
+constexpr int32_t max_chunk_tokens(int32_t rs, int32_t nhl, int32_t tpi, int32_t group, int32_t head_dim) {
+    return 4 * (tpi == 1 ? 2 : 4 * tpi) * (rs * nhl / tpi) * group * head_dim > 40 * 1024 ? 2048
+                                                                                           : kMaxSplitTokens;
 }
 
 }  // namespace pkv
