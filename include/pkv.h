@@ -189,9 +189,10 @@ pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indi
  * Plan one decode step (host only, no device work).  [P2] s.3: chooses the
  * path from M_eff = B * G and the declared shared prefix; [P1] "When source
  * beats intuition": the host metadata step before the kernels.  Also fixes the
- * split of each request's tokens into work items (by logical position, so
- * results do not depend on page size or page placement) and the workspace
- * size.  tuning may be NULL (gfx950 defaults).  The problem's kv_indptr is
+ * paged pass's work items -- the attended positions of all requests, request
+ * after request, cut into equal chunks (by logical position, so results do
+ * not depend on page size or page placement) -- the prefix pass's ranges and
+ * the workspace size.  tuning may be NULL (gfx950 defaults).  The problem's kv_indptr is
  * read during the call and not kept.  *out receives a new handle that the
  * caller frees with pkv_plan_destroy; it can be reused on any stream for any
  * step with the same problem.
@@ -301,7 +302,9 @@ pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
  * and DENSE run the prefix pass over kv_indices[kv_indptr[0] ..
  * + prefix_tokens) (request 0's shared pages), the paged pass over each
  * request's suffix, and one kernel that combines both passes' partial
- * states (kept in the workspace).  With concurrent_prefix set in the plan's
+ * states (kept in the workspace).  On a DENSE plan that meets the tuning's
+ * fuse_cascade rule the two passes are one launch whose workgroups run
+ * either a prefix item or a suffix chunk.  Otherwise, with concurrent_prefix set in the plan's
  * tuning, the prefix pass is enqueued on a side stream that the library
  * creates once per device (default priority), forked from and joined back
  * to `stream` with events, so the MFMA-bound prefix pass and the
