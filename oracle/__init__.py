@@ -23,10 +23,14 @@ Contents and what each part follows:
 * ``planner``   -- the per-step dispatcher on M_eff = realized batch x GQA
                    group ("GraniKV: asymmetric KV cache paging for
                    shared-prefix agents", section 3 "Per-step dispatcher").
+* ``groups``    -- several shared prefixes in one step: groups of requests on
+                   the same leading whole pages, each planned on its own
+                   ("Track C · Document 10", block-size paragraph and the
+                   table of prompt-layout mistakes; "GraniKV", sections 2-3).
 * ``batch``     -- runs the above over a whole synthetic batch.
 
 Parity unpinned: none of the functions here.  The planner's tuning constants
 are inputs; whether their gfx950 values are the right ones is a measurement,
 not an oracle question.
 """
-from . import values, attention, lowering, planner, batch  # noqa: F401
+from . import values, attention, lowering, planner, groups, batch  # noqa: F401

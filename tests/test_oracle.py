@@ -431,3 +431,224 @@ def test_mutant_fp8_caught():
 def test_mutant_lowering_caught(mutant):
     with pytest.raises((AssertionError, IndexError)):
         check_lowering(mutant)
+
+
+# ---------------------------------------------------------- prefix groups ---
+
+from oracle import groups as og  # noqa: E402
+
+
+def tables_from_blocks(requests, p, seed=0):
+    """Page tables for requests given as lists of per-block contents: a
+    physical page is shared exactly when the content up to and including its
+    block is the same (exact, block-aligned prefix matching).  Page numbers
+    are scrambled by a seeded permutation."""
+    ids = {}
+    tables = []
+    for blocks in requests:
+        tables.append([ids.setdefault(tuple(blocks[:j + 1]), len(ids)) for j in range(len(blocks))])
+    perm = np.random.default_rng(seed).permutation(max(1, len(ids)))
+    page_indptr = np.zeros(len(requests) + 1, np.int64)
+    for b, t in enumerate(tables):
+        page_indptr[b + 1] = page_indptr[b] + len(t)
+    page_indices = np.array([perm[x] for t in tables for x in t], np.int64)
+    return page_indptr, page_indices
+
+
+def _token_blocks(tokens, p):
+    return [tuple(tokens[j:j + p]) for j in range(0, len(tokens), p)]
+
+
+def golden_group_case(c, p):
+    if "requests" in c:
+        reqs = c["requests"]
+        lens = [p * len(r) for r in reqs]
+        return reqs, lens
+    P = c["prefix_tokens"]
+    reqs, lens = [], []
+    for b, n in enumerate(c["own_tokens"]):
+        toks = ["P"] * P + [f"own{b}"] * n
+        reqs.append(_token_blocks(toks, p))
+        lens.append(len(toks))
+    return reqs, lens
+
+
+def check_group_golden(detect, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "prefix_groups.json")))
+    p = g["block_size"]
+    for c in g["cases"]:
+        reqs, lens = golden_group_case(c, p)
+        for seed in (0, 1):
+            ptr, pages = tables_from_blocks(reqs, p, seed)
+            got = detect(p, ptr, pages, lens)
+            want = [{"members": x["members"], "shared_pages": x["shared_blocks"]} for x in c["groups"]]
+            assert got == want, (c["name"], got)
+
+
+def test_prefix_groups_golden(golden_dir):
+    check_group_golden(og.detect_prefix_groups, golden_dir)
+
+
+def _groups_bruteforce(p, ptr, pages, lens):
+    """Pairwise statement of the grouping: two requests are grouped when they
+    hold the same physical page as first full page; a group's shared pages
+    are the largest k for which every member holds k full pages and all
+    members agree on the first k pages."""
+    B = len(lens)
+    tab = [list(pages[ptr[b]:ptr[b + 1]]) for b in range(B)]
+    full = [lens[b] // p for b in range(B)]
+    seen, out = set(), []
+    for b in range(B):
+        if b in seen or full[b] == 0:
+            continue
+        mem = [c for c in range(B) if full[c] > 0 and tab[c][0] == tab[b][0]]
+        seen.update(mem)
+        if len(mem) < 2:
+            continue
+        k = 0
+        while all(full[c] >= k + 1 for c in mem) and all(tab[c][k] == tab[mem[0]][k] for c in mem):
+            k += 1
+        out.append({"members": mem, "shared_pages": k})
+    return out
+
+
+def _random_group_tables(rng, p):
+    """Requests drawn from a few system prompts of random lengths (in tokens),
+    some continued by one of two shared follow-ups (nested sharing), each
+    followed by its own tokens; some requests have no prompt."""
+    n_prompts = int(rng.integers(0, 4))
+    prompts = [int(rng.integers(0, 5 * p)) for _ in range(n_prompts)]
+    follow = [[int(rng.integers(1, 3 * p)) for _ in range(2)] for _ in range(n_prompts)]
+    B = int(rng.integers(0, 9))
+    reqs, lens = [], []
+    for b in range(B):
+        k = int(rng.integers(-1, n_prompts)) if n_prompts else -1
+        toks = []
+        if k >= 0:
+            toks = [f"s{k}"] * prompts[k]
+            j = int(rng.integers(-1, 2))
+            if j >= 0:
+                toks += [f"f{k}.{j}"] * follow[k][j]
+        toks += [f"o{b}"] * int(rng.integers(0, 3 * p))
+        reqs.append(_token_blocks(toks, p))
+        lens.append(len(toks))
+    return reqs, lens
+
+
+def test_prefix_groups_match_bruteforce():
+    check_groups_bruteforce(og.detect_prefix_groups)
+    # the random tables do exercise groups, including ones whose members
+    # share runs of different lengths
+    rng = np.random.default_rng(7)
+    n_groups = 0
+    for it in range(400):
+        p = int(rng.choice([1, 2, 4, 16]))
+        reqs, lens = _random_group_tables(rng, p)
+        ptr, pages = tables_from_blocks(reqs, p, it)
+        n_groups += len(og.detect_prefix_groups(p, ptr, pages, lens))
+    assert n_groups > 100
+
+
+def test_plan_groups_is_the_single_prefix_rule_per_group():
+    # Two groups of 200 and 2 requests on 4096-token prompts, one loner:
+    # the large group passes the gate, the small one does not (A100 constants).
+    p = 16
+    reqs = [["A%d" % j for j in range(256)] + ["a%d" % b] for b in range(200)]
+    reqs += [["B%d" % j for j in range(256)] + ["b%d" % b] for b in range(2)]
+    reqs += [["C"]]
+    lens = [p * len(r) for r in reqs]
+    ptr, pages = tables_from_blocks(reqs, p)
+    tune = dict(t_dense=1024, gate_ratio=3, launch_bytes=10_000_000)
+    kept, group_of = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                                    page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
+    one = op.plan(B=200, H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                  seq_lens=lens[:200], shared_prefix_len=4096, force_path=-1, **tune)
+    assert len(kept) == 1 and kept[0]["members"] == list(range(200))
+    assert kept[0]["path"] == one["path"] == "CASCADE" and kept[0]["m_eff"] == 800
+    assert kept[0]["prefix_tokens"] == 4096 and group_of[:200] == [0] * 200 and group_of[200:] == [-1] * 3
+    # forced: every group takes the forced prefix path, the loner stays alone
+    kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                             page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=2, **tune)
+    assert [g["path"] for g in kept] == ["DENSE", "DENSE"] and [len(g["members"]) for g in kept] == [200, 2]
+    # fp8 K/V has no prefix kernel: nothing is kept unless forced, which is refused
+    kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="fp8", page_size=p,
+                             page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
+    assert kept == []
+    with pytest.raises(op.PlanError):
+        og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="fp8", page_size=p, page_indptr=ptr,
+                       page_indices=pages, seq_lens=lens, force_path=1, **tune)
+
+
+def test_lower_groups_partitions_every_request():
+    rng = np.random.default_rng(11)
+    for it in range(200):
+        p = int(rng.choice([1, 4, 16]))
+        reqs, lens = _random_group_tables(rng, p)
+        ptr, pages = tables_from_blocks(reqs, p, it)
+        kept, group_of = og.plan_groups(H_q=8, H_kv=2, d=64, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                                        page_indptr=ptr, page_indices=pages, seq_lens=lens,
+                                        force_path=int(rng.choice([-1, 1, 2])), t_dense=8, gate_ratio=0,
+                                        launch_bytes=0)
+        suf_ptr, suf, pre_ptr, pre = og.lower_groups(p, ptr, pages, lens, kept, group_of)
+        kv_ptr, kv = ol.lower_page_table(p, ptr, pages, lens)
+        for b in range(len(lens)):
+            full = list(kv[kv_ptr[b]:kv_ptr[b + 1]])
+            mine = list(suf[suf_ptr[b]:suf_ptr[b + 1]])
+            if group_of[b] >= 0:
+                g = group_of[b]
+                shared = list(pre[pre_ptr[g]:pre_ptr[g + 1]])
+                assert len(shared) % p == 0 and len(shared) > 0
+                assert shared + mine == full        # prefix ++ suffix is the request
+            else:
+                assert mine == full
+
+
+def _mut_groups_max_run(p, ptr, pages, lens):
+    """Takes the longest run any member shares with the first member instead
+    of the run all members share."""
+    out = og.detect_prefix_groups(p, ptr, pages, lens)
+    B = len(lens)
+    tab = [list(pages[ptr[b]:ptr[b + 1]]) for b in range(B)]
+    for g in out:
+        m0, best = g["members"][0], 0
+        for c in g["members"][1:]:
+            k = 0
+            while k < min(lens[m0], lens[c]) // p and tab[c][k] == tab[m0][k]:
+                k += 1
+            best = max(best, k)
+        g["shared_pages"] = best
+    return out
+
+
+def _mut_groups_partial_page(p, ptr, pages, lens):
+    """Counts a partly filled last page as shareable."""
+    return og.detect_prefix_groups(p, ptr, pages, [((x + p - 1) // p) * p for x in lens])
+
+
+def _mut_groups_pairwise_first(p, ptr, pages, lens):
+    """Shared run measured against the first member only, with the wrong
+    member: the last one's full-page count is ignored."""
+    out = og.detect_prefix_groups(p, ptr, pages, lens)
+    for g in out:
+        g["shared_pages"] = min(lens[g["members"][0]] // p, g["shared_pages"] + 1)
+    return out
+
+
+def check_groups_bruteforce(detect, n=400):
+    rng = np.random.default_rng(7)
+    for it in range(n):
+        p = int(rng.choice([1, 2, 4, 16]))
+        reqs, lens = _random_group_tables(rng, p)
+        ptr, pages = tables_from_blocks(reqs, p, it)
+        assert detect(p, ptr, pages, lens) == _groups_bruteforce(p, ptr, pages, lens)
+
+
+@pytest.mark.parametrize("mutant", [_mut_groups_max_run, _mut_groups_partial_page, _mut_groups_pairwise_first])
+def test_mutant_groups_caught(mutant, golden_dir):
+    caught = 0
+    for check in (lambda: check_group_golden(mutant, golden_dir), lambda: check_groups_bruteforce(mutant)):
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
