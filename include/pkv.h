@@ -142,6 +142,8 @@ typedef struct pkv_plan_info {
     int32_t prefix_splits;      /* prefix pass: ranges the prefix is cut into */
     int64_t num_work_items;     /* paged pass: workgroups launched (chunks x head blocks) */
     int64_t workspace_bytes;    /* device scratch the plan's calls need (0 allowed) */
+    int32_t num_groups;         /* grouped plans: prefix groups that run a prefix pass (else 0) */
+    int64_t metadata_ints;      /* grouped plans: int32 entries of the metadata block (else 0) */
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
@@ -203,6 +205,57 @@ pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indi
  */
 pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning* tuning,
                            pkv_plan** out);
+
+/*
+ * Plan a decode step whose requests may share several prefixes, found in the
+ * page table itself (host only).  [P3] block-size paragraph and table of
+ * prompt-layout mistakes: prefix matching is exact and aligned to blocks from
+ * the start of a sequence, so requests share a prefix exactly when their page
+ * tables start with the same physical pages (two system prompts make two
+ * separate trees); [P2] s.2-3: each shared prefix is read once for the
+ * requests on it, with its own dispatcher decision from its own realized
+ * batch.  Rules:
+ *   - a request holds floor(L_b / page_size) whole pages; a partly filled
+ *     last page is never shared;
+ *   - requests whose first whole page is the same physical page form a
+ *     group; its shared pages are the longest leading run of pages that every
+ *     member holds whole and all members agree on; a group needs two members;
+ *   - each group is planned as pkv_plan_create plans a step of its members
+ *     alone with its shared tokens as the declared prefix (gate, DENSE or
+ *     CASCADE, force_path); a group planned PAGED is dissolved;
+ *   - groups are numbered by their first member, members in request order.
+ * The problem's kv_indptr is ignored (may be NULL) and its shared_prefix_len
+ * must be 0.  page_indptr [B+1], page_indices, seq_lens [B] are host arrays
+ * as for pkv_lower_page_table, read during the call.  The plan holds the
+ * lowered indices of the step in its metadata block (pkv_plan_metadata),
+ * which the caller copies to the device once for pkv_decode_step_grouped.
+ * Plan info: path is PAGED without groups, DENSE if a group runs DENSE, else
+ * CASCADE; m_eff is the largest group's; shared_pages and prefix_tokens are
+ * summed over groups; prefix_splits is the most ranges of any group.
+ * Errors: as pkv_plan_create and pkv_lower_page_table; EINVAL also for a
+ * non-zero shared_prefix_len.
+ */
+pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv_tuning* tuning,
+                                   const int32_t* page_indptr, const int32_t* page_indices,
+                                   const int32_t* seq_lens, pkv_plan** out);
+
+/*
+ * Copy a grouped plan's metadata block (info.metadata_ints int32 entries)
+ * to host memory out[capacity].  Layout, each array right after the one
+ * before (NG = info.num_groups):
+ *   suffix_indptr  [B+1]   token offsets of each request's own tokens
+ *   suffix_indices [suffix_indptr[B]]  slots of request b's tokens after its
+ *                  group's shared tokens (all of its tokens without a group)
+ *   group_indptr   [NG+1]  offsets into group_members
+ *   group_members  [group_indptr[NG]]  requests of each group
+ *   prefix_indptr  [NG+1]  offsets into prefix_indices
+ *   prefix_indices [prefix_indptr[NG]]  slots of each group's shared tokens
+ *   request_group  [B]     group of each request, -1 for none
+ *   followed by tables only the kernels read.
+ * Errors: EINVAL (null plan, plan not from pkv_plan_create_grouped, null out
+ * with a non-empty block), ERANGE (capacity too small).
+ */
+pkv_status pkv_plan_metadata(const pkv_plan* plan, int32_t* out, int64_t capacity);
 
 /* Copy a plan's decisions and sizes into *info.  EINVAL on null pointers. */
 pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);
@@ -318,6 +371,22 @@ pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step of a grouped plan: one prefix pass over every group's
+ * shared tokens (each read once for the group's requests; DENSE groups and
+ * CASCADE groups in one launch each), the paged pass over every request's
+ * suffix, and one kernel that combines, per row, its group's prefix ranges
+ * and its suffix chunks into o (and lse).  The result is that of attention
+ * over each request's whole sequence.
+ *   metadata  device copy of the plan's metadata block (pkv_plan_metadata)
+ * Other arguments as pkv_decode_step; o is required, lse is nullable.
+ * Errors: EINVAL (null plan/q/metadata/o, plan not grouped, pool not
+ * matching), EWORKSPACE, EHIP.
+ */
+pkv_status pkv_decode_step_grouped(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                                   const int32_t* metadata, float sm_scale, void* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid: read `bytes` of device memory at `buf` once (each of
  * num_workgroups workgroups of 256 threads streams one contiguous block with
  * 16-byte non-temporal loads) and write one word per workgroup to
@@ -331,6 +400,17 @@ pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* 
  */
 pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_workgroups,
                                  void* stream);
+
+/*
+ * Measurement aid: fill `bytes` of device memory at `buf` with the 32-bit
+ * `value` (each of num_workgroups workgroups of 256 threads writes one
+ * contiguous block with 16-byte stores).  Its bytes are known exactly, so
+ * the write-traffic counters of a profiler can be calibrated against it
+ * before they are read for the attention kernels.
+ * Errors: EINVAL (null buf, bytes not a multiple of 16, misaligned buf,
+ * num_workgroups < 1), EHIP.
+ */
+pkv_status pkv_stream_write_probe(void* buf, int64_t bytes, uint32_t value, int32_t num_workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,7 +64,8 @@ class pkv_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("m_eff", ctypes.c_int32), ("shared_pages", ctypes.c_int32),
                 ("prefix_tokens", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
-                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("num_groups", ctypes.c_int32), ("metadata_ints", ctypes.c_int64)]
 
 
 _SIGS = {
@@ -76,6 +77,9 @@ _SIGS = {
     "pkv_validate_indices": (ctypes.c_int32, [_i32p, _i32p, ctypes.c_int32, ctypes.c_int64]),
     "pkv_plan_create": (ctypes.c_int32, [ctypes.POINTER(pkv_problem), ctypes.POINTER(pkv_tuning),
                                          ctypes.POINTER(_vp)]),
+    "pkv_plan_create_grouped": (ctypes.c_int32, [ctypes.POINTER(pkv_problem), ctypes.POINTER(pkv_tuning),
+                                                 _i32p, _i32p, _i32p, ctypes.POINTER(_vp)]),
+    "pkv_plan_metadata": (ctypes.c_int32, [_vp, _i32p, ctypes.c_int64]),
     "pkv_plan_get_info": (ctypes.c_int32, [_vp, ctypes.POINTER(pkv_plan_info)]),
     "pkv_plan_destroy": (None, [_vp]),
     "pkv_paged_decode_attn": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp,
@@ -88,7 +92,10 @@ _SIGS = {
                                           _vp, _vp]),
     "pkv_decode_step": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]),
+    "pkv_decode_step_grouped": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, ctypes.c_float, _vp,
+                                                 _vp, _vp, ctypes.c_size_t, _vp]),
     "pkv_stream_read_probe": (ctypes.c_int32, [_vp, ctypes.c_int64, _vp, ctypes.c_int32, _vp]),
+    "pkv_stream_write_probe": (ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -209,6 +216,51 @@ def pkv_plan_create(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_d
                               shared_prefix_len=shared_prefix_len, force_path=force_path))
 
 
+def pkv_plan_create_grouped(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, page_size,
+                            page_indptr, page_indices, seq_lens, force_path=-1, tuning=None) -> Plan:
+    """Plan a step whose requests may share several prefixes, found in the
+    page table (host arrays)."""
+    ptr, ptr_p = _host_i32(page_indptr)
+    pages, pages_p = _host_i32(page_indices if len(page_indices) else np.zeros(1, np.int32))
+    lens, lens_p = _host_i32(seq_lens if len(seq_lens) else np.zeros(1, np.int32))
+    pr = pkv_problem(batch, num_q_heads, num_kv_heads, head_dim, DTYPE_CODES.get(q_dtype, q_dtype),
+                     DTYPE_CODES.get(kv_dtype, kv_dtype), page_size, None, 0, force_path)
+    tp = None
+    if tuning is not None:
+        d = pkv_tuning_defaults()
+        d.update(tuning)
+        tp = ctypes.byref(pkv_tuning(**d))
+    h = _vp()
+    _check(_lib.pkv_plan_create_grouped(ctypes.byref(pr), tp, ptr_p, pages_p, lens_p, ctypes.byref(h)),
+           "pkv_plan_create_grouped")
+    return Plan(h.value, dict(batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                              q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=page_size, force_path=force_path,
+                              grouped=True))
+
+
+def pkv_plan_metadata(plan: Plan):
+    """The grouped plan's metadata block as a numpy int32 array."""
+    n = plan.info["metadata_ints"]
+    out = np.zeros(max(n, 1), np.int32)
+    _check(_lib.pkv_plan_metadata(plan.handle, out.ctypes.data_as(_i32p), n), "pkv_plan_metadata")
+    return out[:n]
+
+
+def split_metadata(block, batch, num_groups):
+    """Views of the public arrays of a metadata block, by name."""
+    out, off = {}, 0
+    for name, n in (("suffix_indptr", batch + 1), ("suffix_indices", None), ("group_indptr", num_groups + 1),
+                    ("group_members", None), ("prefix_indptr", num_groups + 1), ("prefix_indices", None),
+                    ("request_group", batch)):
+        if n is None:
+            ptr = out[{"suffix_indices": "suffix_indptr", "group_members": "group_indptr",
+                       "prefix_indices": "prefix_indptr"}[name]]
+            n = int(ptr[-1])
+        out[name] = block[off:off + n]
+        off += n
+    return out
+
+
 def pkv_plan_get_info(plan: Plan) -> dict:
     return dict(plan.info)
 
@@ -289,6 +341,21 @@ def pkv_decode_step(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None,
                               _dev(kv_indices, "kv_indices", (torch.int32,)), float(sm_scale), _dev(o, "o"),
                               _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
     _check(st, "pkv_decode_step")
+
+
+def pkv_decode_step_grouped(plan, q, pool, metadata, sm_scale, o, lse=None, workspace=None, stream=None):
+    import torch
+    ws, wsb = _ws(workspace, plan)
+    st = _lib.pkv_decode_step_grouped(plan.handle, _dev(q, "q"), ctypes.byref(pool),
+                                      _dev(metadata, "metadata", (torch.int32,)), float(sm_scale), _dev(o, "o"),
+                                      _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
+    _check(st, "pkv_decode_step_grouped")
+
+
+def pkv_stream_write_probe(buf, value, num_workgroups, stream=None):
+    """Write all of ``buf`` (a CUDA tensor) once with the 32-bit ``value``."""
+    _check(_lib.pkv_stream_write_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(), int(value) & 0xFFFFFFFF,
+                                       int(num_workgroups), _stream(stream)), "pkv_stream_write_probe")
 
 
 def pkv_stream_read_probe(buf, out, num_workgroups, stream=None):

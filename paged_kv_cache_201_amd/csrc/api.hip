@@ -194,7 +194,7 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* pl, const void* q, const pkv_po
                                  const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
                                  void* o, float* o_f32, float* lse, void* ws, size_t ws_bytes,
                                  void* stream) {
-    if (!pl) return PKV_EINVAL;
+    if (!pl || pl->grouped) return PKV_EINVAL;
     if (!o && !o_f32) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
@@ -210,7 +210,7 @@ pkv_status pkv_paged_decode_attn_pages(const pkv_plan* pl, const void* q, const 
                                        const int32_t* kv_indptr, const int32_t* page_indptr,
                                        const int32_t* page_indices, float sm_scale, void* o, float* o_f32,
                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
-    if (!pl) return PKV_EINVAL;
+    if (!pl || pl->grouped) return PKV_EINVAL;
     if (!o && !o_f32) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
@@ -228,7 +228,7 @@ pkv_status pkv_paged_decode_attn_pages(const pkv_plan* pl, const void* q, const 
 pkv_status pkv_cascade_prefix_attn(const pkv_plan* pl, const void* q, const pkv_pool* pool,
                                    const int32_t* prefix_indices, int32_t prefix_len, float sm_scale,
                                    float* o_p, float* lse_p, void* ws, size_t ws_bytes, void* stream) {
-    if (!pl) return PKV_EINVAL;
+    if (!pl || pl->grouped) return PKV_EINVAL;
     if (pl->path == PKV_PATH_PAGED) return PKV_EINVAL;
     if (prefix_len != pl->prefix_tokens) return PKV_EINVAL;
     if (!q || !prefix_indices || !o_p || !lse_p) return PKV_EINVAL;
@@ -255,6 +255,7 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
                            const int32_t* kv_indices, float sm_scale, void* o, float* lse, void* ws,
                            size_t ws_bytes, void* stream) {
     if (!pl || !o) return PKV_EINVAL;
+    if (pl->grouped) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);
@@ -297,6 +298,65 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     r.pre_acc = pa.part_acc;
     r.pre_ml = pa.part_ml;
     r.pre_splits = pl->prefix_splits;
+    r.o = o;
+    r.lse = lse;
+    return hip_status(pkv::launch_split_reduce(r, s));
+}
+
+pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* meta,
+                                   float sm_scale, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!pl || !o || !pl->grouped) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    st = check_workspace(pl, ws, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (pl->B == 0) return PKV_OK;
+    if (!q || !meta) return PKV_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t* suffix_indptr = meta + pl->meta_suffix_indptr;
+    const int32_t* suffix_indices = meta + pl->meta_suffix_indices;
+    pkv::PagedArgs sa = paged_args(pl, q, pool, suffix_indptr, suffix_indices, sm_scale);
+    sa.token_offset = 0;
+    if (pl->num_groups == 0) {
+        // no shared prefix anywhere: a plain paged step over every token
+        return run_paged_args(pl, sa, o, nullptr, lse, ws, s);
+    }
+    // Prefix pass: items of the DENSE groups, then of the CASCADE groups,
+    // each set in one launch; partial states per (request, range).
+    pkv::PrefixArgs pa{};
+    pa.q = q;
+    pa.k = pool->k;
+    pa.v = pool->v;
+    pa.prefix_indices = meta + pl->meta_prefix_indices;
+    pa.B = pl->B;
+    pa.H_kv = pl->H_kv;
+    pa.G = pl->G;
+    pa.D = pl->D;
+    pa.num_splits = pl->prefix_splits;
+    pa.scale_log2 = sm_scale * kLog2e;
+    pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
+    pa.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
+    pa.force_partial = 1;
+    pa.groups = meta + pl->meta_desc;
+    pa.members = meta + pl->meta_members;
+    pa.num_groups = pl->num_groups;
+    pa.item_base = 0;
+    pa.num_items = pl->dense_items;
+    if (pl->dense_items > 0 && pkv::launch_prefix_attn(pa, pkv::kDenseRowsPerWg, s) != hipSuccess) return PKV_EHIP;
+    pa.item_base = pl->dense_items;
+    pa.num_items = pl->tiled_items;
+    if (pl->tiled_items > 0 && pkv::launch_prefix_attn(pa, pkv::kTiledRowsPerWg, s) != hipSuccess) return PKV_EHIP;
+    // Suffix pass, then the combine of each row's prefix ranges (its group's
+    // count) and suffix chunks.
+    sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
+    sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
+    sa.force_partial = 1;
+    if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    pkv::SplitReduceArgs r = chunk_reduce_args(pl, sa);
+    r.pre_acc = pa.part_acc;
+    r.pre_ml = pa.part_ml;
+    r.pre_splits = pl->prefix_splits;
+    r.pre_count = meta + pl->meta_pre_count;
     r.o = o;
     r.lse = lse;
     return hip_status(pkv::launch_split_reduce(r, s));

@@ -6,6 +6,8 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <unordered_map>
+#include <vector>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -71,6 +73,151 @@ bool paged_geometry(int32_t kv_dtype, int32_t head_dim, int32_t group, int32_t n
 }
 
 }  // namespace pkv
+
+namespace {
+
+// Checks shared by both planners: tuning ranges, sizes, head counts.
+pkv_status check_problem(const pkv_problem* pr, const pkv_tuning* tuning, pkv_tuning* tu) {
+    if (tuning) {
+        *tu = *tuning;
+    } else {
+        pkv_tuning_defaults(tu);
+    }
+    if (tu->t_dense < 1 || tu->gate_ratio < 0 || tu->launch_bytes < 0 || tu->target_workgroups < 1 ||
+        tu->min_split_tokens < 1 || tu->concurrent_prefix < 0 || tu->concurrent_prefix > 1 ||
+        tu->fuse_cascade < 0 || tu->prefix_target_workgroups < 1 || tu->min_prefix_split_tokens < 1 ||
+        tu->max_heads_per_item < 0)
+        return PKV_EINVAL;
+    const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
+    if (B < 0 || H_kv < 1 || H_q < 1 || pr->page_size < 1 || pr->head_dim < 1) return PKV_EINVAL;
+    if (H_q % H_kv) return PKV_EINVAL;
+    return PKV_OK;
+}
+
+// Shapes and dtypes the kernels are built for.
+pkv_status check_support(const pkv_problem* pr, const pkv_tuning& tu, pkv::PagedGeometry* geo) {
+    const int32_t G = pr->num_q_heads / pr->num_kv_heads;
+    const int32_t D = pr->head_dim;
+    if ((D != 64 && D != 128) || !dtype_pair_supported(pr->q_dtype, pr->kv_dtype) || !group_supported(G))
+        return PKV_EUNSUPPORTED;
+    if (!pkv::paged_geometry(pr->kv_dtype, D, G, pr->num_kv_heads, tu.max_heads_per_item, geo))
+        return PKV_EUNSUPPORTED;
+    return PKV_OK;
+}
+
+// The dispatcher for n_shared requests on prefix_tokens shared tokens
+// (whole pages), rows query rows and M_eff = m_eff, in order: a forced path;
+// PAGED without two sharers, a shared page or a prefix kernel for the dtype
+// pair; PAGED when the bytes saved are under gate_ratio x the combine's
+// state traffic plus the launch term; DENSE at M_eff >= t_dense; CASCADE.
+pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_shared, int64_t prefix_tokens,
+                       int64_t rows, int64_t m_eff, int32_t* path) {
+    const bool capable = prefix_pair_supported(pr->q_dtype, pr->kv_dtype);
+    if (pr->force_path >= 0) {
+        *path = pr->force_path;
+        if (*path != PKV_PATH_PAGED) {
+            if (!capable) return PKV_EUNSUPPORTED;
+            if (prefix_tokens == 0) return PKV_EINVAL;
+        }
+        return PKV_OK;
+    }
+    if (!capable || n_shared < 2 || prefix_tokens == 0) {
+        *path = PKV_PATH_PAGED;
+        return PKV_OK;
+    }
+    const int64_t D = pr->head_dim;
+    const int64_t kv_bytes = 2LL * dtype_bytes(pr->kv_dtype);
+    const int64_t saved = (n_shared - 1) * prefix_tokens * pr->num_kv_heads * D * kv_bytes;
+    const int64_t overhead = 4 * rows * (D + 1) * 4 + tu.launch_bytes;
+    if (saved < (int64_t)tu.gate_ratio * overhead)
+        *path = PKV_PATH_PAGED;
+    else if (m_eff >= tu.t_dense)
+        *path = PKV_PATH_DENSE;
+    else
+        *path = PKV_PATH_CASCADE;
+    return PKV_OK;
+}
+
+void fill_problem(pkv_plan* pl, const pkv_problem* pr, const pkv_tuning& tu, const pkv::PagedGeometry& geo) {
+    pl->B = pr->batch;
+    pl->H_q = pr->num_q_heads;
+    pl->H_kv = pr->num_kv_heads;
+    pl->D = pr->head_dim;
+    pl->G = pr->num_q_heads / pr->num_kv_heads;
+    pl->q_dtype = pr->q_dtype;
+    pl->kv_dtype = pr->kv_dtype;
+    pl->page_size = pr->page_size;
+    pl->geo = geo;
+    pl->head_blocks = pr->num_kv_heads / geo.hb;
+    pl->concurrent_prefix = tu.concurrent_prefix;
+}
+
+// Prefix ranges for prefix_tokens shared tokens read by `tiles` (query tile,
+// KV head) pairs, aiming at `target` workgroups: multiples of the token
+// quantum, at least the tuning's minimum, at most what the kernel stages.
+void prefix_ranges(const pkv_tuning& tu, int64_t prefix_tokens, int64_t tiles, int64_t target, int32_t* split_tokens,
+                   int32_t* splits) {
+    const int64_t want = std::max<int64_t>(1, ceil_div(target, tiles));
+    int64_t ps = align_up(ceil_div(prefix_tokens, want), pkv::kPrefixTokenQuantum);
+    ps = std::max<int64_t>(ps, align_up(tu.min_prefix_split_tokens, pkv::kPrefixTokenQuantum));
+    ps = std::min<int64_t>(ps, pkv::kMaxPrefixSplitTokens);
+    *split_tokens = (int32_t)ps;
+    *splits = (int32_t)ceil_div(prefix_tokens, ps);
+}
+
+// Paged-pass chunking over `total` positions, n_of(b) of them request b's:
+// chunk size from the workgroup target, partial states per request.
+template <class LenFn>
+void plan_chunks(pkv_plan* pl, const pkv_tuning& tu, int64_t total, int64_t target, LenFn n_of, bool* spans,
+                 bool* any_empty) {
+    pl->paged_tokens = total;
+    const int64_t per_item = ceil_div(total * pl->head_blocks, target);
+    int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
+    chunk = align_up(chunk, pkv::kSplitQuantum);
+    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(pl->geo.rs, pl->geo.nhl, pl->geo.tpi, pl->G, pl->D));
+    pl->split_tokens = (int32_t)chunk;
+    pl->num_chunks = ceil_div(total, chunk);
+    pl->num_work_items = pl->num_chunks * pl->head_blocks;
+    // Partial states per request: the chunks its range touches.
+    int64_t pos = 0, max_parts = 1;
+    *spans = *any_empty = false;
+    for (int32_t b = 0; b < pl->B; ++b) {
+        const int64_t n = n_of(b);
+        if (n > 0) {
+            const int64_t parts = (pos + n - 1) / chunk - pos / chunk + 1;
+            max_parts = std::max(max_parts, parts);
+            *spans |= parts > 1;
+        }
+        *any_empty |= n == 0;
+        pos += n;
+    }
+    pl->num_splits = (int32_t)max_parts;
+}
+
+// Workspace: chunk partials of the paged pass (if kept) and prefix_splits
+// prefix partials per row, 256-byte aligned.
+void layout_workspace(pkv_plan* pl, bool paged_partials, int32_t prefix_splits) {
+    int64_t off = 0;
+    const int64_t rows = (int64_t)pl->B * pl->H_q;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = off;
+        off = align_up(off + bytes, kAlign);
+        return at;
+    };
+    pl->ws_paged_acc = pl->ws_paged_ml = -1;
+    pl->ws_prefix_acc = pl->ws_prefix_ml = -1;
+    if (paged_partials) {
+        pl->ws_paged_acc = take(rows * pl->num_splits * pl->D * 4);
+        pl->ws_paged_ml = take(rows * pl->num_splits * 2 * 4);
+    }
+    if (prefix_splits > 0) {
+        pl->ws_prefix_acc = take(rows * prefix_splits * pl->D * 4);
+        pl->ws_prefix_ml = take(rows * prefix_splits * 2 * 4);
+    }
+    pl->workspace_bytes = off;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -174,92 +321,46 @@ pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indi
 pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_plan** out) {
     if (!pr || !out) return PKV_EINVAL;
     pkv_tuning tu;
-    if (tuning) {
-        tu = *tuning;
-    } else {
-        pkv_tuning_defaults(&tu);
-    }
-    if (tu.t_dense < 1 || tu.gate_ratio < 0 || tu.launch_bytes < 0 || tu.target_workgroups < 1 ||
-        tu.min_split_tokens < 1 ||
-        tu.concurrent_prefix < 0 || tu.concurrent_prefix > 1 || tu.fuse_cascade < 0 ||
-        tu.prefix_target_workgroups < 1 ||
-        tu.min_prefix_split_tokens < 1 || tu.max_heads_per_item < 0)
-        return PKV_EINVAL;
-
-    // Checks, in the same order as the planner's reference statement.
+    pkv::PagedGeometry geo;
+    pkv_status st = check_problem(pr, tuning, &tu);
+    if (st != PKV_OK) return st;
     const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
     const int32_t D = pr->head_dim, p = pr->page_size;
-    if (B < 0 || H_kv < 1 || H_q < 1 || p < 1 || D < 1) return PKV_EINVAL;
-    if (H_q % H_kv) return PKV_EINVAL;
     if (B > 0 && !pr->kv_indptr) return PKV_EINVAL;
-    int64_t min_len = INT64_MAX, max_len = 0;
+    int64_t min_len = INT64_MAX;
     for (int32_t b = 0; b < B; ++b) {
         const int64_t L = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b];
         if (L < 0) return PKV_EINVAL;
         min_len = std::min(min_len, L);
-        max_len = std::max(max_len, L);
     }
     if (B > 0 && pr->kv_indptr[0] < 0) return PKV_EINVAL;
     const int32_t P = pr->shared_prefix_len;
     if (P < 0 || (B > 0 && P > min_len)) return PKV_EINVAL;
     if (pr->force_path < -1 || pr->force_path > 2) return PKV_EINVAL;
+    st = check_support(pr, tu, &geo);
+    if (st != PKV_OK) return st;
     const int32_t G = H_q / H_kv;
-    if ((D != 64 && D != 128) || !dtype_pair_supported(pr->q_dtype, pr->kv_dtype) ||
-        !group_supported(G))
-        return PKV_EUNSUPPORTED;
-    pkv::PagedGeometry geo;
-    if (!pkv::paged_geometry(pr->kv_dtype, D, G, H_kv, tu.max_heads_per_item, &geo)) return PKV_EUNSUPPORTED;
 
     // Path choice.
     const int64_t n_shared = P > 0 ? B : 0;
     const int64_t shared_pages = n_shared ? P / p : 0;
     int64_t prefix_tokens = shared_pages * p;
     const int64_t m_eff = (int64_t)B * G;
-    const bool capable = prefix_pair_supported(pr->q_dtype, pr->kv_dtype);
     int32_t path;
-    if (pr->force_path >= 0) {
-        path = pr->force_path;
-        if (path != PKV_PATH_PAGED) {
-            if (!capable) return PKV_EUNSUPPORTED;
-            if (prefix_tokens == 0) return PKV_EINVAL;
-        }
-    } else if (!capable || n_shared < 2 || shared_pages == 0) {
-        path = PKV_PATH_PAGED;
-    } else {
-        const int64_t rows = (int64_t)B * H_q;
-        const int64_t kv_bytes = 2LL * dtype_bytes(pr->kv_dtype);
-        const int64_t saved = (n_shared - 1) * prefix_tokens * H_kv * D * kv_bytes;
-        const int64_t overhead = 4 * rows * (D + 1) * 4 + tu.launch_bytes;
-        if (saved < (int64_t)tu.gate_ratio * overhead)
-            path = PKV_PATH_PAGED;
-        else if (m_eff >= tu.t_dense)
-            path = PKV_PATH_DENSE;
-        else
-            path = PKV_PATH_CASCADE;
-    }
+    st = choose_path(pr, tu, n_shared, prefix_tokens, (int64_t)B * H_q, m_eff, &path);
+    if (st != PKV_OK) return st;
     if (path == PKV_PATH_PAGED) prefix_tokens = 0;
     if (m_eff > INT32_MAX) return PKV_EUNSUPPORTED;
 
-    pkv_plan* pl = new (std::nothrow) pkv_plan;
+    pkv_plan* pl = new (std::nothrow) pkv_plan();
     if (!pl) return PKV_ENOMEM;
-    std::memset(pl, 0, sizeof(*pl));
-    pl->B = B;
-    pl->H_q = H_q;
-    pl->H_kv = H_kv;
-    pl->D = D;
-    pl->G = G;
-    pl->q_dtype = pr->q_dtype;
-    pl->kv_dtype = pr->kv_dtype;
-    pl->page_size = p;
+    fill_problem(pl, pr, tu, geo);
     pl->indptr0 = B > 0 ? pr->kv_indptr[0] : 0;
     pl->prefix_len = P;
     pl->path = path;
     pl->m_eff = (int32_t)m_eff;
     pl->shared_pages = (int32_t)shared_pages;
     pl->prefix_tokens = (int32_t)prefix_tokens;
-    pl->geo = geo;
-    pl->head_blocks = H_kv / geo.hb;
-    pl->concurrent_prefix = tu.concurrent_prefix;
     pl->fuse_cascade = tu.fuse_cascade && path == PKV_PATH_DENSE;
 
     // Prefix pass: M_eff query rows per KV head in tiles, the prefix cut into
@@ -269,12 +370,8 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->prefix_splits = 0;
     if (path != PKV_PATH_PAGED) {
         const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
-        const int64_t want = std::max<int64_t>(1, ceil_div(tu.prefix_target_workgroups, tiles));
-        int64_t ps = align_up(ceil_div(prefix_tokens, want), pkv::kPrefixTokenQuantum);
-        ps = std::max<int64_t>(ps, align_up(tu.min_prefix_split_tokens, pkv::kPrefixTokenQuantum));
-        ps = std::min<int64_t>(ps, pkv::kMaxPrefixSplitTokens);
-        pl->prefix_split_tokens = (int32_t)ps;
-        pl->prefix_splits = (int32_t)ceil_div(prefix_tokens, ps);
+        prefix_ranges(tu, prefix_tokens, tiles, tu.prefix_target_workgroups, &pl->prefix_split_tokens,
+                      &pl->prefix_splits);
     }
     // Workgroups of the prefix pass (a multiple of 8 for the XCD placement).
     const int64_t prefix_wgs =
@@ -284,14 +381,11 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     // Paged pass: the attended positions [prefix_tokens, L_b) of all
     // requests, request after request, form one flat sequence that is cut
     // into equal chunks, one workgroup per (chunk, head block).
+    const auto n_of = [&](int32_t b) {
+        return (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
+    };
     int64_t total = 0;
-    bool any_empty = false;
-    for (int32_t b = 0; b < B; ++b) {
-        const int64_t n = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
-        total += n;
-        any_empty |= n == 0;
-    }
-    pl->paged_tokens = total;
+    for (int32_t b = 0; b < B; ++b) total += n_of(b);
     // One launch runs both passes of a DENSE step when the prefix pass is
     // heavy enough to hide suffix streaming under it and its items take at
     // most half of the workgroup slots; the suffix chunks then fill the rest.
@@ -303,53 +397,235 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     }
     int64_t target = tu.target_workgroups;
     if (pl->fuse_cascade) target -= prefix_wgs;
-    const int64_t per_item = ceil_div(total * pl->head_blocks, target);
-    int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
-    chunk = align_up(chunk, pkv::kSplitQuantum);
-    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(geo.rs, geo.nhl, geo.tpi, G, D));
-    pl->split_tokens = (int32_t)chunk;
-    pl->num_chunks = ceil_div(total, chunk);
-    pl->num_work_items = pl->num_chunks * pl->head_blocks;
-    // Partial states per request: the chunks its range touches.
-    int64_t pos = 0, max_parts = 1;
-    bool spans = false;
-    for (int32_t b = 0; b < B; ++b) {
-        const int64_t n = (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
-        if (n > 0) {
-            const int64_t parts = (pos + n - 1) / chunk - pos / chunk + 1;
-            max_parts = std::max(max_parts, parts);
-            spans |= parts > 1;
-        }
-        pos += n;
-    }
-    pl->num_splits = (int32_t)max_parts;
+    bool spans = false, any_empty = false;
+    plan_chunks(pl, tu, total, target, n_of, &spans, &any_empty);
     // A combine kernel follows the paged pass for a cascade step, when a
     // request spans chunks, or to write the output of empty requests.
     pl->needs_reduce = path != PKV_PATH_PAGED || spans || any_empty;
 
-    // Workspace layout.
+    // Workspace layout.  A cascade step keeps both passes as partial states
+    // (prefix ranges, then suffix chunks) that one kernel combines; a request
+    // inside one chunk of a paged pass has its output written directly.
+    layout_workspace(pl, spans || path != PKV_PATH_PAGED, path != PKV_PATH_PAGED ? pl->prefix_splits : 0);
+    *out = pl;
+    return PKV_OK;
+}
+
+pkv_status pkv_plan_create_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const int32_t* page_indptr,
+                                   const int32_t* page_indices, const int32_t* seq_lens, pkv_plan** out) {
+    if (!pr || !out) return PKV_EINVAL;
+    pkv_tuning tu;
+    pkv::PagedGeometry geo;
+    pkv_status st = check_problem(pr, tuning, &tu);
+    if (st != PKV_OK) return st;
+    const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
+    const int32_t D = pr->head_dim, p = pr->page_size;
+    if (pr->shared_prefix_len != 0 || pr->force_path < -1 || pr->force_path > 2) return PKV_EINVAL;
+    if (B > 0 && (!page_indptr || !seq_lens)) return PKV_EINVAL;
+    st = check_support(pr, tu, &geo);
+    if (st != PKV_OK) return st;
+    const int32_t G = H_q / H_kv;
+    // The page table, checked as pkv_lower_page_table checks it.
+    int64_t total_tokens = 0;
+    if (B > 0 && page_indptr[0] != 0) return PKV_EINVAL;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t n = (int64_t)page_indptr[b + 1] - page_indptr[b];
+        const int64_t L = seq_lens[b];
+        if (n < 0 || L < 0) return PKV_EINVAL;
+        if (n != ceil_div(L, p)) return PKV_ERANGE;
+        if (n > 0 && !page_indices) return PKV_EINVAL;
+        for (int64_t j = 0; j < n; ++j) {
+            const int32_t pg = page_indices[page_indptr[b] + j];
+            if (pg < 0 || (int64_t)pg * p + (p - 1) > INT32_MAX) return PKV_ERANGE;
+        }
+        total_tokens += L;
+    }
+    if (total_tokens > INT32_MAX || (int64_t)B * G > INT32_MAX) return PKV_ERANGE;
+
+    // Groups: requests whose first whole page is the same physical page, in
+    // the order of their first member; shared pages = the leading run of
+    // pages that every member holds in full and all members agree on.
+    std::unordered_map<int32_t, int32_t> root_of;  // first page -> candidate
+    std::vector<std::vector<int32_t>> cand;
+    for (int32_t b = 0; b < B; ++b) {
+        if (seq_lens[b] / p == 0) continue;
+        const int32_t root = page_indices[page_indptr[b]];
+        auto it = root_of.find(root);
+        if (it == root_of.end()) {
+            root_of.emplace(root, (int32_t)cand.size());
+            cand.push_back({b});
+        } else {
+            cand[it->second].push_back(b);
+        }
+    }
+    struct Group {
+        std::vector<int32_t> members;
+        int32_t shared_pages, prefix_tokens, path, m_eff, rows_per_wg, row_tiles, split_tokens, splits;
+        int64_t items;
+    };
+    std::vector<Group> groups;
+    std::vector<int32_t> group_of(B, -1);
+    for (auto& mem : cand) {
+        if (mem.size() < 2) continue;
+        int32_t k = INT32_MAX;
+        for (int32_t b : mem) k = std::min(k, seq_lens[b] / p);
+        const int32_t* first = page_indices + page_indptr[mem[0]];
+        for (size_t i = 1; i < mem.size(); ++i) {
+            const int32_t* mine = page_indices + page_indptr[mem[i]];
+            int32_t j = 0;
+            while (j < k && mine[j] == first[j]) ++j;
+            k = j;
+        }
+        // each group is planned as the step it would be on its own
+        const int64_t n = (int64_t)mem.size();
+        int32_t path;
+        st = choose_path(pr, tu, n, (int64_t)k * p, n * H_q, n * G, &path);
+        if (st != PKV_OK) return st;
+        if (path == PKV_PATH_PAGED) continue;
+        Group g;
+        g.members = mem;
+        g.shared_pages = k;
+        g.prefix_tokens = k * p;
+        g.path = path;
+        g.m_eff = (int32_t)(n * G);
+        g.rows_per_wg = path == PKV_PATH_DENSE ? pkv::kDenseRowsPerWg : pkv::kTiledRowsPerWg;
+        g.row_tiles = (int32_t)ceil_div(g.m_eff, g.rows_per_wg);
+        for (int32_t b : mem) group_of[b] = (int32_t)groups.size();
+        groups.push_back(std::move(g));
+    }
+    const int32_t NG = (int32_t)groups.size();
+
+    // Prefix ranges: each group gets the share of the prefix pass's target
+    // workgroups that its flops (M_eff x P) are of the step's, and is cut
+    // as a single-prefix step with that target would be.
+    unsigned __int128 work = 0;
+    for (auto& g : groups) work += (unsigned __int128)g.m_eff * g.prefix_tokens;
+    int64_t dense_items = 0, tiled_items = 0;
+    int32_t max_splits = 0;
+    for (auto& g : groups) {
+        const int64_t share = (int64_t)((unsigned __int128)tu.prefix_target_workgroups * g.m_eff * g.prefix_tokens / work);
+        prefix_ranges(tu, g.prefix_tokens, (int64_t)H_kv * g.row_tiles, std::max<int64_t>(1, share), &g.split_tokens,
+                      &g.splits);
+        g.items = (int64_t)g.row_tiles * H_kv * g.splits;
+        (g.path == PKV_PATH_DENSE ? dense_items : tiled_items) += g.items;
+        max_splits = std::max(max_splits, g.splits);
+    }
+    if (dense_items > INT32_MAX || tiled_items > INT32_MAX) return PKV_EUNSUPPORTED;
+
+    pkv_plan* pl = new (std::nothrow) pkv_plan();
+    if (!pl) return PKV_ENOMEM;
+    fill_problem(pl, pr, tu, geo);
+    pl->grouped = 1;
+    pl->num_groups = NG;
+    pl->dense_items = (int32_t)dense_items;
+    pl->tiled_items = (int32_t)tiled_items;
+    pl->prefix_splits = max_splits;
+    pl->path = PKV_PATH_PAGED;
+    int64_t prefix_sum = 0, pages_sum = 0;
+    for (auto& g : groups) {
+        if (g.path == PKV_PATH_DENSE) pl->path = PKV_PATH_DENSE;
+        else if (pl->path == PKV_PATH_PAGED) pl->path = PKV_PATH_CASCADE;
+        pl->m_eff = std::max(pl->m_eff, g.m_eff);
+        prefix_sum += g.prefix_tokens;
+        pages_sum += g.shared_pages;
+    }
+    pl->prefix_tokens = (int32_t)prefix_sum;
+    pl->shared_pages = (int32_t)pages_sum;
+
+    // Metadata block (int32): the public arrays, then the kernels' tables.
+    int64_t suffix_total = 0, members_total = 0;
+    for (int32_t b = 0; b < B; ++b)
+        suffix_total += seq_lens[b] - (group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0);
+    for (auto& g : groups) members_total += (int64_t)g.members.size();
     int64_t off = 0;
-    const int64_t rows = (int64_t)B * H_q;
-    auto take = [&](int64_t bytes) {
+    const auto take = [&](int64_t n) {
         const int64_t at = off;
-        off = align_up(off + bytes, kAlign);
+        off += n;
         return at;
     };
-    pl->ws_paged_acc = pl->ws_paged_ml = -1;
-    pl->ws_prefix_acc = pl->ws_prefix_ml = -1;
-    // A cascade step keeps both passes as partial states (prefix ranges, then
-    // suffix chunks) that one kernel combines; a request inside one chunk of
-    // a paged pass has its output written directly.
-    if (spans || path != PKV_PATH_PAGED) {
-        pl->ws_paged_acc = take(rows * pl->num_splits * D * 4);
-        pl->ws_paged_ml = take(rows * pl->num_splits * 2 * 4);
+    pl->meta_suffix_indptr = take(B + 1);
+    pl->meta_suffix_indices = take(suffix_total);
+    pl->meta_group_indptr = take(NG + 1);
+    pl->meta_members = take(members_total);
+    pl->meta_prefix_indptr = take(NG + 1);
+    pl->meta_prefix_indices = take(prefix_sum);
+    pl->meta_request_group = take(B);
+    pl->meta_pre_count = take(B);
+    pl->meta_desc = take((int64_t)NG * pkv::kGroupDescInts);
+    try {
+        pl->meta.assign(off, 0);
+    } catch (const std::bad_alloc&) {
+        delete pl;
+        return PKV_ENOMEM;
     }
-    if (path != PKV_PATH_PAGED) {
-        pl->ws_prefix_acc = take(rows * pl->prefix_splits * D * 4);
-        pl->ws_prefix_ml = take(rows * pl->prefix_splits * 2 * 4);
+    int32_t* m = pl->meta.data();
+    const auto lower = [&](int32_t b, int32_t t0, int32_t t1, int32_t* dst) {
+        const int32_t* pages = page_indices + page_indptr[b];
+        for (int32_t t = t0; t < t1; ++t) *dst++ = pages[t / p] * p + t % p;
+    };
+    {
+        int32_t* ptr = m + pl->meta_suffix_indptr;
+        int32_t* idx = m + pl->meta_suffix_indices;
+        ptr[0] = 0;
+        for (int32_t b = 0; b < B; ++b) {
+            const int32_t skip = group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0;
+            lower(b, skip, seq_lens[b], idx + ptr[b]);
+            ptr[b + 1] = ptr[b] + (seq_lens[b] - skip);
+        }
+        int32_t* gptr = m + pl->meta_group_indptr;
+        int32_t* mem = m + pl->meta_members;
+        int32_t* pptr = m + pl->meta_prefix_indptr;
+        int32_t* pidx = m + pl->meta_prefix_indices;
+        gptr[0] = pptr[0] = 0;
+        for (int32_t i = 0; i < NG; ++i) {
+            const Group& g = groups[i];
+            std::copy(g.members.begin(), g.members.end(), mem + gptr[i]);
+            gptr[i + 1] = gptr[i] + (int32_t)g.members.size();
+            lower(g.members[0], 0, g.prefix_tokens, pidx + pptr[i]);
+            pptr[i + 1] = pptr[i] + g.prefix_tokens;
+        }
+        for (int32_t b = 0; b < B; ++b) {
+            m[pl->meta_request_group + b] = group_of[b];
+            m[pl->meta_pre_count + b] = group_of[b] >= 0 ? groups[group_of[b]].splits : 0;
+        }
+        // group table in launch order: DENSE groups' items, then CASCADE's
+        int32_t row = 0, end = 0;
+        for (int pass = 0; pass < 2; ++pass)
+            for (int32_t i = 0; i < NG; ++i) {
+                const Group& g = groups[i];
+                if ((g.path == PKV_PATH_DENSE) != (pass == 0)) continue;
+                int32_t* d = m + pl->meta_desc + (int64_t)row++ * pkv::kGroupDescInts;
+                end += (int32_t)g.items;
+                d[0] = end;
+                d[1] = pptr[i];
+                d[2] = g.prefix_tokens;
+                d[3] = g.split_tokens;
+                d[4] = g.splits;
+                d[5] = g.row_tiles;
+                d[6] = gptr[i];
+                d[7] = (int32_t)g.members.size();
+            }
     }
-    pl->workspace_bytes = off;
+
+    // Paged pass over every request's suffix (all of its tokens if it is in
+    // no group); with groups every request leaves partial states for the
+    // combine.
+    const int32_t* sptr = m + pl->meta_suffix_indptr;
+    const auto n_of = [&](int32_t b) { return (int64_t)sptr[b + 1] - sptr[b]; };
+    bool spans = false, any_empty = false;
+    plan_chunks(pl, tu, suffix_total, tu.target_workgroups, n_of, &spans, &any_empty);
+    pl->needs_reduce = NG > 0 || spans || any_empty;
+    layout_workspace(pl, NG > 0 || spans, max_splits);
     *out = pl;
+    return PKV_OK;
+}
+
+pkv_status pkv_plan_metadata(const pkv_plan* pl, int32_t* out, int64_t capacity) {
+    if (!pl || !pl->grouped) return PKV_EINVAL;
+    const int64_t n = (int64_t)pl->meta.size();
+    if (capacity < n) return PKV_ERANGE;
+    if (n > 0 && !out) return PKV_EINVAL;
+    std::copy(pl->meta.begin(), pl->meta.end(), out);
     return PKV_OK;
 }
 
@@ -365,6 +641,8 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     info->prefix_splits = pl->prefix_splits;
     info->num_work_items = pl->num_work_items;
     info->workspace_bytes = pl->workspace_bytes;
+    info->num_groups = pl->num_groups;
+    info->metadata_ints = (int64_t)pl->meta.size();
     return PKV_OK;
 }
 

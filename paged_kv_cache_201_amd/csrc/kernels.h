@@ -49,7 +49,9 @@ hipError_t launch_paged_split(const pkv_plan& plan, const PagedArgs& a, hipStrea
 // Combine partial states row by row, in order: first the pre_splits
 // partials of the shared-prefix pass (optional; [B][pre_splits][H_q]), then
 // the chunk partials of the paged pass (optional; [B][max_parts][H_q]), whose
-// count per request follows from kv_indptr and the chunking.  With
+// count per request follows from kv_indptr and the chunking.  With pre_count,
+// request b has pre_count[b] prefix partials (pre_splits is then the stride
+// only).  With
 // skip_whole, rows of non-empty requests that lie inside one chunk are left
 // alone (the paged kernel wrote them).  A row with nothing to combine gets
 // o = 0, lse = -inf.
@@ -58,6 +60,7 @@ struct SplitReduceArgs {
     const float* pre_acc;     // nullable
     const float* pre_ml;
     int32_t pre_splits;
+    const int32_t* pre_count; // [B], nullable
     const float* part_acc;    // nullable
     const float* part_ml;
     int32_t max_parts;
@@ -90,6 +93,18 @@ struct PrefixArgs {
     float* part_acc;          // num_splits > 1: [B][num_splits][H_q][D]
     float* part_ml;           // num_splits > 1: [B][num_splits][H_q][2]
     int32_t force_partial;    // write partials even with one split (cascade step)
+    // Several prefix groups (groups != nullptr): each item's group, prefix
+    // range and query rows come from the group table (kGroupDescInts ints
+    // per group, in launch order) instead of the fields above; prefix_indices
+    // is then the base that the table's offsets index, members lists the
+    // requests of each group, num_splits is the partial-state stride and
+    // force_partial must be set.  The launch runs items
+    // [item_base, item_base + num_items) of the table.
+    const int32_t* groups;
+    const int32_t* members;
+    int32_t num_groups;
+    int32_t item_base;
+    int32_t num_items;
 };
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream);
 

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <vector>
 
 #include "pkv.h"
 
@@ -35,6 +36,11 @@ constexpr int32_t kTiledRowsPerWg = 64;
 // Prefix tokens are split in multiples of this many, at most
 // kMaxPrefixSplitTokens per range (the kernel stages a range's indices in LDS).
 constexpr int32_t kPrefixTokenQuantum = 64;
+// Ints per row of the prefix-group table a grouped step hands the prefix
+// kernel: running end of the group's items, offset and length of its prefix
+// indices, range size, ranges, query-row tiles, offset and count of its
+// members.
+constexpr int32_t kGroupDescInts = 8;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // Paged-pass chunks hold a multiple of this many tokens, and at most
 // max_chunk_tokens(...): the kernel stages a chunk's slot indices in LDS next
@@ -75,4 +81,12 @@ struct pkv_plan {
     int64_t ws_paged_acc, ws_paged_ml;
     int64_t ws_prefix_acc, ws_prefix_ml;
     int64_t workspace_bytes;
+    // several prefix groups (pkv_plan_create_grouped)
+    int32_t grouped;
+    int32_t num_groups;               // groups that run a prefix pass
+    int32_t dense_items, tiled_items; // prefix work items per launch
+    // offsets (in ints) of the metadata block's arrays
+    int64_t meta_suffix_indptr, meta_suffix_indices, meta_group_indptr, meta_members;
+    int64_t meta_prefix_indptr, meta_prefix_indices, meta_request_group, meta_pre_count, meta_desc;
+    std::vector<int32_t> meta;        // the block itself, copied out by pkv_plan_metadata
 };

@@ -92,13 +92,37 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     // XCD-aware placement: workgroups are handed to the 8 XCDs round robin,
     // so give each XCD a contiguous run of logical items; row tiles that read
     // the same (KV head, prefix range) then share one L2.
-    const int N = a.row_tiles * a.H_kv * a.num_splits;
+    const int N = a.groups ? a.num_items : a.row_tiles * a.H_kv * a.num_splits;
     const int per_xcd = (N + 7) / 8;
-    const int item = (p % 8) * per_xcd + p / 8;
+    int item = (p % 8) * per_xcd + p / 8;
     if (item >= N) return;
-    const int tile = item % a.row_tiles;
-    const int g = (item / a.row_tiles) % a.H_kv;
-    const int split = item / (a.row_tiles * a.H_kv);
+    // This item's prefix group: the whole batch with one shared prefix, or
+    // one row of the group table (items of a group are consecutive; the
+    // table's first column is the running end of each group's items).
+    int row_tiles = a.row_tiles, prefix_len = a.prefix_len, split_tokens = a.split_tokens;
+    int M = a.B * a.G;
+    const int32_t* prefix = a.prefix_indices;
+    const int32_t* members = nullptr;
+    if (a.groups) {
+        item += a.item_base;
+        int lo = 0, hi = a.num_groups - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (a.groups[mid * kGroupDescInts] > item) hi = mid;
+            else lo = mid + 1;
+        }
+        const int32_t* gd = a.groups + lo * kGroupDescInts;
+        item -= lo ? a.groups[(lo - 1) * kGroupDescInts] : 0;
+        prefix += gd[1];
+        prefix_len = gd[2];
+        split_tokens = gd[3];
+        row_tiles = gd[5];
+        members = a.members + gd[6];
+        M = gd[7] * a.G;
+    }
+    const int tile = item % row_tiles;
+    const int g = (item / row_tiles) % a.H_kv;
+    const int split = item / (row_tiles * a.H_kv);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -106,19 +130,18 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     const int lr = lane & 31;
     const int G = a.G;
     const int H_q = a.H_kv * G;
-    const int M = a.B * G;
-    const int ts = split * a.split_tokens;
-    const int te = min(ts + a.split_tokens, a.prefix_len);
+    const int ts = split * split_tokens;
+    const int te = min(ts + split_tokens, prefix_len);
     const int n_tok = te - ts;
     const int ntiles = (n_tok + KT - 1) / KT;
 
     // the range's slot indices, padded with the last one to whole tiles
-    for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = a.prefix_indices[ts + min(i, n_tok - 1)];
+    for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = prefix[ts + min(i, n_tok - 1)];
 
-    // This lane's query row.
+    // This lane's query row: (request, query head) of the item's rows.
     const int r = tile * 32 * NW + wave * 32 + lr;
     const bool row_ok = r < M;
-    const int rb = row_ok ? r / G : 0;
+    const int rb = row_ok ? (members ? members[r / G] : r / G) : 0;
     const int rq = row_ok ? g * G + r % G : 0;
     const size_t qrow = (size_t)rb * H_q + rq;
     bf16x8_t qreg[NKS];

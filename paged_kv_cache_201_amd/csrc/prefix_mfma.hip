@@ -10,9 +10,9 @@ __global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_kernel
 }
 
 hipError_t launch_prefix_attn(const PrefixArgs& a, int rows_per_wg, hipStream_t stream) {
-    const int N = a.row_tiles * a.H_kv * a.num_splits;
+    const int N = a.groups ? a.num_items : a.row_tiles * a.H_kv * a.num_splits;
     if (N == 0) return hipSuccess;
-    if (a.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
+    if (!a.groups && a.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
     const int grid = prefix_blocks(N);
     // DENSE: 4 waves x 32 rows share each tile; CASCADE: 2 waves x 32 rows
     // (small query tiles, more workgroups per CU).  Both stay within 256

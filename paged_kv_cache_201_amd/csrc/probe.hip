@@ -45,6 +45,17 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4_t* __restr
     }
 }
 
+// The write-side companion: each workgroup fills one contiguous block with
+// 16-byte stores of a constant.  Its bytes are known exactly, which is what a
+// write-traffic counter is calibrated against.
+__global__ void __launch_bounds__(256) stream_write_kernel(u32x4_t* __restrict__ dst, size_t n16, uint32_t value) {
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t beg = (size_t)blockIdx.x * per;
+    const size_t end = beg + per < n16 ? beg + per : n16;
+    const u32x4_t v = {value, value, value, value};
+    for (size_t i = beg + threadIdx.x; i < end; i += 256) dst[i] = v;
+}
+
 }  // namespace pkv
 
 extern "C" pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_workgroups,
@@ -54,5 +65,14 @@ extern "C" pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint
         return PKV_EINVAL;
     pkv::stream_read_kernel<<<num_workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const pkv::u32x4_t*>(buf), (size_t)(bytes / 16), out);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+extern "C" pkv_status pkv_stream_write_probe(void* buf, int64_t bytes, uint32_t value, int32_t num_workgroups,
+                                             void* stream) {
+    if (!buf || bytes < 0 || num_workgroups < 1 || (bytes % 16) || (reinterpret_cast<uintptr_t>(buf) % 16))
+        return PKV_EINVAL;
+    pkv::stream_write_kernel<<<num_workgroups, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<pkv::u32x4_t*>(buf), (size_t)(bytes / 16), value);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
     if (row >= a.B * a.H_q) return;
     const int b = row / a.H_q;
     const int qh = row % a.H_q;
-    const int npre = a.pre_acc ? a.pre_splits : 0;
+    const int npre = a.pre_acc ? (a.pre_count ? a.pre_count[b] : a.pre_splits) : 0;
     int nparts = 0;
     if (a.kv_indptr) {
         // the chunks that request b's positions [ob, on) of the flat sequence touch

@@ -10,9 +10,9 @@ import math
 import numpy as np
 import torch
 
-from . import (Plan, make_pool, pkv_cascade_prefix_attn, pkv_decode_step, pkv_lower_page_table,
-               pkv_merge_states, pkv_paged_decode_attn, pkv_paged_decode_attn_pages, pkv_plan_create,
-               workspace_for)
+from . import (Plan, make_pool, pkv_cascade_prefix_attn, pkv_decode_step, pkv_decode_step_grouped,
+               pkv_lower_page_table, pkv_merge_states, pkv_paged_decode_attn, pkv_paged_decode_attn_pages,
+               pkv_plan_create, pkv_plan_create_grouped, pkv_plan_metadata, workspace_for)
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 _NAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}
@@ -38,8 +38,11 @@ class DeviceBatch:
         self.kv_indices_host = kv_indices_host
         self.kv_indptr = torch.from_numpy(self.kv_indptr_host).to(dev)
         self.kv_indices = torch.from_numpy(kv_indices_host if len(kv_indices_host) else np.zeros(1, np.int32)).to(dev)
-        self.page_indptr = torch.from_numpy(np.asarray(page_indptr, np.int32)).to(dev)
-        pages = np.asarray(page_indices, np.int32)
+        self.page_indptr_host = np.asarray(page_indptr, np.int32)
+        self.page_indices_host = np.asarray(page_indices, np.int32)
+        self.seq_lens_host = np.asarray(seq_lens, np.int32)
+        self.page_indptr = torch.from_numpy(self.page_indptr_host).to(dev)
+        pages = self.page_indices_host
         self.page_indices = torch.from_numpy(pages if len(pages) else np.zeros(1, np.int32)).to(dev)
         self.pool = make_pool(self.k_pool, self.v_pool, self.page_size, self.k_scale, self.v_scale)
         self.sm_scale = 1.0 / math.sqrt(self.d)
@@ -55,6 +58,25 @@ class DeviceBatch:
                                q_dtype=self.q_dtype, kv_dtype=self.kv_dtype, page_size=self.page_size,
                                kv_indptr=self.kv_indptr_host, shared_prefix_len=shared_prefix_len,
                                force_path=force_path, tuning=tuning)
+
+    def plan_grouped(self, force_path=-1, tuning=None) -> Plan:
+        """Plan with the prefix groups found in the page table."""
+        return pkv_plan_create_grouped(batch=self.B, num_q_heads=self.H_q, num_kv_heads=self.H_kv, head_dim=self.d,
+                                       q_dtype=self.q_dtype, kv_dtype=self.kv_dtype, page_size=self.page_size,
+                                       page_indptr=self.page_indptr_host, page_indices=self.page_indices_host,
+                                       seq_lens=self.seq_lens_host, force_path=force_path, tuning=tuning)
+
+    def metadata(self, plan):
+        """Device copy of a grouped plan's metadata block."""
+        m = pkv_plan_metadata(plan)
+        return torch.from_numpy(m if len(m) else np.zeros(1, np.int32)).to(self.device)
+
+    def step_grouped(self, plan, meta, o=None, lse=None, ws=None, sm_scale=None, stream=None):
+        o = self.new_out() if o is None else o
+        lse = self.new_lse() if lse is None else lse
+        pkv_decode_step_grouped(plan, self.q, self.pool, meta, self.sm_scale if sm_scale is None else sm_scale, o,
+                                lse, self.workspace(plan) if ws is None else ws, stream)
+        return o, lse
 
     def workspace(self, plan):
         return workspace_for(plan, self.device)

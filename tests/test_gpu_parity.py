@@ -478,3 +478,91 @@ def test_abi_rejects_bad_arguments_without_launching():
     with pytest.raises(ValueError):
         pkv.pkv_paged_decode_attn(plan, db.q.cpu(), db.pool, db.kv_indptr, db.kv_indices, 0.125,
                                   o=db.new_out(), workspace=db.workspace(plan))
+
+
+# ------------------------------------------------------------ prefix groups --
+
+def _grouped_imports():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    from workloads import make_grouped_batch
+    return pkv, DeviceBatch, ob, make_grouped_batch
+
+
+def _garbage_workspace(db, plan):
+    ws = db.workspace(plan)
+    if ws is not None:
+        ws.fill_(0xFF)  # NaN bytes: nothing may rely on a cleared workspace
+    return ws
+
+
+def _grouped_run(db, plan, ws=None):
+    meta = db.metadata(plan)
+    say(f"grouped step B={db.B} groups={plan.info['num_groups']} path={plan.info['path_name']}")
+    o, lse = db.step_grouped(plan, meta, ws=_garbage_workspace(db, plan) if ws is None else ws)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("force", [-1, 0, 1, 2])
+def test_grouped_step_small_vs_oracle(force):
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    # three prefixes (one with a tail that does not fill a page), loners, and
+    # requests with no tokens of their own or none at all
+    b = make_grouped_batch(seed=501, B=24, H_q=32, H_kv=8, d=128, groups=[(8, 1000), (5, 300), (2, 64)],
+                           own_len=(0, 200), page_size=16)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan_grouped(force_path=force, tuning=dict(gate_ratio=0))
+    assert plan.info["num_groups"] == (0 if force == 0 else 3)
+    o, lse = _grouped_run(db, plan)
+    check_close("bf16", o, lse, o_ref, lse_ref, f"grouped force={force}")
+    o2, lse2 = _grouped_run(db, plan)
+    assert same_bits(o, o2) and same_bits(lse, lse2), "grouped step not repeatable"
+
+
+def test_grouped_step_dense_and_tiled_groups_in_one_step():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    b = make_grouped_batch(seed=502, B=40, H_q=16, H_kv=4, d=128, groups=[(20, 700), (6, 129), (3, 2048)],
+                           own_len=(1, 300), page_size=8)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    # M_eff = 80, 24, 12: the first DENSE, the other two tiled
+    plan = db.plan_grouped(tuning=dict(gate_ratio=0, t_dense=64, prefix_target_workgroups=97))
+    assert plan.info["num_groups"] == 3 and plan.info["path_name"] == "DENSE"
+    o, lse = _grouped_run(db, plan)
+    check_close("bf16", o, lse, o_ref, lse_ref, "grouped dense+tiled")
+
+
+def test_grouped_step_without_groups_is_the_paged_step_bitwise():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    for kv in ("bf16", "fp8"):
+        # fp8 K/V has no prefix kernel: its groups are dissolved
+        b = make_grouped_batch(seed=503, B=12, H_q=32, H_kv=8, d=128, groups=[(4, 512)] if kv == "fp8" else [],
+                               own_len=(0, 900), page_size=16, kv_dtype=kv)
+        o_ref, lse_ref = ob.batch_reference(b)
+        db = DeviceBatch.from_batch(b)
+        plan = db.plan_grouped()
+        assert plan.info["num_groups"] == 0 and plan.info["path_name"] == "PAGED"
+        o, lse = _grouped_run(db, plan)
+        check_close(kv, o, lse, o_ref, lse_ref, f"grouped no-groups {kv}")
+        ref_plan = db.plan(force_path=0)
+        say(f"paged reference {kv}")
+        o2, lse2 = db.step(ref_plan)
+        torch.cuda.synchronize()
+        assert same_bits(o, o2) and same_bits(lse, lse2), "grouped PAGED step differs from the paged step"
+
+
+def test_grouped_step_full_size_sampled():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    # Llama-3.1-8B layer shape: 256 requests, four prompts of 4096 .. 512
+    # tokens (48 requests each) and 64 requests on no prompt
+    b = make_grouped_batch(seed=504, B=256, H_q=32, H_kv=8, d=128,
+                           groups=[(48, 4096), (48, 2048), (48, 1024), (48, 512)], own_len=(64, 512), page_size=16)
+    reqs = [int(np.flatnonzero(b.group_of == g)[i]) for g in range(4) for i in (0, -1)]
+    reqs += [int(x) for x in np.flatnonzero(b.group_of < 0)[:2]]
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan_grouped()
+    assert plan.info["num_groups"] == 4 and plan.info["path_name"] == "DENSE"
+    o, lse = _grouped_run(db, plan)
+    check_close("bf16", o[reqs], lse[reqs], o_ref, lse_ref, "grouped full")

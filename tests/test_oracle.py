@@ -438,25 +438,9 @@ def test_mutant_lowering_caught(mutant):
 from oracle import groups as og  # noqa: E402
 
 
-def tables_from_blocks(requests, p, seed=0):
-    """Page tables for requests given as lists of per-block contents: a
-    physical page is shared exactly when the content up to and including its
-    block is the same (exact, block-aligned prefix matching).  Page numbers
-    are scrambled by a seeded permutation."""
-    ids = {}
-    tables = []
-    for blocks in requests:
-        tables.append([ids.setdefault(tuple(blocks[:j + 1]), len(ids)) for j in range(len(blocks))])
-    perm = np.random.default_rng(seed).permutation(max(1, len(ids)))
-    page_indptr = np.zeros(len(requests) + 1, np.int64)
-    for b, t in enumerate(tables):
-        page_indptr[b + 1] = page_indptr[b] + len(t)
-    page_indices = np.array([perm[x] for t in tables for x in t], np.int64)
-    return page_indptr, page_indices
-
-
-def _token_blocks(tokens, p):
-    return [tuple(tokens[j:j + p]) for j in range(0, len(tokens), p)]
+from workloads.groups import random_group_tables as _random_group_tables  # noqa: E402
+from workloads.groups import tables_from_blocks  # noqa: E402
+from workloads.groups import token_blocks as _token_blocks  # noqa: E402
 
 
 def golden_group_case(c, p):
@@ -510,29 +494,6 @@ def _groups_bruteforce(p, ptr, pages, lens):
             k += 1
         out.append({"members": mem, "shared_pages": k})
     return out
-
-
-def _random_group_tables(rng, p):
-    """Requests drawn from a few system prompts of random lengths (in tokens),
-    some continued by one of two shared follow-ups (nested sharing), each
-    followed by its own tokens; some requests have no prompt."""
-    n_prompts = int(rng.integers(0, 4))
-    prompts = [int(rng.integers(0, 5 * p)) for _ in range(n_prompts)]
-    follow = [[int(rng.integers(1, 3 * p)) for _ in range(2)] for _ in range(n_prompts)]
-    B = int(rng.integers(0, 9))
-    reqs, lens = [], []
-    for b in range(B):
-        k = int(rng.integers(-1, n_prompts)) if n_prompts else -1
-        toks = []
-        if k >= 0:
-            toks = [f"s{k}"] * prompts[k]
-            j = int(rng.integers(-1, 2))
-            if j >= 0:
-                toks += [f"f{k}.{j}"] * follow[k][j]
-        toks += [f"o{b}"] * int(rng.integers(0, 3 * p))
-        reqs.append(_token_blocks(toks, p))
-        lens.append(len(toks))
-    return reqs, lens
 
 
 def test_prefix_groups_match_bruteforce():

@@ -11,3 +11,10 @@ from .synth import (  # noqa: F401
     make_decode_batch,
     relayout,
 )
+from .groups import (  # noqa: F401
+    GroupedBatch,
+    make_grouped_batch,
+    random_group_tables,
+    tables_from_blocks,
+    token_blocks,
+)
