@@ -1,6 +1,6 @@
 """Decode-attention benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c1,c2,...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c1,c2,...,groups4]
 
 A step is one whole decode-attention step of one layer as the planner chose
 it (pkv_decode_step: the paged pass, or prefix pass + suffix pass + merge),
@@ -11,8 +11,8 @@ the same inputs are reused every step (warm caches, no admission ramp).
 The headline line is the Llama-3.1-8B-shaped layer (B=32, 32 query / 8 KV
 heads, head_dim 128, 4096 tokens each, bf16, token-flat indices at page size
 1): ``value`` is its algorithmic HBM throughput in GB/s.  The other workloads
-(tiny fp32, shared-prefix cascade, short prefix, long-context fp8) are
-reported under ``extra``.  Prints one JSON line on stdout.
+(tiny fp32, shared-prefix cascade, short prefix, long-context fp8, several
+prompts in one step) are reported under ``extra``.  Prints one JSON line on stdout.
 """
 import argparse
 import itertools
@@ -137,6 +137,148 @@ def bench_prefix_config(name, steps, warmup, legs=None):
     return out
 
 
+def grouped_algorithmic_bytes(batch, plan_meta, rows_grouped):
+    """Bytes a grouped step must move: each kept group's prefix once, every
+    request's own tokens, the queries twice (both passes), the partial states
+    of the grouped rows (written and read as fp32 (o, m, l)), the output."""
+    bkv = BYTES[batch.kv_dtype] * 2
+    bq = BYTES[batch.q_dtype]
+    Hkv, d, rows = batch.H_kv, batch.d, batch.B * batch.H_q
+    n_pre = int(plan_meta["prefix_indptr"][-1])
+    n_suf = int(plan_meta["suffix_indptr"][-1])
+    return ((n_pre + n_suf) * (Hkv * d * bkv + 4) + 2 * rows * d * bq + 4 * rows_grouped * (d + 1) * 4
+            + rows * d * bq)
+
+
+def bench_groups_config(name, steps, warmup):
+    """Several prompts in one step: PAGED over the shared pages, every group
+    forced to the tiled cascade, and the planner's choice (DENSE here)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_201_amd as pkv
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_group_config
+    b = make_group_config(name, device="cuda")
+    db = DeviceBatch.from_batch(b)
+    o, lse = db.new_out(), db.new_lse()
+    out = dict(workload=name, B=b.B, groups=[[int(n), int(P)] for n, P in
+                                             zip(np.bincount(b.group_of[b.group_of >= 0]), b.prefix_lens)])
+    plan = db.plan(force_path=0)
+    ws = db.workspace(plan)
+    ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
+    nb = algorithmic_bytes(b, "PAGED")
+    out["paged_shared"] = dict(path="PAGED", us_per_step=ms * 1e3, algorithmic_bytes=nb, gbs=nb / (ms * 1e-3) / 1e9)
+    del ws
+    for label, force in (("grouped_cascade", 1), ("grouped_planned", -1)):
+        plan = db.plan_grouped(force_path=force)
+        meta = db.metadata(plan)
+        ws = db.workspace(plan)
+        ms = time_steps(lambda: db.step_grouped(plan, meta, o, lse, ws), steps, warmup)
+        m = pkv.split_metadata(pkv.pkv_plan_metadata(plan), b.B, plan.info["num_groups"])
+        rows_grouped = int((m["request_group"] >= 0).sum()) * b.H_q
+        nb = grouped_algorithmic_bytes(b, m, rows_grouped)
+        out[label] = dict(path=plan.info["path_name"], num_groups=plan.info["num_groups"], us_per_step=ms * 1e3,
+                          algorithmic_bytes=nb, gbs=nb / (ms * 1e-3) / 1e9)
+        del ws, meta
+    out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["grouped_planned"]["us_per_step"]
+    del db, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def page_control(steps, warmup):
+    """Page size as a control ("The 25% Page-Size Slowdown That Wasn't",
+    section "A backend where pages really do reach the kernel"): the paged
+    pass reading the page table (page-aware) and reading token-flat indices,
+    at page sizes 16, 64 and 128, on distinct K/V (16 requests of 8192 own
+    tokens: the DRAM-bound regime) and on a shared prefix (32 requests on
+    the same 8192 tokens in shared physical pages: the reuse regime).  Each
+    leg issues exactly warmup + steps paged-pass dispatches, in the order
+    listed, so that counter runs can attribute dispatches to legs."""
+    import torch
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_decode_batch, relayout
+    legs = []
+    cases = (("distinct", dict(seed=1007, B=16, own_len=(8192, 8192), prefix_len=0)),
+             ("shared", dict(seed=1008, B=32, own_len=(0, 0), prefix_len=8192)))
+    for case, kw in cases:
+        base = make_decode_batch(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=16,
+                                 layout="shared", device="cuda", **kw)
+        for p in (16, 64, 128):
+            b = base if p == 16 else relayout(base, page_size=p, seed=2007, layout="shared", device="cuda")
+            db = DeviceBatch.from_batch(b)
+            plan = db.plan(force_path=0)
+            o, lse, ws = db.new_out(), db.new_lse(), db.workspace(plan)
+            for mode in ("page_table", "token_flat"):
+                fn = ((lambda: db.paged_pages(plan, o=o, lse=lse, ws=ws)) if mode == "page_table"
+                      else (lambda: db.paged(plan, o=o, lse=lse, ws=ws)))
+                ms = time_steps(fn, steps, warmup)
+                nb = algorithmic_bytes(b, "PAGED")
+                legs.append(dict(case=case, page_size=p, mode=mode, us_per_step=ms * 1e3,
+                                 requested_gbs=nb / (ms * 1e-3) / 1e9, dispatches=steps + warmup,
+                                 page_entries=int(b.page_indptr[-1]), tokens=int(b.seq_lens.sum())))
+            del db, o, lse, ws
+            if b is not base:
+                del b
+            torch.cuda.empty_cache()
+        del base
+        torch.cuda.empty_cache()
+    return legs
+
+
+def write_page_control(run_json, vmem_dir, tcc_dir, commands):
+    """profiles/paged_split_kernel.page_size_control.md from one timing run
+    and two counter runs of --page-control."""
+    import statistics
+    rec = json.loads(open(run_json).read().strip().splitlines()[-1])
+    legs = rec["page_control"]
+
+    def per_leg(d, counter):
+        # the counter run's own legs (its stdout, saved next to its output
+        # folder) say how many dispatches each leg issued
+        import csv
+        import glob
+        run_legs = json.loads(open(d.rstrip("/") + ".json").read().strip().splitlines()[-1])["page_control"]
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter and "paged_split_kernel" in r["Kernel_Name"]:
+                    rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        rows.sort()
+        vals, at = [], 0
+        for leg in run_legs:
+            chunk = [v for _, v in rows[at:at + leg["dispatches"]]]
+            at += leg["dispatches"]
+            vals.append(statistics.median(chunk) if chunk else None)
+        return vals
+
+    vmem = per_leg(vmem_dir, "SQ_INSTS_VMEM_RD")
+    hit = per_leg(tcc_dir, "TCC_HIT_sum")
+    miss = per_leg(tcc_dir, "TCC_MISS_sum")
+    lines = ["# Page size as a control: paged_split_kernel, page-table reads vs token-flat indices", "",
+             "Commands:", "", "```"] + [commands[k] for k in ("time", "vmem", "tcc", "summary")] + ["```", "",
+             "Distinct: 16 requests x 8192 own tokens (537 MB of K/V per step, DRAM-bound). Shared: 32 requests "
+             "on one 8192-token prefix in shared physical pages (the same 16.8 MB re-read by every request). "
+             "Same plan at every page size (work is cut by logical position). `vmem_rd` = vector-memory read "
+             "instructions per dispatch (`SQ_INSTS_VMEM_RD`), `L2 hit` = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+             "| case | page size | reads | page entries | us/step | requested GB/s | vmem_rd per dispatch | L2 hit |",
+             "|---|---|---|---|---|---|---|---|"]
+    for leg, v, h, m in zip(legs, vmem, hit, miss):
+        rate = f"{100 * h / (h + m):.1f} %" if h is not None and m is not None and h + m > 0 else "-"
+        lines.append(f"| {leg['case']} | {leg['page_size']} | {leg['mode']} | "
+                     f"{leg['page_entries'] if leg['mode'] == 'page_table' else leg['tokens']} | "
+                     f"{leg['us_per_step']:.1f} | {leg['requested_gbs']:.0f} | "
+                     f"{v:.0f} | {rate} |" if v is not None else
+                     f"| {leg['case']} | {leg['page_size']} | {leg['mode']} | - | {leg['us_per_step']:.1f} | "
+                     f"{leg['requested_gbs']:.0f} | - | {rate} |")
+    lines.append("")
+    lines.append(f"Source sha256 of the profiled library: `{rec.get('source_sha256')}`")
+    path = os.path.join(ROOT, "profiles", "paged_split_kernel.page_size_control.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def read_ceiling(steps=20, warmup=5, gib=4):
     """Streaming-read bandwidth of this GPU (GB/s), through the library's read
     probe over a buffer far larger than the 256 MB Infinity Cache."""
@@ -144,7 +286,9 @@ def read_ceiling(steps=20, warmup=5, gib=4):
     import paged_kv_cache_201_amd as pkv
     n = gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
+    # filled by the library's write probe: a write of known size for the
+    # write-traffic counter's calibration
+    pkv.pkv_stream_write_probe(buf, 0x01010101, 1024)
     best = None
     for wgs in (512, 1024, 2048):
         out = torch.empty(wgs, dtype=torch.int32, device="cuda")
@@ -240,10 +384,10 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
     med = lambda v: sorted(v)[len(v) // 2]
-    # calibration: the read probe reads its 4 GiB buffer once; torch's fill
-    # writes it once
+    # calibration: the read probe reads its 4 GiB buffer once; the write
+    # probe writes it once
     probe = [v for (k, _), vs in fetch.items() if "stream_read_kernel" in k for v in vs]
-    fills = [max(vs) for (k, _), vs in write.items() if "FillFunctor" in k]
+    fills = [max(vs) for (k, _), vs in write.items() if "stream_write_kernel" in k]
     nbytes = 4 << 30
     fetch_scale = nbytes / (med(probe) * 1024)
     write_scale = nbytes / (max(fills) * 1024)
@@ -262,8 +406,8 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
     rec = dict(workload="Llama-3.1-8B decode layer, B=32, 4096 tokens, bf16, page size 1 and 128 (same plan)",
                commands=commands, source_sha256=sha, fetch_scale=fetch_scale,
                write_scale=write_scale,
-               calibration="FETCH_SIZE of the streaming-read probe over 4 GiB; WRITE_SIZE of torch's fill of "
-                           "the same 4 GiB buffer",
+               calibration="FETCH_SIZE of the streaming-read probe over 4 GiB; WRITE_SIZE of the streaming-write "
+                           "probe filling the same 4 GiB buffer",
                kernels=kernels, traffic_bytes_per_step=sum(v["bytes"] for v in kernels.values()))
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -385,7 +529,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--configs", default="c1,c2,c3,c4,c5")
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,groups4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", metavar="CONFIG:LEG[,LEG]",
                     help="time only these legs of one shared-prefix workload (e.g. c3:paged_unique) and exit; "
@@ -394,6 +538,11 @@ def main():
                     help="write the prefix-traffic summary from two FETCH_SIZE runs (see --only) and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CONFIGS"),
                     help="write profiles/kernels.<configs>.trace.md from a kernel-trace run of --configs CONFIGS")
+    ap.add_argument("--page-control", action="store_true",
+                    help="time the page-size control (page-table vs token-flat reads, distinct vs shared K/V) "
+                         "and exit")
+    ap.add_argument("--summarize-page-control", nargs=3, metavar=("RUN_JSON", "VMEM_DIR", "TCC_DIR"),
+                    help="write the page-size control summary from a --page-control run and two counter runs")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
     args = ap.parse_args()
@@ -427,6 +576,18 @@ def main():
         rec = write_profile_summaries(t, f, w, cmds)
         print(json.dumps(rec["kernels"], indent=1))
         return
+    if args.summarize_page_control:
+        r, v, t = args.summarize_page_control
+        prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && "
+        run = "-- python bench.py --page-control --steps 5 --warmup 2"
+        cmds = dict(time=f"python bench.py --page-control > {r}",
+                    vmem=f"{prof}timeout -s KILL 120 rocprofv3 --pmc SQ_INSTS_VMEM_RD --output-format csv -d {v} "
+                         f"-o run {run}",
+                    tcc=f"{prof}timeout -s KILL 120 rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
+                        f"-d {t} -o run {run}",
+                    summary=f"python bench.py --summarize-page-control {r} {v} {t}")
+        print(write_page_control(r, v, t, cmds))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(the decode step shards by request or KV head with no exchange).", file=sys.stderr)
@@ -434,6 +595,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.page_control:
+        legs = page_control(args.steps, args.warmup)
+        print(json.dumps(dict(page_control=legs, steps=args.steps, warmup=args.warmup,
+                              source_sha256=kernel_source_hash())), flush=True)
+        return
     if args.only:
         name, legs = args.only.split(":")
         read_ceiling(steps=1, warmup=0)  # a known 4 GiB read, to scale FETCH_SIZE by
@@ -482,6 +648,10 @@ def main():
         elif name in ("c3", "c4"):
             log(f"bench {name}")
             extra[name] = bench_prefix_config(name, args.steps, args.warmup)
+            log(json.dumps(extra[name]))
+        elif name == "groups4":
+            log(f"bench {name}")
+            extra[name] = bench_groups_config(name, args.steps, args.warmup)
             log(json.dumps(extra[name]))
 
     extra["host_us"] = host_timing()

@@ -46,6 +46,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every function below is exported from libpkv.so; the library's internal
+ * symbols are not. */
+#if defined(PKV_BUILDING_LIBRARY)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -147,13 +155,13 @@ typedef struct pkv_plan_info {
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
-const char* pkv_status_string(int32_t status);
+PKV_API const char* pkv_status_string(int32_t status);
 
 /* Library version string (static storage). */
-const char* pkv_version(void);
+PKV_API const char* pkv_version(void);
 
 /* Fill *out with the gfx950 planner constants. */
-void pkv_tuning_defaults(pkv_tuning* out);
+PKV_API void pkv_tuning_defaults(pkv_tuning* out);
 
 /*
  * Page table -> token-flat indices (host).  [P1] "Four meanings of page size":
@@ -171,7 +179,7 @@ void pkv_tuning_defaults(pkv_tuning* out);
  * page index is negative or its slots overflow int32, or the output capacity
  * is too small).  Nothing is written on error.
  */
-pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size,
+PKV_API pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size,
                                 const int32_t* page_indptr, const int32_t* page_indices,
                                 const int32_t* seq_lens,
                                 int32_t* kv_indptr_out, int32_t* kv_indices_out,
@@ -184,7 +192,7 @@ pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size,
  * Errors: EINVAL (null pointer, B < 0, bad indptr), ERANGE (an index outside
  * the pool).
  */
-pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indices,
+PKV_API pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indices,
                                 int32_t batch, int64_t num_slots);
 
 /*
@@ -203,7 +211,7 @@ pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indi
  * shared page), EUNSUPPORTED (head_dim, dtype pair, or group size not built;
  * forced prefix path for a dtype pair without a prefix kernel), ENOMEM.
  */
-pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning* tuning,
+PKV_API pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning* tuning,
                            pkv_plan** out);
 
 /*
@@ -235,7 +243,7 @@ pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning* tuning,
  * Errors: as pkv_plan_create and pkv_lower_page_table; EINVAL also for a
  * non-zero shared_prefix_len.
  */
-pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv_tuning* tuning,
+PKV_API pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv_tuning* tuning,
                                    const int32_t* page_indptr, const int32_t* page_indices,
                                    const int32_t* seq_lens, pkv_plan** out);
 
@@ -255,13 +263,13 @@ pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv_tuning*
  * Errors: EINVAL (null plan, plan not from pkv_plan_create_grouped, null out
  * with a non-empty block), ERANGE (capacity too small).
  */
-pkv_status pkv_plan_metadata(const pkv_plan* plan, int32_t* out, int64_t capacity);
+PKV_API pkv_status pkv_plan_metadata(const pkv_plan* plan, int32_t* out, int64_t capacity);
 
 /* Copy a plan's decisions and sizes into *info.  EINVAL on null pointers. */
-pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);
+PKV_API pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);
 
 /* Free a plan handle (NULL is allowed). */
-void pkv_plan_destroy(pkv_plan* plan);
+PKV_API void pkv_plan_destroy(pkv_plan* plan);
 
 /*
  * Paged decode attention ([P1] "Four meanings of page size"; [P3]
@@ -285,7 +293,7 @@ void pkv_plan_destroy(pkv_plan* plan);
  * Errors: EINVAL (null plan/q/indices, no output, pool not matching the plan,
  * missing fp8 scales), EWORKSPACE, EHIP.
  */
-pkv_status pkv_paged_decode_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+PKV_API pkv_status pkv_paged_decode_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                                  const int32_t* kv_indptr, const int32_t* kv_indices,
                                  float sm_scale, void* o, float* o_f32, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
@@ -307,7 +315,7 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* plan, const void* q, const pkv_
  * Errors: EINVAL (null plan/q/indptr/page table, no output, pool not matching
  * the plan, missing fp8 scales), EWORKSPACE, EHIP.
  */
-pkv_status pkv_paged_decode_attn_pages(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+PKV_API pkv_status pkv_paged_decode_attn_pages(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                                        const int32_t* kv_indptr, const int32_t* page_indptr,
                                        const int32_t* page_indices, float sm_scale, void* o,
                                        float* o_f32, float* lse, void* workspace,
@@ -328,7 +336,7 @@ pkv_status pkv_paged_decode_attn_pages(const pkv_plan* plan, const void* q, cons
  * Errors: EINVAL (PAGED plan, null pointers, prefix_len mismatch, pool not
  * matching), EWORKSPACE, EHIP.
  */
-pkv_status pkv_cascade_prefix_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+PKV_API pkv_status pkv_cascade_prefix_attn(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                                    const int32_t* prefix_indices, int32_t prefix_len,
                                    float sm_scale, float* o_p, float* lse_p,
                                    void* workspace, size_t workspace_bytes, void* stream);
@@ -345,7 +353,7 @@ pkv_status pkv_cascade_prefix_attn(const pkv_plan* plan, const void* q, const pk
  * Errors: EINVAL (null pointers, rows < 0, d not in {64,128}),
  * EUNSUPPORTED (out_dtype), EHIP.
  */
-pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
+PKV_API pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
                             const float* o_a, const float* lse_a,
                             const float* o_b, const float* lse_b,
                             void* o_out, int32_t out_dtype, float* lse_out, void* stream);
@@ -365,7 +373,7 @@ pkv_status pkv_merge_states(int32_t rows, int32_t head_dim,
  * `stream` as a whole and can be captured into a graph.  Arguments as in
  * pkv_paged_decode_attn; o is required, lse is nullable.
  */
-pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+PKV_API pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            float sm_scale, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -382,7 +390,7 @@ pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pkv_pool* 
  * Errors: EINVAL (null plan/q/metadata/o, plan not grouped, pool not
  * matching), EWORKSPACE, EHIP.
  */
-pkv_status pkv_decode_step_grouped(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+PKV_API pkv_status pkv_decode_step_grouped(const pkv_plan* plan, const void* q, const pkv_pool* pool,
                                    const int32_t* metadata, float sm_scale, void* o, float* lse,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
@@ -398,7 +406,7 @@ pkv_status pkv_decode_step_grouped(const pkv_plan* plan, const void* q, const pk
  * Errors: EINVAL (null pointers, bytes not a multiple of 16, misaligned buf,
  * num_workgroups < 1), EHIP.
  */
-pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_workgroups,
+PKV_API pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t num_workgroups,
                                  void* stream);
 
 /*
@@ -410,7 +418,7 @@ pkv_status pkv_stream_read_probe(const void* buf, int64_t bytes, uint32_t* out, 
  * Errors: EINVAL (null buf, bytes not a multiple of 16, misaligned buf,
  * num_workgroups < 1), EHIP.
  */
-pkv_status pkv_stream_write_probe(void* buf, int64_t bytes, uint32_t value, int32_t num_workgroups, void* stream);
+PKV_API pkv_status pkv_stream_write_probe(void* buf, int64_t bytes, uint32_t value, int32_t num_workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,9 @@ HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "cascade_fused.hip", 
 HOST_SOURCES = ["host.cpp"]
 
 ARCH = "gfx950"
-COMMON = ["-std=c++17", "-fPIC", "-O3", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+# Only the C ABI of include/pkv.h is exported (PKV_API); internal C++ symbols stay hidden.
+COMMON = ["-std=c++17", "-fPIC", "-O3", "-fvisibility=hidden", "-DPKV_BUILDING_LIBRARY", f"-I{INCLUDE}",
+          f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Packed fp32 VALU instructions stay off on this target.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-result"]

@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -411,8 +412,24 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     return PKV_OK;
 }
 
+namespace {
+pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const int32_t* page_indptr,
+                        const int32_t* page_indices, const int32_t* seq_lens, pkv_plan** out);
+}  // namespace
+
 pkv_status pkv_plan_create_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const int32_t* page_indptr,
                                    const int32_t* page_indices, const int32_t* seq_lens, pkv_plan** out) {
+    // host containers may throw; nothing may cross the C boundary
+    try {
+        return plan_grouped(pr, tuning, page_indptr, page_indices, seq_lens, out);
+    } catch (const std::bad_alloc&) {
+        return PKV_ENOMEM;
+    }
+}
+
+namespace {
+pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const int32_t* page_indptr,
+                        const int32_t* page_indices, const int32_t* seq_lens, pkv_plan** out) {
     if (!pr || !out) return PKV_EINVAL;
     pkv_tuning tu;
     pkv::PagedGeometry geo;
@@ -552,12 +569,8 @@ pkv_status pkv_plan_create_grouped(const pkv_problem* pr, const pkv_tuning* tuni
     pl->meta_request_group = take(B);
     pl->meta_pre_count = take(B);
     pl->meta_desc = take((int64_t)NG * pkv::kGroupDescInts);
-    try {
-        pl->meta.assign(off, 0);
-    } catch (const std::bad_alloc&) {
-        delete pl;
-        return PKV_ENOMEM;
-    }
+    std::unique_ptr<pkv_plan> owner(pl);
+    pl->meta.assign(off, 0);
     int32_t* m = pl->meta.data();
     const auto lower = [&](int32_t b, int32_t t0, int32_t t1, int32_t* dst) {
         const int32_t* pages = page_indices + page_indptr[b];
@@ -616,9 +629,10 @@ pkv_status pkv_plan_create_grouped(const pkv_problem* pr, const pkv_tuning* tuni
     plan_chunks(pl, tu, suffix_total, tu.target_workgroups, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;
     layout_workspace(pl, NG > 0 || spans, max_splits);
-    *out = pl;
+    *out = owner.release();
     return PKV_OK;
 }
+}  // namespace
 
 pkv_status pkv_plan_metadata(const pkv_plan* pl, int32_t* out, int64_t capacity) {
     if (!pl || !pl->grouped) return PKV_EINVAL;

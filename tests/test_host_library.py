@@ -32,6 +32,13 @@ def test_library_exports_every_declared_function():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(pkv.EXPORTS) == declared
+    # and nothing else: the internal C++ symbols are hidden
+    import shutil
+    import subprocess
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True, text=True).stdout
+        text_syms = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+        assert text_syms == declared, text_syms
 
 
 def test_status_strings_and_version():

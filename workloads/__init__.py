@@ -12,7 +12,9 @@ from .synth import (  # noqa: F401
     relayout,
 )
 from .groups import (  # noqa: F401
+    GROUP_CONFIGS,
     GroupedBatch,
+    make_group_config,
     make_grouped_batch,
     random_group_tables,
     tables_from_blocks,

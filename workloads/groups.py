@@ -234,3 +234,21 @@ def make_grouped_batch(*, seed, B, H_q, H_kv, d, groups, own_len, q_dtype="bf16"
     out.page_indices = page_indices.astype(np.int32)
     out.k_pool, out.v_pool = pools
     return out
+
+
+# Several prompts live in one step (the pages' "two system prompts, two
+# trees" case, at the Llama-3.1-8B layer shape): 256 requests, four prompts of
+# 4096, 2048, 1024 and 512 tokens with 48 requests each, 64 requests on no
+# prompt, own tokens U{64..512}, bf16, page size 16.
+GROUP_CONFIGS = {
+    "groups4": dict(B=256, H_q=32, H_kv=8, d=128, groups=[(48, 4096), (48, 2048), (48, 1024), (48, 512)],
+                    own_len=(64, 512), q_dtype="bf16", kv_dtype="bf16", page_size=16),
+}
+GROUP_CONFIG_SEED = {"groups4": 1006}
+
+
+def make_group_config(name: str, **overrides) -> GroupedBatch:
+    kw = dict(GROUP_CONFIGS[name])
+    kw.update(overrides)
+    kw.setdefault("seed", GROUP_CONFIG_SEED[name])
+    return make_grouped_batch(**kw)
