@@ -342,16 +342,24 @@ pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_
     pa.num_groups = pl->num_groups;
     pa.item_base = 0;
     pa.num_items = pl->dense_items;
-    if (pl->dense_items > 0 && pkv::launch_prefix_attn(pa, pkv::kDenseRowsPerWg, s) != hipSuccess) return PKV_EHIP;
-    pa.item_base = pl->dense_items;
-    pa.num_items = pl->tiled_items;
-    if (pl->tiled_items > 0 && pkv::launch_prefix_attn(pa, pkv::kTiledRowsPerWg, s) != hipSuccess) return PKV_EHIP;
-    // Suffix pass, then the combine of each row's prefix ranges (its group's
-    // count) and suffix chunks.
     sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
     sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
     sa.force_partial = 1;
-    if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    if (pl->fuse_cascade) {
+        // every group DENSE: prefix items and suffix chunks in one launch
+        if (pkv::launch_cascade_fused(*pl, pa, sa, s) != hipSuccess) return PKV_EHIP;
+    } else {
+        if (pl->dense_items > 0 && pkv::launch_prefix_attn(pa, pkv::kDenseRowsPerWg, s) != hipSuccess)
+            return PKV_EHIP;
+        pa.item_base = pl->dense_items;
+        pa.num_items = pl->tiled_items;
+        if (pl->tiled_items > 0 && pkv::launch_prefix_attn(pa, pkv::kTiledRowsPerWg, s) != hipSuccess)
+            return PKV_EHIP;
+        // suffix pass
+        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    }
+    // the combine of each row's prefix ranges (its group's count) and
+    // suffix chunks
     pkv::SplitReduceArgs r = chunk_reduce_args(pl, sa);
     r.pre_acc = pa.part_acc;
     r.pre_ml = pa.part_ml;

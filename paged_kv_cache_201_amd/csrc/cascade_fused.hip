@@ -61,7 +61,7 @@ struct FusedLaunch {
         if constexpr (KV != PKV_BF16) {
             return hipErrorInvalidValue;
         } else {
-            const int np = prefix_blocks(pa.row_tiles * pa.H_kv * pa.num_splits);
+            const int np = prefix_blocks(pa.groups ? pa.num_items : pa.row_tiles * pa.H_kv * pa.num_splits);
             const int64_t ns = p.num_chunks * p.head_blocks;
             if (np + ns > INT32_MAX) return hipErrorInvalidValue;
             if (np + ns == 0) return hipSuccess;
@@ -74,7 +74,7 @@ struct FusedLaunch {
 }  // namespace
 
 hipError_t launch_cascade_fused(const pkv_plan& p, const PrefixArgs& pa, const PagedArgs& sa, hipStream_t s) {
-    if (pa.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
+    if (!pa.groups && pa.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
     return dispatch_kv<PKV_BF16>(p, FusedLaunch{p, pa, sa, s});
 }
 

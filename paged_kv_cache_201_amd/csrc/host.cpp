@@ -622,11 +622,24 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
 
     // Paged pass over every request's suffix (all of its tokens if it is in
     // no group); with groups every request leaves partial states for the
-    // combine.
+    // combine.  When every group runs DENSE, the two passes share one launch
+    // under the single-prefix step's rule (prefix flops per suffix byte, and
+    // at most half the workgroup slots for prefix items).
     const int32_t* sptr = m + pl->meta_suffix_indptr;
     const auto n_of = [&](int32_t b) { return (int64_t)sptr[b + 1] - sptr[b]; };
+    int64_t target = tu.target_workgroups;
+    if (tu.fuse_cascade && NG > 0 && tiled_items == 0) {
+        int64_t prefix_flops = 0;
+        for (auto& g : groups) prefix_flops += 4LL * g.m_eff * g.prefix_tokens * D * H_kv;
+        const int64_t suffix_bytes = suffix_total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+        const int64_t prefix_wgs = align_up(dense_items, 8);
+        if (2 * prefix_wgs <= tu.target_workgroups && prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes) {
+            pl->fuse_cascade = 1;
+            target -= prefix_wgs;
+        }
+    }
     bool spans = false, any_empty = false;
-    plan_chunks(pl, tu, suffix_total, tu.target_workgroups, n_of, &spans, &any_empty);
+    plan_chunks(pl, tu, suffix_total, target, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;
     layout_workspace(pl, NG > 0 || spans, max_splits);
     *out = owner.release();

@@ -53,7 +53,10 @@ constexpr float kPrefixLazySlack = 8.0f;
 // distinct banks.
 template <int D, int KT>
 struct PrefixSmem {
-    static constexpr int STAGES = 4;
+#ifndef PKV_PREFIX_STAGES
+#define PKV_PREFIX_STAGES 4
+#endif
+    static constexpr int STAGES = PKV_PREFIX_STAGES;
     uint16_t k[STAGES][KT * D];
     uint16_t v[STAGES][KT * D];
     int idx[kMaxPrefixSplitTokens];
@@ -66,6 +69,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `younger` tiles' copies (PER operations each) are in
+// flight, younger in 0..K (a run-time count turned into the immediate that
+// s_waitcnt needs).
+template <int K, int PER>
+__device__ __forceinline__ void wait_younger(int younger) {
+    if constexpr (K == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (younger >= K) wait_vmcnt<K * PER>();
+        else wait_younger<K - 1, PER>(younger);
+    }
 }
 
 // Number of prefix blocks to launch for N work items (a multiple of 8, see
@@ -214,11 +230,13 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     // S^T = K . Q^T for tile n (one 32x32 block per 32 tokens; lane holds row
     // lr and tokens tb*32 + (i/4)*8 + h*4 + i%4), in two independent
     // accumulation chains (even and odd k-steps) so that consecutive MFMAs
-    // do not wait on each other's results.  Padded tail tokens get -inf.
-    auto qk = [&](int n, int buf, f32x16_t (&s)[NTB]) {
+    // do not wait on each other's results.  The chains are added where the
+    // scores are used, a tile later, when the matrix cores are long done.
+    auto qk = [&](int buf, f32x16_t (&se)[NTB], f32x16_t (&so)[NTB]) {
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            f32x16_t s_even = f32x16_t{}, s_odd = f32x16_t{};
+            se[tb] = f32x16_t{};
+            so[tb] = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ks += 2) {
                 const bf16x8_t ka0 = __builtin_bit_cast(
@@ -227,42 +245,16 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
                 const bf16x8_t ka1 = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(
                                   &s_k[buf][(tb * 32 + lr) * D + (((ks * 2 + 2 + h) ^ kr_swz) << 3)]));
-                s_even = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], s_even, 0, 0, 0);
-                s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], s_odd, 0, 0, 0);
+                se[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], se[tb], 0, 0, 0);
+                so[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], so[tb], 0, 0, 0);
             }
-            s[tb] = s_even + s_odd;
-        }
-        const int valid = n_tok - n * KT;
-        if (valid < KT) {
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (tb * 32 + (i / 4) * 8 + h * 4 + (i % 4) >= valid) s[tb][i] = -INFINITY;
         }
     };
 
-    // Online softmax of one tile's scores and O^T += V^T . P^T.
-    auto softmax_pv = [&](const f32x16_t (&s)[NTB], int buf) {
-        // running max over raw scores (the scale is positive)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-        const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-        }
-        const float mneg = (m == -INFINITY) ? 0.f : -m;
+    // Probabilities 2^(s*scale - m) of a tile against max m, packed to bf16
+    // as the B operand of P.V, and their sum.
+    auto probs = [&](const f32x16_t (&s)[NTB], float mneg, bf16x8_t (&pb)[2 * NTB]) {
         float ps = 0.f;
-        bf16x8_t pb[2 * NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
@@ -277,12 +269,53 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
                 }
                 pb[tb * 2 + c] = __builtin_bit_cast(bf16x8_t, x);
             }
+        return ps;
+    };
+
+    // Online softmax of tile n's scores and O^T += V^T . P^T.  The
+    // probabilities are first taken against the running max; only when the
+    // tile raises the max by more than the lazy slack (a uniform, rare
+    // branch) are the accumulators rescaled and the probabilities taken
+    // again.  The common path has no branch, so the scores of the next tile
+    // (already issued to the matrix cores) overlap this arithmetic.
+    auto softmax_pv = [&](const f32x16_t (&se)[NTB], const f32x16_t (&so)[NTB], int n, int buf) {
+        f32x16_t s[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) s[tb] = se[tb] + so[tb];
+        const int valid = n_tok - n * KT;
+        if (valid < KT) {  // padded tail tokens get -inf
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (tb * 32 + (i / 4) * 8 + h * 4 + (i % 4) >= valid) s[tb][i] = -INFINITY;
+        }
+        // running max over raw scores (the scale is positive)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        bf16x8_t pb[2 * NTB];
+        float ps = probs(s, (m == -INFINITY) ? 0.f : -m, pb);
+        const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mn = fmaxf(m, mx);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            ps = probs(s, (m == -INFINITY) ? 0.f : -m, pb);
+        }
         l += ps;
-        // O^T += V^T . P^T over 16-token chunks
+        // O^T += V^T . P^T over 16-token chunks; the head-dim blocks are the
+        // inner loop, so that consecutive MFMAs update different accumulators
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int c = 0; c < 2 * NTB; ++c) {
 #pragma unroll
-            for (int c = 0; c < 2 * NTB; ++c) {
+            for (int db = 0; db < NDB; ++db) {
                 typedef short v4s_t __attribute__((ext_vector_type(4)));
                 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
                 const uint16_t* vb = &s_v[buf][c * 16 * D];
@@ -303,35 +336,35 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     wait_vmcnt<0>();
     __syncthreads();  // s_idx ready
     for (int n = 0; n < S - 1 && n < ntiles; ++n) issue_tile(n);
-    static_assert(S == 4, "wait counts below assume four stages");
+    static_assert(S >= 3 && 2 * PER_WAVE * (S - 2) < 64, "ring depth within the vmcnt range");
     // Wait until this wave's copies of tile n have landed: at most the copies
-    // of the tiles issued after it (up to tile `last`) may still be in flight.
-    auto wait_tile = [&](int n, int last) {
-        const int younger = min(ntiles - 1, last) - n;
-        if (younger >= 2) wait_vmcnt<4 * PER_WAVE>();
-        else if (younger == 1) wait_vmcnt<2 * PER_WAVE>();
-        else wait_vmcnt<0>();
-    };
+    // of the tiles issued after it (up to tile `last`) may still be in flight
+    // (two per block: K and V).
+    auto wait_tile = [&](int n, int last) { wait_younger<S - 2, 2 * PER_WAVE>(min(ntiles - 1, last) - n); };
     // Software pipeline: while the softmax and P.V of tile n run, the scores
     // of tile n + 1 are already on the matrix cores and tiles n + 2, n + 3
-    // are on their way into the ring.
-    f32x16_t s_cur[NTB], s_next[NTB];
-    if (ntiles > 0) {
-        wait_tile(0, S - 2);
-        __syncthreads();
-        qk(0, 0, s_cur);
-    }
-    for (int n = 0; n < ntiles; ++n) {
+    // are on their way into the ring.  Two score buffers alternate (the loop
+    // takes two tiles per trip), so no scores are copied between them.
+    f32x16_t sa_e[NTB], sa_o[NTB], sb_e[NTB], sb_o[NTB];
+    auto step = [&](int n, const f32x16_t (&ce)[NTB], const f32x16_t (&co)[NTB], f32x16_t (&ne)[NTB],
+                    f32x16_t (&no)[NTB]) {
         if (n + 1 < ntiles) {
             // tiles 0 .. n + S - 2 have been issued
             wait_tile(n + 1, n + S - 2);
             __syncthreads();  // tile n + 1 visible; every wave is done with tile n - 1
             if (n + S - 1 < ntiles) issue_tile(n + S - 1);  // into the stage of tile n - 1
-            qk(n + 1, (n + 1) % S, s_next);
+            qk((n + 1) % S, ne, no);
         }
-        softmax_pv(s_cur, n % S);
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) s_cur[tb] = s_next[tb];
+        softmax_pv(ce, co, n, n % S);
+    };
+    if (ntiles > 0) {
+        wait_tile(0, S - 2);
+        __syncthreads();
+        qk(0, sa_e, sa_o);
+    }
+    for (int n = 0; n < ntiles; n += 2) {
+        step(n, sa_e, sa_o, sb_e, sb_o);
+        if (n + 1 < ntiles) step(n + 1, sb_e, sb_o, sa_e, sa_o);
     }
 
     // Row totals: the two halves of the wave hold disjoint tokens of a row.

@@ -566,3 +566,27 @@ def test_grouped_step_full_size_sampled():
     assert plan.info["num_groups"] == 4 and plan.info["path_name"] == "DENSE"
     o, lse = _grouped_run(db, plan)
     check_close("bf16", o[reqs], lse[reqs], o_ref, lse_ref, "grouped full")
+
+
+def test_grouped_fused_launch_matches_separate_launches():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    # prefix-heavy: the all-DENSE grouped step takes the fused launch
+    b = make_grouped_batch(seed=505, B=40, H_q=32, H_kv=8, d=128, groups=[(16, 2048), (12, 1024), (6, 700)],
+                           own_len=(0, 96), page_size=16)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    outs = []
+    for fuse in (12, 0):
+        plan = db.plan_grouped(tuning=dict(fuse_cascade=fuse, gate_ratio=0))  # keep every group
+        assert plan.info["num_groups"] == 3 and plan.info["path_name"] == "DENSE"
+        o, lse = _grouped_run(db, plan)
+        check_close("bf16", o, lse, o_ref, lse_ref, f"grouped fuse={fuse}")
+        o2, lse2 = _grouped_run(db, plan)
+        assert same_bits(o, o2) and same_bits(lse, lse2), f"fuse={fuse} not repeatable"
+        outs.append((o.float(), lse))
+    # the two launches order the same arithmetic the same way up to the
+    # chunking of the suffix, so they agree far inside the tolerance
+    assert (outs[0][0] - outs[1][0]).abs().max().item() <= 8e-3
+    fin = torch.isfinite(outs[0][1])
+    assert torch.equal(fin, torch.isfinite(outs[1][1]))
+    assert (outs[0][1][fin] - outs[1][1][fin]).abs().max().item() <= 1e-4

@@ -337,11 +337,8 @@ def test_grouped_plan_reduces_to_the_single_prefix_plan():
                                         kv_dtype="bf16", page_size=p, page_indptr=ptr, page_indices=pages,
                                         seq_lens=lens).info
         indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        # (the single-prefix step's fused launch is left out: grouped steps run
-        # their passes as separate launches)
         one = pkv.pkv_plan_create(batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
-                                  kv_dtype="bf16", page_size=p, kv_indptr=indptr, shared_prefix_len=P,
-                                  tuning=dict(fuse_cascade=0)).info
+                                  kv_dtype="bf16", page_size=p, kv_indptr=indptr, shared_prefix_len=P).info
         assert g["path"] == one["path"]
         if one["path_name"] == "PAGED":
             assert g["num_groups"] == 0 and g["prefix_tokens"] == one["prefix_tokens"] == 0
