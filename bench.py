@@ -99,6 +99,7 @@ def bench_prefix_config(name, steps, warmup, legs=None):
     import torch
     from paged_kv_cache_201_amd.step import DeviceBatch
     from workloads import make_config, relayout
+    from workloads.synth import RELAYOUT_SEED
     b = make_config(name, device="cuda")
     P = b.prefix_len
     out = dict(workload=name, B=b.B, prefix=P)
@@ -117,8 +118,22 @@ def bench_prefix_config(name, steps, warmup, legs=None):
         del ws
     del db
     torch.cuda.empty_cache()
+    if not legs or "planned_contiguous_prefix" in legs:
+        # the prefix stored contiguously ("GraniKV", prefix placement: the
+        # read-once prefix as a plain strided operand) under the same plan
+        c = relayout(b, page_size=b.page_size, seed=RELAYOUT_SEED[name] + 1000, layout="shared", perm="prefix_first",
+                     device="cuda")
+        dc = DeviceBatch.from_batch(c)
+        plan = dc.plan(shared_prefix_len=P)
+        ws = dc.workspace(plan)
+        ms = time_steps(lambda: dc.step(plan, o, lse, ws), steps, warmup)
+        nbytes = algorithmic_bytes(c, plan.info["path_name"], plan.info["prefix_tokens"])
+        out["planned_contiguous_prefix"] = dict(path=plan.info["path_name"], us_per_step=ms * 1e3,
+                                                gbs=nbytes / (ms * 1e-3) / 1e9, algorithmic_bytes=nbytes)
+        del dc, c, ws
+        torch.cuda.empty_cache()
     if not legs or "paged_unique" in legs:
-        u = relayout(b, page_size=b.page_size, seed=2000 + int(name[1:]), layout="unique", device="cuda")
+        u = relayout(b, page_size=b.page_size, seed=RELAYOUT_SEED[name], layout="unique", device="cuda")
         du = DeviceBatch.from_batch(u)
         plan = du.plan(force_path=0)
         ws = du.workspace(plan)
@@ -529,7 +544,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,groups4")
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,c3_fp8,groups4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", metavar="CONFIG:LEG[,LEG]",
                     help="time only these legs of one shared-prefix workload (e.g. c3:paged_unique) and exit; "
@@ -645,7 +660,7 @@ def main():
             log(json.dumps(r))
             del db
             torch.cuda.empty_cache()
-        elif name in ("c3", "c4"):
+        elif name in ("c3", "c4", "c3_fp8"):
             log(f"bench {name}")
             extra[name] = bench_prefix_config(name, args.steps, args.warmup)
             log(json.dumps(extra[name]))

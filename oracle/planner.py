@@ -24,14 +24,19 @@ Rule, in order (all arithmetic in Python integers):
 
 Problem checks mirror what the library accepts: d in {64, 128}; (q, kv)
 dtype in {(f32, f32), (bf16, bf16), (bf16, fp8)}; G in {1, 2, 4, 8}; the
-prefix kernels take bf16 queries over bf16 K/V.
+prefix kernels take bf16 queries over bf16 K/V, or over fp8 K/V at d = 128.
 """
 PAGED, CASCADE, DENSE = "PAGED", "CASCADE", "DENSE"
 PATH_NAMES = (PAGED, CASCADE, DENSE)
 
 BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 SUPPORTED_DTYPES = {("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8")}
-PREFIX_DTYPES = {("bf16", "bf16")}
+PREFIX_DTYPES = {("bf16", "bf16"), ("bf16", "fp8")}
+
+
+def prefix_capable(q_dtype, kv_dtype, d):
+    """Whether a prefix kernel exists for this pair (fp8 K/V: d = 128 only)."""
+    return (q_dtype, kv_dtype) in PREFIX_DTYPES and (kv_dtype != "fp8" or d == 128)
 
 
 class PlanError(ValueError):
@@ -66,7 +71,7 @@ def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
     shared_pages = shared_prefix_len // page_size if n_shared else 0
     prefix_tokens = shared_pages * page_size
     m_eff = B * G
-    capable = (q_dtype, kv_dtype) in PREFIX_DTYPES
+    capable = prefix_capable(q_dtype, kv_dtype, d)
     out = dict(m_eff=m_eff, shared_pages=shared_pages, prefix_tokens=prefix_tokens)
     if force_path >= 0:
         path = PATH_NAMES[force_path]

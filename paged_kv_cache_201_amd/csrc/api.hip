@@ -147,6 +147,9 @@ pkv::PrefixArgs prefix_args(const pkv_plan* pl, const void* q, const pkv_pool* p
     a.q = q;
     a.k = pool->k;
     a.v = pool->v;
+    a.kv_dtype = pl->kv_dtype;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
     a.prefix_indices = prefix_indices;
     a.B = pl->B;
     a.H_kv = pl->H_kv;
@@ -327,6 +330,9 @@ pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_
     pa.q = q;
     pa.k = pool->k;
     pa.v = pool->v;
+    pa.kv_dtype = pl->kv_dtype;
+    pa.k_scale = pool->k_scale;
+    pa.v_scale = pool->v_scale;
     pa.prefix_indices = meta + pl->meta_prefix_indices;
     pa.B = pl->B;
     pa.H_kv = pl->H_kv;

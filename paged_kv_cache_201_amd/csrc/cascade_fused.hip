@@ -1,4 +1,5 @@
-// One launch for both passes of a DENSE cascade step.
+// One launch for both passes of a DENSE cascade step (bf16 K/V, or fp8 K/V
+// at head_dim 128).
 //
 // The prefix pass is bound by MFMA and LDS work (the prefix is read once for
 // all requests: "GraniKV: asymmetric KV cache paging for shared-prefix
@@ -12,6 +13,8 @@
 // use 256 threads and at most 256 VGPRs per lane, and they share the LDS
 // allocation.  Results are the same partial states the two separate kernels
 // write.
+#include <type_traits>
+
 #include "paged_dispatch.h"
 #include "prefix_kernel.h"
 
@@ -34,20 +37,20 @@ __device__ __forceinline__ void fused_role(const int i, const int np, const int 
     idx = 8 * groups + (is_prefix ? j : j - rest_prefix);
 }
 
-template <int D, int G, int NHL, int TPI>
+template <int KV, int D, int G, int NHL, int TPI>
 __global__ void __launch_bounds__(kPagedWaves * 64, 2)
     cascade_fused_kernel(const PrefixArgs pa, const PagedArgs sa, const int np, const int ns, const int hblks) {
-    using PS = PrefixSmem<D, 32>;
-    using SS = PagedSmem<PKV_BF16, D, G, NHL, TPI>;
+    using PS = typename std::conditional<KV == PKV_FP8_E4M3, PrefixSmem8<D, 32>, PrefixSmem<D, 32>>::type;
+    using SS = PagedSmem<KV, D, G, NHL, TPI>;
     constexpr size_t kBytes = sizeof(PS) > sizeof(SS) ? sizeof(PS) : sizeof(SS);
     __shared__ __attribute__((aligned(16))) char smem[kBytes];
     bool is_prefix;
     int idx;
     fused_role(blockIdx.x, np, ns, is_prefix, idx);
     if (is_prefix)
-        prefix_item<D, kPagedWaves, 32>(pa, *reinterpret_cast<PS*>(smem), idx);
+        prefix_item<KV, D, kPagedWaves, 32>(pa, *reinterpret_cast<PS*>(smem), idx);
     else
-        paged_chunk<PKV_BF16, D, G, NHL, TPI>(sa, *reinterpret_cast<SS*>(smem), idx / hblks, idx % hblks);
+        paged_chunk<KV, D, G, NHL, TPI>(sa, *reinterpret_cast<SS*>(smem), idx / hblks, idx % hblks);
 }
 
 namespace {
@@ -58,14 +61,15 @@ struct FusedLaunch {
     hipStream_t s;
     template <int KV, int D, int G, int NHL, int TPI>
     hipError_t run() const {
-        if constexpr (KV != PKV_BF16) {
+        // bf16, or fp8 at head_dim 128 (the fp8 prefix kernel's shape)
+        if constexpr (KV == PKV_F32 || (KV == PKV_FP8_E4M3 && D != 128)) {
             return hipErrorInvalidValue;
         } else {
             const int np = prefix_blocks(pa.groups ? pa.num_items : pa.row_tiles * pa.H_kv * pa.num_splits);
             const int64_t ns = p.num_chunks * p.head_blocks;
             if (np + ns > INT32_MAX) return hipErrorInvalidValue;
             if (np + ns == 0) return hipSuccess;
-            cascade_fused_kernel<D, G, NHL, TPI>
+            cascade_fused_kernel<KV, D, G, NHL, TPI>
                 <<<(uint32_t)(np + ns), kPagedWaves * 64, 0, s>>>(pa, sa, np, (int)ns, p.head_blocks);
             return hipGetLastError();
         }
@@ -75,6 +79,7 @@ struct FusedLaunch {
 
 hipError_t launch_cascade_fused(const pkv_plan& p, const PrefixArgs& pa, const PagedArgs& sa, hipStream_t s) {
     if (!pa.groups && pa.split_tokens > kMaxPrefixSplitTokens) return hipErrorInvalidValue;
+    if (p.kv_dtype == PKV_FP8_E4M3) return dispatch_kv<PKV_FP8_E4M3>(p, FusedLaunch{p, pa, sa, s});
     return dispatch_kv<PKV_BF16>(p, FusedLaunch{p, pa, sa, s});
 }
 

@@ -34,8 +34,11 @@ bool dtype_pair_supported(int32_t q, int32_t kv) {
            (q == PKV_BF16 && kv == PKV_FP8_E4M3);
 }
 
-// The prefix kernels run bf16 MFMA: bf16 queries over bf16 K/V.
-bool prefix_pair_supported(int32_t q, int32_t kv) { return q == PKV_BF16 && kv == PKV_BF16; }
+// The prefix kernels run bf16 MFMA: bf16 queries over bf16 K/V, or over fp8
+// e4m3 K/V widened in LDS (head_dim 128).
+bool prefix_pair_supported(int32_t q, int32_t kv, int32_t d) {
+    return q == PKV_BF16 && (kv == PKV_BF16 || (kv == PKV_FP8_E4M3 && d == 128));
+}
 
 bool group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
@@ -113,7 +116,7 @@ pkv_status check_support(const pkv_problem* pr, const pkv_tuning& tu, pkv::Paged
 // state traffic plus the launch term; DENSE at M_eff >= t_dense; CASCADE.
 pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_shared, int64_t prefix_tokens,
                        int64_t rows, int64_t m_eff, int32_t* path) {
-    const bool capable = prefix_pair_supported(pr->q_dtype, pr->kv_dtype);
+    const bool capable = prefix_pair_supported(pr->q_dtype, pr->kv_dtype, pr->head_dim);
     if (pr->force_path >= 0) {
         *path = pr->force_path;
         if (*path != PKV_PATH_PAGED) {
@@ -362,6 +365,8 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->m_eff = (int32_t)m_eff;
     pl->shared_pages = (int32_t)shared_pages;
     pl->prefix_tokens = (int32_t)prefix_tokens;
+    // (the fused launch is built for the DENSE prefix kernels: bf16 K/V, or
+    // fp8 K/V at head_dim 128)
     pl->fuse_cascade = tu.fuse_cascade && path == PKV_PATH_DENSE;
 
     // Prefix pass: M_eff query rows per KV head in tiles, the prefix cut into

@@ -75,12 +75,16 @@ struct SplitReduceArgs {
 };
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t stream);
 
-// Shared-prefix pass (bf16 MFMA).  Rows r = b * G + j of KV head g attend
+// Shared-prefix pass (bf16 MFMA; fp8 K/V widened to bf16 in LDS).  Rows
+// r = b * G + j of KV head g attend
 // over prefix tokens [split * split_tokens, ...) listed by prefix_indices.
 struct PrefixArgs {
     const void* q;            // [B][H_q][D] bf16
-    const void* k;            // pool, bf16
+    const void* k;            // pool, bf16 or fp8 e4m3 (kv_dtype)
     const void* v;
+    int32_t kv_dtype;
+    const float* k_scale;     // [H_kv], fp8 only
+    const float* v_scale;
     const int32_t* prefix_indices;
     int32_t B, H_kv, G, D;
     int32_t prefix_len;

@@ -41,24 +41,40 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kPrefixLazySlack = 8.0f;
 
-// NW waves of 32 query rows each share KT-token K/V tiles through a
-// double-buffered LDS ring: while the waves compute tile n from one buffer,
-// tile n+1 (loaded into registers at the top of the iteration) is written
-// into the other, so one barrier per tile suffices.  The range's slot
-// indices are staged in LDS once, so no tile waits on an index load.
-// LDS of one prefix workgroup: a ring of STAGES K and V tiles and the slot
-// indices of the workgroup's prefix range.  Tile rows are D bf16 with no
+// NW waves of 32 query rows each share KT-token K/V tiles through an LDS
+// ring that global memory fills asynchronously, S - 1 tiles ahead of the
+// one being computed.  The range's slot indices are staged in LDS once, so
+// no tile waits on an index load.
+#ifndef PKV_PREFIX_STAGES
+#define PKV_PREFIX_STAGES 4
+#endif
+// LDS of one bf16 prefix workgroup: a ring of STAGES K and V tiles and the
+// slot indices of the workgroup's prefix range.  Tile rows are D bf16 with no
 // padding; the 16-byte chunks of row t are stored XOR-swizzled (chunk c at
 // position c ^ (t mod D/8)) so that the operand reads of 16 or 32 rows hit
 // distinct banks.
 template <int D, int KT>
 struct PrefixSmem {
-#ifndef PKV_PREFIX_STAGES
-#define PKV_PREFIX_STAGES 4
-#endif
     static constexpr int STAGES = PKV_PREFIX_STAGES;
+    static constexpr int BUFS = STAGES;   // tiles the products read from
     uint16_t k[STAGES][KT * D];
     uint16_t v[STAGES][KT * D];
+    int idx[kMaxPrefixSplitTokens];
+};
+
+// LDS of one fp8 (e4m3) prefix workgroup ("Track C · Document 10", fp8
+// cache section: the cache stored at one byte per value): the ring holds the
+// stored codes, row-major, half the bytes of a bf16 tile; each landed tile
+// is widened once per workgroup, exactly, into one of two bf16 tiles in the
+// swizzled layout above, which the same MFMA products then read.
+template <int D, int KT>
+struct PrefixSmem8 {
+    static constexpr int STAGES = PKV_PREFIX_STAGES;
+    static constexpr int BUFS = 2;
+    uint8_t k8[STAGES][KT * D];
+    uint8_t v8[STAGES][KT * D];
+    uint16_t k[BUFS][KT * D];
+    uint16_t v[BUFS][KT * D];
     int idx[kMaxPrefixSplitTokens];
 };
 
@@ -89,16 +105,20 @@ __device__ __forceinline__ void wait_younger(int younger) {
 __host__ __device__ inline int prefix_blocks(int n_items) { return (n_items + 7) / 8 * 8; }
 
 // One prefix work item, run by all NW * 64 threads of a workgroup.  p is the
-// workgroup's index among the prefix workgroups of the launch.
-template <int D, int NW, int KT>
-__device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, KT>& sm, const int p) {
-    constexpr int CPR = D / 8;                  // 16-byte chunks per tile row
-    constexpr int S = PrefixSmem<D, KT>::STAGES;
+// workgroup's index among the prefix workgroups of the launch.  KV is the
+// stored dtype (bf16, or fp8 e4m3 with per-KV-head scales); SM is the
+// matching LDS layout.
+template <int KV, int D, int NW, int KT, class SM>
+__device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const int p) {
+    constexpr bool F8 = KV == PKV_FP8_E4M3;
+    constexpr int CPR = D / 8;                  // 16-byte bf16 chunks per tile row
+    constexpr int S = SM::STAGES;
+    constexpr int NBUF = SM::BUFS;
     constexpr int NKS = D / 16;    // k-steps of the first product
     constexpr int NDB = D / 32;    // 32-wide head-dim blocks of the output
     constexpr int NTB = KT / 32;   // 32-token blocks per tile
     constexpr int NT = NW * 64;
-    constexpr int BLOCKS = KT * D * 2 / 1024;   // 1 KB wave-wide LDS copies per K (or V) tile
+    constexpr int BLOCKS = KT * D * (F8 ? 1 : 2) / 1024;   // 1 KB wave-wide LDS copies per K (or V) tile
     static_assert(BLOCKS % NW == 0, "each wave copies whole 1 KB blocks of a tile");
     constexpr int PER_WAVE = BLOCKS / NW;
     auto& s_k = sm.k;
@@ -170,10 +190,11 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
         }
     }
 
-    const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
-    const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
-    const size_t slot_stride = (size_t)a.H_kv * D;
+    const size_t slot_stride = (size_t)a.H_kv * D;   // elements
     const size_t head_off = (size_t)g * D;
+    // fp8 codes are widened exactly; the per-head scales multiply the scores
+    // (folded into the exp2 scale) and the output
+    const float sl2 = F8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2;
 
     // Tile n goes to ring stage n % S straight from global memory with
     // gfx950's global_load_lds_dwordx4: lane l of a wave-wide copy fetches one
@@ -188,9 +209,16 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     // uses M0.
     typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
     // LDS byte addresses of the two rings (M0 takes a 32-bit LDS address)
-    const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_k[0][0]);
-    const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_v[0][0]);
-    auto lds_copy16 = [](const uint16_t* src, uint32_t m0) {
+    uint32_t k_lds, v_lds;
+    if constexpr (F8) {
+        typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+        k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8_t*)&sm.k8[0][0]);
+        v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8_t*)&sm.v8[0][0]);
+    } else {
+        k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_k[0][0]);
+        v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_v[0][0]);
+    }
+    auto lds_copy16 = [](const void* src, uint32_t m0) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
     };
     auto issue_tile = [&](int n) {
@@ -199,12 +227,47 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
         for (int j = 0; j < PER_WAVE; ++j) {
             const int blk = wave * PER_WAVE + j;
             const int p = blk * 64 + lane;
-            const int t = p / CPR;
-            const int c = (p % CPR) ^ (t & (CPR - 1));
-            const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + c * 8;
-            const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
-            lds_copy16(kpool + off, k_lds + dst);
-            lds_copy16(vpool + off, v_lds + dst);
+            if constexpr (F8) {
+                // plain rows of D codes: chunk p is row p / (D/16), codes 16 (p mod D/16) ..
+                const int t = p / (D / 16);
+                const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + (p % (D / 16)) * 16;
+                const uint32_t dst = (uint32_t)(stage * KT * D + blk * 1024);
+                lds_copy16(static_cast<const uint8_t*>(a.k) + off, k_lds + dst);
+                lds_copy16(static_cast<const uint8_t*>(a.v) + off, v_lds + dst);
+            } else {
+                const int t = p / CPR;
+                const int c = (p % CPR) ^ (t & (CPR - 1));
+                const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + c * 8;
+                const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
+                lds_copy16(static_cast<const uint16_t*>(a.k) + off, k_lds + dst);
+                lds_copy16(static_cast<const uint16_t*>(a.v) + off, v_lds + dst);
+            }
+        }
+    };
+    // fp8: widen the codes of tile n (ring stage n % S) into bf16 buffer
+    // n % 2, 16 codes of one row per thread and pass, into the swizzled
+    // chunks 2c and 2c + 1 of that row.
+    auto widen_tile = [&](int n) {
+        if constexpr (F8) {
+            const int st = n % S, cb = n % NBUF;
+            for (int i = threadIdx.x; i < KT * D / 16; i += NT) {
+                const int t = i / (D / 16), c = 2 * (i % (D / 16));
+                const int sw = t & (CPR - 1);
+                const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(&sm.k8[st][i * 16]);
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&sm.v8[st][i * 16]);
+                const u32x4_t k0 = {fp8x2_to_bf16x2<false>(xk[0]), fp8x2_to_bf16x2<true>(xk[0]),
+                                    fp8x2_to_bf16x2<false>(xk[1]), fp8x2_to_bf16x2<true>(xk[1])};
+                const u32x4_t k1 = {fp8x2_to_bf16x2<false>(xk[2]), fp8x2_to_bf16x2<true>(xk[2]),
+                                    fp8x2_to_bf16x2<false>(xk[3]), fp8x2_to_bf16x2<true>(xk[3])};
+                const u32x4_t v0 = {fp8x2_to_bf16x2<false>(xv[0]), fp8x2_to_bf16x2<true>(xv[0]),
+                                    fp8x2_to_bf16x2<false>(xv[1]), fp8x2_to_bf16x2<true>(xv[1])};
+                const u32x4_t v1 = {fp8x2_to_bf16x2<false>(xv[2]), fp8x2_to_bf16x2<true>(xv[2]),
+                                    fp8x2_to_bf16x2<false>(xv[3]), fp8x2_to_bf16x2<true>(xv[3])};
+                *reinterpret_cast<u32x4_t*>(&s_k[cb][t * D + ((c ^ sw) << 3)]) = k0;
+                *reinterpret_cast<u32x4_t*>(&s_k[cb][t * D + (((c + 1) ^ sw) << 3)]) = k1;
+                *reinterpret_cast<u32x4_t*>(&s_v[cb][t * D + ((c ^ sw) << 3)]) = v0;
+                *reinterpret_cast<u32x4_t*>(&s_v[cb][t * D + (((c + 1) ^ sw) << 3)]) = v1;
+            }
         }
     };
     // Transposed-read addresses of this lane for the V^T operand: lane group
@@ -262,8 +325,8 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
                 u32x4_t x;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const float p0 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w], a.scale_log2, mneg));
-                    const float p1 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w + 1], a.scale_log2, mneg));
+                    const float p0 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w], sl2, mneg));
+                    const float p1 = fast_exp2(fmaf(s[tb][c * 8 + 2 * w + 1], sl2, mneg));
                     ps += p0 + p1;
                     x[w] = pack_bf16x2(p0, p1);
                 }
@@ -296,7 +359,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
         bf16x8_t pb[2 * NTB];
         float ps = probs(s, (m == -INFINITY) ? 0.f : -m, pb);
         const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
@@ -346,20 +409,32 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     // are on their way into the ring.  Two score buffers alternate (the loop
     // takes two tiles per trip), so no scores are copied between them.
     f32x16_t sa_e[NTB], sa_o[NTB], sb_e[NTB], sb_o[NTB];
+    // fp8 adds a widening pass and a second barrier per tile: the bf16
+    // buffer of tile n + 1 is rewritten only after every wave has finished
+    // P.V of tile n - 1 (the first barrier), and read only after the
+    // widening (the second).
     auto step = [&](int n, const f32x16_t (&ce)[NTB], const f32x16_t (&co)[NTB], f32x16_t (&ne)[NTB],
                     f32x16_t (&no)[NTB]) {
         if (n + 1 < ntiles) {
             // tiles 0 .. n + S - 2 have been issued
             wait_tile(n + 1, n + S - 2);
-            __syncthreads();  // tile n + 1 visible; every wave is done with tile n - 1
+            __syncthreads();  // tile n + 1 landed; every wave is done with tile n - 1
             if (n + S - 1 < ntiles) issue_tile(n + S - 1);  // into the stage of tile n - 1
-            qk((n + 1) % S, ne, no);
+            if constexpr (F8) {
+                widen_tile(n + 1);
+                __syncthreads();
+            }
+            qk((n + 1) % NBUF, ne, no);
         }
-        softmax_pv(ce, co, n, n % S);
+        softmax_pv(ce, co, n, n % NBUF);
     };
     if (ntiles > 0) {
         wait_tile(0, S - 2);
         __syncthreads();
+        if constexpr (F8) {
+            widen_tile(0);
+            __syncthreads();
+        }
         qk(0, sa_e, sa_o);
     }
     for (int n = 0; n < ntiles; n += 2) {
@@ -376,9 +451,10 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, PrefixSmem<D, K
     if (direct) {
         out = a.o + qrow * D;
         scale = L > 0.f ? 1.f / L : 0.f;
+        if constexpr (F8) scale *= a.v_scale[g];
     } else {
         out = a.part_acc + (((size_t)rb * a.num_splits + split) * H_q + rq) * D;
-        scale = 1.f;
+        scale = F8 ? a.v_scale[g] : 1.f;
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -536,9 +536,9 @@ def test_grouped_step_dense_and_tiled_groups_in_one_step():
 def test_grouped_step_without_groups_is_the_paged_step_bitwise():
     pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
     for kv in ("bf16", "fp8"):
-        # fp8 K/V has no prefix kernel: its groups are dissolved
-        b = make_grouped_batch(seed=503, B=12, H_q=32, H_kv=8, d=128, groups=[(4, 512)] if kv == "fp8" else [],
-                               own_len=(0, 900), page_size=16, kv_dtype=kv)
+        # fp8 K/V at head_dim 64 has no prefix kernel: its groups are dissolved
+        b = make_grouped_batch(seed=503, B=12, H_q=32 if kv == "bf16" else 64, H_kv=8, d=128 if kv == "bf16" else 64,
+                               groups=[(4, 512)] if kv == "fp8" else [], own_len=(0, 900), page_size=16, kv_dtype=kv)
         o_ref, lse_ref = ob.batch_reference(b)
         db = DeviceBatch.from_batch(b)
         plan = db.plan_grouped()
@@ -590,3 +590,80 @@ def test_grouped_fused_launch_matches_separate_launches():
     fin = torch.isfinite(outs[0][1])
     assert torch.equal(fin, torch.isfinite(outs[1][1]))
     assert (outs[0][1][fin] - outs[1][1][fin]).abs().max().item() <= 1e-4
+
+
+
+# ------------------------------------------------------- fp8 shared prefix --
+
+def test_cascade_fp8_small_all_paths():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    for B, P, own in ((24, 512, (0, 100)), (5, 1000, (1, 3)), (70, 300, (20, 60))):
+        b = make_decode_batch(seed=41 + B, B=B, H_q=32, H_kv=8, d=128, own_len=own, prefix_len=P, page_size=16,
+                              kv_dtype="fp8", pool_factor=2)
+        o_ref, lse_ref = ob.batch_reference(b)
+        db, res = _cascade_paths(DeviceBatch, b, ob)
+        for force, (o, lse, plan) in res.items():
+            check_close("fp8", o, lse, o_ref, lse_ref, f"fp8 B={B} P={P} path={force}")
+        plan = res[2][2]
+        n = plan.info["prefix_tokens"]
+        say(f"fp8 cascade_prefix_attn B={B} n={n}")
+        o_p, lse_p = db.prefix(plan)
+        torch.cuda.synchronize()
+        op_ref, lp_ref = ob.prefix_reference(b, n)
+        check_close("fp8", o_p, lse_p, op_ref, lp_ref, f"fp8 prefix B={B}")
+        # prefix tiles of 1 and of several ranges, tiled and dense
+        for force in (1, 2):
+            plan = db.plan(shared_prefix_len=P, force_path=force,
+                           tuning=dict(prefix_target_workgroups=4096, min_prefix_split_tokens=64))
+            say(f"fp8 many ranges force={force} splits={plan.info['prefix_splits']}")
+            o, lse = db.step(plan)
+            torch.cuda.synchronize()
+            check_close("fp8", o, lse, o_ref, lse_ref, f"fp8 ranges B={B} force={force}")
+
+
+def test_c3_fp8_full_sampled():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    reqs = [0, 100, 255]
+    b = make_config("c3", kv_dtype="fp8")
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(shared_prefix_len=b.prefix_len)
+    assert plan.info["path_name"] == "DENSE"
+    say("c3 fp8 full decode_step")
+    o, lse = db.step(plan)
+    torch.cuda.synchronize()
+    check_close("fp8", o[reqs], lse[reqs], o_ref, lse_ref, "c3 fp8 DENSE")
+
+
+def test_grouped_step_fp8():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    b = make_grouped_batch(seed=506, B=30, H_q=64, H_kv=8, d=128, groups=[(9, 1500), (6, 400), (3, 77)],
+                           own_len=(0, 150), page_size=16, kv_dtype="fp8")
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    for t_dense in (1, 40):  # every group DENSE; the small groups tiled
+        plan = db.plan_grouped(tuning=dict(gate_ratio=0, t_dense=t_dense))
+        assert plan.info["num_groups"] == 3
+        o, lse = _grouped_run(db, plan)
+        check_close("fp8", o, lse, o_ref, lse_ref, f"grouped fp8 t_dense={t_dense}")
+
+
+def test_fp8_fused_cascade_launch_matches_separate_launches():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_decode_batch(seed=47, B=48, H_q=32, H_kv=8, d=128, own_len=(1, 64), prefix_len=1536, page_size=16,
+                          kv_dtype="fp8")
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    outs = []
+    for fuse in (12, 0):
+        plan = db.plan(shared_prefix_len=b.prefix_len, force_path=2, tuning=dict(fuse_cascade=fuse))
+        say(f"fp8 DENSE fuse={fuse}")
+        o, lse = db.step(plan)
+        torch.cuda.synchronize()
+        check_close("fp8", o, lse, o_ref, lse_ref, f"fp8 fuse={fuse}")
+        o2, lse2 = db.step(plan)
+        torch.cuda.synchronize()
+        assert same_bits(o, o2) and same_bits(lse, lse2), f"fp8 fuse={fuse} not repeatable"
+        outs.append((o.float(), lse))
+    assert (outs[0][0] - outs[1][0]).abs().max().item() <= 8e-3
+    assert (outs[0][1] - outs[1][1]).abs().max().item() <= 1e-4

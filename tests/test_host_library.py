@@ -159,7 +159,9 @@ def test_planner_forced_paths_and_errors_match_oracle():
     for force in (0, 1, 2):
         for P in (0, 8, 16, 4096):
             _both(16, 4, P, 16, L=P + 5, force=force)
-    _both(16, 4, 4096, 16, L=5000, kv="fp8", force=2)            # EUNSUPPORTED
+    _both(16, 4, 4096, 16, L=5000, kv="fp8", force=2)            # fp8 prefix kernel (d = 128)
+    _both(16, 4, 4096, 16, L=5000, kv="fp8", d=64, force=2)      # EUNSUPPORTED (fp8 prefix: d = 128 only)
+    _both(256, 4, 4096, 16, L=5000, kv="fp8")                    # fp8 cascade by the gate
     _both(16, 4, 64, 16, L=5000, q="f32", kv="f32", H_kv=2, d=64)
     _both(16, 4, 64, 16, L=5000, d=96)                           # EUNSUPPORTED
     _both(4, 4, 64, 16, L=[100, 100, 20, 100])                   # prefix longer than a request
@@ -298,7 +300,8 @@ def test_grouped_plan_errors_match_oracle_and_abi():
     reqs = [["A", "a0"], ["A", "a1"], ["B"]]
     ptr, pages = tables_from_blocks(reqs, 16)
     lens = [32, 32, 16]
-    _grouped_both(16, ptr, pages, lens, kv="fp8", force=2)        # EUNSUPPORTED
+    _grouped_both(16, ptr, pages, lens, kv="fp8", force=2)        # EUNSUPPORTED (d = 64)
+    _grouped_both(16, ptr, pages, lens, kv="fp8", d=128, force=2)  # fp8 prefix kernel
     _grouped_both(16, ptr, pages, lens, G=3)                      # G = 3 not built
     plan = _grouped_both(16, ptr, pages, lens, force=1)
     assert plan.info["num_groups"] == 1 and plan.info["path_name"] == "CASCADE"

@@ -309,11 +309,18 @@ def test_planner_gate_and_alignment():
     assert _plan(4, 4, 16, launch_bytes=0)["path"] == "PAGED"
     assert _plan(4, 4, 256, launch_bytes=0)["path"] == "CASCADE"
     assert _plan(4, 4, 256, launch_bytes=10**12)["path"] == "PAGED"
-    # fp8 K/V has no prefix kernel: paged, and forcing a prefix path is refused
-    assert _plan(256, 4, 4096, kv_dtype="fp8")["path"] == "PAGED"
+    # fp8 K/V: a prefix kernel at d = 128 (the gate counts one byte per
+    # value); none at d = 64, where forcing a prefix path is refused
+    assert _plan(256, 4, 4096, kv_dtype="fp8")["path"] == "DENSE"     # M_eff = 1024 at the A100 threshold
+    assert _plan(256, 4, 4096, d=64, kv_dtype="fp8")["path"] == "PAGED"
     with pytest.raises(op.PlanError) as e:
-        _plan(256, 4, 4096, kv_dtype="fp8", force_path=2)
+        _plan(256, 4, 4096, d=64, kv_dtype="fp8", force_path=2)
     assert e.value.code == "EUNSUPPORTED"
+    # the gate sees half the bytes saved: 3 requests on 64 pages pass with
+    # bf16 K/V (8.4 MB saved) and not with fp8 (4.2 MB) against a 5.2 MB
+    # overhead (launch term 5 MB, R = 1)
+    assert _plan(3, 4, 1024, launch_bytes=5 * 10**6)["path"] == "CASCADE"
+    assert _plan(3, 4, 1024, launch_bytes=5 * 10**6, kv_dtype="fp8")["path"] == "PAGED"
     with pytest.raises(op.PlanError) as e:
         _plan(256, 4, 8, force_path=1)
     assert e.value.code == "EINVAL"
@@ -531,13 +538,17 @@ def test_plan_groups_is_the_single_prefix_rule_per_group():
     kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
                              page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=2, **tune)
     assert [g["path"] for g in kept] == ["DENSE", "DENSE"] and [len(g["members"]) for g in kept] == [200, 2]
-    # fp8 K/V has no prefix kernel: nothing is kept unless forced, which is refused
-    kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="fp8", page_size=p,
+    # fp8 K/V at d = 64 has no prefix kernel: nothing is kept unless forced,
+    # which is refused; at d = 128 the group is kept (half the bytes saved)
+    kept, _ = og.plan_groups(H_q=32, H_kv=8, d=64, q_dtype="bf16", kv_dtype="fp8", page_size=p,
                              page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
     assert kept == []
     with pytest.raises(op.PlanError):
-        og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="fp8", page_size=p, page_indptr=ptr,
+        og.plan_groups(H_q=32, H_kv=8, d=64, q_dtype="bf16", kv_dtype="fp8", page_size=p, page_indptr=ptr,
                        page_indices=pages, seq_lens=lens, force_path=1, **tune)
+    kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="fp8", page_size=p,
+                             page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
+    assert [len(g["members"]) for g in kept] == [200]
 
 
 def test_lower_groups_partitions_every_request():

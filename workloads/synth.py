@@ -216,6 +216,10 @@ def relayout(
         order = rng.permutation(pool_pages).astype(np.int64)
     elif perm == "identity":
         order = np.arange(pool_pages, dtype=np.int64)
+    elif perm == "prefix_first":
+        # the shared prefix in the first pages of the pool, in order (stored
+        # contiguously); every other page randomly placed after it
+        order = np.concatenate([np.arange(n_shared), n_shared + rng.permutation(pool_pages - n_shared)]).astype(np.int64)
     else:
         raise ValueError(perm)
     shared_pages = order[:n_shared]
@@ -289,8 +293,12 @@ CONFIGS = {
                kv_dtype="fp8", page_size=16, pool_factor=2),
 }
 
-CONFIG_SEED = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005}
-RELAYOUT_SEED = {"c1": 2001, "c2": 2002, "c3": 2003, "c4": 2004, "c5": 2005}
+# The shared-prefix workload with an fp8 cache: the same shapes, K/V stored
+# as e4m3 codes with per-KV-head scales (its own seed).
+CONFIGS["c3_fp8"] = dict(CONFIGS["c3"], kv_dtype="fp8")
+
+CONFIG_SEED = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c3_fp8": 1013}
+RELAYOUT_SEED = {"c1": 2001, "c2": 2002, "c3": 2003, "c4": 2004, "c5": 2005, "c3_fp8": 2013}
 
 
 def make_config(name: str, **overrides) -> DecodeBatch:
