@@ -169,6 +169,14 @@ void prefix_ranges(const pkv_tuning& tu, int64_t prefix_tokens, int64_t tiles, i
     *splits = (int32_t)ceil_div(prefix_tokens, ps);
 }
 
+// Prefix workgroups to aim for when the prefix pass shares one launch with
+// the suffix pass: a quarter of the workgroup target (measured: long prefix
+// items beside many suffix chunks beat more, shorter items), at most the
+// unfused target.
+int64_t fused_prefix_target(const pkv_tuning& tu) {
+    return std::max<int64_t>(1, std::min<int64_t>(tu.prefix_target_workgroups, tu.target_workgroups / 4));
+}
+
 // Paged-pass chunking over `total` positions, n_of(b) of them request b's:
 // chunk size from the workgroup target, partial states per request.
 template <class LenFn>
@@ -369,21 +377,6 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     // fp8 K/V at head_dim 128)
     pl->fuse_cascade = tu.fuse_cascade && path == PKV_PATH_DENSE;
 
-    // Prefix pass: M_eff query rows per KV head in tiles, the prefix cut into
-    // ranges so that the grid fills the GPU.
-    pl->prefix_rows_per_wg = path == PKV_PATH_DENSE ? pkv::kDenseRowsPerWg : pkv::kTiledRowsPerWg;
-    pl->prefix_split_tokens = 0;
-    pl->prefix_splits = 0;
-    if (path != PKV_PATH_PAGED) {
-        const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
-        prefix_ranges(tu, prefix_tokens, tiles, tu.prefix_target_workgroups, &pl->prefix_split_tokens,
-                      &pl->prefix_splits);
-    }
-    // Workgroups of the prefix pass (a multiple of 8 for the XCD placement).
-    const int64_t prefix_wgs =
-        pl->prefix_splits ? align_up((int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg) * pl->prefix_splits, 8)
-                          : 0;
-
     // Paged pass: the attended positions [prefix_tokens, L_b) of all
     // requests, request after request, form one flat sequence that is cut
     // into equal chunks, one workgroup per (chunk, head block).
@@ -392,14 +385,34 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     };
     int64_t total = 0;
     for (int32_t b = 0; b < B; ++b) total += n_of(b);
-    // One launch runs both passes of a DENSE step when the prefix pass is
-    // heavy enough to hide suffix streaming under it and its items take at
-    // most half of the workgroup slots; the suffix chunks then fill the rest.
-    if (pl->fuse_cascade) {
-        const int64_t prefix_flops = 4 * m_eff * prefix_tokens * D * H_kv;
-        const int64_t suffix_bytes = total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
-        if (2 * prefix_wgs > tu.target_workgroups || prefix_flops < (int64_t)tu.fuse_cascade * suffix_bytes)
-            pl->fuse_cascade = 0;
+
+    // Prefix pass: M_eff query rows per KV head in tiles, the prefix cut into
+    // ranges so that the grid fills the GPU.  One launch runs both passes of
+    // a DENSE step when the prefix pass is heavy enough to hide suffix
+    // streaming under it (fuse_cascade MFMA flops per suffix byte); its
+    // prefix ranges then aim at a quarter of the workgroup target (long
+    // items, most slots left to the suffix chunks), and it fuses only if the
+    // prefix items take at most half of the slots.
+    pl->prefix_rows_per_wg = path == PKV_PATH_DENSE ? pkv::kDenseRowsPerWg : pkv::kTiledRowsPerWg;
+    pl->prefix_split_tokens = 0;
+    pl->prefix_splits = 0;
+    int64_t prefix_wgs = 0;
+    if (path != PKV_PATH_PAGED) {
+        const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
+        if (pl->fuse_cascade) {
+            const int64_t prefix_flops = 4 * m_eff * prefix_tokens * D * H_kv;
+            const int64_t suffix_bytes = total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+            pl->fuse_cascade = prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes;
+        }
+        if (pl->fuse_cascade) {
+            prefix_ranges(tu, prefix_tokens, tiles, fused_prefix_target(tu), &pl->prefix_split_tokens,
+                          &pl->prefix_splits);
+            prefix_wgs = align_up(tiles * pl->prefix_splits, 8);  // a multiple of 8 for the XCD placement
+            pl->fuse_cascade = 2 * prefix_wgs <= tu.target_workgroups;
+        }
+        if (!pl->fuse_cascade)
+            prefix_ranges(tu, prefix_tokens, tiles, tu.prefix_target_workgroups, &pl->prefix_split_tokens,
+                          &pl->prefix_splits);
     }
     int64_t target = tu.target_workgroups;
     if (pl->fuse_cascade) target -= prefix_wgs;
@@ -517,21 +530,46 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     }
     const int32_t NG = (int32_t)groups.size();
 
+    // Own tokens of every request (all of them without a kept group).
+    int64_t suffix_total = 0;
+    for (int32_t b = 0; b < B; ++b)
+        suffix_total += seq_lens[b] - (group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0);
+
     // Prefix ranges: each group gets the share of the prefix pass's target
     // workgroups that its flops (M_eff x P) are of the step's, and is cut
-    // as a single-prefix step with that target would be.
+    // as a single-prefix step with that target would be.  When every group
+    // runs DENSE the two passes may share one launch under the single-prefix
+    // step's rule (flops per suffix byte; ranges against the fused target;
+    // prefix items at most half the slots).
     unsigned __int128 work = 0;
-    for (auto& g : groups) work += (unsigned __int128)g.m_eff * g.prefix_tokens;
+    int64_t prefix_flops = 0;
+    bool all_dense = NG > 0;
+    for (auto& g : groups) {
+        work += (unsigned __int128)g.m_eff * g.prefix_tokens;
+        prefix_flops += 4LL * g.m_eff * g.prefix_tokens * D * H_kv;
+        all_dense &= g.path == PKV_PATH_DENSE;
+    }
     int64_t dense_items = 0, tiled_items = 0;
     int32_t max_splits = 0;
-    for (auto& g : groups) {
-        const int64_t share = (int64_t)((unsigned __int128)tu.prefix_target_workgroups * g.m_eff * g.prefix_tokens / work);
-        prefix_ranges(tu, g.prefix_tokens, (int64_t)H_kv * g.row_tiles, std::max<int64_t>(1, share), &g.split_tokens,
-                      &g.splits);
-        g.items = (int64_t)g.row_tiles * H_kv * g.splits;
-        (g.path == PKV_PATH_DENSE ? dense_items : tiled_items) += g.items;
-        max_splits = std::max(max_splits, g.splits);
+    const auto plan_ranges = [&](int64_t target) {
+        dense_items = tiled_items = 0;
+        max_splits = 0;
+        for (auto& g : groups) {
+            const int64_t share = (int64_t)((unsigned __int128)target * g.m_eff * g.prefix_tokens / work);
+            prefix_ranges(tu, g.prefix_tokens, (int64_t)H_kv * g.row_tiles, std::max<int64_t>(1, share),
+                          &g.split_tokens, &g.splits);
+            g.items = (int64_t)g.row_tiles * H_kv * g.splits;
+            (g.path == PKV_PATH_DENSE ? dense_items : tiled_items) += g.items;
+            max_splits = std::max(max_splits, g.splits);
+        }
+    };
+    const int64_t suffix_bytes = suffix_total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+    bool fuse = tu.fuse_cascade && all_dense && prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes;
+    if (fuse) {
+        plan_ranges(fused_prefix_target(tu));
+        fuse = 2 * align_up(dense_items, 8) <= tu.target_workgroups;
     }
+    if (!fuse) plan_ranges(tu.prefix_target_workgroups);
     if (dense_items > INT32_MAX || tiled_items > INT32_MAX) return PKV_EUNSUPPORTED;
 
     pkv_plan* pl = new (std::nothrow) pkv_plan();
@@ -539,6 +577,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     fill_problem(pl, pr, tu, geo);
     pl->grouped = 1;
     pl->num_groups = NG;
+    pl->fuse_cascade = fuse;
     pl->dense_items = (int32_t)dense_items;
     pl->tiled_items = (int32_t)tiled_items;
     pl->prefix_splits = max_splits;
@@ -555,9 +594,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     pl->shared_pages = (int32_t)pages_sum;
 
     // Metadata block (int32): the public arrays, then the kernels' tables.
-    int64_t suffix_total = 0, members_total = 0;
-    for (int32_t b = 0; b < B; ++b)
-        suffix_total += seq_lens[b] - (group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0);
+    int64_t members_total = 0;
     for (auto& g : groups) members_total += (int64_t)g.members.size();
     int64_t off = 0;
     const auto take = [&](int64_t n) {
@@ -627,22 +664,11 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
 
     // Paged pass over every request's suffix (all of its tokens if it is in
     // no group); with groups every request leaves partial states for the
-    // combine.  When every group runs DENSE, the two passes share one launch
-    // under the single-prefix step's rule (prefix flops per suffix byte, and
-    // at most half the workgroup slots for prefix items).
+    // combine.
     const int32_t* sptr = m + pl->meta_suffix_indptr;
     const auto n_of = [&](int32_t b) { return (int64_t)sptr[b + 1] - sptr[b]; };
     int64_t target = tu.target_workgroups;
-    if (tu.fuse_cascade && NG > 0 && tiled_items == 0) {
-        int64_t prefix_flops = 0;
-        for (auto& g : groups) prefix_flops += 4LL * g.m_eff * g.prefix_tokens * D * H_kv;
-        const int64_t suffix_bytes = suffix_total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
-        const int64_t prefix_wgs = align_up(dense_items, 8);
-        if (2 * prefix_wgs <= tu.target_workgroups && prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes) {
-            pl->fuse_cascade = 1;
-            target -= prefix_wgs;
-        }
-    }
+    if (fuse) target -= align_up(dense_items, 8);
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, suffix_total, target, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;
