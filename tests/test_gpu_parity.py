@@ -667,3 +667,34 @@ def test_fp8_fused_cascade_launch_matches_separate_launches():
         outs.append((o.float(), lse))
     assert (outs[0][0] - outs[1][0]).abs().max().item() <= 8e-3
     assert (outs[0][1] - outs[1][1]).abs().max().item() <= 1e-4
+
+
+# ------------------------------------------------------------- maximum sizes --
+
+def test_pool_larger_than_4gib_addresses_rows_past_4gib():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    # 196,608 pages of 16 slots x 8 KV heads x 128 bf16: 6.4 GB per K (and V)
+    # pool; the few live pages are scattered through all of it, so most row
+    # offsets are beyond 4 GiB
+    b = make_decode_batch(seed=61, B=3, H_q=32, H_kv=8, d=128, own_len=(200, 700), page_size=16,
+                          pool_pages=196608, device="cuda")
+    top = int(b.page_indices.max()) * 16 * 8 * 128 * 2
+    assert top > (1 << 32), top
+    o_ref, lse_ref = ob.batch_reference(b)
+    for tune in (None, dict(min_split_tokens=16, target_workgroups=100000)):
+        say(f"big pool tune={tune}")
+        o, lse, _ = run_paged(DeviceBatch, b, tuning=tune)
+        check_close("bf16", o, lse, o_ref, lse_ref, f"big pool {tune}")
+    del b
+    torch.cuda.empty_cache()
+
+
+def test_one_long_request_in_thousands_of_chunks():
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    b = make_decode_batch(seed=62, B=1, H_q=8, H_kv=2, d=128, own_len=(100_000, 100_000), page_size=16,
+                          device="cuda")
+    o_ref, lse_ref = ob.batch_reference(b)
+    say("long request, 16-token chunks")
+    o, lse, plan = run_paged(DeviceBatch, b, tuning=dict(min_split_tokens=16, target_workgroups=10**8))
+    assert plan.info["num_splits"] == 6250
+    check_close("bf16", o, lse, o_ref, lse_ref, "long request, many chunks")
