@@ -19,7 +19,9 @@ Rule, in order (all arithmetic in Python integers):
    dtype pair the prefix kernels do not handle -> PAGED;
 3. saved    = (n_shared - 1) * prefix_tokens * H_kv * d * (b_k + b_v)
    overhead = 4 * rows * (d + 1) * 4 + launch_bytes
-   saved < gate_ratio * overhead -> PAGED;
+   saved < gate_ratio * overhead -> PAGED;  (b_k, b_v: an fp8 value counts
+   as 2 bytes, the bf16 width: the library's fp8 paged pass is bound by the
+   vector ALU, so its tokens cost about the time of bf16 tokens; measured)
 4. M_eff >= t_dense -> DENSE, else CASCADE.
 
 Problem checks mirror what the library accepts: d in {64, 128}; (q, kv)
@@ -88,7 +90,8 @@ def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
         out.update(path=PAGED, prefix_tokens=0)
         return out
     rows = B * H_q
-    saved = (n_shared - 1) * prefix_tokens * H_kv * d * (BYTES[kv_dtype] * 2)
+    gate_bytes = 2 if kv_dtype == "fp8" else BYTES[kv_dtype]
+    saved = (n_shared - 1) * prefix_tokens * H_kv * d * (gate_bytes * 2)
     overhead = 4 * rows * (d + 1) * 4 + launch_bytes
     if saved < gate_ratio * overhead:
         out.update(path=PAGED, prefix_tokens=0)

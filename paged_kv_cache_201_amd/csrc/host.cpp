@@ -130,7 +130,10 @@ pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_sh
         return PKV_OK;
     }
     const int64_t D = pr->head_dim;
-    const int64_t kv_bytes = 2LL * dtype_bytes(pr->kv_dtype);
+    // An fp8 value counts as 2 bytes (bf16's width): the fp8 paged pass is
+    // bound by the vector ALU, so a token of it takes about as long to
+    // stream as a bf16 token (measured forced-path sweep).
+    const int64_t kv_bytes = 2LL * (pr->kv_dtype == PKV_FP8_E4M3 ? 2 : dtype_bytes(pr->kv_dtype));
     const int64_t saved = (n_shared - 1) * prefix_tokens * pr->num_kv_heads * D * kv_bytes;
     const int64_t overhead = 4 * rows * (D + 1) * 4 + tu.launch_bytes;
     if (saved < (int64_t)tu.gate_ratio * overhead)

@@ -316,11 +316,12 @@ def test_planner_gate_and_alignment():
     with pytest.raises(op.PlanError) as e:
         _plan(256, 4, 4096, d=64, kv_dtype="fp8", force_path=2)
     assert e.value.code == "EUNSUPPORTED"
-    # the gate sees half the bytes saved: 3 requests on 64 pages pass with
-    # bf16 K/V (8.4 MB saved) and not with fp8 (4.2 MB) against a 5.2 MB
-    # overhead (launch term 5 MB, R = 1)
-    assert _plan(3, 4, 1024, launch_bytes=5 * 10**6)["path"] == "CASCADE"
-    assert _plan(3, 4, 1024, launch_bytes=5 * 10**6, kv_dtype="fp8")["path"] == "PAGED"
+    # the gate counts an fp8 value at bf16's 2 bytes: 3 requests on 64 pages
+    # save 8.4 MB either way, against a 5.2 MB overhead (launch term 5 MB,
+    # R = 1) and not against a 9.2 MB one
+    for kv in ("bf16", "fp8"):
+        assert _plan(3, 4, 1024, launch_bytes=5 * 10**6, kv_dtype=kv)["path"] == "CASCADE"
+        assert _plan(3, 4, 1024, launch_bytes=9 * 10**6, kv_dtype=kv)["path"] == "PAGED"
     with pytest.raises(op.PlanError) as e:
         _plan(256, 4, 8, force_path=1)
     assert e.value.code == "EINVAL"
