@@ -109,6 +109,11 @@ pkv_status check_support(const pkv_problem* pr, const pkv_tuning& tu, pkv::Paged
     return PKV_OK;
 }
 
+// Bytes per stored value as the planner's rules count them: an fp8 value
+// counts as 2 (bf16's width), because the fp8 paged pass is bound by the
+// vector ALU and a token of it takes about as long as a bf16 token.
+int64_t rule_bytes(int32_t kv_dtype) { return kv_dtype == PKV_FP8_E4M3 ? 2 : dtype_bytes(kv_dtype); }
+
 // The dispatcher for n_shared requests on prefix_tokens shared tokens
 // (whole pages), rows query rows and M_eff = m_eff, in order: a forced path;
 // PAGED without two sharers, a shared page or a prefix kernel for the dtype
@@ -130,10 +135,7 @@ pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_sh
         return PKV_OK;
     }
     const int64_t D = pr->head_dim;
-    // An fp8 value counts as 2 bytes (bf16's width): the fp8 paged pass is
-    // bound by the vector ALU, so a token of it takes about as long to
-    // stream as a bf16 token (measured forced-path sweep).
-    const int64_t kv_bytes = 2LL * (pr->kv_dtype == PKV_FP8_E4M3 ? 2 : dtype_bytes(pr->kv_dtype));
+    const int64_t kv_bytes = 2LL * rule_bytes(pr->kv_dtype);
     const int64_t saved = (n_shared - 1) * prefix_tokens * pr->num_kv_heads * D * kv_bytes;
     const int64_t overhead = 4 * rows * (D + 1) * 4 + tu.launch_bytes;
     if (saved < (int64_t)tu.gate_ratio * overhead)
@@ -404,7 +406,7 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
         const int64_t tiles = (int64_t)H_kv * ceil_div(m_eff, pl->prefix_rows_per_wg);
         if (pl->fuse_cascade) {
             const int64_t prefix_flops = 4 * m_eff * prefix_tokens * D * H_kv;
-            const int64_t suffix_bytes = total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+            const int64_t suffix_bytes = total * H_kv * D * 2 * rule_bytes(pr->kv_dtype);
             pl->fuse_cascade = prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes;
         }
         if (pl->fuse_cascade) {
@@ -566,7 +568,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
             max_splits = std::max(max_splits, g.splits);
         }
     };
-    const int64_t suffix_bytes = suffix_total * H_kv * D * 2 * dtype_bytes(pr->kv_dtype);
+    const int64_t suffix_bytes = suffix_total * H_kv * D * 2 * rule_bytes(pr->kv_dtype);
     bool fuse = tu.fuse_cascade && all_dense && prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes;
     if (fuse) {
         plan_ranges(fused_prefix_target(tu));
