@@ -66,3 +66,41 @@ def test_unused_slots_are_poison():
     used.update(kv_indices.tolist())
     unused = [s for s in range(b.num_slots) if s not in used]
     assert torch.isnan(b.k_pool[unused]).all()
+
+
+# ------------------------------------------------------------ grouped batches --
+
+from workloads import make_grouped_batch  # noqa: E402
+from oracle import groups as og  # noqa: E402
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("p", [1, 4, 16])
+def test_grouped_pool_holds_logical_tokens_and_the_groups(kv, p):
+    groups = [(4, 37), (3, 16), (2, 5)]
+    b = make_grouped_batch(seed=9, B=12, H_q=8, H_kv=2, d=64, groups=groups, own_len=(0, 30), page_size=p,
+                           kv_dtype=kv, pool_factor=2)
+    _gathered_matches_logical(b)
+    # the requests drawn on a prefix share exactly its whole pages, so the
+    # oracle's grouping finds the drawn groups (a prefix shorter than one
+    # page shares nothing)
+    found = {tuple(g["members"]): g["shared_pages"] for g in
+             og.detect_prefix_groups(p, b.page_indptr, b.page_indices, b.seq_lens)}
+    want = {}
+    for g, (n, P) in enumerate(groups):
+        members = tuple(int(x) for x in np.flatnonzero(b.group_of == g))
+        assert len(members) == n
+        if P // p >= 1:
+            want[members] = P // p
+    # own tokens never share a page, but a whole-page prefix run can be
+    # followed by nothing else in common
+    assert found == want, (found, want)
+
+
+def test_grouped_unused_slots_are_poison():
+    b = make_grouped_batch(seed=3, B=6, H_q=8, H_kv=2, d=64, groups=[(3, 20)], own_len=(1, 9), page_size=4,
+                           kv_dtype="bf16", pool_factor=3)
+    kv_indptr, kv_indices = ol.lower_page_table(b.page_size, b.page_indptr, b.page_indices, b.seq_lens)
+    used = np.zeros(b.k_pool.shape[0], bool)
+    used[kv_indices] = True
+    assert torch.isnan(b.k_pool[torch.from_numpy(~used)].float()).all()
