@@ -216,22 +216,28 @@ PKV_API pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning*
 
 /*
  * Plan a decode step whose requests may share several prefixes, found in the
- * page table itself (host only).  [P3] block-size paragraph and table of
- * prompt-layout mistakes: prefix matching is exact and aligned to blocks from
- * the start of a sequence, so requests share a prefix exactly when their page
- * tables start with the same physical pages (two system prompts make two
- * separate trees); [P2] s.2-3: each shared prefix is read once for the
- * requests on it, with its own dispatcher decision from its own realized
- * batch.  Rules:
+ * page table itself (host only).  [P3] block-size paragraph, table of
+ * prompt-layout mistakes and engine comparison: prefix matching is exact and
+ * aligned to blocks from the start of a sequence (two system prompts make two
+ * separate trees), and a prefix cache keeps its matches as a radix tree keyed
+ * on shared beginnings, so requests share a run of pages exactly when their
+ * page tables name the same physical pages there; [P2] s.2-3: each shared
+ * run is read once for the requests on it, with its own dispatcher decision
+ * from its own realized batch.  Rules:
  *   - a request holds floor(L_b / page_size) whole pages; a partly filled
  *     last page is never shared;
- *   - requests whose first whole page is the same physical page form a
- *     group; its shared pages are the longest leading run of pages that every
- *     member holds whole and all members agree on; a group needs two members;
+ *   - the groups are the nodes of the radix tree of the requests' page lists
+ *     that two or more requests share: requests whose first whole page is the
+ *     same physical page form a root; a group's run is the longest stretch of
+ *     pages, from where its parent's run ends, that every member holds whole
+ *     and all agree on; members that hold the page after it and agree on it
+ *     form a child group (two or more of them);
  *   - each group is planned as pkv_plan_create plans a step of its members
- *     alone with its shared tokens as the declared prefix (gate, DENSE or
- *     CASCADE, force_path); a group planned PAGED is dissolved;
- *   - groups are numbered by their first member, members in request order.
+ *     alone with its run's tokens as the declared prefix (gate, DENSE or
+ *     CASCADE, force_path); a group planned PAGED is dissolved (its run is
+ *     read in the paged pass; its children are still planned);
+ *   - groups are numbered depth first (parents first, siblings by first
+ *     member), members in request order.
  * The problem's kv_indptr is ignored (may be NULL) and its shared_prefix_len
  * must be 0.  page_indptr [B+1], page_indices, seq_lens [B] are host arrays
  * as for pkv_lower_page_table, read during the call.  The plan holds the
@@ -239,7 +245,8 @@ PKV_API pkv_status pkv_plan_create(const pkv_problem* problem, const pkv_tuning*
  * which the caller copies to the device once for pkv_decode_step_grouped.
  * Plan info: path is PAGED without groups, DENSE if a group runs DENSE, else
  * CASCADE; m_eff is the largest group's; shared_pages and prefix_tokens are
- * summed over groups; prefix_splits is the most ranges of any group.
+ * summed over the groups' runs; prefix_splits is the most prefix partial
+ * states of any request (the ranges of all of its groups).
  * Errors: as pkv_plan_create and pkv_lower_page_table; EINVAL also for a
  * non-zero shared_prefix_len.
  */
@@ -252,13 +259,13 @@ PKV_API pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv
  * to host memory out[capacity].  Layout, each array right after the one
  * before (NG = info.num_groups):
  *   suffix_indptr  [B+1]   token offsets of each request's own tokens
- *   suffix_indices [suffix_indptr[B]]  slots of request b's tokens after its
- *                  group's shared tokens (all of its tokens without a group)
+ *   suffix_indices [suffix_indptr[B]]  slots of request b's tokens outside
+ *                  the runs of its kept groups, in logical order
  *   group_indptr   [NG+1]  offsets into group_members
  *   group_members  [group_indptr[NG]]  requests of each group
  *   prefix_indptr  [NG+1]  offsets into prefix_indices
- *   prefix_indices [prefix_indptr[NG]]  slots of each group's shared tokens
- *   request_group  [B]     group of each request, -1 for none
+ *   prefix_indices [prefix_indptr[NG]]  slots of each group's run of tokens
+ *   group_parent   [NG]    nearest enclosing kept group, -1 for none
  *   followed by tables only the kernels read.
  * Errors: EINVAL (null plan, plan not from pkv_plan_create_grouped, null out
  * with a non-empty block), ERANGE (capacity too small).
@@ -379,11 +386,12 @@ PKV_API pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pk
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One decode step of a grouped plan: one prefix pass over every group's
- * shared tokens (each read once for the group's requests; DENSE groups and
- * CASCADE groups in one launch each), the paged pass over every request's
- * suffix, and one kernel that combines, per row, its group's prefix ranges
- * and its suffix chunks into o (and lse).  The result is that of attention
+ * One decode step of a grouped plan: one prefix pass over every group's run
+ * (each read once for the group's requests; DENSE groups and CASCADE groups
+ * in one launch each, or with the suffix pass in one launch when every group
+ * is DENSE), the paged pass over every request's suffix, and one kernel that
+ * combines, per row, the prefix ranges of all its groups and its suffix
+ * chunks into o (and lse).  The result is that of attention
  * over each request's whole sequence.
  *   metadata  device copy of the plan's metadata block (pkv_plan_metadata)
  * Other arguments as pkv_decode_step; o is required, lse is nullable.

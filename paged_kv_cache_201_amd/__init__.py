@@ -251,7 +251,7 @@ def split_metadata(block, batch, num_groups):
     out, off = {}, 0
     for name, n in (("suffix_indptr", batch + 1), ("suffix_indices", None), ("group_indptr", num_groups + 1),
                     ("group_members", None), ("prefix_indptr", num_groups + 1), ("prefix_indices", None),
-                    ("request_group", batch)):
+                    ("group_parent", num_groups)):
         if n is None:
             ptr = out[{"suffix_indices": "suffix_indptr", "group_members": "group_indptr",
                        "prefix_indices": "prefix_indptr"}[name]]

@@ -482,63 +482,109 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     }
     if (total_tokens > INT32_MAX || (int64_t)B * G > INT32_MAX) return PKV_ERANGE;
 
-    // Groups: requests whose first whole page is the same physical page, in
-    // the order of their first member; shared pages = the leading run of
-    // pages that every member holds in full and all members agree on.
-    std::unordered_map<int32_t, int32_t> root_of;  // first page -> candidate
-    std::vector<std::vector<int32_t>> cand;
-    for (int32_t b = 0; b < B; ++b) {
-        if (seq_lens[b] / p == 0) continue;
-        const int32_t root = page_indices[page_indptr[b]];
-        auto it = root_of.find(root);
-        if (it == root_of.end()) {
-            root_of.emplace(root, (int32_t)cand.size());
-            cand.push_back({b});
-        } else {
-            cand[it->second].push_back(b);
+    // Groups: the nodes of the radix tree of the requests' page lists that
+    // two or more requests share.  Requests whose first whole page is the
+    // same physical page form a root; a group's run is the longest stretch
+    // of pages from its parent's end that every member holds in full and
+    // all agree on; members that hold the page after the run and agree on it
+    // form a child (two or more of them).  Depth-first order, parents before
+    // children, siblings by first member.
+    struct Node {
+        std::vector<int32_t> members;
+        int32_t start, end, parent;
+    };
+    std::vector<Node> nodes;
+    // members of `mem` holding page `at` in full, grouped by that page, in
+    // order of first member; groups of two or more only
+    const auto split = [&](const std::vector<int32_t>& mem, int32_t at) {
+        std::unordered_map<int32_t, int32_t> slot;
+        std::vector<std::vector<int32_t>> parts;
+        for (int32_t b : mem) {
+            if (seq_lens[b] / p <= at) continue;
+            const int32_t pg = page_indices[page_indptr[b] + at];
+            auto it = slot.find(pg);
+            if (it == slot.end()) {
+                slot.emplace(pg, (int32_t)parts.size());
+                parts.push_back({b});
+            } else {
+                parts[it->second].push_back(b);
+            }
+        }
+        std::vector<std::vector<int32_t>> out;
+        for (auto& x : parts)
+            if (x.size() >= 2) out.push_back(std::move(x));
+        return out;
+    };
+    {
+        struct Todo {
+            std::vector<int32_t> members;
+            int32_t start, parent;
+        };
+        std::vector<Todo> stack;
+        std::vector<int32_t> all(B);
+        for (int32_t b = 0; b < B; ++b) all[b] = b;
+        auto roots = split(all, 0);
+        for (auto it = roots.rbegin(); it != roots.rend(); ++it) stack.push_back({std::move(*it), 0, -1});
+        while (!stack.empty()) {
+            Todo t = std::move(stack.back());
+            stack.pop_back();
+            int32_t end = INT32_MAX;
+            for (int32_t b : t.members) end = std::min(end, seq_lens[b] / p);
+            const int32_t* first = page_indices + page_indptr[t.members[0]];
+            for (size_t i = 1; i < t.members.size(); ++i) {
+                const int32_t* mine = page_indices + page_indptr[t.members[i]];
+                int32_t j = t.start;
+                while (j < end && mine[j] == first[j]) ++j;
+                end = j;
+            }
+            const int32_t me = (int32_t)nodes.size();
+            auto kids = split(t.members, end);
+            nodes.push_back({std::move(t.members), t.start, end, t.parent});
+            for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back({std::move(*it), end, me});
         }
     }
+    // Each group is planned as the step it would be on its own over its own
+    // run; a group planned PAGED is dissolved (its children still planned).
     struct Group {
         std::vector<int32_t> members;
-        int32_t shared_pages, prefix_tokens, path, m_eff, rows_per_wg, row_tiles, split_tokens, splits;
+        int32_t start_tokens, prefix_tokens, parent, path, m_eff, rows_per_wg, row_tiles, split_tokens, splits;
+        int32_t slot_base;
         int64_t items;
     };
     std::vector<Group> groups;
-    std::vector<int32_t> group_of(B, -1);
-    for (auto& mem : cand) {
-        if (mem.size() < 2) continue;
-        int32_t k = INT32_MAX;
-        for (int32_t b : mem) k = std::min(k, seq_lens[b] / p);
-        const int32_t* first = page_indices + page_indptr[mem[0]];
-        for (size_t i = 1; i < mem.size(); ++i) {
-            const int32_t* mine = page_indices + page_indptr[mem[i]];
-            int32_t j = 0;
-            while (j < k && mine[j] == first[j]) ++j;
-            k = j;
-        }
-        // each group is planned as the step it would be on its own
-        const int64_t n = (int64_t)mem.size();
+    std::vector<int32_t> kept_at(nodes.size(), -1);
+    std::vector<std::vector<int32_t>> path_of(B);  // kept groups of each request, outermost first
+    for (size_t i = 0; i < nodes.size(); ++i) {
+        const Node& nd = nodes[i];
+        const int64_t n = (int64_t)nd.members.size();
         int32_t path;
-        st = choose_path(pr, tu, n, (int64_t)k * p, n * H_q, n * G, &path);
+        st = choose_path(pr, tu, n, (int64_t)(nd.end - nd.start) * p, n * H_q, n * G, &path);
         if (st != PKV_OK) return st;
         if (path == PKV_PATH_PAGED) continue;
+        int32_t a = nd.parent;  // nearest kept ancestor
+        while (a >= 0 && kept_at[a] < 0) a = nodes[a].parent;
         Group g;
-        g.members = mem;
-        g.shared_pages = k;
-        g.prefix_tokens = k * p;
+        g.members = nd.members;
+        g.start_tokens = nd.start * p;
+        g.prefix_tokens = (nd.end - nd.start) * p;
+        g.parent = a >= 0 ? kept_at[a] : -1;
         g.path = path;
         g.m_eff = (int32_t)(n * G);
         g.rows_per_wg = path == PKV_PATH_DENSE ? pkv::kDenseRowsPerWg : pkv::kTiledRowsPerWg;
         g.row_tiles = (int32_t)ceil_div(g.m_eff, g.rows_per_wg);
-        for (int32_t b : mem) group_of[b] = (int32_t)groups.size();
+        kept_at[i] = (int32_t)groups.size();
+        for (int32_t b : nd.members) path_of[b].push_back(kept_at[i]);
         groups.push_back(std::move(g));
     }
     const int32_t NG = (int32_t)groups.size();
 
-    // Own tokens of every request (all of them without a kept group).
+    // Own tokens of every request: all of its tokens outside the runs of
+    // its kept groups.
     int64_t suffix_total = 0;
-    for (int32_t b = 0; b < B; ++b)
-        suffix_total += seq_lens[b] - (group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0);
+    for (int32_t b = 0; b < B; ++b) {
+        suffix_total += seq_lens[b];
+        for (int32_t gi : path_of[b]) suffix_total -= groups[gi].prefix_tokens;
+    }
 
     // Prefix ranges: each group gets the share of the prefix pass's target
     // workgroups that its flops (M_eff x P) are of the step's, and is cut
@@ -575,6 +621,13 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         fuse = 2 * align_up(dense_items, 8) <= tu.target_workgroups;
     }
     if (!fuse) plan_ranges(tu.prefix_target_workgroups);
+    // A request's prefix partial states: its groups' ranges, outermost group
+    // first (each group's slots start after its kept ancestors').
+    int32_t max_slots = 0;
+    for (auto& g : groups) {
+        g.slot_base = g.parent >= 0 ? groups[g.parent].slot_base + groups[g.parent].splits : 0;
+        max_slots = std::max(max_slots, g.slot_base + g.splits);
+    }
     if (dense_items > INT32_MAX || tiled_items > INT32_MAX) return PKV_EUNSUPPORTED;
 
     pkv_plan* pl = new (std::nothrow) pkv_plan();
@@ -585,7 +638,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     pl->fuse_cascade = fuse;
     pl->dense_items = (int32_t)dense_items;
     pl->tiled_items = (int32_t)tiled_items;
-    pl->prefix_splits = max_splits;
+    pl->prefix_splits = max_slots;
     pl->path = PKV_PATH_PAGED;
     int64_t prefix_sum = 0, pages_sum = 0;
     for (auto& g : groups) {
@@ -593,7 +646,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         else if (pl->path == PKV_PATH_PAGED) pl->path = PKV_PATH_CASCADE;
         pl->m_eff = std::max(pl->m_eff, g.m_eff);
         prefix_sum += g.prefix_tokens;
-        pages_sum += g.shared_pages;
+        pages_sum += g.prefix_tokens / p;
     }
     pl->prefix_tokens = (int32_t)prefix_sum;
     pl->shared_pages = (int32_t)pages_sum;
@@ -613,7 +666,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     pl->meta_members = take(members_total);
     pl->meta_prefix_indptr = take(NG + 1);
     pl->meta_prefix_indices = take(prefix_sum);
-    pl->meta_request_group = take(B);
+    pl->meta_group_parent = take(NG);
     pl->meta_pre_count = take(B);
     pl->meta_desc = take((int64_t)NG * pkv::kGroupDescInts);
     std::unique_ptr<pkv_plan> owner(pl);
@@ -628,9 +681,18 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         int32_t* idx = m + pl->meta_suffix_indices;
         ptr[0] = 0;
         for (int32_t b = 0; b < B; ++b) {
-            const int32_t skip = group_of[b] >= 0 ? groups[group_of[b]].prefix_tokens : 0;
-            lower(b, skip, seq_lens[b], idx + ptr[b]);
-            ptr[b + 1] = ptr[b] + (seq_lens[b] - skip);
+            // the tokens outside the runs of b's kept groups (outermost
+            // first, so the runs come in increasing position)
+            int32_t t = 0, n = 0;
+            for (int32_t gi : path_of[b]) {
+                const Group& g = groups[gi];
+                lower(b, t, g.start_tokens, idx + ptr[b] + n);
+                n += g.start_tokens - t;
+                t = g.start_tokens + g.prefix_tokens;
+            }
+            lower(b, t, seq_lens[b], idx + ptr[b] + n);
+            n += seq_lens[b] - t;
+            ptr[b + 1] = ptr[b] + n;
         }
         int32_t* gptr = m + pl->meta_group_indptr;
         int32_t* mem = m + pl->meta_members;
@@ -641,12 +703,13 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
             const Group& g = groups[i];
             std::copy(g.members.begin(), g.members.end(), mem + gptr[i]);
             gptr[i + 1] = gptr[i] + (int32_t)g.members.size();
-            lower(g.members[0], 0, g.prefix_tokens, pidx + pptr[i]);
+            lower(g.members[0], g.start_tokens, g.start_tokens + g.prefix_tokens, pidx + pptr[i]);
             pptr[i + 1] = pptr[i] + g.prefix_tokens;
         }
+        for (int32_t i = 0; i < NG; ++i) m[pl->meta_group_parent + i] = groups[i].parent;
         for (int32_t b = 0; b < B; ++b) {
-            m[pl->meta_request_group + b] = group_of[b];
-            m[pl->meta_pre_count + b] = group_of[b] >= 0 ? groups[group_of[b]].splits : 0;
+            const int32_t last = path_of[b].empty() ? -1 : path_of[b].back();
+            m[pl->meta_pre_count + b] = last >= 0 ? groups[last].slot_base + groups[last].splits : 0;
         }
         // group table in launch order: DENSE groups' items, then CASCADE's
         int32_t row = 0, end = 0;
@@ -664,6 +727,8 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
                 d[5] = g.row_tiles;
                 d[6] = gptr[i];
                 d[7] = (int32_t)g.members.size();
+                d[8] = g.slot_base;
+                d[9] = 0;
             }
     }
 
@@ -677,7 +742,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, suffix_total, target, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;
-    layout_workspace(pl, NG > 0 || spans, max_splits);
+    layout_workspace(pl, NG > 0 || spans, max_slots);
     *out = owner.release();
     return PKV_OK;
 }

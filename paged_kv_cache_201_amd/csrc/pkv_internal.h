@@ -39,8 +39,8 @@ constexpr int32_t kPrefixTokenQuantum = 64;
 // Ints per row of the prefix-group table a grouped step hands the prefix
 // kernel: running end of the group's items, offset and length of its prefix
 // indices, range size, ranges, query-row tiles, offset and count of its
-// members.
-constexpr int32_t kGroupDescInts = 8;
+// members, first partial-state slot of its ranges, one unused.
+constexpr int32_t kGroupDescInts = 10;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // Paged-pass chunks hold a multiple of this many tokens, and at most
 // max_chunk_tokens(...): the kernel stages a chunk's slot indices in LDS next
@@ -87,6 +87,6 @@ struct pkv_plan {
     int32_t dense_items, tiled_items; // prefix work items per launch
     // offsets (in ints) of the metadata block's arrays
     int64_t meta_suffix_indptr, meta_suffix_indices, meta_group_indptr, meta_members;
-    int64_t meta_prefix_indptr, meta_prefix_indices, meta_request_group, meta_pre_count, meta_desc;
+    int64_t meta_prefix_indptr, meta_prefix_indices, meta_group_parent, meta_pre_count, meta_desc;
     std::vector<int32_t> meta;        // the block itself, copied out by pkv_plan_metadata
 };

@@ -139,6 +139,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     int M = a.B * a.G;
     const int32_t* prefix = a.prefix_indices;
     const int32_t* members = nullptr;
+    int slot_base = 0;  // first partial-state slot of this group's ranges
     if (a.groups) {
         item += a.item_base;
         int lo = 0, hi = a.num_groups - 1;
@@ -155,6 +156,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         row_tiles = gd[5];
         members = a.members + gd[6];
         M = gd[7] * a.G;
+        slot_base = gd[8];
     }
     const int tile = item % row_tiles;
     const int g = (item / row_tiles) % a.H_kv;
@@ -453,7 +455,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         scale = L > 0.f ? 1.f / L : 0.f;
         if constexpr (F8) scale *= a.v_scale[g];
     } else {
-        out = a.part_acc + (((size_t)rb * a.num_splits + split) * H_q + rq) * D;
+        out = a.part_acc + (((size_t)rb * a.num_splits + slot_base + split) * H_q + rq) * D;
         scale = F8 ? a.v_scale[g] : 1.f;
     }
 #pragma unroll
@@ -468,7 +470,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         if (direct) {
             a.lse[qrow] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
         } else {
-            float* ml = a.part_ml + (((size_t)rb * a.num_splits + split) * H_q + rq) * 2;
+            float* ml = a.part_ml + (((size_t)rb * a.num_splits + slot_base + split) * H_q + rq) * 2;
             ml[0] = m;
             ml[1] = L;
         }

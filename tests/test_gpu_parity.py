@@ -698,3 +698,24 @@ def test_one_long_request_in_thousands_of_chunks():
     o, lse, plan = run_paged(DeviceBatch, b, tuning=dict(min_split_tokens=16, target_workgroups=10**8))
     assert plan.info["num_splits"] == 6250
     check_close("bf16", o, lse, o_ref, lse_ref, "long request, many chunks")
+
+
+# --------------------------------------------------------- nested prefixes --
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_nested_prefix_groups_vs_oracle(kv):
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    from workloads import make_tree_batch
+    # a system prompt under two conversations (one with a longer shared
+    # branch), a second prompt, and loners; runs cross page boundaries
+    tree = [(14, 700, -1), (6, 300, 0), (5, 250, 0), (3, 120, 1), (4, 333, -1)]
+    b = make_tree_batch(seed=507, B=24, H_q=32, H_kv=8, d=128, tree=tree, own_len=(0, 90), page_size=16,
+                        kv_dtype=kv)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    for t in (dict(gate_ratio=0), dict(gate_ratio=0, t_dense=40), dict(gate_ratio=0, fuse_cascade=0)):
+        plan = db.plan_grouped(tuning=t)
+        meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), b.B, plan.info["num_groups"])
+        assert plan.info["num_groups"] == 5 and (meta["group_parent"] >= 0).sum() == 3
+        o, lse = _grouped_run(db, plan)
+        check_close(kv, o, lse, o_ref, lse_ref, f"nested {kv} {t}")

@@ -262,29 +262,29 @@ def _grouped_both(p, ptr, pages, lens, G=4, H_kv=2, d=64, q="bf16", kv="bf16", f
     assert err_ref == err_got, (err_ref, err_got)
     if ref is None:
         return None
-    kept, group_of = ref
+    kept, path_of = ref
     info = plan.info
     NG = info["num_groups"]
     assert NG == len(kept)
     meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), B, NG)
-    assert list(meta["request_group"]) == group_of
+    assert list(meta["group_parent"]) == [g["parent"] for g in kept]
     gptr = meta["group_indptr"]
     for i, g in enumerate(kept):
         assert list(meta["group_members"][gptr[i]:gptr[i + 1]]) == g["members"]
-    s_ptr, s_idx, p_ptr, p_idx = og.lower_groups(p, ptr, pages, lens, kept, group_of)
+    s_ptr, s_idx, p_ptr, p_idx = og.lower_groups(p, ptr, pages, lens, kept, path_of)
     assert np.array_equal(meta["suffix_indptr"], s_ptr) and np.array_equal(meta["suffix_indices"], s_idx)
     assert np.array_equal(meta["prefix_indptr"], p_ptr) and np.array_equal(meta["prefix_indices"], p_idx)
     want_path = "PAGED" if not kept else ("DENSE" if any(g["path"] == "DENSE" for g in kept) else "CASCADE")
     assert info["path_name"] == want_path
     assert info["m_eff"] == max([g["m_eff"] for g in kept], default=0)
-    assert info["shared_pages"] == sum(g["shared_pages"] for g in kept)
+    assert info["shared_pages"] == sum(g["prefix_tokens"] // p for g in kept)
     assert info["prefix_tokens"] == sum(g["prefix_tokens"] for g in kept)
     return plan
 
 
 def test_grouped_plan_matches_oracle_on_random_tables():
     rng = np.random.default_rng(3)
-    n_kept = 0
+    n_kept = n_nested = 0
     for it in range(300):
         p = int(rng.choice([1, 2, 4, 16]))
         reqs, lens = random_group_tables(rng, p, max_batch=12)
@@ -292,8 +292,11 @@ def test_grouped_plan_matches_oracle_on_random_tables():
         tune = dict(t_dense=int(rng.integers(1, 40)), gate_ratio=int(rng.integers(0, 2)),
                     launch_bytes=int(rng.integers(0, 3)) * 1000)
         plan = _grouped_both(p, ptr, pages, lens, force=int(rng.choice([-1, -1, 0, 1, 2])), tune=tune)
-        n_kept += plan.info["num_groups"] if plan is not None else 0
-    assert n_kept > 100
+        if plan is not None:
+            n_kept += plan.info["num_groups"]
+            meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), len(lens), plan.info["num_groups"])
+            n_nested += int((meta["group_parent"] >= 0).sum())
+    assert n_kept > 100 and n_nested > 10
 
 
 def test_grouped_plan_errors_match_oracle_and_abi():

@@ -472,7 +472,7 @@ def check_group_golden(detect, golden_dir):
         reqs, lens = golden_group_case(c, p)
         for seed in (0, 1):
             ptr, pages = tables_from_blocks(reqs, p, seed)
-            got = detect(p, ptr, pages, lens)
+            got = [{"members": g["members"], "shared_pages": g["shared_pages"]} for g in detect(p, ptr, pages, lens)]
             want = [{"members": x["members"], "shared_pages": x["shared_blocks"]} for x in c["groups"]]
             assert got == want, (c["name"], got)
 
@@ -482,26 +482,33 @@ def test_prefix_groups_golden(golden_dir):
 
 
 def _groups_bruteforce(p, ptr, pages, lens):
-    """Pairwise statement of the grouping: two requests are grouped when they
-    hold the same physical page as first full page; a group's shared pages
-    are the largest k for which every member holds k full pages and all
-    members agree on the first k pages."""
+    """The tree from its definition by prefixes: for every request b and
+    page count k, the set of requests whose first k whole pages are b's;
+    each distinct such set with two or more members is a group, its run
+    ending at the largest k that gives the set and starting at the largest k
+    that gives a strictly larger set (0 if none).  Returned as a set of
+    (members, start, end, parent members)."""
     B = len(lens)
     tab = [list(pages[ptr[b]:ptr[b + 1]]) for b in range(B)]
     full = [lens[b] // p for b in range(B)]
-    seen, out = set(), []
+    sets = {}
     for b in range(B):
-        if b in seen or full[b] == 0:
-            continue
-        mem = [c for c in range(B) if full[c] > 0 and tab[c][0] == tab[b][0]]
-        seen.update(mem)
-        if len(mem) < 2:
-            continue
-        k = 0
-        while all(full[c] >= k + 1 for c in mem) and all(tab[c][k] == tab[mem[0]][k] for c in mem):
-            k += 1
-        out.append({"members": mem, "shared_pages": k})
+        for k in range(1, full[b] + 1):
+            S = tuple(c for c in range(B) if full[c] >= k and tab[c][:k] == tab[b][:k])
+            if len(S) >= 2:
+                lo, hi = sets.get(S, (k, k))
+                sets[S] = (min(lo, k), max(hi, k))
+    out = set()
+    for S, (lo, hi) in sets.items():
+        parents = [T for T in sets if set(S) < set(T)]
+        parent = min(parents, key=len) if parents else None
+        out.add((S, lo - 1, hi, parent))
     return out
+
+
+def _as_tree(groups):
+    return {(tuple(g["members"]), g["start_pages"], g["shared_pages"],
+             tuple(groups[g["parent"]]["members"]) if g["parent"] >= 0 else None) for g in groups}
 
 
 def test_prefix_groups_match_bruteforce():
@@ -528,13 +535,13 @@ def test_plan_groups_is_the_single_prefix_rule_per_group():
     lens = [p * len(r) for r in reqs]
     ptr, pages = tables_from_blocks(reqs, p)
     tune = dict(t_dense=1024, gate_ratio=3, launch_bytes=10_000_000)
-    kept, group_of = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
-                                    page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
+    kept, path_of = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                                   page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1, **tune)
     one = op.plan(B=200, H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
                   seq_lens=lens[:200], shared_prefix_len=4096, force_path=-1, **tune)
     assert len(kept) == 1 and kept[0]["members"] == list(range(200))
     assert kept[0]["path"] == one["path"] == "CASCADE" and kept[0]["m_eff"] == 800
-    assert kept[0]["prefix_tokens"] == 4096 and group_of[:200] == [0] * 200 and group_of[200:] == [-1] * 3
+    assert kept[0]["prefix_tokens"] == 4096 and path_of[:200] == [[0]] * 200 and path_of[200:] == [[]] * 3
     # forced: every group takes the forced prefix path, the loner stays alone
     kept, _ = og.plan_groups(H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=p,
                              page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=2, **tune)
@@ -554,26 +561,32 @@ def test_plan_groups_is_the_single_prefix_rule_per_group():
 
 def test_lower_groups_partitions_every_request():
     rng = np.random.default_rng(11)
+    n_nested = 0
     for it in range(200):
         p = int(rng.choice([1, 4, 16]))
         reqs, lens = _random_group_tables(rng, p)
         ptr, pages = tables_from_blocks(reqs, p, it)
-        kept, group_of = og.plan_groups(H_q=8, H_kv=2, d=64, q_dtype="bf16", kv_dtype="bf16", page_size=p,
-                                        page_indptr=ptr, page_indices=pages, seq_lens=lens,
-                                        force_path=int(rng.choice([-1, 1, 2])), t_dense=8, gate_ratio=0,
-                                        launch_bytes=0)
-        suf_ptr, suf, pre_ptr, pre = og.lower_groups(p, ptr, pages, lens, kept, group_of)
+        kept, path_of = og.plan_groups(H_q=8, H_kv=2, d=64, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                                       page_indptr=ptr, page_indices=pages, seq_lens=lens,
+                                       force_path=int(rng.choice([-1, 1, 2])), t_dense=8, gate_ratio=0,
+                                       launch_bytes=0)
+        suf_ptr, suf, pre_ptr, pre = og.lower_groups(p, ptr, pages, lens, kept, path_of)
         kv_ptr, kv = ol.lower_page_table(p, ptr, pages, lens)
         for b in range(len(lens)):
             full = list(kv[kv_ptr[b]:kv_ptr[b + 1]])
-            mine = list(suf[suf_ptr[b]:suf_ptr[b + 1]])
-            if group_of[b] >= 0:
-                g = group_of[b]
-                shared = list(pre[pre_ptr[g]:pre_ptr[g + 1]])
-                assert len(shared) % p == 0 and len(shared) > 0
-                assert shared + mine == full        # prefix ++ suffix is the request
-            else:
-                assert mine == full
+            covered = np.zeros(len(full), bool)
+            for gi in path_of[b]:
+                g = kept[gi]
+                assert b in g["members"]
+                run = list(pre[pre_ptr[gi]:pre_ptr[gi + 1]])
+                lo = g["start_tokens"]
+                assert len(run) % p == 0 and len(run) > 0 and lo % p == 0
+                assert run == full[lo:lo + len(run)]          # the run is b's tokens there
+                assert not covered[lo:lo + len(run)].any()    # runs on a path do not overlap
+                covered[lo:lo + len(run)] = True
+            assert list(suf[suf_ptr[b]:suf_ptr[b + 1]]) == [x for x, c in zip(full, covered) if not c]
+            n_nested += len(path_of[b]) > 1
+    assert n_nested > 0
 
 
 def _mut_groups_max_run(p, ptr, pages, lens):
@@ -613,7 +626,7 @@ def check_groups_bruteforce(detect, n=400):
         p = int(rng.choice([1, 2, 4, 16]))
         reqs, lens = _random_group_tables(rng, p)
         ptr, pages = tables_from_blocks(reqs, p, it)
-        assert detect(p, ptr, pages, lens) == _groups_bruteforce(p, ptr, pages, lens)
+        assert _as_tree(detect(p, ptr, pages, lens)) == _groups_bruteforce(p, ptr, pages, lens)
 
 
 @pytest.mark.parametrize("mutant", [_mut_groups_max_run, _mut_groups_partial_page, _mut_groups_pairwise_first])

@@ -104,3 +104,23 @@ def test_grouped_unused_slots_are_poison():
     used = np.zeros(b.k_pool.shape[0], bool)
     used[kv_indices] = True
     assert torch.isnan(b.k_pool[torch.from_numpy(~used)].float()).all()
+
+
+from workloads import make_tree_batch  # noqa: E402
+
+
+@pytest.mark.parametrize("p", [1, 5, 16])
+def test_tree_pool_holds_logical_tokens_and_the_tree(p):
+    tree = [(9, 40, -1), (4, 21, 0), (3, 16, 0), (2, 9, 1), (3, 33, -1)]
+    b = make_tree_batch(seed=4, B=14, H_q=8, H_kv=2, d=64, tree=tree, own_len=(0, 20), page_size=p,
+                        kv_dtype="bf16", pool_factor=2)
+    _gathered_matches_logical(b)
+    # every drawn node whose members share at least one whole page more than
+    # its parent's is a group of the oracle's tree with exactly those members
+    found = {tuple(g["members"]) for g in og.detect_prefix_groups(p, b.page_indptr, b.page_indices, b.seq_lens)}
+    cum = {}
+    for i, (n, T, parent) in enumerate(tree):
+        cum[i] = T + (cum[parent] if parent >= 0 else 0)
+        base = cum[parent] if parent >= 0 else 0
+        if cum[i] // p > base // p:
+            assert tuple(b.node_members[i]) in found, (i, b.node_members[i], found)

@@ -14,7 +14,9 @@ from .synth import (  # noqa: F401
 from .groups import (  # noqa: F401
     GROUP_CONFIGS,
     GroupedBatch,
+    TreeBatch,
     make_group_config,
+    make_tree_batch,
     make_grouped_batch,
     random_group_tables,
     tables_from_blocks,

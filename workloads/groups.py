@@ -252,3 +252,146 @@ def make_group_config(name: str, **overrides) -> GroupedBatch:
     kw.update(overrides)
     kw.setdefault("seed", GROUP_CONFIG_SEED[name])
     return make_grouped_batch(**kw)
+
+
+@dataclass
+class TreeBatch:
+    """One decode step whose requests share runs of tokens as a tree.
+
+    Request b's logical tokens are ``tokens[b]`` (indices into the value
+    tables ``k_all``, ``v_all``): the tokens of the tree nodes on its path,
+    root first, then its own.
+    """
+
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    q_dtype: str
+    kv_dtype: str
+    page_size: int
+    tokens: list                  # per request: int64 array of token ids
+    seq_lens: np.ndarray          # int32 [B]
+    q: torch.Tensor
+    k_all: torch.Tensor           # [tokens, H_kv, d] stored dtype (cpu)
+    v_all: torch.Tensor
+    node_members: list            # per tree node: its requests
+    k_scale: Optional[np.ndarray]
+    v_scale: Optional[np.ndarray]
+    num_pages: int = 0
+    page_indptr: np.ndarray = field(default=None)
+    page_indices: np.ndarray = field(default=None)
+    k_pool: torch.Tensor = field(default=None)
+    v_pool: torch.Tensor = field(default=None)
+
+    @property
+    def G(self) -> int:
+        return self.H_q // self.H_kv
+
+    def logical_kv(self, b: int):
+        idx = torch.from_numpy(self.tokens[b])
+        return self.k_all[idx], self.v_all[idx]
+
+    def bits(self, t: torch.Tensor, dtype: str) -> np.ndarray:
+        return t.contiguous().view(_BITS_DTYPE[dtype]).numpy()
+
+
+def make_tree_batch(*, seed, B, H_q, H_kv, d, tree, own_len, q_dtype="bf16", kv_dtype="bf16", page_size=16,
+                    pool_factor=1, device=None) -> TreeBatch:
+    """Draw a batch whose requests share token runs along a tree.
+
+    ``tree = [(members, tokens, parent), ...]``, parents before children:
+    node i takes ``members`` requests from its parent's (from all requests
+    for a root), disjoint from its earlier siblings' (and from earlier
+    roots'), and adds ``tokens`` tokens.  Pages are content addressed, as a
+    prefix cache that matches exact block-aligned prefixes would lay them
+    out: two requests share a physical page exactly when their token
+    sequences agree up to the end of that page.
+
+    Draw order (one ``default_rng(seed)``): node memberships, own lengths
+    (integers, uniform inclusive), Q, K then V for the node tokens in node
+    order followed by each request's own tokens, the cast, the page
+    permutation.
+    """
+    assert H_q % H_kv == 0
+    rng = np.random.default_rng(seed)
+    taken_root = set()
+    taken_child = {}
+    members_of = []
+    for n, _, parent in tree:
+        if parent < 0:
+            free = [b for b in range(B) if b not in taken_root]
+        else:
+            used = taken_child.setdefault(parent, set())
+            free = [b for b in members_of[parent] if b not in used]
+        assert len(free) >= n, "tree does not fit the batch"
+        pick = sorted(int(x) for x in rng.permutation(free)[:n])
+        (taken_root if parent < 0 else taken_child[parent]).update(pick)
+        members_of.append(pick)
+    lo, hi = own_len
+    own = rng.integers(lo, hi + 1, size=B).astype(np.int64)
+    q32 = rng.standard_normal((B, H_q, d), dtype=np.float32)
+    node_off = np.cumsum([0] + [T for _, T, _ in tree])
+    own_off = node_off[-1] + np.concatenate([[0], np.cumsum(own)])
+    T_all = int(own_off[-1])
+    k32 = rng.standard_normal((T_all, H_kv, d), dtype=np.float32)
+    v32 = rng.standard_normal((T_all, H_kv, d), dtype=np.float32)
+    k_scale = v_scale = None
+    if kv_dtype == "fp8":
+        k_scale, v_scale = _fp8_scale(k32), _fp8_scale(v32)
+    q = _cast(q32, q_dtype)
+    k_all = _cast(k32, kv_dtype, k_scale)
+    v_all = _cast(v32, kv_dtype, v_scale)
+    del k32, v32
+    # each request's token ids: its path's node tokens, then its own
+    path = [[] for _ in range(B)]
+    for i, (n, T, parent) in enumerate(tree):
+        for b in members_of[i]:
+            path[b].append(i)
+    tokens = []
+    for b in range(B):
+        parts = [np.arange(node_off[i], node_off[i + 1]) for i in path[b]]
+        parts.append(np.arange(own_off[b], own_off[b + 1]))
+        tokens.append(np.concatenate(parts).astype(np.int64))
+    seq_lens = np.array([len(t) for t in tokens], np.int32)
+    # content-addressed pages: (previous page, this block's token ids)
+    p = int(page_size)
+    page_id, page_tokens, tables = {}, [], []
+    for b in range(B):
+        prev, tab = -1, []
+        for j in range(0, len(tokens[b]), p):
+            key = (prev, tuple(tokens[b][j:j + p]))
+            if key not in page_id:
+                page_id[key] = len(page_tokens)
+                page_tokens.append(tokens[b][j:j + p])
+            prev = page_id[key]
+            tab.append(prev)
+        tables.append(tab)
+    live = max(1, len(page_tokens))
+    pool_pages = live * pool_factor
+    perm = rng.permutation(pool_pages).astype(np.int64)
+    page_indptr = np.zeros(B + 1, np.int64)
+    for b in range(B):
+        page_indptr[b + 1] = page_indptr[b] + len(tables[b])
+    page_indices = np.array([perm[x] for t in tables for x in t], np.int64)
+
+    dev = torch.device(device) if device else torch.device("cpu")
+    dt = _TORCH_DTYPE[kv_dtype]
+    out = TreeBatch(B=B, H_q=H_q, H_kv=H_kv, d=d, q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=p, tokens=tokens,
+                    seq_lens=seq_lens, q=q, k_all=k_all, v_all=v_all, node_members=members_of, k_scale=k_scale,
+                    v_scale=v_scale)
+    pools = []
+    for src in (k_all, v_all):
+        pool = torch.empty((pool_pages, p, H_kv, d), dtype=dt)
+        if kv_dtype == "fp8":
+            pool.view(torch.uint8).fill_(0x7F)
+        else:
+            pool.fill_(float("nan"))
+        for i, ids in enumerate(page_tokens):
+            pool[int(perm[i]), :len(ids)] = src[torch.from_numpy(np.asarray(ids, np.int64))]
+        pools.append(pool.view(pool_pages * p, H_kv, d).to(dev))
+    out.num_pages = pool_pages
+    out.page_indptr = page_indptr.astype(np.int32)
+    out.page_indices = page_indices.astype(np.int32)
+    out.k_pool, out.v_pool = pools
+    return out
