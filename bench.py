@@ -1,6 +1,6 @@
 """Decode-attention benchmark on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c1,c2,...,groups4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c1,c2,...,tree4]
 
 A step is one whole decode-attention step of one layer as the planner chose
 it (pkv_decode_step: the paged pass, or prefix pass + suffix pass + merge),
@@ -12,7 +12,7 @@ The headline line is the Llama-3.1-8B-shaped layer (B=32, 32 query / 8 KV
 heads, head_dim 128, 4096 tokens each, bf16, token-flat indices at page size
 1): ``value`` is its algorithmic HBM throughput in GB/s.  The other workloads
 (tiny fp32, shared-prefix cascade, short prefix, long-context fp8, several
-prompts in one step) are reported under ``extra``.  Prints one JSON line on stdout.
+prompts in one step, prompts nested as a tree) are reported under ``extra``.  Prints one JSON line on stdout.
 """
 import argparse
 import itertools
@@ -152,32 +152,38 @@ def bench_prefix_config(name, steps, warmup, legs=None):
     return out
 
 
-def grouped_algorithmic_bytes(batch, plan_meta, rows_grouped):
+def grouped_algorithmic_bytes(batch, plan_meta, group_rows):
     """Bytes a grouped step must move: each kept group's prefix once, every
-    request's own tokens, the queries twice (both passes), the partial states
-    of the grouped rows (written and read as fp32 (o, m, l)), the output."""
+    request's own tokens, the queries twice (both passes), one partial state
+    per (kept group, member row) (written and read as fp32 (o, m, l)), the
+    output.  ``group_rows`` counts a row once per kept group on its path."""
     bkv = BYTES[batch.kv_dtype] * 2
     bq = BYTES[batch.q_dtype]
     Hkv, d, rows = batch.H_kv, batch.d, batch.B * batch.H_q
     n_pre = int(plan_meta["prefix_indptr"][-1])
     n_suf = int(plan_meta["suffix_indptr"][-1])
-    return ((n_pre + n_suf) * (Hkv * d * bkv + 4) + 2 * rows * d * bq + 4 * rows_grouped * (d + 1) * 4
+    return ((n_pre + n_suf) * (Hkv * d * bkv + 4) + 2 * rows * d * bq + 4 * group_rows * (d + 1) * 4
             + rows * d * bq)
 
 
 def bench_groups_config(name, steps, warmup):
-    """Several prompts in one step: PAGED over the shared pages, every group
-    forced to the tiled cascade, and the planner's choice (DENSE here)."""
+    """Several prompts in one step (side by side, or nested as a tree):
+    PAGED over the shared pages, every group forced to the tiled cascade,
+    and the planner's choice."""
     import numpy as np
     import torch
     import paged_kv_cache_201_amd as pkv
     from paged_kv_cache_201_amd.step import DeviceBatch
-    from workloads import make_group_config
-    b = make_group_config(name, device="cuda")
+    from workloads import make_group_config, make_tree_config
+    if name.startswith("tree"):
+        b = make_tree_config(name, device="cuda")
+        out = dict(workload=name, B=b.B, tree_node_requests=[len(m) for m in b.node_members])
+    else:
+        b = make_group_config(name, device="cuda")
+        out = dict(workload=name, B=b.B, groups=[[int(n), int(P)] for n, P in
+                                                 zip(np.bincount(b.group_of[b.group_of >= 0]), b.prefix_lens)])
     db = DeviceBatch.from_batch(b)
     o, lse = db.new_out(), db.new_lse()
-    out = dict(workload=name, B=b.B, groups=[[int(n), int(P)] for n, P in
-                                             zip(np.bincount(b.group_of[b.group_of >= 0]), b.prefix_lens)])
     plan = db.plan(force_path=0)
     ws = db.workspace(plan)
     ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
@@ -190,8 +196,7 @@ def bench_groups_config(name, steps, warmup):
         ws = db.workspace(plan)
         ms = time_steps(lambda: db.step_grouped(plan, meta, o, lse, ws), steps, warmup)
         m = pkv.split_metadata(pkv.pkv_plan_metadata(plan), b.B, plan.info["num_groups"])
-        rows_grouped = int((m["request_group"] >= 0).sum()) * b.H_q
-        nb = grouped_algorithmic_bytes(b, m, rows_grouped)
+        nb = grouped_algorithmic_bytes(b, m, len(m["group_members"]) * b.H_q)
         out[label] = dict(path=plan.info["path_name"], num_groups=plan.info["num_groups"], us_per_step=ms * 1e3,
                           algorithmic_bytes=nb, gbs=nb / (ms * 1e-3) / 1e9)
         del ws, meta
@@ -544,7 +549,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,c3_fp8,groups4")
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,c3_fp8,groups4,tree4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", metavar="CONFIG:LEG[,LEG]",
                     help="time only these legs of one shared-prefix workload (e.g. c3:paged_unique) and exit; "
@@ -664,7 +669,7 @@ def main():
             log(f"bench {name}")
             extra[name] = bench_prefix_config(name, args.steps, args.warmup)
             log(json.dumps(extra[name]))
-        elif name == "groups4":
+        elif name in ("groups4", "tree4"):
             log(f"bench {name}")
             extra[name] = bench_groups_config(name, args.steps, args.warmup)
             log(json.dumps(extra[name]))

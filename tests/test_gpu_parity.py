@@ -719,3 +719,22 @@ def test_nested_prefix_groups_vs_oracle(kv):
         assert plan.info["num_groups"] == 5 and (meta["group_parent"] >= 0).sum() == 3
         o, lse = _grouped_run(db, plan)
         check_close(kv, o, lse, o_ref, lse_ref, f"nested {kv} {t}")
+
+
+def test_nested_prefix_groups_full_size_sampled():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    from workloads import make_tree_config
+    # Llama-3.1-8B layer shape: a 2048-token system prompt under four
+    # conversations of 48 requests (1024 more shared tokens each), 64 loners
+    b = make_tree_config("tree4")
+    inner = set(int(x) for m in b.node_members for x in m)
+    reqs = [int(b.node_members[k][i]) for k in range(1, 5) for i in (0, -1)]
+    reqs += [x for x in range(b.B) if x not in inner][:2]
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan_grouped()
+    meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), b.B, plan.info["num_groups"])
+    assert plan.info["num_groups"] == 5 and plan.info["path_name"] == "DENSE"
+    assert list(meta["group_parent"]) == [-1, 0, 0, 0, 0]
+    o, lse = _grouped_run(db, plan)
+    check_close("bf16", o[reqs], lse[reqs], o_ref, lse_ref, "nested full")

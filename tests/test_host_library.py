@@ -236,7 +236,7 @@ def test_plan_workspace_and_geometry():
 
 # ------------------------------------------------------------ prefix groups --
 
-from workloads.groups import random_group_tables, tables_from_blocks  # noqa: E402
+from workloads.groups import random_group_tables, tables_from_blocks, token_blocks  # noqa: E402
 
 
 def _grouped_both(p, ptr, pages, lens, G=4, H_kv=2, d=64, q="bf16", kv="bf16", force=-1, tune=None):
@@ -353,3 +353,22 @@ def test_grouped_plan_reduces_to_the_single_prefix_plan():
             for k in ("m_eff", "shared_pages", "prefix_tokens", "prefix_splits", "split_tokens", "num_splits",
                       "num_work_items"):
                 assert g[k] == one[k], (B, P, p, k, g[k], one[k])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_grouped_plan_of_a_system_prompt_under_conversations(kv):
+    # Llama-3.1-8B layer shape: a 2048-token system prompt under four
+    # conversations of 48 requests (1024 more shared tokens each), 64 loners,
+    # own tokens 64 .. 512; the default tuning keeps all five runs
+    rng = np.random.default_rng(11)
+    p = 16
+    reqs, lens = [], []
+    for b in range(256):
+        toks = (["S"] * 2048 + [f"c{b // 48}"] * 1024) if b < 192 else []
+        toks += [f"own{b}"] * int(rng.integers(64, 513))
+        reqs.append(token_blocks(toks, p))
+        lens.append(len(toks))
+    ptr, pages = tables_from_blocks(reqs, p, 11)
+    plan = _grouped_both(p, ptr, pages, lens, H_kv=8, d=128, kv=kv)
+    meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), 256, plan.info["num_groups"])
+    assert list(meta["group_parent"]) == [-1, 0, 0, 0, 0] and plan.info["path_name"] == "DENSE"

@@ -17,6 +17,7 @@ from .groups import (  # noqa: F401
     TreeBatch,
     make_group_config,
     make_tree_batch,
+    make_tree_config,
     make_grouped_batch,
     random_group_tables,
     tables_from_blocks,

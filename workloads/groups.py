@@ -395,3 +395,22 @@ def make_tree_batch(*, seed, B, H_q, H_kv, d, tree, own_len, q_dtype="bf16", kv_
     out.page_indices = page_indices.astype(np.int32)
     out.k_pool, out.v_pool = pools
     return out
+
+
+# A system prompt under several conversations (nested sharing, the radix
+# tree of a prefix cache), at the Llama-3.1-8B layer shape: 256 requests, a
+# 2048-token prompt shared by 192 of them, four conversations of 48 requests
+# each sharing 1024 more tokens, 64 requests on nothing, own tokens
+# U{64..512}, bf16, page size 16.
+TREE_CONFIGS = {
+    "tree4": dict(B=256, H_q=32, H_kv=8, d=128, tree=[(192, 2048, -1)] + [(48, 1024, 0)] * 4,
+                  own_len=(64, 512), q_dtype="bf16", kv_dtype="bf16", page_size=16),
+}
+TREE_CONFIG_SEED = {"tree4": 1007}
+
+
+def make_tree_config(name: str, **overrides) -> TreeBatch:
+    kw = dict(TREE_CONFIGS[name])
+    kw.update(overrides)
+    kw.setdefault("seed", TREE_CONFIG_SEED[name])
+    return make_tree_batch(**kw)
