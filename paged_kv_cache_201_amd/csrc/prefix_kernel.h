@@ -50,9 +50,9 @@ constexpr float kPrefixLazySlack = 8.0f;
 #endif
 // LDS of one bf16 prefix workgroup: a ring of STAGES K and V tiles and the
 // slot indices of the workgroup's prefix range.  Tile rows are D bf16 with no
-// padding; the 16-byte chunks of row t are stored XOR-swizzled (chunk c at
-// position c ^ (t mod D/8)) so that the operand reads of 16 or 32 rows hit
-// distinct banks.
+// padding; the 16-byte chunks of row t are stored XOR-swizzled, chunk c at
+// position c ^ chunk_swizzle(t), so that both operand reads are free of bank
+// conflicts (see chunk_swizzle).
 template <int D, int KT>
 struct PrefixSmem {
     static constexpr int STAGES = PKV_PREFIX_STAGES;
@@ -98,6 +98,21 @@ __device__ __forceinline__ void wait_younger(int younger) {
         if (younger >= K) wait_vmcnt<K * PER>();
         else wait_younger<K - 1, PER>(younger);
     }
+}
+
+// Swizzle of tile row t, CPR 16-byte chunks per row.  A 256-byte row (D =
+// 128) spans all 64 LDS banks, so rows differ only by this XOR.  The K reads
+// take one chunk of eight consecutive rows per cycle group, which needs eight
+// distinct values over any eight consecutive rows; the transposed V reads
+// take two adjacent chunks (2k, 2k + 1) of four consecutive rows, which needs
+// distinct values of swizzle / 2 over any four consecutive rows.  t mod 16
+// rotated left by one bit gives both (t mod 16 alone gives the first only:
+// rows 2i and 2i + 1 then share the banks of a chunk pair).  A 128-byte row
+// (D = 64) fills half the banks, so even and odd rows never collide and
+// t mod 8 serves.  Rows 16 apart share a swizzle.
+template <int CPR>
+__host__ __device__ constexpr int chunk_swizzle(int t) {
+    return CPR == 16 ? (((t << 1) | ((t >> 3) & 1)) & 15) : (t & (CPR - 1));
 }
 
 // Number of prefix blocks to launch for N work items (a multiple of 8, see
@@ -238,7 +253,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
                 lds_copy16(static_cast<const uint8_t*>(a.v) + off, v_lds + dst);
             } else {
                 const int t = p / CPR;
-                const int c = (p % CPR) ^ (t & (CPR - 1));
+                const int c = (p % CPR) ^ chunk_swizzle<CPR>(t);
                 const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + c * 8;
                 const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
                 lds_copy16(static_cast<const uint16_t*>(a.k) + off, k_lds + dst);
@@ -254,7 +269,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
             const int st = n % S, cb = n % NBUF;
             for (int i = threadIdx.x; i < KT * D / 16; i += NT) {
                 const int t = i / (D / 16), c = 2 * (i % (D / 16));
-                const int sw = t & (CPR - 1);
+                const int sw = chunk_swizzle<CPR>(t);
                 const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(&sm.k8[st][i * 16]);
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&sm.v8[st][i * 16]);
                 const u32x4_t k0 = {fp8x2_to_bf16x2<false>(xk[0]), fp8x2_to_bf16x2<true>(xk[0]),
@@ -276,16 +291,16 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     // (h, dh) of 16 lanes covers columns db*32 + dh*16 .. +15 and tokens
     // c*16 + h*4 (+8 for the second read); lane s of the group reads token
     // s/4 of those four at columns 4*(s%4) .. +3 of the group's sixteen.
-    // Rows c*16 + r keep the swizzle of row r (16 is a multiple of CPR).
+    // Rows c*16 + r keep the swizzle of row r.
     const int tr_s = lane & 15;
     const int tr_dh = (lane >> 4) & 1;
     const int tr_row = (tr_s >> 2) + h * 4;
     const int tr_chunk = tr_dh * 2 + ((tr_s & 3) >> 1);  // chunk within a 32-column block
     const int tr_elem = (tr_s & 1) * 4;
     auto tr_off = [&](int row, int db) {
-        return row * D + (((db * 4 + tr_chunk) ^ (row & (CPR - 1))) << 3) + tr_elem;
+        return row * D + (((db * 4 + tr_chunk) ^ chunk_swizzle<CPR>(row)) << 3) + tr_elem;
     };
-    const int kr_swz = lr & (CPR - 1);  // swizzle of the K rows this lane reads
+    const int kr_swz = chunk_swizzle<CPR>(lr);  // swizzle of the K rows this lane reads (rows tb*32 + lr)
 
     f32x16_t acc[NDB];
 #pragma unroll
