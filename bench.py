@@ -299,16 +299,19 @@ def write_page_control(run_json, vmem_dir, tcc_dir, commands):
     return path
 
 
-def read_ceiling(steps=20, warmup=5, gib=4):
+def read_ceiling(steps=20, warmup=5, nbytes=4 << 30):
     """Streaming-read bandwidth of this GPU (GB/s), through the library's read
-    probe over a buffer far larger than the 256 MB Infinity Cache."""
+    probe: by default over 4 GiB, far more than the 256 MB Infinity Cache;
+    with ``nbytes`` set to a step's byte count, what one contiguous read of
+    that size reaches (launch ramp and tail included)."""
     import torch
     import paged_kv_cache_201_amd as pkv
-    n = gib << 30
+    n = nbytes // 16 * 16
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
-    # filled by the library's write probe: a write of known size for the
-    # write-traffic counter's calibration
-    pkv.pkv_stream_write_probe(buf, 0x01010101, 1024)
+    if nbytes == 4 << 30:
+        # filled by the library's write probe: a write of known size for the
+        # write-traffic counter's calibration
+        pkv.pkv_stream_write_probe(buf, 0x01010101, 1024)
     best = None
     for wgs in (512, 1024, 2048):
         out = torch.empty(wgs, dtype=torch.int32, device="cuda")
@@ -404,9 +407,10 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
     med = lambda v: sorted(v)[len(v) // 2]
-    # calibration: the read probe reads its 4 GiB buffer once; the write
-    # probe writes it once
+    # calibration: the read probe reads its 4 GiB buffer once (smaller probe
+    # reads of a step's size are left out); the write probe writes it once
     probe = [v for (k, _), vs in fetch.items() if "stream_read_kernel" in k for v in vs]
+    probe = [v for v in probe if v > 0.5 * max(probe)]
     fills = [max(vs) for (k, _), vs in write.items() if "stream_write_kernel" in k]
     nbytes = 4 << 30
     fetch_scale = nbytes / (med(probe) * 1024)
@@ -640,6 +644,9 @@ def main():
     rec1, b1, db1, plan1 = bench_paged_config("c2", args.steps, args.warmup, page_size=1)
     add_ceiling(rec1, ceiling)
     log(json.dumps(rec1))
+    # the same number of bytes as one contiguous streaming read
+    same = read_ceiling(nbytes=rec1["algorithmic_bytes"])
+    log(f"read of the step's {rec1['algorithmic_bytes'] / 1e6:.1f} MB as one stream: {same:.0f} GB/s")
     del db1
     torch.cuda.empty_cache()
     log("bench c2 p=128")
@@ -710,7 +717,10 @@ def main():
                      "frac": rec1["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "paged decode step: paged_split_kernel + split_reduce_kernel, timed together "
                                "(events cannot split one library call)",
-                     "read_ceiling_gbs": ceiling},
+                     "read_ceiling_gbs": ceiling,
+                     # one contiguous streaming read of exactly the step's bytes
+                     "read_ceiling_same_bytes_gbs": same,
+                     "frac_of_same_bytes_read": rec1["gbs"] / same},
         "cpu_baseline": cpu,
         "source_sha256": kernel_source_hash(),
         "extra": extra,

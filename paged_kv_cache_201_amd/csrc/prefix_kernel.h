@@ -115,6 +115,17 @@ __host__ __device__ constexpr int chunk_swizzle(int t) {
     return CPR == 16 ? (((t << 1) | ((t >> 3) & 1)) & 15) : (t & (CPR - 1));
 }
 
+// This lane's value and that of lane l ^ 32, exchanged between the two
+// halves of the wave in registers (gfx950 v_permlane32_swap swaps the upper
+// half of its first operand with the lower half of its second; with both
+// equal to x, lane l ends up holding x[l] and x[l ^ 32] in its two results)
+// rather than through an LDS permute, which queues behind the tile traffic.
+__device__ __forceinline__ void halves_pair(float x, float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
 // Number of prefix blocks to launch for N work items (a multiple of 8, see
 // prefix_item).
 __host__ __device__ inline int prefix_blocks(int n_items) { return (n_items + 7) / 8 * 8; }
@@ -376,7 +387,11 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        {
+            float x0, x1;
+            halves_pair(mx, x0, x1);
+            mx = fmaxf(x0, x1) * sl2;
+        }
         bf16x8_t pb[2 * NTB];
         float ps = probs(s, (m == -INFINITY) ? 0.f : -m, pb);
         const bool need = (mx > m + kPrefixLazySlack) || (m == -INFINITY && mx != -INFINITY);
@@ -460,7 +475,12 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     }
 
     // Row totals: the two halves of the wave hold disjoint tokens of a row.
-    const float L = l + __shfl_xor(l, 32);
+    float L;
+    {
+        float l0, l1;
+        halves_pair(l, l0, l1);
+        L = l0 + l1;
+    }
     if (!row_ok) return;
     const bool direct = a.num_splits == 1 && !a.force_partial;
     float* out;
