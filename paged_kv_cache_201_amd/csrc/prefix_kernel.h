@@ -249,6 +249,18 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     auto lds_copy16 = [](const void* src, uint32_t m0) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
     };
+    // The slot of the tile row each of this lane's copies reads.  They are
+    // read from LDS a tile ahead (read_slots), so that issuing a tile right
+    // after the barrier does not wait on an LDS round trip.
+    int next_slot[PER_WAVE];
+    auto read_slots = [&](int n) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int p = (wave * PER_WAVE + j) * 64 + lane;
+            next_slot[j] = s_idx[n * KT + (F8 ? p / (D / 16) : p / CPR)];
+        }
+    };
+    // Issue the copies of tile n, whose slots read_slots(n) has fetched.
     auto issue_tile = [&](int n) {
         const int stage = n % S;
 #pragma unroll
@@ -257,15 +269,14 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
             const int p = blk * 64 + lane;
             if constexpr (F8) {
                 // plain rows of D codes: chunk p is row p / (D/16), codes 16 (p mod D/16) ..
-                const int t = p / (D / 16);
-                const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + (p % (D / 16)) * 16;
+                const size_t off = (size_t)next_slot[j] * slot_stride + head_off + (p % (D / 16)) * 16;
                 const uint32_t dst = (uint32_t)(stage * KT * D + blk * 1024);
                 lds_copy16(static_cast<const uint8_t*>(a.k) + off, k_lds + dst);
                 lds_copy16(static_cast<const uint8_t*>(a.v) + off, v_lds + dst);
             } else {
                 const int t = p / CPR;
                 const int c = (p % CPR) ^ chunk_swizzle<CPR>(t);
-                const size_t off = (size_t)s_idx[n * KT + t] * slot_stride + head_off + c * 8;
+                const size_t off = (size_t)next_slot[j] * slot_stride + head_off + c * 8;
                 const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
                 lds_copy16(static_cast<const uint16_t*>(a.k) + off, k_lds + dst);
                 lds_copy16(static_cast<const uint16_t*>(a.v) + off, v_lds + dst);
@@ -430,7 +441,11 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     // vmcnt waits count only the copies.
     wait_vmcnt<0>();
     __syncthreads();  // s_idx ready
-    for (int n = 0; n < S - 1 && n < ntiles; ++n) issue_tile(n);
+    for (int n = 0; n < S - 1 && n < ntiles; ++n) {
+        read_slots(n);
+        issue_tile(n);
+    }
+    if (S - 1 < ntiles) read_slots(S - 1);
     static_assert(S >= 3 && 2 * PER_WAVE * (S - 2) < 64, "ring depth within the vmcnt range");
     // Wait until this wave's copies of tile n have landed: at most the copies
     // of the tiles issued after it (up to tile `last`) may still be in flight
@@ -451,7 +466,10 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
             // tiles 0 .. n + S - 2 have been issued
             wait_tile(n + 1, n + S - 2);
             __syncthreads();  // tile n + 1 landed; every wave is done with tile n - 1
-            if (n + S - 1 < ntiles) issue_tile(n + S - 1);  // into the stage of tile n - 1
+            if (n + S - 1 < ntiles) {
+                issue_tile(n + S - 1);  // into the stage of tile n - 1
+                if (n + S < ntiles) read_slots(n + S);
+            }
             if constexpr (F8) {
                 widen_tile(n + 1);
                 __syncthreads();
