@@ -738,3 +738,81 @@ def test_nested_prefix_groups_full_size_sampled():
     assert list(meta["group_parent"]) == [-1, 0, 0, 0, 0]
     o, lse = _grouped_run(db, plan)
     check_close("bf16", o[reqs], lse[reqs], o_ref, lse_ref, "nested full")
+
+
+# ------------------------------------------------------ randomized sweep --
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes_vs_oracle(case):
+    """Seeded random mixes of dtype, head_dim, GQA group, KV heads, page size,
+    batch and lengths (empty requests included), shared prefix, forced path
+    and tuning, every request checked against the oracle."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    rng = np.random.default_rng(9000 + case)
+    kv = str(rng.choice(["f32", "bf16", "fp8"], p=[0.2, 0.5, 0.3]))
+    q = "f32" if kv == "f32" else "bf16"
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    H_kv = int(rng.choice([1, 2, 3, 4, 8]))
+    p = int(rng.choice([1, 3, 8, 16, 64]))
+    B = int(rng.integers(1, 33))
+    lo = int(rng.integers(0, 40))
+    hi = lo + int(rng.integers(0, 600))
+    P = int(rng.integers(1, 700)) if rng.random() < 0.7 else 0
+    prefix_ok = q == "bf16" and (kv == "bf16" or d == 128) and P >= p and B >= 1
+    force = int(rng.choice([-1, 0, 1, 2])) if prefix_ok else int(rng.choice([-1, 0]))
+    tune = dict(target_workgroups=int(rng.choice([64, 256, 512, 1024])),
+                min_split_tokens=int(rng.choice([16, 64, 256])), gate_ratio=int(rng.choice([0, 3])),
+                fuse_cascade=int(rng.choice([0, 1, 12])), t_dense=int(rng.choice([1, 64, 4096])))
+    layout = str(rng.choice(["shared", "unique"])) if P else "shared"
+    b = make_decode_batch(seed=9000 + case, B=B, H_q=G * H_kv, H_kv=H_kv, d=d, own_len=(lo, hi), prefix_len=P,
+                          q_dtype=q, kv_dtype=kv, page_size=p, layout=layout)
+    what = f"case {case}: {kv} d={d} G={G} H_kv={H_kv} p={p} B={B} L=P{P}+U{{{lo}..{hi}}} force={force} {tune}"
+    say(what)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(shared_prefix_len=P, force_path=force, tuning=tune)
+    o, lse = db.step(plan, ws=_garbage_workspace(db, plan))
+    torch.cuda.synchronize()
+    check_close(kv, o, lse, o_ref, lse_ref, what + f" path={plan.info['path_name']}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_prefix_trees_vs_oracle(case):
+    """Seeded random trees of shared runs (roots with nested children, loners,
+    runs crossing page boundaries) planned from the page table."""
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    from workloads import make_tree_batch
+    rng = np.random.default_rng(9100 + case)
+    kv = str(rng.choice(["bf16", "fp8"]))
+    d = 128 if kv == "fp8" else int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    H_kv = int(rng.choice([1, 2, 4, 8]))
+    p = int(rng.choice([4, 16, 32]))
+    B = int(rng.integers(6, 40))
+    tree, free = [], B
+    for _ in range(int(rng.integers(1, 4))):          # roots
+        n = int(rng.integers(2, max(3, free // 2 + 1)))
+        if n > free:
+            break
+        free -= n
+        r = len(tree)
+        tree.append((n, int(rng.integers(1, 600)), -1))
+        left = n
+        for _ in range(int(rng.integers(0, 3))):      # children of this root
+            m = int(rng.integers(2, max(3, left // 2 + 1)))
+            if m > left:
+                break
+            left -= m
+            tree.append((m, int(rng.integers(1, 300)), r))
+    tune = dict(gate_ratio=int(rng.choice([0, 0, 0, 3])), t_dense=int(rng.choice([1, 16, 4096])),
+                fuse_cascade=int(rng.choice([0, 1, 12])))
+    b = make_tree_batch(seed=9100 + case, B=B, H_q=G * H_kv, H_kv=H_kv, d=d, tree=tree,
+                        own_len=(0, int(rng.integers(1, 200))), page_size=p, kv_dtype=kv)
+    what = f"tree case {case}: {kv} d={d} G={G} H_kv={H_kv} p={p} B={B} tree={tree} {tune}"
+    say(what)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan_grouped(tuning=tune)
+    o, lse = _grouped_run(db, plan)
+    check_close(kv, o, lse, o_ref, lse_ref, what + f" groups={plan.info['num_groups']} path={plan.info['path_name']}")
