@@ -478,6 +478,41 @@ def write_prefix_traffic(name, unique_dir, separate_dir, commands):
     return rec
 
 
+PREFIX_MFMA_COUNTERS = "MfmaUtil MfmaFlopsBF16 SQ_INSTS_MFMA SQ_INSTS_VALU SQ_BUSY_CYCLES"
+PREFIX_LDS_COUNTERS = "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_WAVE_CYCLES GRBM_GUI_ACTIVE"
+
+
+def write_prefix_counters(name, mfma_dir, lds_dir, commands):
+    """MFMA utilisation, MFMA flops and LDS / wait counters of a shared-prefix
+    workload's prefix pass (run as its own launch), per dispatch."""
+    import statistics
+    from workloads import make_config
+    b = make_config(name)
+    flops = 4 * b.B * b.G * b.prefix_len * b.d * b.H_kv
+    med = {}
+    for d, names in ((mfma_dir, PREFIX_MFMA_COUNTERS), (lds_dir, PREFIX_LDS_COUNTERS)):
+        for c in names.split():
+            vals = [v for (k, _), vs in pmc_per_dispatch(d, c).items() if "prefix_attn" in k for v in vs]
+            med[c] = statistics.median(vals) if vals else None
+    try:
+        sha = json.loads(open(mfma_dir.rstrip("/") + ".json").read().strip().splitlines()[-1])["source_sha256"]
+    except (OSError, ValueError, KeyError, IndexError):
+        sha = kernel_source_hash()
+    ratio = lambda x, y: (x / y) if (x is not None and y) else None  # noqa: E731
+    rec = dict(workload=f"{name}: prefix pass of B={b.B} requests over a {b.prefix_len}-token prefix, "
+                        f"M_eff={b.B * b.G}, {b.H_kv} KV heads, d={b.d}, {b.kv_dtype}",
+               commands=commands, source_sha256=sha, algorithmic_flops=flops, counters_median_per_dispatch=med,
+               mfma_util_pct=med.get("MfmaUtil"),
+               mfma_flops_over_algorithmic=ratio(med.get("MfmaFlopsBF16"), flops),
+               lds_bank_conflict_over_lds_active=ratio(med.get("SQ_LDS_BANK_CONFLICT"), med.get("SQ_LDS_IDX_ACTIVE")),
+               wait_over_wave_cycles=ratio(med.get("SQ_WAIT_ANY"), med.get("SQ_WAVE_CYCLES")),
+               active_inst_over_wave_cycles=ratio(med.get("SQ_ACTIVE_INST_ANY"), med.get("SQ_WAVE_CYCLES")))
+    path = os.path.join(ROOT, "profiles", f"prefix_attn_kernel.{name}_shared_prefix.counters.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def measured_traffic():
     """Scaled HBM bytes per decode step of the headline workload from the
     committed counter summary, or None when the sources changed since."""
@@ -571,7 +606,20 @@ def main():
                     help="write the page-size control summary from a --page-control run and two counter runs")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
+    ap.add_argument("--summarize-prefix-counters", nargs=3, metavar=("CONFIG", "MFMA_DIR", "LDS_DIR"),
+                    help="write the prefix pass's MFMA/LDS counter summary from two counter runs of "
+                         "--only CONFIG:dense_separate and exit")
     args = ap.parse_args()
+    if args.summarize_prefix_counters:
+        name, m, l = args.summarize_prefix_counters
+        prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc"
+        run = f"-o run -- python bench.py --only {name}:dense_separate --steps 10 --warmup 2"
+        cmds = dict(mfma=f"{prof} {PREFIX_MFMA_COUNTERS} --output-format csv -d {m} {run}",
+                    lds=f"{prof} {PREFIX_LDS_COUNTERS} --output-format csv -d {l} {run}",
+                    summary=f"python bench.py --summarize-prefix-counters {name} {m} {l}")
+        rec = write_prefix_counters(name, m, l, cmds)
+        print(json.dumps({k: v for k, v in rec.items() if k != "commands"}, indent=1))
+        return
     if args.summarize_prefix_traffic:
         name, u, c = args.summarize_prefix_traffic
         prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE"
