@@ -513,6 +513,57 @@ def write_prefix_counters(name, mfma_dir, lds_dir, commands):
     return rec
 
 
+PAGED_VALU_COUNTERS = ("SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_THREAD_CYCLES_VALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+                       "SQ_WAIT_ANY SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE")
+# the paged kernel of each workload in a `--configs c2,c5` run (kernel name, grid size)
+PAGED_COUNTER_KERNELS = {"c2": ("pkv::paged_split_kernel<1, 128, 4, 1, 1>", 131072),
+                         "c5": ("pkv::paged_split_kernel<2, 128, 8, 1, 1>", 131072)}
+
+
+def write_paged_counters(valu_dir, fetch_dir, commands):
+    """Vector-ALU and wait counters of the paged kernel on the Llama layer
+    (bf16, G = 4) and the long fp8 workload (G = 8), per dispatch; and a
+    repeat of the headline FETCH_SIZE pass, against the committed traffic
+    summary (byte-count drift between two profiles of the same step)."""
+    import statistics
+    from workloads import make_config
+    out = {}
+    for name, key in PAGED_COUNTER_KERNELS.items():
+        b = make_config(name)
+        tokens = int(sum(int(x) for x in b.seq_lens))
+        med = {}
+        for c in PAGED_VALU_COUNTERS.split():
+            vals = pmc_per_dispatch(valu_dir, c).get(key, [])
+            med[c] = statistics.median(vals) if vals else None
+        ratio = lambda x, y: (x / y) if (x is not None and y) else None  # noqa: E731
+        out[name] = dict(kernel=f"{key[0]} grid={key[1]}", tokens=tokens, kv_heads=b.H_kv, group=b.G,
+                         kv_dtype=b.kv_dtype, counters_median_per_dispatch=med,
+                         valu_insts_per_token_and_kv_head=ratio(med["SQ_INSTS_VALU"], tokens * b.H_kv),
+                         active_valu_over_wave_cycles=ratio(med["SQ_ACTIVE_INST_VALU"], med["SQ_WAVE_CYCLES"]),
+                         wait_over_wave_cycles=ratio(med["SQ_WAIT_ANY"], med["SQ_WAVE_CYCLES"]),
+                         active_inst_over_wave_cycles=ratio(med["SQ_ACTIVE_INST_ANY"], med["SQ_WAVE_CYCLES"]),
+                         valu_lane_use=ratio(med["SQ_THREAD_CYCLES_VALU"],
+                                             None if med["SQ_ACTIVE_INST_VALU"] is None
+                                             else 64 * med["SQ_ACTIVE_INST_VALU"]))
+    # FETCH_SIZE repeat of the headline step against the committed summary
+    prev = json.load(open(TRAFFIC_FILE))
+    fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    repeat = {}
+    for (k, grid), vs in fetch.items():
+        label = f"{k} grid={grid}"
+        if label in prev["kernels"]:
+            now = statistics.median(vs)
+            was = prev["kernels"][label]["fetch_kib_median"]
+            repeat[label] = dict(fetch_kib_median=now, committed_fetch_kib_median=was, drift=(now - was) / was,
+                                 dispatches=len(vs))
+    rec = dict(commands=commands, source_sha256=kernel_source_hash(), workloads=out,
+               fetch_repeat_of_committed_traffic=repeat)
+    path = os.path.join(ROOT, "profiles", "paged_split_kernel.c2_c5.counters.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def measured_traffic():
     """Scaled HBM bytes per decode step of the headline workload from the
     committed counter summary, or None when the sources changed since."""
@@ -606,10 +657,24 @@ def main():
                     help="write the page-size control summary from a --page-control run and two counter runs")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 output of the headline workload and exit")
+    ap.add_argument("--summarize-paged-counters", nargs=2, metavar=("VALU_DIR", "FETCH_DIR"),
+                    help="write the paged kernel's vector-ALU counter summary (Llama layer and long fp8) and the "
+                         "repeat of the headline FETCH_SIZE pass from two counter runs and exit")
     ap.add_argument("--summarize-prefix-counters", nargs=3, metavar=("CONFIG", "MFMA_DIR", "LDS_DIR"),
                     help="write the prefix pass's MFMA/LDS counter summary from two counter runs of "
                          "--only CONFIG:dense_separate and exit")
     args = ap.parse_args()
+    if args.summarize_paged_counters:
+        v, f = args.summarize_paged_counters
+        prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc"
+        cmds = dict(valu=f"{prof} {PAGED_VALU_COUNTERS} --output-format csv -d {v} -o run -- python bench.py "
+                         "--configs c2,c5 --steps 10 --warmup 2 --no-cpu",
+                    fetch=f"{prof} FETCH_SIZE --output-format csv -d {f} -o run -- python bench.py --configs c2 "
+                          "--steps 20 --warmup 5 --no-cpu",
+                    summary=f"python bench.py --summarize-paged-counters {v} {f}")
+        rec = write_paged_counters(v, f, cmds)
+        print(json.dumps({k: v for k, v in rec.items() if k != "commands"}, indent=1))
+        return
     if args.summarize_prefix_counters:
         name, m, l = args.summarize_prefix_counters
         prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc"
