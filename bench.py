@@ -93,7 +93,7 @@ PREFIX_LEGS = (("paged_shared", 0, None), ("cascade", 1, None), ("dense", 2, Non
                ("dense_separate", 2, dict(fuse_cascade=0)), ("planned", -1, None))
 
 
-def bench_prefix_config(name, steps, warmup, legs=None):
+def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
     """PAGED over unique prefix copies, PAGED over shared pages, each prefix
     path (DENSE also as two launches), and the planner's choice."""
     import torch
@@ -143,6 +143,11 @@ def bench_prefix_config(name, steps, warmup, legs=None):
                                    pct_peak=100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                    algorithmic_bytes=nbytes)
         del du, u, ws
+    if oracle:
+        n, runs = ORACLE_SAMPLE[name]
+        out["oracle"] = oracle_sample(b, list(range(n)), runs)
+        if "planned" in out:
+            out["oracle"]["gpu_speedup"] = out["oracle"]["ms_per_step"] / (out["planned"]["us_per_step"] / 1e3)
     del b
     torch.cuda.empty_cache()
     if "planned" in out and "paged_unique" in out:
@@ -636,6 +641,39 @@ def cpu_baseline(batch, min_seconds=10.0, max_steps=200):
     return total / n, threads, n, total
 
 
+def oracle_sample(batch, requests, runs=1):
+    """The oracle on a bounded sample of one workload's requests, on the host
+    cores: gathering each request's contiguous K/V (stored values widened to
+    float64) timed apart from the attention itself; the median of `runs`
+    passes, scaled from the sample to the whole step."""
+    import statistics
+    from oracle import attention as oa
+    from oracle import batch as ob
+    gather, attend = [], []
+    for _ in range(runs):
+        tg = ta = 0.0
+        for b in requests:
+            t0 = time.perf_counter()
+            q, k, v = ob.request_inputs(batch, b)
+            t1 = time.perf_counter()
+            oa.decode_attention(q, k, v, ob.default_scale(batch.d))
+            t2 = time.perf_counter()
+            tg += t1 - t0
+            ta += t2 - t1
+        gather.append(tg)
+        attend.append(ta)
+    scale = batch.B / len(requests)
+    g, a = statistics.median(gather) * scale, statistics.median(attend) * scale
+    return dict(ms_per_step=(g + a) * 1e3, gather_ms=g * 1e3, attention_ms=a * 1e3, runs=runs,
+                sample=f"{len(requests)} of {batch.B} requests (first ones), scaled by {scale:g}",
+                kind="oracle")
+
+
+# requests the per-workload oracle timing samples, and passes (bounded: a few
+# seconds each on the host)
+ORACLE_SAMPLE = {"c1": (None, 5), "c3": (8, 1), "c4": (16, 1), "c5": (2, 1), "c3_fp8": (8, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -782,14 +820,19 @@ def main():
     for name in wanted:
         if name in ("c1", "c5"):
             log(f"bench {name}")
-            r, _, db, _ = bench_paged_config(name, args.steps, args.warmup)
+            r, bb, db, _ = bench_paged_config(name, args.steps, args.warmup)
             extra[name] = add_ceiling(r, ceiling)
-            log(json.dumps(r))
             del db
             torch.cuda.empty_cache()
+            if not args.no_cpu:
+                n, runs = ORACLE_SAMPLE[name]
+                r["oracle"] = oracle_sample(bb, list(range(n or bb.B)), runs)
+                r["oracle"]["gpu_speedup"] = r["oracle"]["ms_per_step"] / (r["us_per_step"] / 1e3)
+            log(json.dumps(r))
+            del bb
         elif name in ("c3", "c4", "c3_fp8"):
             log(f"bench {name}")
-            extra[name] = bench_prefix_config(name, args.steps, args.warmup)
+            extra[name] = bench_prefix_config(name, args.steps, args.warmup, oracle=not args.no_cpu)
             log(json.dumps(extra[name]))
         elif name in ("groups4", "tree4"):
             log(f"bench {name}")

@@ -27,15 +27,22 @@ def _kv64(batch, t, which):
     return stored_to_f64(batch.bits(t, batch.kv_dtype), batch.kv_dtype, scale)
 
 
-def request_reference(batch, b, sm_scale=None, token_range=None):
-    """(o [H_q, d], lse [H_q]) of request ``b`` over its logical tokens
-    ``token_range = (lo, hi)`` (default: all of them)."""
-    sm_scale = default_scale(batch.d) if sm_scale is None else sm_scale
+def request_inputs(batch, b, token_range=None):
+    """Request ``b``'s query and contiguous K, V over its logical tokens
+    ``token_range = (lo, hi)`` (default: all of them), stored values widened
+    exactly to float64: (q [H_q, d], k [L, H_kv, d], v [L, H_kv, d])."""
     k, v = batch.logical_kv(b)
     if token_range is not None:
         lo, hi = token_range
         k, v = k[lo:hi], v[lo:hi]
-    return decode_attention(_q64(batch, b), _kv64(batch, k, "k"), _kv64(batch, v, "v"), sm_scale)
+    return _q64(batch, b), _kv64(batch, k, "k"), _kv64(batch, v, "v")
+
+
+def request_reference(batch, b, sm_scale=None, token_range=None):
+    """(o [H_q, d], lse [H_q]) of request ``b`` over its logical tokens
+    ``token_range = (lo, hi)`` (default: all of them)."""
+    sm_scale = default_scale(batch.d) if sm_scale is None else sm_scale
+    return decode_attention(*request_inputs(batch, b, token_range), sm_scale)
 
 
 def batch_reference(batch, sm_scale=None, requests=None, token_start=0):
