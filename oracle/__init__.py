@@ -29,6 +29,16 @@ Contents and what each part follows:
                    table of prompt-layout mistakes; "GraniKV", sections 2-3).
 * ``batch``     -- runs the above over a whole synthetic batch.
 
+Pins (tests/test_oracle.py, each with planted mistakes that it rejects):
+widening against torch's own bit reinterpretation and fp8 decode (all 256
+codes, random fp32 and bf16 patterns with zeros, subnormals, infinities and
+NaNs); the default softmax scale against the Llama layer's stated 1/sqrt(128);
+a request's inputs against torch-widened values with unlike K and V scales;
+attention against torch's SDPA in float64, brute force and closed forms; the
+merge against splits at every point; the batch and prefix references against
+SDPA on torch-widened inputs; lowering, planner and groups against brute force
+and the pages' worked examples.
+
 Parity unpinned: none of the functions here.  The planner's tuning constants
 are inputs; whether their gfx950 values are the right ones is a measurement,
 not an oracle question.

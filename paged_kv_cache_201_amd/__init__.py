@@ -132,6 +132,33 @@ def _dev(t, name, dtypes=None, allow_none=False):
     return t.data_ptr()
 
 
+def _torch_of_code(code):
+    import torch
+    return {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16}[code]
+
+
+def _check_sizes(plan, **tensors):
+    """Sizes and dtypes of the step's tensors against the plan's problem,
+    before any pointer reaches the library (which trusts them)."""
+    import torch
+    pr = plan.problem
+    B, H_q, d = pr["batch"], pr["num_q_heads"], pr["head_dim"]
+    qd = _torch_of_code(DTYPE_CODES.get(pr["q_dtype"], pr["q_dtype"]))
+    want = {"q": (B * H_q * d, (qd,)), "o": (B * H_q * d, (qd,)), "o_f32": (B * H_q * d, (torch.float32,)),
+            "o_p": (B * H_q * d, (torch.float32,)), "lse": (B * H_q, (torch.float32,)),
+            "lse_p": (B * H_q, (torch.float32,)), "kv_indptr": (B + 1, (torch.int32,)),
+            "page_indptr": (B + 1, (torch.int32,)),
+            "metadata": (plan.info.get("metadata_ints", 0), (torch.int32,))}
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        n, dtypes = want[name]
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}; the plan needs {dtypes[0]}")
+        if (t.numel() < n) if name == "metadata" else (t.numel() != n):
+            raise ValueError(f"{name} has {t.numel()} elements; the plan needs {n}")
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -289,6 +316,7 @@ def _ws(workspace, plan):
 def pkv_paged_decode_attn(plan, q, pool, kv_indptr, kv_indices, sm_scale, o=None, o_f32=None, lse=None,
                           workspace=None, stream=None):
     import torch
+    _check_sizes(plan, q=q, o=o, o_f32=o_f32, lse=lse, kv_indptr=kv_indptr)
     ws, wsb = _ws(workspace, plan)
     st = _lib.pkv_paged_decode_attn(plan.handle, _dev(q, "q"), ctypes.byref(pool),
                                     _dev(kv_indptr, "kv_indptr", (torch.int32,)),
@@ -301,6 +329,7 @@ def pkv_paged_decode_attn(plan, q, pool, kv_indptr, kv_indices, sm_scale, o=None
 def pkv_paged_decode_attn_pages(plan, q, pool, kv_indptr, page_indptr, page_indices, sm_scale, o=None, o_f32=None,
                                 lse=None, workspace=None, stream=None):
     import torch
+    _check_sizes(plan, q=q, o=o, o_f32=o_f32, lse=lse, kv_indptr=kv_indptr, page_indptr=page_indptr)
     ws, wsb = _ws(workspace, plan)
     i32 = (torch.int32,)
     st = _lib.pkv_paged_decode_attn_pages(plan.handle, _dev(q, "q"), ctypes.byref(pool),
@@ -314,6 +343,11 @@ def pkv_paged_decode_attn_pages(plan, q, pool, kv_indptr, page_indptr, page_indi
 def pkv_cascade_prefix_attn(plan, q, pool, prefix_indices, prefix_len, sm_scale, o_p, lse_p, workspace=None,
                             stream=None):
     import torch
+    _check_sizes(plan, o_p=o_p, lse_p=lse_p)   # q: bf16, checked below
+    if q is not None and q.numel() != o_p.numel():
+        raise ValueError(f"q has {q.numel()} elements; the plan needs {o_p.numel()}")
+    if prefix_indices is not None and prefix_indices.numel() < int(prefix_len):
+        raise ValueError(f"prefix_indices has {prefix_indices.numel()} entries; prefix_len is {prefix_len}")
     ws, wsb = _ws(workspace, plan)
     st = _lib.pkv_cascade_prefix_attn(plan.handle, _dev(q, "q", (torch.bfloat16,)), ctypes.byref(pool),
                                       _dev(prefix_indices, "prefix_indices", (torch.int32,)), int(prefix_len),
@@ -327,6 +361,10 @@ def pkv_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out=None, stream=None):
     f32 = (torch.float32,)
     rows = lse_a.numel()
     d = o_a.shape[-1]
+    for name, t, n in (("lse_b", lse_b, rows), ("o_a", o_a, rows * d), ("o_b", o_b, rows * d),
+                       ("o_out", o_out, rows * d), ("lse_out", lse_out, rows)):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements; {n} expected for {rows} rows of {d}")
     st = _lib.pkv_merge_states(rows, d, _dev(o_a, "o_a", f32), _dev(lse_a, "lse_a", f32), _dev(o_b, "o_b", f32),
                                _dev(lse_b, "lse_b", f32), _dev(o_out, "o_out", (torch.float32, torch.bfloat16)),
                                _torch_dtype_code(o_out), _dev(lse_out, "lse_out", f32, True), _stream(stream))
@@ -335,6 +373,7 @@ def pkv_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out=None, stream=None):
 
 def pkv_decode_step(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None, workspace=None, stream=None):
     import torch
+    _check_sizes(plan, q=q, o=o, lse=lse, kv_indptr=kv_indptr)
     ws, wsb = _ws(workspace, plan)
     st = _lib.pkv_decode_step(plan.handle, _dev(q, "q"), ctypes.byref(pool),
                               _dev(kv_indptr, "kv_indptr", (torch.int32,)),
@@ -345,6 +384,7 @@ def pkv_decode_step(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None,
 
 def pkv_decode_step_grouped(plan, q, pool, metadata, sm_scale, o, lse=None, workspace=None, stream=None):
     import torch
+    _check_sizes(plan, q=q, o=o, lse=lse, metadata=metadata)
     ws, wsb = _ws(workspace, plan)
     st = _lib.pkv_decode_step_grouped(plan.handle, _dev(q, "q"), ctypes.byref(pool),
                                       _dev(metadata, "metadata", (torch.int32,)), float(sm_scale), _dev(o, "o"),

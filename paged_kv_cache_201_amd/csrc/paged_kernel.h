@@ -613,7 +613,9 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
         if (hi <= lo) continue;  // empty request
         const bool whole = lo == ob && hi == on;
         const int slot = (whole && !a.force_partial) ? -1 : (int)(w - ob / C);
-        if (slot >= a.max_parts) return;  // kv_indptr does not describe the planned batch
+        // kv_indptr does not describe the planned batch: a partial state the
+        // workspace has no room for (or no partial buffer at all)
+        if (slot >= a.max_parts || (slot >= 0 && a.part_acc == nullptr)) return;
         if (!first) __syncthreads();  // the previous segment is done with LDS
         first = false;
         // the first segment starts at c0: its indices are staged already

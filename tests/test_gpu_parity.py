@@ -50,11 +50,11 @@ def check_close(kv_dtype, o, lse, o_ref, lse_ref, what):
         err_o = np.abs(o - o_ref).max(axis=-1)
         bound = 1e-5 * np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
         assert (err_o <= bound).all(), f"{what}: o rel err {(err_o / bound).max() * 1e-5:.3g}"
-        err_l = np.abs(lse - lse_ref)[fin]
+        err_l = np.abs(lse[fin] - lse_ref[fin])   # only finite entries: no inf - inf
         assert (err_l <= 1e-5 * np.maximum(1, np.abs(lse_ref[fin]))).all(), f"{what}: lse err {err_l.max():.3g}"
     else:
         err_o = np.abs(o - o_ref).max()
-        err_l = np.abs(lse - lse_ref)[fin].max() if fin.any() else 0.0
+        err_l = np.abs(lse[fin] - lse_ref[fin]).max() if fin.any() else 0.0
         assert err_o <= 2e-2, f"{what}: o err {err_o:.4g}"
         assert err_l <= 2e-2, f"{what}: lse err {err_l:.4g}"
     assert not np.isnan(o).any(), f"{what}: NaN in output"
@@ -70,6 +70,21 @@ def run_paged(DeviceBatch, batch, tuning=None, want_f32=False):
 
 def same_bits(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def spread_requests(batch, plan, n=32):
+    """n requests spread over the batch, half of them (where there are that
+    many) requests that the plan's paged pass cuts at chunk edges (their
+    partial states go through the combine), half whole ones."""
+    P = plan.info["prefix_tokens"]
+    C = plan.info["split_tokens"]
+    own = np.asarray(batch.seq_lens, np.int64) - P
+    start = np.concatenate([[0], np.cumsum(own)[:-1]])
+    cut = [b for b in range(batch.B) if own[b] > 0 and (start[b] + own[b] - 1) // C != start[b] // C]
+    whole = [b for b in range(batch.B) if b not in set(cut)]
+    pick = lambda xs, k: [xs[i] for i in np.linspace(0, len(xs) - 1, min(k, len(xs))).astype(int)] if xs else []
+    reqs = sorted(set(pick(cut, n // 2)) | set(pick(whole, n - min(n // 2, len(cut)))) | {0, batch.B - 1})
+    return reqs, sum(1 for b in reqs if b in set(cut))
 
 
 # ----------------------------------------------------------------- c1 ------
@@ -114,12 +129,12 @@ def test_c2_full_sampled_page1_vs_page128():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b128 = make_config("c2")
     b1 = relayout(b128, page_size=1, seed=2002)
-    reqs = [0, 13, 31]
-    o_ref, lse_ref = ob.batch_reference(b128, requests=reqs)
+    say("c2 full: oracle over every request")
+    o_ref, lse_ref = ob.batch_reference(b128)
     say("c2 full p=128")
     o128, l128, plan = run_paged(DeviceBatch, b128)
     assert plan.info["num_splits"] > 1
-    check_close("bf16", o128[reqs], l128[reqs], o_ref, lse_ref, "c2 p=128")
+    check_close("bf16", o128, l128, o_ref, lse_ref, "c2 p=128")
     del b128
     say("c2 full p=1")
     o1, l1, _ = run_paged(DeviceBatch, b1)
@@ -141,14 +156,15 @@ def test_c5_fp8_small():
     assert same_bits(o, o2) and same_bits(lse, l2)
 
 
-def test_c5_full_sampled():
+def test_c5_full_every_request():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_config("c5")
-    reqs = [0, 7, 15]
-    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+    say("c5 full: oracle over every request")
+    o_ref, lse_ref = ob.batch_reference(b)
     say("c5 full fp8")
     o, lse, plan = run_paged(DeviceBatch, b)
-    check_close("fp8", o[reqs], lse[reqs], o_ref, lse_ref, "c5 full")
+    assert plan.info["num_splits"] > 1
+    check_close("fp8", o, lse, o_ref, lse_ref, "c5 full")
 
 
 # --------------------------------------------------------- shared prefix ---
@@ -190,12 +206,15 @@ def test_cascade_small_all_paths_and_layouts():
         assert same_bits(ou, res[0][0]) and same_bits(lu, res[0][1]), "layout changed the bits"
 
 
-def _full_prefix_case(name, reqs):
+def _full_prefix_case(name):
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     b = make_config(name)
-    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
     db = DeviceBatch.from_batch(b)
     plan = db.plan(shared_prefix_len=b.prefix_len)
+    reqs, n_cut = spread_requests(b, plan)
+    assert len(reqs) >= 32 and n_cut >= 8, (len(reqs), n_cut)
+    say(f"{name} full: oracle over {len(reqs)} requests ({n_cut} cut by chunk edges)")
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
     say(f"{name} full plan={plan.info['path_name']} decode_step")
     o, lse = db.step(plan)
     torch.cuda.synchronize()
@@ -214,12 +233,12 @@ def _full_prefix_case(name, reqs):
 
 
 def test_c3_full_sampled():
-    plan = _full_prefix_case("c3", [0, 100, 255])
+    plan = _full_prefix_case("c3")
     assert plan.info["m_eff"] == 1024
 
 
 def test_c4_full_sampled():
-    plan = _full_prefix_case("c4", [0, 311, 511])
+    plan = _full_prefix_case("c4")
     assert plan.info["m_eff"] == 2048
 
 
@@ -468,6 +487,15 @@ def test_abi_rejects_bad_arguments_without_launching():
         pkv.pkv_cascade_prefix_attn(plan, db.q.bfloat16(), db.pool, db.kv_indices, 0, 0.125,
                                     db.new_out(torch.float32), db.new_lse())
     assert e.value.name == "EINVAL"   # a PAGED plan has no prefix pass
+    # the binding checks sizes and dtypes against the plan before any call
+    for kw in (dict(o=db.new_out()[:2]), dict(o=db.new_out(), lse=db.new_lse()[:1]),
+               dict(o=db.new_out(torch.bfloat16)), dict(o_f32=db.new_out(torch.float32)[1:])):
+        with pytest.raises(ValueError):
+            pkv.pkv_paged_decode_attn(plan, db.q, db.pool, db.kv_indptr, db.kv_indices, 0.125,
+                                      workspace=db.workspace(plan), **kw)
+    with pytest.raises(ValueError):
+        pkv.pkv_paged_decode_attn(plan, db.q, db.pool, db.kv_indptr[:-1], db.kv_indices, 0.125,
+                                  o=db.new_out(), workspace=db.workspace(plan))
     with pytest.raises(pkv.PkvError) as e:   # page-table form: missing page table
         pkv._check(pkv._lib.pkv_paged_decode_attn_pages(plan.handle, db.q.data_ptr(), pkv.ctypes.byref(db.pool),
                                                         db.kv_indptr.data_ptr(), None, None, 0.125,
@@ -623,12 +651,14 @@ def test_cascade_fp8_small_all_paths():
 
 def test_c3_fp8_full_sampled():
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
-    reqs = [0, 100, 255]
     b = make_config("c3", kv_dtype="fp8")
-    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
     db = DeviceBatch.from_batch(b)
     plan = db.plan(shared_prefix_len=b.prefix_len)
     assert plan.info["path_name"] == "DENSE"
+    reqs, n_cut = spread_requests(b, plan)
+    assert len(reqs) >= 32 and n_cut >= 8, (len(reqs), n_cut)
+    say(f"c3 fp8 full: oracle over {len(reqs)} requests ({n_cut} cut by chunk edges)")
+    o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
     say("c3 fp8 full decode_step")
     o, lse = db.step(plan)
     torch.cuda.synchronize()

@@ -49,6 +49,125 @@ def test_bf16_widening_matches_torch():
     assert np.array_equal(ref[~nan], got[~nan])
 
 
+F32_SPECIAL_BITS = np.array([0x00000000, 0x80000000, 0x00000001, 0x807FFFFF, 0x00800000, 0x3F800000,
+                             0xBF800000, 0x7F7FFFFF, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001],
+                            np.uint32)
+
+
+def check_f32_widening(widen):
+    """The tiny workload stores fp32 values; its bits must reach float64 as a
+    bit-view, not as integers.  Torch's own reinterpretation of the same bits
+    is the reference: random patterns plus signed zeros, subnormals, the
+    largest finite value, infinities and NaNs."""
+    bits = np.concatenate([RNG.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32),
+                           F32_SPECIAL_BITS])
+    stored = bits.view(np.int32)  # the dtype the workloads keep fp32 bits in
+    ref = torch.from_numpy(stored.copy()).view(torch.float32).to(torch.float64).numpy()
+    got = widen(stored)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))  # -0.0 stays negative
+
+
+def test_f32_widening_matches_torch():
+    check_f32_widening(ov.f32_bits_to_f64)
+    # and through the dtype switch the batch code uses
+    check_f32_widening(lambda b: ov.stored_to_f64(b, "f32"))
+
+
+def check_default_scale(default_scale):
+    """The Llama-layer workload states its softmax scale, 1/sqrt(128); the
+    reading taken for the other workloads is 1/sqrt(d) (tiny: d = 64 -> 1/8)."""
+    s = default_scale(128)
+    assert abs(s * s * 128 - 1) < 1e-15 and s > 0
+    assert default_scale(64) == 0.125
+
+
+def test_default_scale_is_the_stated_one():
+    from oracle import batch as ob
+    check_default_scale(ob.default_scale)
+
+
+def _small_batch(kv_dtype, q_dtype, seed=5, **kw):
+    from workloads import make_decode_batch
+    args = dict(seed=seed, B=3, H_q=8, H_kv=2, d=16, own_len=(1, 9), prefix_len=5, q_dtype=q_dtype,
+                kv_dtype=kv_dtype, page_size=4)
+    args.update(kw)
+    return make_decode_batch(**args)
+
+
+def _torch_widened(batch, b):
+    """Request b's stored query, keys and values widened by torch's own
+    conversions (fp8: torch's float8_e4m3fn decode times the head's scale)."""
+    k, v = batch.logical_kv(b)
+    q = batch.q[b].to(torch.float64).numpy()
+    k, v = k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
+    if batch.kv_dtype == "fp8":
+        k = k * np.asarray(batch.k_scale, np.float64)[None, :, None]
+        v = v * np.asarray(batch.v_scale, np.float64)[None, :, None]
+    return q, k, v
+
+
+def check_request_inputs(request_inputs):
+    """K is widened with the K scales and V with the V scales: an fp8 batch
+    whose V scales are made unlike its K scales (x3 on every head) must give
+    torch's decode of each times its own scale; bf16 and fp32 batches
+    likewise, and a token range selects those logical tokens."""
+    for kv, qd in (("fp8", "bf16"), ("bf16", "bf16"), ("f32", "f32")):
+        batch = _small_batch(kv, qd)
+        if kv == "fp8":
+            batch.v_scale = (np.asarray(batch.v_scale, np.float32) * np.float32(3.0)).astype(np.float32)
+            assert not np.allclose(batch.k_scale, batch.v_scale)
+        for b in range(batch.B):
+            q, k, v = request_inputs(batch, b)
+            tq, tk, tv = _torch_widened(batch, b)
+            assert np.array_equal(q, tq) and np.array_equal(k, tk) and np.array_equal(v, tv), (kv, b)
+            L = int(batch.seq_lens[b])
+            q2, k2, v2 = request_inputs(batch, b, (2, L - 1))
+            assert np.array_equal(k2, tk[2:L - 1]) and np.array_equal(v2, tv[2:L - 1]), (kv, b)
+
+
+def test_request_inputs_widen_k_and_v_with_their_own_scales():
+    from oracle import batch as ob
+    check_request_inputs(ob.request_inputs)
+
+
+def check_batch_reference(batch_reference, prefix_reference):
+    """A whole batch against torch's SDPA in float64 on torch-widened inputs
+    (scale 1/sqrt(d)), the suffix form (tokens from token_start on) and the
+    prefix form (the first tokens)."""
+    for kv, qd in (("fp8", "bf16"), ("bf16", "bf16"), ("f32", "f32")):
+        batch = _small_batch(kv, qd, seed=9)
+        if kv == "fp8":
+            batch.v_scale = (np.asarray(batch.v_scale, np.float32) * np.float32(0.5)).astype(np.float32)
+        G, d = batch.G, batch.d
+
+        def sdpa(q, k, v):
+            qt = torch.from_numpy(q)[None, :, None, :]
+            kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+            vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+            o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=d ** -0.5)[0, :, 0]
+            lse = torch.logsumexp((qt @ kt.transpose(-1, -2))[0, :, 0] * d ** -0.5, dim=-1)
+            return o.numpy(), lse.numpy()
+
+        o, lse = batch_reference(batch)
+        o_s, lse_s = batch_reference(batch, token_start=3)
+        o_p, lse_p = prefix_reference(batch, 4)
+        for b in range(batch.B):
+            q, k, v = _torch_widened(batch, b)
+            for got, (lo, hi) in (((o[b], lse[b]), (0, len(k))), ((o_s[b], lse_s[b]), (3, len(k))),
+                                  ((o_p[b], lse_p[b]), (0, 4))):
+                ro, rl = sdpa(q, k[lo:hi], v[lo:hi])
+                assert np.allclose(got[0], ro, rtol=0, atol=1e-12), (kv, b, lo, hi)
+                assert np.allclose(got[1], rl, rtol=0, atol=1e-12), (kv, b, lo, hi)
+
+
+def test_batch_reference_matches_sdpa_on_torch_widened_inputs():
+    from oracle import batch as ob
+    check_batch_reference(ob.batch_reference, ob.prefix_reference)
+
+
 def test_fp8_scale_applies_per_head():
     bits = np.array([[[0x38, 0x40], [0x38, 0x40]]], np.uint8)  # 1.0, 2.0 per head
     x = ov.stored_to_f64(bits, "fp8", np.array([0.5, 3.0], np.float32))
@@ -309,8 +428,8 @@ def test_planner_gate_and_alignment():
     assert _plan(4, 4, 16, launch_bytes=0)["path"] == "PAGED"
     assert _plan(4, 4, 256, launch_bytes=0)["path"] == "CASCADE"
     assert _plan(4, 4, 256, launch_bytes=10**12)["path"] == "PAGED"
-    # fp8 K/V: a prefix kernel at d = 128 (the gate counts one byte per
-    # value); none at d = 64, where forcing a prefix path is refused
+    # fp8 K/V: a prefix kernel at d = 128; none at d = 64, where forcing a
+    # prefix path is refused
     assert _plan(256, 4, 4096, kv_dtype="fp8")["path"] == "DENSE"     # M_eff = 1024 at the A100 threshold
     assert _plan(256, 4, 4096, d=64, kv_dtype="fp8")["path"] == "PAGED"
     with pytest.raises(op.PlanError) as e:
@@ -433,6 +552,65 @@ def test_mutant_merge_caught(mutant):
 def test_mutant_fp8_caught():
     with pytest.raises(AssertionError):
         check_fp8_table(_mut_fp8_bias8)
+
+
+def _mut_f32_astype(bits):              # converts the integers instead of viewing the bits
+    return np.asarray(bits).astype(np.float64)
+
+
+def _mut_scale_over_d(d):               # 1/d instead of 1/sqrt(d)
+    return 1.0 / d
+
+
+def _mut_request_inputs_swapped(batch, b, token_range=None):   # V widened with the K scales
+    from oracle import batch as ob
+    q, k, v = ob.request_inputs(batch, b, token_range)
+    if batch.kv_dtype == "fp8":
+        k = k / np.asarray(batch.k_scale, np.float64)[None, :, None] * np.asarray(batch.v_scale, np.float64)[None, :, None]
+        v = v / np.asarray(batch.v_scale, np.float64)[None, :, None] * np.asarray(batch.k_scale, np.float64)[None, :, None]
+    return q, k, v
+
+
+def _mut_request_inputs_range(batch, b, token_range=None):     # token range one late
+    from oracle import batch as ob
+    if token_range is not None:
+        token_range = (token_range[0] + 1, token_range[1] + 1)
+    return ob.request_inputs(batch, b, token_range)
+
+
+def _mut_batch_reference_scale(batch, sm_scale=None, requests=None, token_start=0):   # scale 1/d
+    from oracle import batch as ob
+    return ob.batch_reference(batch, 1.0 / batch.d if sm_scale is None else sm_scale, requests, token_start)
+
+
+def _mut_prefix_reference_short(batch, prefix_tokens, sm_scale=None, requests=None):  # drops the last prefix token
+    from oracle import batch as ob
+    return ob.prefix_reference(batch, prefix_tokens - 1, sm_scale, requests)
+
+
+def test_mutant_f32_widening_caught():
+    with pytest.raises(AssertionError):
+        check_f32_widening(_mut_f32_astype)
+
+
+def test_mutant_default_scale_caught():
+    with pytest.raises(AssertionError):
+        check_default_scale(_mut_scale_over_d)
+
+
+@pytest.mark.parametrize("mutant", [_mut_request_inputs_swapped, _mut_request_inputs_range])
+def test_mutant_request_inputs_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_request_inputs(mutant)
+
+
+@pytest.mark.parametrize("mutants", [("scale", _mut_batch_reference_scale, None),
+                                     ("prefix", None, _mut_prefix_reference_short)])
+def test_mutant_batch_reference_caught(mutants):
+    from oracle import batch as ob
+    _, br, pr = mutants
+    with pytest.raises(AssertionError):
+        check_batch_reference(br or ob.batch_reference, pr or ob.prefix_reference)
 
 
 @pytest.mark.parametrize("mutant", [_mut_lower_swapped, _mut_lower_offbyone])
