@@ -75,5 +75,24 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+SANITIZE_EXE = os.path.join(BUILD, "host_sanitize")
+
+
+def build_host_sanitize(verbose: bool = False) -> str:
+    """The host half (host.cpp: lowering, validation, planners) linked into
+    the seeded driver tests/host_sanitize.cpp with AddressSanitizer and
+    UndefinedBehaviorSanitizer, as a CPU executable (g++ only, no device
+    code); returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    _run(["g++", "-std=c++17", "-g", "-O1", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+          "-fno-sanitize-recover=all", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",
+          os.path.join(CSRC, "host.cpp"), os.path.join(ROOT, "tests", "host_sanitize.cpp"), "-o", SANITIZE_EXE],
+         verbose)
+    return SANITIZE_EXE
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_host_sanitize(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
