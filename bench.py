@@ -49,38 +49,137 @@ def algorithmic_bytes(batch, path, prefix_tokens=0):
             + rows * d * bq)
 
 
-def time_steps(fn, steps, warmup):
-    """Warmup, then exactly `steps` calls between two events on the launch stream."""
+WINDOWS = 7             # timed windows of --steps steps per leg
+STABLE_TOL = 0.01       # warm until two consecutive windows agree this closely
+MAX_WARM_S = 3.0        # ... or until this much warming has passed
+
+
+def time_windows(fn, steps, warmup, windows=WINDOWS):
+    """`warmup` untimed calls; then windows of `steps` back-to-back calls, each
+    between two events on the launch stream, until two consecutive windows
+    agree within STABLE_TOL (a steady clock and warm caches; at most
+    MAX_WARM_S of such warming); then `windows` timed windows.  Returns the
+    median, min and max ms per step over the timed windows, the warm-up
+    windows it took and the total number of calls."""
+    import statistics
     import torch
+    stream = torch.cuda.current_stream()
+    calls = 0
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per step
+        calls += 1
+
+    def window():
+        nonlocal calls
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        end.synchronize()
+        calls += steps
+        return start.elapsed_time(end) / steps
+
+    t0 = time.perf_counter()
+    warm = [window()]
+    while True:
+        warm.append(window())
+        a, b = warm[-2], warm[-1]
+        if abs(a - b) <= STABLE_TOL * min(a, b):
+            stable = True
+            break
+        if time.perf_counter() - t0 > MAX_WARM_S:
+            stable = False
+            break
+    vals = [window() for _ in range(windows)]
+    return dict(ms=statistics.median(vals), ms_min=min(vals), ms_max=max(vals), windows=windows,
+                warm_windows=len(warm), warm_stable=stable, calls=calls)
+
+
+def time_steps(fn, steps, warmup):
+    """Median ms per step (see time_windows)."""
+    return time_windows(fn, steps, warmup)["ms"]
+
+
+# Peaks of one MI355X (vendor figures): HBM3E bandwidth, dense bf16 MFMA, and
+# fp32 vector ALU (256 CUs x 4 SIMDs x 2.4 GHz x 64 flops per SIMD-cycle).
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+PEAK_VALU_F32_TFLOPS = 157.3
+
+
+def roofline(us, hbm_bytes, mfma_flops=0, valu_flops=0, note=None):
+    """Floors of a step at the chip's peaks: HBM bytes / 8 TB/s, MFMA flops /
+    2.5 PFLOP/s (bf16 dense), vector-ALU flops / 157.3 TFLOP/s; the step's
+    roofline is the largest of them and frac = that floor / measured time."""
+    fl = dict(hbm_us=hbm_bytes / (PEAK_HBM_GBS * 1e3), mfma_us=mfma_flops / (PEAK_MFMA_BF16_TFLOPS * 1e6),
+              valu_us=valu_flops / (PEAK_VALU_F32_TFLOPS * 1e6))
+    bound = max(fl, key=fl.get)
+    floor = fl[bound]
+    out = dict(bound={"hbm_us": "hbm", "mfma_us": "mfma", "valu_us": "alu"}[bound], floor_us=floor,
+               frac=floor / us if us > 0 else None, floors_us=fl)
+    if note:
+        out["note"] = note
+    return out
+
+
+def leg(t, nbytes, **roof):
+    """One timed leg: median (min, max) us per step, GB/s of the algorithmic
+    bytes at the median, and the roofline at the median."""
+    us = t["ms"] * 1e3
+    note = roof.pop("note", None)
+    return dict(us_per_step=us, us_min=t["ms_min"] * 1e3, us_max=t["ms_max"] * 1e3, windows=t["windows"],
+                warm_windows=t["warm_windows"], warm_stable=t["warm_stable"], algorithmic_bytes=nbytes,
+                gbs=nbytes / us / 1e3, roofline=roofline(us, nbytes, note=note, **roof))
+
+
+def valu_flops(tokens, batch):
+    """Vector-ALU flops of attending `tokens` (token, request) positions: one
+    multiply-add (2 flops) per query-head element for each of q.k and p.v."""
+    return 4 * tokens * batch.H_q * batch.d
+
+
+def mfma_flops(m_eff, prefix_tokens, batch):
+    """Matrix-core flops of the prefix contraction: S = Q K^T and O = P V for
+    M_eff query rows per KV head over the prefix."""
+    return 4 * m_eff * prefix_tokens * batch.d * batch.H_kv
 
 
 def bench_paged_config(name, steps, warmup, **overrides):
-    import torch
     from paged_kv_cache_201_amd.step import DeviceBatch
     from workloads import make_config
     b = make_config(name, device="cuda", **overrides)
     db = DeviceBatch.from_batch(b)
     plan = db.plan()
     o, lse, ws = db.new_out(), db.new_lse(), db.workspace(plan)
-    ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
+    t = time_windows(lambda: db.step(plan, o, lse, ws), steps, warmup)
     nbytes = algorithmic_bytes(b, plan.info["path_name"])
-    rec = dict(workload=name, page_size=b.page_size, path=plan.info["path_name"], us_per_step=ms * 1e3,
-               algorithmic_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, num_splits=plan.info["num_splits"],
+    tokens = int(sum(int(x) for x in b.seq_lens))
+    rec = dict(workload=name, page_size=b.page_size, path=plan.info["path_name"],
+               **leg(t, nbytes, valu_flops=valu_flops(tokens, b)), num_splits=plan.info["num_splits"],
                split_tokens=plan.info["split_tokens"], work_items=plan.info["num_work_items"])
     rec["pct_peak"] = 100.0 * rec["gbs"] / PEAK_HBM_GBS
+    issue = valu_issue_floor(name)
+    if issue:
+        rec["roofline"]["valu_issue"] = issue
     return rec, b, db, plan
+
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "paged_split_kernel.c2_c5.counters.json")
+
+
+def valu_issue_floor(name):
+    """Vector-instruction issue floor of a workload's paged kernel from the
+    committed counter summary: wave64 VALU instructions per step (median per
+    dispatch), at one instruction per 4 cycles on each of the 1,024 SIMDs at
+    2.4 GHz.  None if the summary does not cover the workload."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+        n = rec["workloads"][name]["counters_median_per_dispatch"]["SQ_INSTS_VALU"]
+    except (OSError, ValueError, KeyError):
+        return None
+    return dict(valu_insts_per_step=n, floor_us=n * 4 / (1024 * 2.4e3),
+                counters_source_matches=rec.get("source_sha256") == kernel_source_hash())
 
 
 def add_ceiling(rec, ceiling):
@@ -91,6 +190,21 @@ def add_ceiling(rec, ceiling):
 # legs of a shared-prefix workload: label, forced path, tuning
 PREFIX_LEGS = (("paged_shared", 0, None), ("cascade", 1, None), ("dense", 2, None),
                ("dense_separate", 2, dict(fuse_cascade=0)), ("planned", -1, None))
+
+SHARED_PAGES_NOTE = ("requested bytes: every request re-reads the shared pages, which mostly hit in L2 / "
+                     "Infinity Cache, so this floor understates the step and frac can exceed 1")
+
+
+def prefix_leg(b, plan, t):
+    """A shared-prefix leg's record with its floors: HBM over the path's
+    algorithmic bytes, MFMA over the prefix contraction, vector ALU over the
+    paged pass's positions."""
+    path = plan.info["path_name"]
+    P = plan.info["prefix_tokens"]
+    nbytes = algorithmic_bytes(b, path, P)
+    tokens = int(sum(int(x) for x in b.seq_lens)) - (b.B * P if path != "PAGED" else 0)
+    return dict(path=path, **leg(t, nbytes, valu_flops=valu_flops(tokens, b),
+                                 mfma_flops=mfma_flops(plan.info["m_eff"], P, b) if path != "PAGED" else 0))
 
 
 def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
@@ -110,11 +224,10 @@ def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
             continue
         plan = db.plan(shared_prefix_len=P, force_path=force, tuning=tune)
         ws = db.workspace(plan)
-        ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
-        path = plan.info["path_name"]
-        nbytes = algorithmic_bytes(b, path, plan.info["prefix_tokens"])
-        out[label] = dict(path=path, us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
-                          algorithmic_bytes=nbytes)
+        t = time_windows(lambda: db.step(plan, o, lse, ws), steps, warmup)
+        out[label] = prefix_leg(b, plan, t)
+        if label == "paged_shared":
+            out[label]["roofline"]["note"] = SHARED_PAGES_NOTE
         del ws
     del db
     torch.cuda.empty_cache()
@@ -126,10 +239,8 @@ def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
         dc = DeviceBatch.from_batch(c)
         plan = dc.plan(shared_prefix_len=P)
         ws = dc.workspace(plan)
-        ms = time_steps(lambda: dc.step(plan, o, lse, ws), steps, warmup)
-        nbytes = algorithmic_bytes(c, plan.info["path_name"], plan.info["prefix_tokens"])
-        out["planned_contiguous_prefix"] = dict(path=plan.info["path_name"], us_per_step=ms * 1e3,
-                                                gbs=nbytes / (ms * 1e-3) / 1e9, algorithmic_bytes=nbytes)
+        t = time_windows(lambda: dc.step(plan, o, lse, ws), steps, warmup)
+        out["planned_contiguous_prefix"] = prefix_leg(c, plan, t)
         del dc, c, ws
         torch.cuda.empty_cache()
     if not legs or "paged_unique" in legs:
@@ -137,11 +248,9 @@ def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
         du = DeviceBatch.from_batch(u)
         plan = du.plan(force_path=0)
         ws = du.workspace(plan)
-        ms = time_steps(lambda: du.step(plan, o, lse, ws), steps, warmup)
-        nbytes = algorithmic_bytes(u, "PAGED")
-        out["paged_unique"] = dict(path="PAGED", us_per_step=ms * 1e3, gbs=nbytes / (ms * 1e-3) / 1e9,
-                                   pct_peak=100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                   algorithmic_bytes=nbytes)
+        t = time_windows(lambda: du.step(plan, o, lse, ws), steps, warmup)
+        out["paged_unique"] = prefix_leg(u, plan, t)
+        out["paged_unique"]["pct_peak"] = 100 * out["paged_unique"]["gbs"] / PEAK_HBM_GBS
         del du, u, ws
     if oracle:
         n, runs = ORACLE_SAMPLE[name]
@@ -171,6 +280,14 @@ def grouped_algorithmic_bytes(batch, plan_meta, group_rows):
             + rows * d * bq)
 
 
+def grouped_mfma_flops(batch, plan_meta):
+    """Matrix-core flops of a grouped step: each kept group's members' rows
+    over its own run."""
+    gp, pp = plan_meta["group_indptr"], plan_meta["prefix_indptr"]
+    return sum(4 * int(gp[i + 1] - gp[i]) * batch.G * int(pp[i + 1] - pp[i]) * batch.d * batch.H_kv
+               for i in range(len(gp) - 1))
+
+
 def bench_groups_config(name, steps, warmup):
     """Several prompts in one step (side by side, or nested as a tree):
     PAGED over the shared pages, every group forced to the tiled cascade,
@@ -191,24 +308,126 @@ def bench_groups_config(name, steps, warmup):
     o, lse = db.new_out(), db.new_lse()
     plan = db.plan(force_path=0)
     ws = db.workspace(plan)
-    ms = time_steps(lambda: db.step(plan, o, lse, ws), steps, warmup)
-    nb = algorithmic_bytes(b, "PAGED")
-    out["paged_shared"] = dict(path="PAGED", us_per_step=ms * 1e3, algorithmic_bytes=nb, gbs=nb / (ms * 1e-3) / 1e9)
+    t = time_windows(lambda: db.step(plan, o, lse, ws), steps, warmup)
+    tokens = int(sum(int(x) for x in b.seq_lens))
+    out["paged_shared"] = dict(path="PAGED", **leg(t, algorithmic_bytes(b, "PAGED"), valu_flops=valu_flops(tokens, b),
+                                                   note=SHARED_PAGES_NOTE))
     del ws
     for label, force in (("grouped_cascade", 1), ("grouped_planned", -1)):
         plan = db.plan_grouped(force_path=force)
         meta = db.metadata(plan)
         ws = db.workspace(plan)
-        ms = time_steps(lambda: db.step_grouped(plan, meta, o, lse, ws), steps, warmup)
+        t = time_windows(lambda: db.step_grouped(plan, meta, o, lse, ws), steps, warmup)
         m = pkv.split_metadata(pkv.pkv_plan_metadata(plan), b.B, plan.info["num_groups"])
         nb = grouped_algorithmic_bytes(b, m, len(m["group_members"]) * b.H_q)
-        out[label] = dict(path=plan.info["path_name"], num_groups=plan.info["num_groups"], us_per_step=ms * 1e3,
-                          algorithmic_bytes=nb, gbs=nb / (ms * 1e-3) / 1e9)
+        out[label] = dict(path=plan.info["path_name"], num_groups=plan.info["num_groups"],
+                          **leg(t, nb, mfma_flops=grouped_mfma_flops(b, m),
+                                valu_flops=valu_flops(int(m["suffix_indptr"][-1]), b)))
         del ws, meta
     out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["grouped_planned"]["us_per_step"]
     del db, b
     torch.cuda.empty_cache()
     return out
+
+
+SWEEP_B = (1, 2, 4, 16, 64, 256, 512)
+SWEEP_G = (1, 4, 8)
+SWEEP_P = (256, 1024, 4096)
+SWEEP_DTYPES = ("bf16", "fp8")
+
+
+def dispatch_sweep(out_path, steps=10, warmup=3):
+    """The dispatcher's refit grid ("GraniKV", section 3: the dense
+    threshold is a per-GPU constant): B x G x P x K/V dtype, 8 KV heads,
+    d = 128, own tokens U{64..512}, page size 16.  Every cell times PAGED
+    over the shared prefix pages and over per-request copies, the tiled
+    cascade and DENSE (forced), and the planner's own choice; then replays
+    the planner over a grid of candidate constants (t_dense, gate_ratio,
+    launch_bytes) against the measured times, and writes every cell and
+    the replay to out_path (JSON)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_201_amd as pkv
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_decode_batch, relayout
+    log = lambda m: print(m, file=sys.stderr, flush=True)  # noqa: E731
+    cells = []
+    t_start = time.perf_counter()
+    seed = 5000
+    for kv, P, G, B in itertools.product(SWEEP_DTYPES, SWEEP_P, SWEEP_G, SWEEP_B):
+        seed += 1
+        b = make_decode_batch(seed=seed, B=B, H_q=8 * G, H_kv=8, d=128, own_len=(64, 512), prefix_len=P,
+                              page_size=16, kv_dtype=kv, device="cuda")
+        db = DeviceBatch.from_batch(b)
+        o, lse = db.new_out(), db.new_lse()
+        cell = dict(B=B, G=G, P=P, kv_dtype=kv, m_eff=B * G, us={})
+        for label, force in (("paged_shared", 0), ("cascade", 1), ("dense", 2), ("planned", -1)):
+            if force > 0 and B < 2:
+                continue  # nothing to share
+            plan = db.plan(shared_prefix_len=P, force_path=force)
+            ws = db.workspace(plan)
+            cell["us"][label] = time_windows(lambda: db.step(plan, o, lse, ws), steps, warmup, windows=3)["ms"] * 1e3
+            if force == -1:
+                cell["planned_path"] = plan.info["path_name"]
+            del ws
+        del db
+        u = relayout(b, page_size=16, seed=seed, layout="unique", device="cuda")
+        du = DeviceBatch.from_batch(u)
+        plan = du.plan(force_path=0)
+        ws = du.workspace(plan)
+        cell["us"]["paged_unique"] = time_windows(lambda: du.step(plan, o, lse, ws), steps, warmup,
+                                                  windows=3)["ms"] * 1e3
+        del du, u, ws, b, o, lse
+        torch.cuda.empty_cache()
+        choices = {k: v for k, v in cell["us"].items() if k in ("paged_shared", "cascade", "dense")}
+        cell["fastest"] = min(choices, key=choices.get)
+        cell["planned_over_fastest"] = cell["us"]["planned"] / choices[cell["fastest"]]
+        cells.append(cell)
+        log(f"sweep {len(cells)}: {kv} P={P} G={G} B={B} planned {cell['planned_path']} "
+            f"{cell['us']['planned']:.1f} us, fastest {cell['fastest']} {choices[cell['fastest']]:.1f} us "
+            f"({time.perf_counter() - t_start:.0f} s)")
+
+    # replay the planner's rule over candidate constants against the measured times
+    leg_of = {"PAGED": "paged_shared", "CASCADE": "cascade", "DENSE": "dense"}
+
+    def decide(cell, tuning):
+        Bc, Gc, Pc = cell["B"], cell["G"], cell["P"]
+        indptr = np.arange(Bc + 1, dtype=np.int32) * (Pc + 288)
+        pl = pkv.pkv_plan_create(batch=Bc, num_q_heads=8 * Gc, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                                 kv_dtype=cell["kv_dtype"], page_size=16, kv_indptr=indptr, shared_prefix_len=Pc,
+                                 tuning=tuning)
+        return pl.info["path_name"]
+
+    replay = []
+    for t_dense, ratio, launch in itertools.product((1, 256, 1024), (1, 2, 3, 4, 6), (0, 5 * 10**6, 10**7, 2 * 10**7)):
+        tune = dict(t_dense=t_dense, gate_ratio=ratio, launch_bytes=launch)
+        ratios = []
+        for cell in cells:
+            path = decide(cell, tune)
+            t = cell["us"].get(leg_of[path], cell["us"]["paged_shared"])
+            best = min(v for k, v in cell["us"].items() if k in ("paged_shared", "cascade", "dense"))
+            ratios.append(t / best)
+        multi = [r for r, c in zip(ratios, cells) if c["B"] >= 2]
+        replay.append(dict(tuning=tune, mean_ratio=float(np.mean(ratios)), worst_ratio=float(np.max(ratios)),
+                           mean_ratio_b_ge_2=float(np.mean(multi)), worst_ratio_b_ge_2=float(np.max(multi))))
+    replay.sort(key=lambda r: (r["worst_ratio_b_ge_2"], r["mean_ratio_b_ge_2"]))
+    defaults = pkv.pkv_tuning_defaults()
+    planned = [c["planned_over_fastest"] for c in cells]
+    planned_multi = [c["planned_over_fastest"] for c in cells if c["B"] >= 2]
+    rec = dict(
+        what="forced-path sweep of the dispatcher: us per step of each path, the planner's choice and its ratio "
+             "to the fastest path on the shared-page layout; paged_unique = PAGED over per-request prefix copies",
+        grid=dict(B=SWEEP_B, G=SWEEP_G, P=SWEEP_P, kv_dtype=SWEEP_DTYPES, H_kv=8, d=128, own_tokens="U{64..512}",
+                  page_size=16, steps=steps, windows=3),
+        defaults={k: defaults[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")},
+        planned_mean_ratio=float(np.mean(planned)), planned_worst_ratio=float(np.max(planned)),
+        planned_mean_ratio_b_ge_2=float(np.mean(planned_multi)),
+        planned_worst_ratio_b_ge_2=float(np.max(planned_multi)),
+        replay_best=replay[:10], cells=cells, source_sha256=kernel_source_hash(),
+        command=f"python bench.py --dispatch-sweep {out_path}")
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def page_control(steps, warmup):
@@ -218,7 +437,7 @@ def page_control(steps, warmup):
     at page sizes 16, 64 and 128, on distinct K/V (16 requests of 8192 own
     tokens: the DRAM-bound regime) and on a shared prefix (32 requests on
     the same 8192 tokens in shared physical pages: the reuse regime).  Each
-    leg issues exactly warmup + steps paged-pass dispatches, in the order
+    leg records how many paged-pass dispatches it issued, in the order
     listed, so that counter runs can attribute dispatches to legs."""
     import torch
     from paged_kv_cache_201_amd.step import DeviceBatch
@@ -237,10 +456,11 @@ def page_control(steps, warmup):
             for mode in ("page_table", "token_flat"):
                 fn = ((lambda: db.paged_pages(plan, o=o, lse=lse, ws=ws)) if mode == "page_table"
                       else (lambda: db.paged(plan, o=o, lse=lse, ws=ws)))
-                ms = time_steps(fn, steps, warmup)
+                t = time_windows(fn, steps, warmup)
+                ms = t["ms"]
                 nb = algorithmic_bytes(b, "PAGED")
                 legs.append(dict(case=case, page_size=p, mode=mode, us_per_step=ms * 1e3,
-                                 requested_gbs=nb / (ms * 1e-3) / 1e9, dispatches=steps + warmup,
+                                 requested_gbs=nb / (ms * 1e-3) / 1e9, dispatches=t["calls"],
                                  page_entries=int(b.page_indptr[-1]), tokens=int(b.seq_lens.sum())))
             del db, o, lse, ws
             if b is not base:
@@ -641,6 +861,17 @@ def cpu_baseline(batch, min_seconds=10.0, max_steps=200):
     return total / n, threads, n, total
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), else what platform says."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def oracle_sample(batch, requests, runs=1):
     """The oracle on a bounded sample of one workload's requests, on the host
     cores: gathering each request's contiguous K/V (stored values widened to
@@ -688,6 +919,8 @@ def main():
                     help="write the prefix-traffic summary from two FETCH_SIZE runs (see --only) and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CONFIGS"),
                     help="write profiles/kernels.<configs>.trace.md from a kernel-trace run of --configs CONFIGS")
+    ap.add_argument("--dispatch-sweep", metavar="OUT_JSON",
+                    help="run the dispatcher's forced-path refit grid, write it to OUT_JSON and exit")
     ap.add_argument("--page-control", action="store_true",
                     help="time the page-size control (page-table vs token-flat reads, distinct vs shared K/V) "
                          "and exit")
@@ -772,6 +1005,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.dispatch_sweep:
+        rec = dispatch_sweep(args.dispatch_sweep)
+        print(json.dumps({k: v for k, v in rec.items() if k != "cells"}), flush=True)
+        return
     if args.page_control:
         legs = page_control(args.steps, args.warmup)
         print(json.dumps(dict(page_control=legs, steps=args.steps, warmup=args.warmup,
@@ -809,9 +1046,9 @@ def main():
     # the same step with the kernel reading the page table (1,024 page entries
     # instead of 131,072 token indices)
     o, lse, ws = db128.new_out(), db128.new_lse(), db128.workspace(plan128)
-    ms = time_steps(lambda: db128.paged_pages(plan128, o=o, lse=lse, ws=ws), args.steps, args.warmup)
+    t = time_windows(lambda: db128.paged_pages(plan128, o=o, lse=lse, ws=ws), args.steps, args.warmup)
     nb = rec128["algorithmic_bytes"] - 4 * 32 * 4096 + 4 * 32 * (4096 // 128)
-    extra["c2_page128_page_table"] = dict(us_per_step=ms * 1e3, gbs=nb / (ms * 1e-3) / 1e9, algorithmic_bytes=nb)
+    extra["c2_page128_page_table"] = leg(t, nb, valu_flops=valu_flops(32 * 4096, b128))
     log(json.dumps(extra["c2_page128_page_table"]))
     del o, lse, ws
     del db128, b128
@@ -849,8 +1086,8 @@ def main():
         nbytes = rec1["algorithmic_bytes"]
         cpu = dict(value=nbytes / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
                    sample=f"the whole Llama-layer step (B=32, 4096 tokens, bf16 widened to fp64) {n_steps} times "
-                          f"back to back, {total:.1f} s: {dt:.2f} s per step on "
-                          f"{platform.processor() or platform.machine()}")
+                          f"back to back, {total:.1f} s: {dt:.2f} s per step",
+                   cpu_model=cpu_model(), cpu_count=os.cpu_count())
 
     ms = rec1["us_per_step"] / 1e3
     line = {
@@ -862,6 +1099,11 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms,
         "us_per_step": rec1["us_per_step"],
+        "us_min": rec1["us_min"],
+        "us_max": rec1["us_max"],
+        "timing": f"median of {rec1['windows']} windows of {args.steps} steps each, after {args.warmup} warm-up "
+                  f"steps and {rec1['warm_windows']} warm-up windows (until two windows agree within "
+                  f"{100 * STABLE_TOL:g} %)",
         "pct_peak": rec1["pct_peak"],
         "pct_read_ceiling": rec1["pct_read_ceiling"],
         "higher_is_better": True,
