@@ -33,8 +33,10 @@
  *     logical token t lives in slot kv_indices[kv_indptr[b] + t].
  *   - An empty token set gives o = 0 and lse = -inf.
  *   - The caller owns every buffer.  The library never allocates device
- *     memory; scratch space is the caller's workspace, sized by the plan.  The
- *     library owns only plan handles (host heap).
+ *     memory; scratch space is the caller's workspace, sized by the plan
+ *     (pkv_decode_step_noalloc instead uses one fixed device array of the
+ *     library's code object per GPU).  The library owns only plan handles
+ *     (host heap).
  *   - Every call returns a pkv_status.  Host-detectable errors return before
  *     anything is enqueued.  Kernels do not bounds-check kv_indices
  *     (pkv_validate_indices does that on the host); a bad index faults on the
@@ -384,6 +386,31 @@ PKV_API pkv_status pkv_decode_step(const pkv_plan* plan, const void* q, const pk
                            const int32_t* kv_indptr, const int32_t* kv_indices,
                            float sm_scale, void* o, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device scratch array behind pkv_decode_step_noalloc (bytes per
+ * GPU, held from the first call on that GPU until the process ends). */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pkv_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same step, same kernels and same results as pkv_decode_step, but the
+ * partial states live in a library-owned device array of
+ * PKV_NOALLOC_SCRATCH_BYTES per GPU instead of a caller's workspace (its
+ * address on the current device is looked up once per device, on the first
+ * call there; nothing is allocated by any call).  The prefix pass always
+ * runs on `stream` (the plan's concurrent_prefix side stream is not used).
+ * The scratch keeps the last call's contents; nothing in it needs clearing.
+ * Calls that overlap on one GPU (on different streams or host threads)
+ * share the array and race: serialise them.
+ *   Arguments as pkv_decode_step, without the workspace; o is required, lse
+ *   is nullable.
+ * Errors: EINVAL (as pkv_decode_step), EWORKSPACE (the plan's workspace_bytes
+ * exceeds PKV_NOALLOC_SCRATCH_BYTES; nothing is enqueued), EHIP.
+ */
+PKV_API pkv_status pkv_decode_step_noalloc(const pkv_plan* plan, const void* q, const pkv_pool* pool,
+                                   const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale,
+                                   void* o, float* lse, void* stream);
 
 /*
  * One decode step of a grouped plan: one prefix pass over every group's run

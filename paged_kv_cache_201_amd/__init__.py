@@ -92,6 +92,8 @@ _SIGS = {
                                           _vp, _vp]),
     "pkv_decode_step": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]),
+    "pkv_decode_step_noalloc": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float,
+                                                 _vp, _vp, _vp]),
     "pkv_decode_step_grouped": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, ctypes.c_float, _vp,
                                                  _vp, _vp, ctypes.c_size_t, _vp]),
     "pkv_stream_read_probe": (ctypes.c_int32, [_vp, ctypes.c_int64, _vp, ctypes.c_int32, _vp]),
@@ -380,6 +382,20 @@ def pkv_decode_step(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None,
                               _dev(kv_indices, "kv_indices", (torch.int32,)), float(sm_scale), _dev(o, "o"),
                               _dev(lse, "lse", (torch.float32,), True), ws, wsb, _stream(stream))
     _check(st, "pkv_decode_step")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def pkv_decode_step_noalloc(plan, q, pool, kv_indptr, kv_indices, sm_scale, o, lse=None, stream=None):
+    """pkv_decode_step with the library's device scratch as workspace."""
+    import torch
+    _check_sizes(plan, q=q, o=o, lse=lse, kv_indptr=kv_indptr)
+    st = _lib.pkv_decode_step_noalloc(plan.handle, _dev(q, "q"), ctypes.byref(pool),
+                                      _dev(kv_indptr, "kv_indptr", (torch.int32,)),
+                                      _dev(kv_indices, "kv_indices", (torch.int32,)), float(sm_scale), _dev(o, "o"),
+                                      _dev(lse, "lse", (torch.float32,), True), _stream(stream))
+    _check(st, "pkv_decode_step_noalloc")
 
 
 def pkv_decode_step_grouped(plan, q, pool, metadata, sm_scale, o, lse=None, workspace=None, stream=None):

@@ -189,6 +189,81 @@ pkv_status run_prefix(const pkv_plan* pl, const void* q, const pkv_pool* pool, c
     return hip_status(pkv::launch_split_reduce(r, stream));
 }
 
+// One decode step as the plan chose it, with the workspace at ws (checked
+// by the caller).  side_stream: the prefix pass may run on the library's
+// side stream when the plan asks for it.
+pkv_status run_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, float sm_scale, void* o, float* lse, void* ws, hipStream_t s,
+                           bool side_stream) {
+    if (pl->path == PKV_PATH_PAGED)
+        return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, nullptr, lse, ws, s);
+    // Cascade: both passes leave partial states in the workspace, and one
+    // kernel combines the prefix ranges and then the suffix chunks of every
+    // row into the output.
+    pkv::PrefixArgs pa = prefix_args(pl, q, pool, kv_indices + pl->indptr0, sm_scale);
+    pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
+    pa.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
+    pa.force_partial = 1;
+    pkv::PagedArgs sa = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
+    sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
+    sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
+    sa.force_partial = 1;
+    if (pl->fuse_cascade) {
+        if (pkv::launch_cascade_fused(*pl, pa, sa, s) != hipSuccess) return PKV_EHIP;
+    } else if (side_stream) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        SideStream* ss = nullptr;
+        if (side_stream_locked(&ss) != hipSuccess) return PKV_EHIP;
+        // fork: the side stream starts after everything already on `s`
+        if (hipEventRecord(ss->fork, s) != hipSuccess) return PKV_EHIP;
+        if (hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) return PKV_EHIP;
+        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, ss->stream) != hipSuccess) return PKV_EHIP;
+        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+        // join: the combine on `s` waits for the prefix pass
+        if (hipEventRecord(ss->join, ss->stream) != hipSuccess) return PKV_EHIP;
+        if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return PKV_EHIP;
+    } else {
+        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
+        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
+    }
+    pkv::SplitReduceArgs r = chunk_reduce_args(pl, sa);
+    r.pre_acc = pa.part_acc;
+    r.pre_ml = pa.part_ml;
+    r.pre_splits = pl->prefix_splits;
+    r.o = o;
+    r.lse = lse;
+    return hip_status(pkv::launch_split_reduce(r, s));
+}
+
+// Workspace of pkv_decode_step_noalloc, for callers that cannot allocate:
+// a fixed array in device memory, one copy per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names only a
+// host-side stand-in; its device address on the current GPU is taken once
+// per device with hipGetSymbolAddress and kept in g_scratch, and only that
+// address is ever handed to a kernel.  No part of it needs clearing: the
+// kernels write every partial state before the combine reads it.
+__device__ __align__(256) static unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch;
+
+hipError_t device_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        it = g_scratch.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,45 +340,24 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     if (st != PKV_OK) return st;
     if (pl->B == 0) return PKV_OK;
     if (!q || !kv_indptr || !kv_indices) return PKV_EINVAL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pl->path == PKV_PATH_PAGED)
-        return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, nullptr, lse, ws, s);
-    // Cascade: both passes leave partial states in the workspace, and one
-    // kernel combines the prefix ranges and then the suffix chunks of every
-    // row into the output.
-    pkv::PrefixArgs pa = prefix_args(pl, q, pool, kv_indices + pl->indptr0, sm_scale);
-    pa.part_acc = ws_at<float>(ws, pl->ws_prefix_acc);
-    pa.part_ml = ws_at<float>(ws, pl->ws_prefix_ml);
-    pa.force_partial = 1;
-    pkv::PagedArgs sa = paged_args(pl, q, pool, kv_indptr, kv_indices, sm_scale);
-    sa.part_acc = ws_at<float>(ws, pl->ws_paged_acc);
-    sa.part_ml = ws_at<float>(ws, pl->ws_paged_ml);
-    sa.force_partial = 1;
-    if (pl->fuse_cascade) {
-        if (pkv::launch_cascade_fused(*pl, pa, sa, s) != hipSuccess) return PKV_EHIP;
-    } else if (pl->concurrent_prefix) {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        SideStream* ss = nullptr;
-        if (side_stream_locked(&ss) != hipSuccess) return PKV_EHIP;
-        // fork: the side stream starts after everything already on `s`
-        if (hipEventRecord(ss->fork, s) != hipSuccess) return PKV_EHIP;
-        if (hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess) return PKV_EHIP;
-        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, ss->stream) != hipSuccess) return PKV_EHIP;
-        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
-        // join: the combine on `s` waits for the prefix pass
-        if (hipEventRecord(ss->join, ss->stream) != hipSuccess) return PKV_EHIP;
-        if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return PKV_EHIP;
-    } else {
-        if (pkv::launch_prefix_attn(pa, pl->prefix_rows_per_wg, s) != hipSuccess) return PKV_EHIP;
-        if (pl->num_chunks > 0 && pkv::launch_paged_split(*pl, sa, s) != hipSuccess) return PKV_EHIP;
-    }
-    pkv::SplitReduceArgs r = chunk_reduce_args(pl, sa);
-    r.pre_acc = pa.part_acc;
-    r.pre_ml = pa.part_ml;
-    r.pre_splits = pl->prefix_splits;
-    r.o = o;
-    r.lse = lse;
-    return hip_status(pkv::launch_split_reduce(r, s));
+    return run_decode_step(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, lse, ws, static_cast<hipStream_t>(stream),
+                           pl->concurrent_prefix != 0);
+}
+
+pkv_status pkv_decode_step_noalloc(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* kv_indptr,
+                                   const int32_t* kv_indices, float sm_scale, void* o, float* lse, void* stream) {
+    if (!pl || !o) return PKV_EINVAL;
+    if (pl->grouped) return PKV_EINVAL;
+    pkv_status st = check_pool(pl, pool);
+    if (st != PKV_OK) return st;
+    if (pl->workspace_bytes > (int64_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_EWORKSPACE;
+    if (pl->B == 0) return PKV_OK;
+    if (!q || !kv_indptr || !kv_indices) return PKV_EINVAL;
+    void* ws = nullptr;
+    if (pl->workspace_bytes > 0 && device_scratch(&ws) != hipSuccess) return PKV_EHIP;
+    // one stream: the side stream of concurrent_prefix would be created here
+    return run_decode_step(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, lse, ws, static_cast<hipStream_t>(stream),
+                           false);
 }
 
 pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* meta,
