@@ -231,17 +231,23 @@ def bench_prefix_config(name, steps, warmup, legs=None, oracle=False):
         del ws
     del db
     torch.cuda.empty_cache()
-    if not legs or "planned_contiguous_prefix" in legs:
-        # the prefix stored contiguously ("GraniKV", prefix placement: the
-        # read-once prefix as a plain strided operand) under the same plan
+    if not legs or "planned_contiguous_prefix" in legs or "contiguous_prefix_gathered" in legs:
+        # the prefix stored contiguously ("GraniKV", section 1, asymmetric
+        # placement): the planner, shown the host indices, reads it as base
+        # + offset; the same pool planned without them reads it slot by slot
         c = relayout(b, page_size=b.page_size, seed=RELAYOUT_SEED[name] + 1000, layout="shared", perm="prefix_first",
                      device="cuda")
         dc = DeviceBatch.from_batch(c)
-        plan = dc.plan(shared_prefix_len=P)
-        ws = dc.workspace(plan)
-        t = time_windows(lambda: dc.step(plan, o, lse, ws), steps, warmup)
-        out["planned_contiguous_prefix"] = prefix_leg(c, plan, t)
-        del dc, c, ws
+        for label, host in (("planned_contiguous_prefix", True), ("contiguous_prefix_gathered", False)):
+            if legs and label not in legs:
+                continue
+            plan = dc.plan(shared_prefix_len=P, host_indices=host)
+            ws = dc.workspace(plan)
+            t = time_windows(lambda: dc.step(plan, o, lse, ws), steps, warmup)
+            out[label] = prefix_leg(c, plan, t)
+            out[label]["prefix_base"] = plan.info["prefix_base"]
+            del ws
+        del dc, c
         torch.cuda.empty_cache()
     if not legs or "paged_unique" in legs:
         u = relayout(b, page_size=b.page_size, seed=RELAYOUT_SEED[name], layout="unique", device="cuda")
@@ -327,6 +333,26 @@ def bench_groups_config(name, steps, warmup):
     out["speedup_vs_paged_shared"] = out["paged_shared"]["us_per_step"] / out["grouped_planned"]["us_per_step"]
     del db, b
     torch.cuda.empty_cache()
+    if not name.startswith("tree"):
+        # every prompt's whole pages stored in consecutive pages ("GraniKV",
+        # section 1): each group's run read as base + offset, against the
+        # same pool with placement switched off
+        c = make_group_config(name, device="cuda", perm="identity")
+        dc = DeviceBatch.from_batch(c)
+        for label, placement in (("grouped_planned_contiguous", 1), ("grouped_contiguous_gathered", 0)):
+            plan = dc.plan_grouped(tuning=dict(prefix_placement=placement))
+            meta = dc.metadata(plan)
+            ws = dc.workspace(plan)
+            t = time_windows(lambda: dc.step_grouped(plan, meta, o, lse, ws), steps, warmup)
+            m = pkv.split_metadata(pkv.pkv_plan_metadata(plan), c.B, plan.info["num_groups"])
+            nb = grouped_algorithmic_bytes(c, m, len(m["group_members"]) * c.H_q)
+            out[label] = dict(path=plan.info["path_name"], num_groups=plan.info["num_groups"],
+                              contiguous_prefixes=plan.info["contiguous_prefixes"],
+                              **leg(t, nb, mfma_flops=grouped_mfma_flops(c, m),
+                                    valu_flops=valu_flops(int(m["suffix_indptr"][-1]), c)))
+            del ws, meta
+        del dc, c
+        torch.cuda.empty_cache()
     return out
 
 

@@ -110,6 +110,11 @@ typedef struct pkv_problem {
     int32_t shared_prefix_len;  /* P: the first P tokens of every request are the same
                                    tokens, stored in shared pages; 0 = no shared prefix */
     int32_t force_path;         /* -1: let the planner choose; else a pkv_path */
+    const int32_t* kv_indices;  /* host, [kv_indptr[B]], optional (NULL: not given): the same
+                                   values as the device indices later passed to the attention
+                                   calls.  Lets the planner find a shared prefix stored as one
+                                   run of consecutive slots ([P2] s.1, asymmetric placement),
+                                   which the prefix pass then reads as base + offset */
 } pkv_problem;
 
 /* Constants of the planner.  pkv_tuning_defaults() returns the gfx950 values. */
@@ -134,6 +139,9 @@ typedef struct pkv_tuning {
                                          (rounded up to a multiple of 64) */
     int32_t max_heads_per_item; /* paged pass: at most this many KV heads per work item
                                    (0: as many as one wave-wide load covers) */
+    int32_t prefix_placement;   /* 1: a shared prefix whose slots are one run of consecutive
+                                   slots is read by the prefix pass as base + offset, without
+                                   per-token slot indices ([P2] s.1); 0: always by slot index */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */
@@ -154,6 +162,10 @@ typedef struct pkv_plan_info {
     int64_t workspace_bytes;    /* device scratch the plan's calls need (0 allowed) */
     int32_t num_groups;         /* grouped plans: prefix groups that run a prefix pass (else 0) */
     int64_t metadata_ints;      /* grouped plans: int32 entries of the metadata block (else 0) */
+    int32_t prefix_base;        /* single-prefix plans: slot of the prefix's first token when the
+                                   prefix pass reads it as one run of consecutive slots, else -1 */
+    int32_t contiguous_prefixes; /* prefix runs the prefix pass reads as base + offset (single
+                                    plan: 0 or 1; grouped plan: kept groups) */
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
@@ -204,10 +216,16 @@ PKV_API pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t*
  * paged pass's work items -- the attended positions of all requests, request
  * after request, cut into equal chunks (by logical position, so results do
  * not depend on page size or page placement) -- the prefix pass's ranges and
- * the workspace size.  tuning may be NULL (gfx950 defaults).  The problem's kv_indptr is
- * read during the call and not kept.  *out receives a new handle that the
- * caller frees with pkv_plan_destroy; it can be reused on any stream for any
- * step with the same problem.
+ * the workspace size.  tuning may be NULL (gfx950 defaults).  The problem's kv_indptr
+ * (and kv_indices, if given) are read during the call and not kept.  Prefix
+ * placement ([P2] s.1: a shared prefix stored contiguously is read as a plain
+ * strided operand): with the problem's kv_indices given, tuning.prefix_placement
+ * set and a CASCADE or DENSE path, a prefix whose slots
+ * kv_indices[kv_indptr[0] + t], t < prefix_tokens, are first + t is read by the
+ * prefix pass as first + t (info.prefix_base = first); otherwise slot by
+ * slot.  *out receives a new handle that the caller frees with
+ * pkv_plan_destroy; it can be reused on any stream for any step with the same
+ * problem.
  * Errors: EINVAL (null pointer, sizes, non-multiple heads, bad indptr, prefix
  * longer than a request, bad force_path, forced prefix path with no whole
  * shared page), EUNSUPPORTED (head_dim, dtype pair, or group size not built;
@@ -268,6 +286,10 @@ PKV_API pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv
  *   prefix_indptr  [NG+1]  offsets into prefix_indices
  *   prefix_indices [prefix_indptr[NG]]  slots of each group's run of tokens
  *   group_parent   [NG]    nearest enclosing kept group, -1 for none
+ *   group_prefix_base [NG] slot of the first token of each group's run when
+ *                  the run is one stretch of consecutive physical pages and the
+ *                  tuning's prefix_placement is set (read as base + offset),
+ *                  else -1
  *   followed by tables only the kernels read.
  * Errors: EINVAL (null plan, plan not from pkv_plan_create_grouped, null out
  * with a non-empty block), ERANGE (capacity too small).
@@ -338,7 +360,10 @@ PKV_API pkv_status pkv_paged_decode_attn_pages(const pkv_plan* plan, const void*
  * prefix_tokens rows listed by prefix_indices.
  *   q              device, [B][H_q][d] bf16
  *   prefix_indices device, [prefix_len] int32 slots (typically request 0's
- *                  first prefix_len entries of kv_indices)
+ *                  first prefix_len entries of kv_indices).  When the plan's
+ *                  prefix_base is set the pass reads slots prefix_base + t
+ *                  instead and does not read this array (it must hold the
+ *                  same slots, as the plan saw them)
  *   prefix_len     must equal the plan's prefix_tokens
  *   o_p            device, [B][H_q][d] fp32, normalised prefix output
  *   lse_p          device, [B][H_q] fp32

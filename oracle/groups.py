@@ -88,14 +88,20 @@ def detect_prefix_groups(page_size, page_indptr, page_indices, seq_lens):
 
 
 def plan_groups(*, H_q, H_kv, d, q_dtype, kv_dtype, page_size, page_indptr, page_indices, seq_lens,
-                force_path, t_dense, gate_ratio, launch_bytes):
+                force_path, t_dense, gate_ratio, launch_bytes, prefix_placement=1):
     """The kept groups, each planned on its own run.
 
     Returns ``(groups, path_of)``: ``groups`` lists the kept groups in
     depth-first order as dicts with ``members``, ``start_tokens``,
     ``prefix_tokens`` (the run's tokens), ``parent`` (index of the nearest
-    kept ancestor, -1 if none), ``path`` and ``m_eff``; ``path_of[b]`` lists
-    the indices of the kept groups request b belongs to, outermost first.
+    kept ancestor, -1 if none), ``path``, ``m_eff`` and ``prefix_base``;
+    ``path_of[b]`` lists the indices of the kept groups request b belongs
+    to, outermost first.
+
+    ``prefix_base`` (prefix placement, "GraniKV" section 1): with placement
+    enabled, a run whose whole pages are consecutive physical pages is one
+    stretch of consecutive slots, read as base + offset from the slot of its
+    first token; otherwise -1.
     """
     p = int(page_size)
     B = len(seq_lens)
@@ -117,8 +123,13 @@ def plan_groups(*, H_q, H_kv, d, q_dtype, kv_dtype, page_size, page_indptr, page
         kept_at[i] = len(kept)
         for b in members:
             path_of[b].append(len(kept))
+        pages = [int(x) for x in page_indices[int(page_indptr[members[0]]):int(page_indptr[members[0] + 1])]]
+        run_pages = pages[g["start_pages"]:g["shared_pages"]]
+        consecutive = all(run_pages[j + 1] == run_pages[j] + 1 for j in range(len(run_pages) - 1))
+        base = run_pages[0] * p if (prefix_placement and consecutive) else -1
         kept.append({"members": list(members), "start_tokens": start, "prefix_tokens": dec["prefix_tokens"],
-                     "parent": kept_at[a] if a >= 0 else -1, "path": dec["path"], "m_eff": dec["m_eff"]})
+                     "parent": kept_at[a] if a >= 0 else -1, "path": dec["path"], "m_eff": dec["m_eff"],
+                     "prefix_base": base})
     return kept, path_of
 
 

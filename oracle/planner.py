@@ -24,6 +24,15 @@ Rule, in order (all arithmetic in Python integers):
    vector ALU, so its tokens cost about the time of bf16 tokens; measured)
 4. M_eff >= t_dense -> DENSE, else CASCADE.
 
+Prefix placement ("GraniKV", section 1, asymmetric paging: the shared prefix
+is placed contiguously when its radix node is created, so that the dense
+kernel reads it as a plain strided operand).  Reading taken: on a CASCADE or
+DENSE plan, when the planner is shown the prefix's slots and placement is
+enabled, a prefix whose slots are first, first + 1, ..., first + P' - 1 (P'
+= prefix_tokens) is read as base + offset with base = first; otherwise (or
+on PAGED) base = -1 and the prefix is read slot by slot.  The result is the
+same either way; only the addressing differs.
+
 Problem checks mirror what the library accepts: d in {64, 128}; (q, kv)
 dtype in {(f32, f32), (bf16, bf16), (bf16, fp8)}; G in {1, 2, 4, 8}; the
 prefix kernels take bf16 queries over bf16 K/V, or over fp8 K/V at d = 128.
@@ -48,7 +57,28 @@ class PlanError(ValueError):
 
 
 def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
-         shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes):
+         shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes, prefix_slots=None,
+         prefix_placement=1):
+    """Returns dict(path, m_eff, shared_pages, prefix_tokens, prefix_base).
+
+    ``prefix_slots`` (optional): the slots of the first request's first
+    tokens, at least ``prefix_tokens`` of them; ``prefix_base`` follows the
+    placement rule above.
+    """
+    out = _plan_path(B=B, H_q=H_q, H_kv=H_kv, d=d, q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=page_size,
+                     seq_lens=seq_lens, shared_prefix_len=shared_prefix_len, force_path=force_path,
+                     t_dense=t_dense, gate_ratio=gate_ratio, launch_bytes=launch_bytes)
+    out["prefix_base"] = -1
+    n = out["prefix_tokens"]
+    if out["path"] != PAGED and prefix_placement and prefix_slots is not None and n > 0:
+        first = int(prefix_slots[0])
+        if first >= 0 and all(int(prefix_slots[t]) == first + t for t in range(n)):
+            out["prefix_base"] = first
+    return out
+
+
+def _plan_path(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
+               shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes):
     """Returns dict(path, m_eff, shared_pages, prefix_tokens).
 
     ``shared_pages`` is floor(P / p) whenever a prefix is declared;

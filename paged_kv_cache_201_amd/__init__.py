@@ -49,7 +49,7 @@ class pkv_problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("kv_indptr", _i32p), ("shared_prefix_len", ctypes.c_int32),
-                ("force_path", ctypes.c_int32)]
+                ("force_path", ctypes.c_int32), ("kv_indices", _i32p)]
 
 
 class pkv_tuning(ctypes.Structure):
@@ -57,7 +57,7 @@ class pkv_tuning(ctypes.Structure):
                 ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
                 ("concurrent_prefix", ctypes.c_int32), ("fuse_cascade", ctypes.c_int32),
                 ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32),
-                ("max_heads_per_item", ctypes.c_int32)]
+                ("max_heads_per_item", ctypes.c_int32), ("prefix_placement", ctypes.c_int32)]
 
 
 class pkv_plan_info(ctypes.Structure):
@@ -65,7 +65,8 @@ class pkv_plan_info(ctypes.Structure):
                 ("prefix_tokens", ctypes.c_int32), ("split_tokens", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
                 ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("num_groups", ctypes.c_int32), ("metadata_ints", ctypes.c_int64)]
+                ("num_groups", ctypes.c_int32), ("metadata_ints", ctypes.c_int64),
+                ("prefix_base", ctypes.c_int32), ("contiguous_prefixes", ctypes.c_int32)]
 
 
 _SIGS = {
@@ -228,11 +229,18 @@ class Plan:
 
 
 def pkv_plan_create(*, batch, num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype, page_size, kv_indptr,
-                    shared_prefix_len=0, force_path=-1, tuning=None) -> Plan:
-    """Plan one step.  q_dtype/kv_dtype: "f32", "bf16" or "fp8" (or the codes)."""
+                    shared_prefix_len=0, force_path=-1, tuning=None, kv_indices=None) -> Plan:
+    """Plan one step.  q_dtype/kv_dtype: "f32", "bf16" or "fp8" (or the codes).
+    kv_indices (host, optional) lets the planner find a contiguously placed
+    prefix."""
     ip, ip_p = _host_i32(kv_indptr)
+    ix_p = None
+    if kv_indices is not None:
+        ix, ix_p = _host_i32(kv_indices if len(kv_indices) else np.zeros(1, np.int32))
+        if len(kv_indices) < int(ip[-1]) if len(ip) else False:
+            raise ValueError("kv_indices is shorter than kv_indptr[B]")
     pr = pkv_problem(batch, num_q_heads, num_kv_heads, head_dim, DTYPE_CODES.get(q_dtype, q_dtype),
-                     DTYPE_CODES.get(kv_dtype, kv_dtype), page_size, ip_p, shared_prefix_len, force_path)
+                     DTYPE_CODES.get(kv_dtype, kv_dtype), page_size, ip_p, shared_prefix_len, force_path, ix_p)
     tp = None
     if tuning is not None:
         d = pkv_tuning_defaults()
@@ -280,7 +288,7 @@ def split_metadata(block, batch, num_groups):
     out, off = {}, 0
     for name, n in (("suffix_indptr", batch + 1), ("suffix_indices", None), ("group_indptr", num_groups + 1),
                     ("group_members", None), ("prefix_indptr", num_groups + 1), ("prefix_indices", None),
-                    ("group_parent", num_groups)):
+                    ("group_parent", num_groups), ("group_prefix_base", num_groups)):
         if n is None:
             ptr = out[{"suffix_indices": "suffix_indptr", "group_members": "group_indptr",
                        "prefix_indices": "prefix_indptr"}[name]]

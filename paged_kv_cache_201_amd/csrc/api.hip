@@ -151,6 +151,7 @@ pkv::PrefixArgs prefix_args(const pkv_plan* pl, const void* q, const pkv_pool* p
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
     a.prefix_indices = prefix_indices;
+    a.prefix_base = pl->prefix_base;
     a.B = pl->B;
     a.H_kv = pl->H_kv;
     a.G = pl->G;
@@ -388,6 +389,7 @@ pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_
     pa.k_scale = pool->k_scale;
     pa.v_scale = pool->v_scale;
     pa.prefix_indices = meta + pl->meta_prefix_indices;
+    pa.prefix_base = -1;  // each group's own placement is in the group table
     pa.B = pl->B;
     pa.H_kv = pl->H_kv;
     pa.G = pl->G;

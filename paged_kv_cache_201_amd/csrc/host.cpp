@@ -90,7 +90,7 @@ pkv_status check_problem(const pkv_problem* pr, const pkv_tuning* tuning, pkv_tu
     if (tu->t_dense < 1 || tu->gate_ratio < 0 || tu->launch_bytes < 0 || tu->target_workgroups < 1 ||
         tu->min_split_tokens < 1 || tu->concurrent_prefix < 0 || tu->concurrent_prefix > 1 ||
         tu->fuse_cascade < 0 || tu->prefix_target_workgroups < 1 || tu->min_prefix_split_tokens < 1 ||
-        tu->max_heads_per_item < 0)
+        tu->max_heads_per_item < 0 || tu->prefix_placement < 0 || tu->prefix_placement > 1)
         return PKV_EINVAL;
     const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
     if (B < 0 || H_kv < 1 || H_q < 1 || pr->page_size < 1 || pr->head_dim < 1) return PKV_EINVAL;
@@ -271,6 +271,7 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->prefix_target_workgroups = 256;
     out->min_prefix_split_tokens = 64;
     out->max_heads_per_item = 0;
+    out->prefix_placement = 1;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -375,6 +376,16 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     pl->indptr0 = B > 0 ? pr->kv_indptr[0] : 0;
     pl->prefix_len = P;
     pl->path = path;
+    // Prefix placement ("GraniKV", s.1): a prefix stored as one run of
+    // consecutive slots is read by the prefix pass as base + offset.
+    pl->prefix_base = -1;
+    if (path != PKV_PATH_PAGED && tu.prefix_placement && pr->kv_indices) {
+        const int32_t* pre = pr->kv_indices + pl->indptr0;
+        bool run = true;
+        for (int64_t t = 1; t < prefix_tokens && run; ++t) run = (int64_t)pre[t] == (int64_t)pre[0] + t;
+        if (run && pre[0] >= 0) pl->prefix_base = pre[0];
+    }
+    pl->contiguous_prefixes = pl->prefix_base >= 0 ? 1 : 0;
     pl->m_eff = (int32_t)m_eff;
     pl->shared_pages = (int32_t)shared_pages;
     pl->prefix_tokens = (int32_t)prefix_tokens;
@@ -549,6 +560,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         std::vector<int32_t> members;
         int32_t start_tokens, prefix_tokens, parent, path, m_eff, rows_per_wg, row_tiles, split_tokens, splits;
         int32_t slot_base;
+        int32_t prefix_base;  // first slot when the run's pages are consecutive, else -1
         int64_t items;
     };
     std::vector<Group> groups;
@@ -572,6 +584,16 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         g.m_eff = (int32_t)(n * G);
         g.rows_per_wg = path == PKV_PATH_DENSE ? pkv::kDenseRowsPerWg : pkv::kTiledRowsPerWg;
         g.row_tiles = (int32_t)ceil_div(g.m_eff, g.rows_per_wg);
+        // Prefix placement ("GraniKV", s.1): a run stored in consecutive
+        // physical pages is one run of consecutive slots, read as base +
+        // offset.
+        g.prefix_base = -1;
+        if (tu.prefix_placement) {
+            const int32_t* pages = page_indices + page_indptr[nd.members[0]];
+            bool run = true;
+            for (int32_t j = nd.start + 1; j < nd.end && run; ++j) run = (int64_t)pages[j] == (int64_t)pages[j - 1] + 1;
+            if (run) g.prefix_base = pages[nd.start] * p;
+        }
         kept_at[i] = (int32_t)groups.size();
         for (int32_t b : nd.members) path_of[b].push_back(kept_at[i]);
         groups.push_back(std::move(g));
@@ -667,6 +689,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     pl->meta_prefix_indptr = take(NG + 1);
     pl->meta_prefix_indices = take(prefix_sum);
     pl->meta_group_parent = take(NG);
+    pl->meta_group_base = take(NG);
     pl->meta_pre_count = take(B);
     pl->meta_desc = take((int64_t)NG * pkv::kGroupDescInts);
     std::unique_ptr<pkv_plan> owner(pl);
@@ -707,6 +730,10 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
             pptr[i + 1] = pptr[i] + g.prefix_tokens;
         }
         for (int32_t i = 0; i < NG; ++i) m[pl->meta_group_parent + i] = groups[i].parent;
+        for (int32_t i = 0; i < NG; ++i) {
+            m[pl->meta_group_base + i] = groups[i].prefix_base;
+            pl->contiguous_prefixes += groups[i].prefix_base >= 0;
+        }
         for (int32_t b = 0; b < B; ++b) {
             const int32_t last = path_of[b].empty() ? -1 : path_of[b].back();
             m[pl->meta_pre_count + b] = last >= 0 ? groups[last].slot_base + groups[last].splits : 0;
@@ -728,7 +755,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
                 d[6] = gptr[i];
                 d[7] = (int32_t)g.members.size();
                 d[8] = g.slot_base;
-                d[9] = 0;
+                d[9] = g.prefix_base;
             }
     }
 
@@ -771,6 +798,8 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     info->workspace_bytes = pl->workspace_bytes;
     info->num_groups = pl->num_groups;
     info->metadata_ints = (int64_t)pl->meta.size();
+    info->prefix_base = pl->grouped ? -1 : pl->prefix_base;
+    info->contiguous_prefixes = pl->contiguous_prefixes;
     return PKV_OK;
 }
 

@@ -86,6 +86,7 @@ struct PrefixArgs {
     const float* k_scale;     // [H_kv], fp8 only
     const float* v_scale;
     const int32_t* prefix_indices;
+    int32_t prefix_base;      // >= 0: prefix token t is slot prefix_base + t (prefix_indices unread)
     int32_t B, H_kv, G, D;
     int32_t prefix_len;
     int32_t split_tokens;

@@ -39,7 +39,8 @@ constexpr int32_t kPrefixTokenQuantum = 64;
 // Ints per row of the prefix-group table a grouped step hands the prefix
 // kernel: running end of the group's items, offset and length of its prefix
 // indices, range size, ranges, query-row tiles, offset and count of its
-// members, first partial-state slot of its ranges, one unused.
+// members, first partial-state slot of its ranges, slot of the run's first
+// token when the run is read as base + offset (else -1).
 constexpr int32_t kGroupDescInts = 10;
 constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // Paged-pass chunks hold a multiple of this many tokens, and at most
@@ -61,6 +62,8 @@ struct pkv_plan {
     int32_t B, H_q, H_kv, D, G, q_dtype, kv_dtype, page_size;
     int32_t indptr0;          // host kv_indptr[0]
     int32_t prefix_len;       // declared shared prefix (tokens)
+    int32_t prefix_base;      // prefix read as slots prefix_base + t (-1: by slot index)
+    int32_t contiguous_prefixes; // prefix runs read as base + offset
     // decisions
     int32_t path, m_eff, shared_pages, prefix_tokens;
     // paged pass
@@ -87,6 +90,6 @@ struct pkv_plan {
     int32_t dense_items, tiled_items; // prefix work items per launch
     // offsets (in ints) of the metadata block's arrays
     int64_t meta_suffix_indptr, meta_suffix_indices, meta_group_indptr, meta_members;
-    int64_t meta_prefix_indptr, meta_prefix_indices, meta_group_parent, meta_pre_count, meta_desc;
+    int64_t meta_prefix_indptr, meta_prefix_indices, meta_group_parent, meta_group_base, meta_pre_count, meta_desc;
     std::vector<int32_t> meta;        // the block itself, copied out by pkv_plan_metadata
 };

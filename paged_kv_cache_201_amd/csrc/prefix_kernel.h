@@ -164,6 +164,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     int row_tiles = a.row_tiles, prefix_len = a.prefix_len, split_tokens = a.split_tokens;
     int M = a.B * a.G;
     const int32_t* prefix = a.prefix_indices;
+    int prefix_base = a.prefix_base;  // >= 0: the run is slots prefix_base + t, no index reads
     const int32_t* members = nullptr;
     int slot_base = 0;  // first partial-state slot of this group's ranges
     if (a.groups) {
@@ -183,7 +184,9 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         members = a.members + gd[6];
         M = gd[7] * a.G;
         slot_base = gd[8];
+        prefix_base = gd[9];
     }
+    prefix_base = __builtin_amdgcn_readfirstlane(prefix_base);
     const int tile = item % row_tiles;
     const int g = (item / row_tiles) % a.H_kv;
     const int split = item / (row_tiles * a.H_kv);
@@ -199,8 +202,10 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     const int n_tok = te - ts;
     const int ntiles = (n_tok + KT - 1) / KT;
 
-    // the range's slot indices, padded with the last one to whole tiles
-    for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = prefix[ts + min(i, n_tok - 1)];
+    // the range's slot indices, padded with the last one to whole tiles (a
+    // prefix placed as one run of slots needs none: "GraniKV", s.1)
+    if (prefix_base < 0)
+        for (int i = threadIdx.x; i < ntiles * KT; i += NT) s_idx[i] = prefix[ts + min(i, n_tok - 1)];
 
     // This lane's query row: (request, query head) of the item's rows.
     const int r = tile * 32 * NW + wave * 32 + lr;
@@ -251,13 +256,16 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     };
     // The slot of the tile row each of this lane's copies reads.  They are
     // read from LDS a tile ahead (read_slots), so that issuing a tile right
-    // after the barrier does not wait on an LDS round trip.
+    // after the barrier does not wait on an LDS round trip; a run placed
+    // contiguously gives them as base + position (padded rows repeat the
+    // last token, as the staged indices do).
     int next_slot[PER_WAVE];
     auto read_slots = [&](int n) {
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
             const int p = (wave * PER_WAVE + j) * 64 + lane;
-            next_slot[j] = s_idx[n * KT + (F8 ? p / (D / 16) : p / CPR)];
+            const int row = n * KT + (F8 ? p / (D / 16) : p / CPR);
+            next_slot[j] = prefix_base >= 0 ? prefix_base + ts + min(row, n_tok - 1) : s_idx[row];
         }
     };
     // Issue the copies of tile n, whose slots read_slots(n) has fetched.

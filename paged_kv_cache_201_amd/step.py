@@ -53,11 +53,14 @@ class DeviceBatch:
         return cls(batch.q, batch.k_pool, batch.v_pool, batch.page_size, batch.page_indptr, batch.page_indices,
                    batch.seq_lens, batch.k_scale, batch.v_scale, device)
 
-    def plan(self, shared_prefix_len=0, force_path=-1, tuning=None) -> Plan:
+    def plan(self, shared_prefix_len=0, force_path=-1, tuning=None, host_indices=True) -> Plan:
+        """host_indices: hand the planner the host kv_indices as well, so that a
+        contiguously placed prefix is found (and read as base + offset)."""
         return pkv_plan_create(batch=self.B, num_q_heads=self.H_q, num_kv_heads=self.H_kv, head_dim=self.d,
                                q_dtype=self.q_dtype, kv_dtype=self.kv_dtype, page_size=self.page_size,
                                kv_indptr=self.kv_indptr_host, shared_prefix_len=shared_prefix_len,
-                               force_path=force_path, tuning=tuning)
+                               force_path=force_path, tuning=tuning,
+                               kv_indices=self.kv_indices_host if host_indices else None)
 
     def plan_grouped(self, force_path=-1, tuning=None) -> Plan:
         """Plan with the prefix groups found in the page table."""

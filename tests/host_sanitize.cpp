@@ -130,6 +130,7 @@ pkv_tuning random_tuning() {
         tu.prefix_target_workgroups = uni(1, 2048);
         tu.min_prefix_split_tokens = uni(1, 2048);
         tu.max_heads_per_item = uni(0, 8);
+        tu.prefix_placement = uni(0, 1);
     }
     return tu;
 }
@@ -159,6 +160,7 @@ void check_plan(const Table& t, int* planned) {
         random_heads(pr);
         pr.page_size = t.p;
         pr.kv_indptr = ptr(ip);
+        pr.kv_indices = uni(0, 1) ? ptr(idx) : nullptr;  // lets the planner look for a contiguous prefix
         pr.shared_prefix_len = t.B > 0 ? uni(0, min_len) : 0;
         pr.force_path = uni(-1, 2);
         pkv_tuning tu = random_tuning();

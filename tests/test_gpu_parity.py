@@ -846,3 +846,71 @@ def test_random_prefix_trees_vs_oracle(case):
     plan = db.plan_grouped(tuning=tune)
     o, lse = _grouped_run(db, plan)
     check_close(kv, o, lse, o_ref, lse_ref, what + f" groups={plan.info['num_groups']} path={plan.info['path_name']}")
+
+
+# ------------------------------------------------------- prefix placement --
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_contiguous_prefix_read_as_base_plus_offset(kv_dtype):
+    """A shared prefix stored as one run of consecutive slots ("GraniKV",
+    section 1, asymmetric placement): the plan finds the run from the host
+    indices and the prefix pass reads slots base + t with no index staging.
+    Same bits as the slot-by-slot read of the same pool, on every prefix
+    path (tiled, DENSE fused and separate) and for the prefix pass alone;
+    within tolerance of the oracle."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    P = 1000
+    b0 = make_decode_batch(seed=81, B=40, H_q=32, H_kv=8, d=128, own_len=(1, 300), prefix_len=P, page_size=16,
+                           kv_dtype=kv_dtype, pool_factor=2)
+    b = relayout(b0, page_size=16, seed=82, layout="shared", perm="prefix_first", pool_factor=2,
+                 prefix_first_page=37)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    for force, tune in ((1, None), (2, None), (2, dict(fuse_cascade=0)), (2, dict(fuse_cascade=1)),
+                        (2, dict(prefix_target_workgroups=4096, min_prefix_split_tokens=64))):
+        strided = db.plan(shared_prefix_len=P, force_path=force, tuning=tune)
+        gathered = db.plan(shared_prefix_len=P, force_path=force, tuning=tune, host_indices=False)
+        assert strided.info["prefix_base"] == 37 * 16 and strided.info["contiguous_prefixes"] == 1
+        assert gathered.info["prefix_base"] == -1 and gathered.info["contiguous_prefixes"] == 0
+        say(f"contiguous prefix {kv_dtype} force={force} tune={tune}: base + offset, then slot by slot")
+        o1, l1 = db.step(strided)
+        o2, l2 = db.step(gathered)
+        torch.cuda.synchronize()
+        check_close(kv_dtype, o1, l1, o_ref, lse_ref, f"contiguous prefix {kv_dtype} force={force}")
+        assert same_bits(o1, o2) and same_bits(l1, l2), f"placement changed the bits ({kv_dtype}, {force}, {tune})"
+    say(f"contiguous prefix {kv_dtype}: prefix pass alone")
+    strided = db.plan(shared_prefix_len=P, force_path=2)
+    gathered = db.plan(shared_prefix_len=P, force_path=2, host_indices=False)
+    p1, q1 = db.prefix(strided)
+    p2, q2 = db.prefix(gathered)
+    torch.cuda.synchronize()
+    n = strided.info["prefix_tokens"]
+    op_ref, lp_ref = ob.prefix_reference(b, n)
+    check_close(kv_dtype, p1, q1, op_ref, lp_ref, f"contiguous prefix pass {kv_dtype}")
+    assert same_bits(p1, p2) and same_bits(q1, q2)
+    # the scattered layout of the same tokens: no run, read slot by slot
+    assert DeviceBatch.from_batch(b0).plan(shared_prefix_len=P, force_path=2).info["prefix_base"] == -1
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_grouped_contiguous_runs_read_as_base_plus_offset(kv_dtype):
+    """Several prefixes each stored in consecutive pages: every kept group's
+    run is read as base + offset (the planner finds it in the page table);
+    same bits as with placement switched off, for DENSE (fused) and tiled
+    groups; within tolerance of the oracle."""
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    b = make_grouped_batch(seed=84, B=40, H_q=32, H_kv=8, d=128, groups=[(12, 700), (9, 300), (5, 64)],
+                           own_len=(0, 120), page_size=16, perm="identity", kv_dtype=kv_dtype)
+    o_ref, lse_ref = ob.batch_reference(b)
+    db = DeviceBatch.from_batch(b)
+    for t_dense in (1, 40):
+        on = db.plan_grouped(tuning=dict(gate_ratio=0, t_dense=t_dense))
+        off = db.plan_grouped(tuning=dict(gate_ratio=0, t_dense=t_dense, prefix_placement=0))
+        assert on.info["num_groups"] == 3 and on.info["contiguous_prefixes"] == 3
+        assert off.info["contiguous_prefixes"] == 0
+        meta = pkv.split_metadata(pkv.pkv_plan_metadata(on), b.B, 3)
+        assert (meta["group_prefix_base"] >= 0).all()
+        o1, l1 = _grouped_run(db, on)
+        o2, l2 = _grouped_run(db, off)
+        check_close(kv_dtype, o1, l1, o_ref, lse_ref, f"grouped contiguous {kv_dtype} t_dense={t_dense}")
+        assert same_bits(o1, o2) and same_bits(l1, l2), f"placement changed the bits ({kv_dtype}, {t_dense})"

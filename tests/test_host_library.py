@@ -52,7 +52,8 @@ def test_status_strings_and_version():
     assert d["concurrent_prefix"] in (0, 1) and 0 <= d["fuse_cascade"] <= 1000
     assert d["prefix_target_workgroups"] >= 1 and 1 <= d["min_prefix_split_tokens"] <= 1024
     assert d["max_heads_per_item"] >= 0
-    assert len(d) == 10
+    assert d["prefix_placement"] in (0, 1)
+    assert len(d) == 11
 
 
 # ---------------------------------------------------------------- lowering --
@@ -112,7 +113,7 @@ def test_validate_indices():
 TUNE = pkv.pkv_tuning_defaults()
 
 
-def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None):
+def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None, kv_indices=None):
     t = dict(TUNE)
     t.update(tune or {})
     lens = [int(x) for x in np.atleast_1d(L)] if np.ndim(L) else [int(L)] * B
@@ -121,14 +122,15 @@ def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None
     try:
         ref = op.plan(B=B, H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype=q, kv_dtype=kv, page_size=p, seq_lens=lens,
                       shared_prefix_len=P, force_path=force, t_dense=t["t_dense"], gate_ratio=t["gate_ratio"],
-                      launch_bytes=t["launch_bytes"])
+                      launch_bytes=t["launch_bytes"], prefix_slots=kv_indices,
+                      prefix_placement=t["prefix_placement"])
     except op.PlanError as e:
         err_ref = e.code
     got = err_got = None
     try:
         got = pkv.pkv_plan_create(batch=B, num_q_heads=H_kv * G, num_kv_heads=H_kv, head_dim=d, q_dtype=q,
                                   kv_dtype=kv, page_size=p, kv_indptr=indptr, shared_prefix_len=P,
-                                  force_path=force, tuning=t).info
+                                  force_path=force, tuning=t, kv_indices=kv_indices).info
     except pkv.PkvError as e:
         err_got = e.name
     assert err_ref == err_got, (B, G, P, p, err_ref, err_got)
@@ -137,7 +139,36 @@ def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None
         assert got["m_eff"] == ref["m_eff"]
         assert got["shared_pages"] == ref["shared_pages"]
         assert got["prefix_tokens"] == ref["prefix_tokens"]
+        assert got["prefix_base"] == ref["prefix_base"], (got["prefix_base"], ref["prefix_base"])
+        assert got["contiguous_prefixes"] == int(ref["prefix_base"] >= 0)
     return got
+
+
+def test_prefix_placement_matches_oracle():
+    """The single-prefix plan finds a prefix stored as one run of slots from
+    the host indices it is shown, bit for bit as the oracle's rule."""
+    rng = np.random.default_rng(17)
+    n_run = 0
+    for it in range(400):
+        B = int(rng.integers(1, 40))
+        p = int(rng.choice([1, 2, 16, 64]))
+        P = int(rng.integers(0, 600))
+        lens = [P + int(rng.integers(0, 100)) for _ in range(B)]
+        total = sum(lens)
+        idx = rng.permutation(4 * total + 8)[:total].astype(np.int32)
+        if it % 3 != 2:
+            # the prefix (request 0's first P tokens) placed as one run
+            first = int(rng.integers(0, 1000))
+            idx[:P] = np.arange(first, first + P)
+            if it % 3 == 1 and P > 1:
+                idx[int(rng.integers(1, P))] += 1  # ... with one slot out of line
+        tune = dict(gate_ratio=int(rng.integers(0, 2)), launch_bytes=0, t_dense=int(rng.integers(1, 300)),
+                    prefix_placement=int(rng.integers(0, 2)) if it % 5 == 0 else 1)
+        got = _both(B, int(rng.choice([1, 2, 4, 8])), P, p, lens, force=int(rng.choice([-1, -1, 0, 1, 2])),
+                    tune=tune, kv_indices=idx) if P >= p or it % 4 else None
+        if got is not None and got["prefix_base"] >= 0:
+            n_run += 1
+    assert n_run > 50
 
 
 def test_planner_grid_matches_oracle():
@@ -249,7 +280,8 @@ def _grouped_both(p, ptr, pages, lens, G=4, H_kv=2, d=64, q="bf16", kv="bf16", f
     try:
         ref = og.plan_groups(H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype=q, kv_dtype=kv, page_size=p, page_indptr=ptr,
                              page_indices=pages, seq_lens=lens, force_path=force, t_dense=t["t_dense"],
-                             gate_ratio=t["gate_ratio"], launch_bytes=t["launch_bytes"])
+                             gate_ratio=t["gate_ratio"], launch_bytes=t["launch_bytes"],
+                             prefix_placement=t["prefix_placement"])
     except op.PlanError as e:
         err_ref = e.code
     plan = err_got = None
@@ -268,6 +300,8 @@ def _grouped_both(p, ptr, pages, lens, G=4, H_kv=2, d=64, q="bf16", kv="bf16", f
     assert NG == len(kept)
     meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), B, NG)
     assert list(meta["group_parent"]) == [g["parent"] for g in kept]
+    assert list(meta["group_prefix_base"]) == [g["prefix_base"] for g in kept]
+    assert info["contiguous_prefixes"] == sum(g["prefix_base"] >= 0 for g in kept)
     gptr = meta["group_indptr"]
     for i, g in enumerate(kept):
         assert list(meta["group_members"][gptr[i]:gptr[i + 1]]) == g["members"]
@@ -284,19 +318,20 @@ def _grouped_both(p, ptr, pages, lens, G=4, H_kv=2, d=64, q="bf16", kv="bf16", f
 
 def test_grouped_plan_matches_oracle_on_random_tables():
     rng = np.random.default_rng(3)
-    n_kept = n_nested = 0
+    n_kept = n_nested = n_contig = 0
     for it in range(300):
         p = int(rng.choice([1, 2, 4, 16]))
         reqs, lens = random_group_tables(rng, p, max_batch=12)
-        ptr, pages = tables_from_blocks(reqs, p, it)
+        ptr, pages = tables_from_blocks(reqs, p, it, scramble=bool(it % 3))
         tune = dict(t_dense=int(rng.integers(1, 40)), gate_ratio=int(rng.integers(0, 2)),
-                    launch_bytes=int(rng.integers(0, 3)) * 1000)
+                    launch_bytes=int(rng.integers(0, 3)) * 1000, prefix_placement=int(it % 7 != 0))
         plan = _grouped_both(p, ptr, pages, lens, force=int(rng.choice([-1, -1, 0, 1, 2])), tune=tune)
         if plan is not None:
             n_kept += plan.info["num_groups"]
+            n_contig += plan.info["contiguous_prefixes"]
             meta = pkv.split_metadata(pkv.pkv_plan_metadata(plan), len(lens), plan.info["num_groups"])
             n_nested += int((meta["group_parent"] >= 0).sum())
-    assert n_kept > 100 and n_nested > 10
+    assert n_kept > 100 and n_nested > 10 and 20 < n_contig < n_kept, (n_kept, n_nested, n_contig)
 
 
 def test_grouped_plan_errors_match_oracle_and_abi():

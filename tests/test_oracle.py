@@ -448,6 +448,35 @@ def test_planner_gate_and_alignment():
     assert r["path"] == "PAGED" and r["prefix_tokens"] == 0 and r["shared_pages"] == 256
 
 
+def check_prefix_placement(plan_fn):
+    """Prefix placement: a prefix whose slots are one ascending run is read
+    from its first slot; any break in the run, a PAGED plan, placement
+    switched off or no slots shown give -1; only the prefix pass's whole
+    pages matter (the tail of a 2,003-token prefix is not part of the run)."""
+    def run(slots, P=64, B=8, **kw):
+        return plan_fn(B=B, H_q=32, H_kv=8, d=128, q_dtype="bf16", kv_dtype="bf16", page_size=16,
+                       seq_lens=[P + 50] * B, shared_prefix_len=P, force_path=kw.pop("force_path", 2),
+                       prefix_slots=slots, **TUNE, **kw)["prefix_base"]
+    assert run(list(range(40, 104))) == 40
+    assert run(list(range(0, 64))) == 0
+    broken = list(range(40, 104))
+    broken[63] = 7
+    assert run(broken) == -1
+    broken = list(range(40, 104))
+    broken[1] = 40
+    assert run(broken) == -1
+    assert run(list(range(100, 36, -1))) == -1                    # descending is not a run
+    assert run(list(range(40, 104)), force_path=0) == -1           # PAGED reads no prefix
+    assert run(list(range(40, 104)), prefix_placement=0) == -1
+    assert run(None) == -1
+    tail = list(range(500, 2500)) + [9, 8, 7]                       # 125 whole pages + 3 tail tokens
+    assert run(tail, P=2003) == 500
+
+
+def test_prefix_placement_rule():
+    check_prefix_placement(op.plan)
+
+
 def test_planner_rejects():
     for kw, code in [(dict(H_q=30), "EINVAL"), (dict(d=96), "EUNSUPPORTED"),
                      (dict(q_dtype="f32"), "EUNSUPPORTED"), (dict(force_path=3), "EINVAL"),
@@ -611,6 +640,25 @@ def test_mutant_batch_reference_caught(mutants):
     _, br, pr = mutants
     with pytest.raises(AssertionError):
         check_batch_reference(br or ob.batch_reference, pr or ob.prefix_reference)
+
+
+def _mut_placement_first_only(**kw):    # takes the first slot without checking the run
+    out = op.plan(**kw)
+    if out["path"] != "PAGED" and kw.get("prefix_slots") is not None and kw.get("prefix_placement", 1):
+        out["prefix_base"] = int(kw["prefix_slots"][0])
+    return out
+
+
+def _mut_placement_ignores_switch(**kw):  # ignores prefix_placement = 0
+    kw = dict(kw)
+    kw["prefix_placement"] = 1
+    return op.plan(**kw)
+
+
+@pytest.mark.parametrize("mutant", [_mut_placement_first_only, _mut_placement_ignores_switch])
+def test_mutant_prefix_placement_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_prefix_placement(mutant)
 
 
 @pytest.mark.parametrize("mutant", [_mut_lower_swapped, _mut_lower_offbyone])
@@ -805,6 +853,51 @@ def check_groups_bruteforce(detect, n=400):
         reqs, lens = _random_group_tables(rng, p)
         ptr, pages = tables_from_blocks(reqs, p, it)
         assert _as_tree(detect(p, ptr, pages, lens)) == _groups_bruteforce(p, ptr, pages, lens)
+
+
+def check_group_placement(plan_groups):
+    """Each kept group's prefix_base against the lowered token-level slots of
+    its first member: the run's slots must be first, first + 1, ... for a
+    base to be set, and then base = first (tables with pages handed out in
+    order, where many runs are contiguous, and scrambled ones)."""
+    rng = np.random.default_rng(11)
+    n_set = n_unset = 0
+    for it in range(200):
+        p = int(rng.choice([1, 2, 4, 16]))
+        reqs, lens = _random_group_tables(rng, p, max_batch=10)
+        ptr, pages = tables_from_blocks(reqs, p, it, scramble=bool(it % 2))
+        for placement in (1, 0):
+            kept, _ = plan_groups(H_q=8, H_kv=2, d=64, q_dtype="bf16", kv_dtype="bf16", page_size=p,
+                                  page_indptr=ptr, page_indices=pages, seq_lens=lens, force_path=-1,
+                                  t_dense=4, gate_ratio=0, launch_bytes=0, prefix_placement=placement)
+            kv_indptr, kv = ol.lower_page_table(p, ptr, pages, lens)
+            for g in kept:
+                lo = int(kv_indptr[g["members"][0]]) + g["start_tokens"]
+                slots = [int(x) for x in kv[lo:lo + g["prefix_tokens"]]]
+                is_run = slots == list(range(slots[0], slots[0] + len(slots)))
+                want = slots[0] if (placement and is_run) else -1
+                assert g["prefix_base"] == want, (it, g, slots[:4])
+                n_set += want >= 0
+                n_unset += want < 0
+    assert n_set > 50 and n_unset > 50
+
+
+def test_group_placement_matches_token_level_slots():
+    check_group_placement(og.plan_groups)
+
+
+def _mut_groups_placement_next_page(**kw):   # base from the page after the run's first
+    kept, path_of = og.plan_groups(**kw)
+    p = kw["page_size"]
+    for g in kept:
+        if g["prefix_base"] >= 0:
+            g["prefix_base"] += p
+    return kept, path_of
+
+
+def test_mutant_group_placement_caught():
+    with pytest.raises(AssertionError):
+        check_group_placement(_mut_groups_placement_next_page)
 
 
 @pytest.mark.parametrize("mutant", [_mut_groups_max_run, _mut_groups_partial_page, _mut_groups_pairwise_first])

@@ -42,18 +42,22 @@ def token_blocks(tokens, p):
     return [tuple(tokens[j:j + p]) for j in range(0, len(tokens), p)]
 
 
-def tables_from_blocks(requests, p, seed=0):
+def tables_from_blocks(requests, p, seed=0, scramble=True):
     """Page tables for requests given as lists of per-block contents.
 
     A physical page is shared exactly when the content up to and including
     its block is the same.  Page numbers are scrambled by a permutation drawn
-    from ``default_rng(seed)``.  Returns (page_indptr, page_indices), int64.
+    from ``default_rng(seed)``; with ``scramble=False`` they are handed out in
+    order of first use (a request's new pages then follow one another, the
+    contiguous placement of a prefix).  Returns (page_indptr, page_indices),
+    int64.
     """
     ids = {}
     tables = []
     for blocks in requests:
         tables.append([ids.setdefault(tuple(blocks[:j + 1]), len(ids)) for j in range(len(blocks))])
-    perm = np.random.default_rng(seed).permutation(max(1, len(ids)))
+    perm = (np.random.default_rng(seed).permutation(max(1, len(ids))) if scramble
+            else np.arange(max(1, len(ids))))
     page_indptr = np.zeros(len(requests) + 1, np.int64)
     for b, t in enumerate(tables):
         page_indptr[b + 1] = page_indptr[b] + len(t)

@@ -191,11 +191,15 @@ def relayout(
     pool_factor: int = 1,
     perm: str = "random",
     device: Optional[str] = None,
+    prefix_first_page: int = 0,
 ) -> DecodeBatch:
     """Place the same logical tokens into a fresh pool.
 
     Draws a new page permutation (from ``rng``, else ``default_rng(seed)``) and
-    returns a copy of ``batch`` with a new page table and pool.
+    returns a copy of ``batch`` with a new page table and pool.  With
+    ``perm="prefix_first"`` the shared prefix's whole pages are stored in
+    order as one run starting at page ``prefix_first_page``, every other page
+    randomly placed around it.
     """
     layout = layout or batch.layout
     p = int(page_size)
@@ -217,9 +221,14 @@ def relayout(
     elif perm == "identity":
         order = np.arange(pool_pages, dtype=np.int64)
     elif perm == "prefix_first":
-        # the shared prefix in the first pages of the pool, in order (stored
-        # contiguously); every other page randomly placed after it
-        order = np.concatenate([np.arange(n_shared), n_shared + rng.permutation(pool_pages - n_shared)]).astype(np.int64)
+        # the shared prefix in consecutive pages, in order (stored
+        # contiguously) from prefix_first_page; every other page randomly
+        # placed around it
+        f0 = int(prefix_first_page)
+        if not 0 <= f0 <= pool_pages - n_shared:
+            raise ValueError("prefix run does not fit in the pool")
+        rest = np.concatenate([np.arange(f0), np.arange(f0 + n_shared, pool_pages)])
+        order = np.concatenate([np.arange(f0, f0 + n_shared), rng.permutation(rest)]).astype(np.int64)
     else:
         raise ValueError(perm)
     shared_pages = order[:n_shared]
