@@ -413,7 +413,48 @@ def dispatch_sweep(out_path, steps=10, warmup=3):
             f"{cell['us']['planned']:.1f} us, fastest {cell['fastest']} {choices[cell['fastest']]:.1f} us "
             f"({time.perf_counter() - t_start:.0f} s)")
 
-    # replay the planner's rule over candidate constants against the measured times
+    replay = replay_sweep(cells)
+    defaults = pkv.pkv_tuning_defaults()
+    planned = [c["planned_over_fastest"] for c in cells]
+    planned_multi = [c["planned_over_fastest"] for c in cells if c["B"] >= 2]
+    rec = dict(
+        what="forced-path sweep of the dispatcher: us per step of each path, the planner's choice and its ratio "
+             "to the fastest path on the shared-page layout; paged_unique = PAGED over per-request prefix copies",
+        grid=dict(B=SWEEP_B, G=SWEEP_G, P=SWEEP_P, kv_dtype=SWEEP_DTYPES, H_kv=8, d=128, own_tokens="U{64..512}",
+                  page_size=16, steps=steps, windows=3),
+        defaults_when_measured={k: defaults[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")},
+        planned_mean_ratio=float(np.mean(planned)), planned_worst_ratio=float(np.max(planned)),
+        planned_mean_ratio_b_ge_2=float(np.mean(planned_multi)),
+        planned_worst_ratio_b_ge_2=float(np.max(planned_multi)),
+        replay_best=replay[:10], cells=cells, source_sha256=kernel_source_hash(),
+        command=f"python bench.py --dispatch-sweep {out_path}")
+    write_sweep_json(out_path, rec)
+    return rec
+
+
+REPLAY_T_DENSE = (1, 64, 256, 1024)
+REPLAY_RATIO = (1, 2, 3, 4, 5, 6, 8)
+REPLAY_LAUNCH_MB = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 15, 20, 30)
+
+
+def write_sweep_json(path, rec):
+    """The sweep record with one line per cell (a short, diffable file)."""
+    head = {k: v for k, v in rec.items() if k != "cells"}
+    lines = json.dumps(head, indent=1)[:-2] + ',\n "cells": [\n'
+    lines += ",\n".join("  " + json.dumps(c, separators=(",", ":")) for c in rec.get("cells", []))
+    with open(path, "w") as f:
+        f.write(lines + "\n ]\n}\n")
+
+
+def replay_sweep(cells):
+    """The planner (the library's own, host only) replayed over a grid of
+    candidate dispatcher constants against the measured times of a sweep:
+    for each candidate, the path it picks in every cell is looked up among
+    the timed paths, and its ratio to the cell's fastest path is averaged
+    and maximised.  Sorted best first (worst ratio over cells with two or
+    more requests, then the mean)."""
+    import numpy as np
+    import paged_kv_cache_201_amd as pkv
     leg_of = {"PAGED": "paged_shared", "CASCADE": "cascade", "DENSE": "dense"}
 
     def decide(cell, tuning):
@@ -425,8 +466,8 @@ def dispatch_sweep(out_path, steps=10, warmup=3):
         return pl.info["path_name"]
 
     replay = []
-    for t_dense, ratio, launch in itertools.product((1, 256, 1024), (1, 2, 3, 4, 6), (0, 5 * 10**6, 10**7, 2 * 10**7)):
-        tune = dict(t_dense=t_dense, gate_ratio=ratio, launch_bytes=launch)
+    for t_dense, ratio, launch in itertools.product(REPLAY_T_DENSE, REPLAY_RATIO, REPLAY_LAUNCH_MB):
+        tune = dict(t_dense=t_dense, gate_ratio=ratio, launch_bytes=launch * 10**6)
         ratios = []
         for cell in cells:
             path = decide(cell, tune)
@@ -436,24 +477,8 @@ def dispatch_sweep(out_path, steps=10, warmup=3):
         multi = [r for r, c in zip(ratios, cells) if c["B"] >= 2]
         replay.append(dict(tuning=tune, mean_ratio=float(np.mean(ratios)), worst_ratio=float(np.max(ratios)),
                            mean_ratio_b_ge_2=float(np.mean(multi)), worst_ratio_b_ge_2=float(np.max(multi))))
-    replay.sort(key=lambda r: (r["worst_ratio_b_ge_2"], r["mean_ratio_b_ge_2"]))
-    defaults = pkv.pkv_tuning_defaults()
-    planned = [c["planned_over_fastest"] for c in cells]
-    planned_multi = [c["planned_over_fastest"] for c in cells if c["B"] >= 2]
-    rec = dict(
-        what="forced-path sweep of the dispatcher: us per step of each path, the planner's choice and its ratio "
-             "to the fastest path on the shared-page layout; paged_unique = PAGED over per-request prefix copies",
-        grid=dict(B=SWEEP_B, G=SWEEP_G, P=SWEEP_P, kv_dtype=SWEEP_DTYPES, H_kv=8, d=128, own_tokens="U{64..512}",
-                  page_size=16, steps=steps, windows=3),
-        defaults={k: defaults[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")},
-        planned_mean_ratio=float(np.mean(planned)), planned_worst_ratio=float(np.max(planned)),
-        planned_mean_ratio_b_ge_2=float(np.mean(planned_multi)),
-        planned_worst_ratio_b_ge_2=float(np.max(planned_multi)),
-        replay_best=replay[:10], cells=cells, source_sha256=kernel_source_hash(),
-        command=f"python bench.py --dispatch-sweep {out_path}")
-    with open(out_path, "w") as f:
-        json.dump(rec, f, indent=1)
-    return rec
+    replay.sort(key=lambda r: (round(r["worst_ratio_b_ge_2"], 3), r["mean_ratio_b_ge_2"]))
+    return replay
 
 
 def page_control(steps, warmup):
@@ -947,6 +972,9 @@ def main():
                     help="write profiles/kernels.<configs>.trace.md from a kernel-trace run of --configs CONFIGS")
     ap.add_argument("--dispatch-sweep", metavar="OUT_JSON",
                     help="run the dispatcher's forced-path refit grid, write it to OUT_JSON and exit")
+    ap.add_argument("--replay-sweep", metavar="SWEEP_JSON",
+                    help="replay the planner over candidate dispatcher constants against a sweep's measured times "
+                         "(host only, no GPU); rewrites the file's replay and exits")
     ap.add_argument("--page-control", action="store_true",
                     help="time the page-size control (page-table vs token-flat reads, distinct vs shared K/V) "
                          "and exit")
@@ -961,6 +989,20 @@ def main():
                     help="write the prefix pass's MFMA/LDS counter summary from two counter runs of "
                          "--only CONFIG:dense_separate and exit")
     args = ap.parse_args()
+    if args.replay_sweep:
+        rec = json.load(open(args.replay_sweep))
+        replay = replay_sweep(rec["cells"])
+        rec["replay_best"] = replay[:12]
+        rec["replay_grid"] = dict(t_dense=REPLAY_T_DENSE, gate_ratio=REPLAY_RATIO, launch_mb=REPLAY_LAUNCH_MB)
+        rec["replay_command"] = f"python bench.py --replay-sweep {args.replay_sweep}"
+        import paged_kv_cache_201_amd as pkv
+        if "defaults" in rec:
+            rec["defaults_when_measured"] = rec.pop("defaults")
+        cur = pkv.pkv_tuning_defaults()
+        rec["defaults_now"] = {k: cur[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")}
+        write_sweep_json(args.replay_sweep, rec)
+        print(json.dumps(replay[:5], indent=1))
+        return
     if args.summarize_paged_counters:
         v, f = args.summarize_paged_counters
         prof = "cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc"

@@ -255,15 +255,18 @@ const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
 void pkv_tuning_defaults(pkv_tuning* out) {
     if (!out) return;
-    // Dispatcher constants refitted on MI355X from a forced-path sweep over
-    // B in {1..512}, G in {1,2,4,8}, P in {256..8192}, suffixes U{64..512}:
-    // DENSE (with its fused launch) was never slower than the tiled path by
+    // Dispatcher constants refitted on MI355X from a forced-path sweep (B in
+    // {1, 2, 4, 16, 64, 256, 512} x G in {1, 4, 8} x P in {256, 1024, 4096},
+    // bf16 and fp8, suffixes U{64..512}, every path timed) and a replay of
+    // this planner over candidate constants against the measured times:
+    // DENSE (with its fused launch) is never slower than the tiled path by
     // more than noise at any M_eff, so every cascade step goes DENSE; the
-    // PAGED gate with R = 3 and a 10 MB launch term picks a path within 15 %
-    // of the fastest in every cell (0.6 % on average).
+    // PAGED gate with R = 3 and a 5 MB launch term picks a path within 19 %
+    // of the fastest in every cell, 0.9 % on average (a 10 MB term kept two
+    // requests on a 4,096-token prefix PAGED, 1.45x slower than DENSE).
     out->t_dense = 1;
     out->gate_ratio = 3;
-    out->launch_bytes = 10LL * 1000 * 1000;
+    out->launch_bytes = 5LL * 1000 * 1000;
     out->target_workgroups = 512;   // two workgroups per CU
     out->min_split_tokens = 64;
     out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
