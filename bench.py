@@ -481,6 +481,75 @@ def replay_sweep(cells):
     return replay
 
 
+def clock_probe(name, steps):
+    """`steps` decode steps of one workload back to back from a cold start
+    (right after the inputs are uploaded, no warm-up), one event pair per
+    step on the launch stream.  For a counter run (GRBM_GUI_ACTIVE with a
+    kernel trace) that sets each dispatch's busy cycles against its
+    duration: the effective clock, cold and warm."""
+    import torch
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_config
+    b = make_config(name, device="cuda")
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan()
+    o, lse, ws = db.new_out(), db.new_lse(), db.workspace(plan)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        db.step(plan, o, lse, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return dict(workload=name, path=plan.info["path_name"], steps=steps,
+                us=[e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+
+
+def write_clock_summary(name, run_json, prof_dir, command):
+    """profiles/paged_split_kernel.<name>_clock.md: per-dispatch duration and
+    effective clock (GRBM_GUI_ACTIVE, summed over the 8 XCDs, divided by 8
+    and by the dispatch's duration) of the paged kernel in a cold-start
+    clock-probe run, by dispatch index."""
+    import csv
+    import glob
+    import statistics
+    rec = json.loads(open(run_json).read().strip().splitlines()[-1])
+    cycles, dur = {}, {}
+    for f in glob.glob(os.path.join(prof_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == "GRBM_GUI_ACTIVE" and "paged_split_kernel" in r["Kernel_Name"]:
+                cycles[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    for f in glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "paged_split_kernel" in r["Kernel_Name"]:
+                dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    ids = sorted(set(cycles) & set(dur))
+    rows = [(i, dur[d], cycles[d] / 8 / dur[d]) for i, d in enumerate(ids)]  # MHz = cycles / us
+    lines = [f"# Effective clock of the paged kernel, {name} ({rec.get('path')}), cold start", "", "Command:", "",
+             "```", command, "```", "",
+             "Each decode step of the workload back to back from a cold start (no warm-up). Per dispatch of "
+             "`paged_split_kernel`: duration from the kernel trace, and effective clock = GRBM_GUI_ACTIVE "
+             "(summed over the 8 XCDs) / 8 / duration. (The run's own event-timed steps are not shown: the "
+             "counter collection serialises the dispatches.)",
+             "", "| dispatches | kernel us (median) | kernel us (min..max) | clock MHz (median) | clock MHz (min..max) |",
+             "|---|---|---|---|---|"]
+    for lo, hi in ((0, 1), (1, 5), (5, 20), (20, 50), (50, 100), (100, 200), (200, len(rows))):
+        part = rows[lo:hi]
+        if not part:
+            continue
+        du = [r[1] for r in part]
+        mh = [r[2] for r in part]
+        lines.append(f"| {lo}..{hi - 1} | {statistics.median(du):.1f} | {min(du):.1f}..{max(du):.1f} | "
+                     f"{statistics.median(mh):.0f} | {min(mh):.0f}..{max(mh):.0f} |")
+    lines.append("")
+    lines.append(f"Source sha256 of the profiled library: `{rec.get('source_sha256')}`")
+    path = os.path.join(ROOT, "profiles", f"paged_split_kernel.{name}_clock.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def page_control(steps, warmup):
     """Page size as a control ("The 25% Page-Size Slowdown That Wasn't",
     section "A backend where pages really do reach the kernel"): the paged
@@ -975,6 +1044,11 @@ def main():
     ap.add_argument("--replay-sweep", metavar="SWEEP_JSON",
                     help="replay the planner over candidate dispatcher constants against a sweep's measured times "
                          "(host only, no GPU); rewrites the file's replay and exits")
+    ap.add_argument("--clock-probe", metavar="CONFIG",
+                    help="run --steps decode steps of one workload from a cold start, one event pair each, print "
+                         "them and exit (for a GRBM_GUI_ACTIVE counter run)")
+    ap.add_argument("--summarize-clock", nargs=3, metavar=("CONFIG", "RUN_JSON", "PROF_DIR"),
+                    help="write profiles/paged_split_kernel.<CONFIG>_clock.md from a clock-probe counter run")
     ap.add_argument("--page-control", action="store_true",
                     help="time the page-size control (page-table vs token-flat reads, distinct vs shared K/V) "
                          "and exit")
@@ -1002,6 +1076,13 @@ def main():
         rec["defaults_now"] = {k: cur[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")}
         write_sweep_json(args.replay_sweep, rec)
         print(json.dumps(replay[:5], indent=1))
+        return
+    if args.summarize_clock:
+        name, r, d = args.summarize_clock
+        cmd = (f"cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -s KILL 120 rocprofv3 --pmc "
+               f"GRBM_GUI_ACTIVE --kernel-trace --output-format csv -d {d} -o run -- python bench.py --clock-probe "
+               f"{name} --steps 300 > {r}")
+        print(write_clock_summary(name, r, d, cmd))
         return
     if args.summarize_paged_counters:
         v, f = args.summarize_paged_counters
@@ -1073,6 +1154,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.clock_probe:
+        rec = clock_probe(args.clock_probe, args.steps)
+        rec["source_sha256"] = kernel_source_hash()
+        print(json.dumps(rec), flush=True)
+        return
     if args.dispatch_sweep:
         rec = dispatch_sweep(args.dispatch_sweep)
         print(json.dumps({k: v for k, v in rec.items() if k != "cells"}), flush=True)
