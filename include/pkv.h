@@ -122,7 +122,10 @@ typedef struct pkv_tuning {
     int32_t t_dense;            /* DENSE when M_eff >= t_dense ([P2] s.3 threshold, refitted) */
     int32_t gate_ratio;         /* PAGED when saved_bytes < gate_ratio * overhead_bytes */
     int64_t launch_bytes;       /* byte-equivalent of the two extra launches of a cascade */
-    int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU */
+    int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU when it is
+                                   an fp8 pass or shares its launch with prefix items; a bf16
+                                   or fp32 pass on its own aims at half of it (one per CU)
+                                   when its chunks then stay within one workgroup's stage */
     int32_t min_split_tokens;   /* paged pass: smallest chunk of positions per workgroup */
     int32_t concurrent_prefix;  /* 1: pkv_decode_step runs the prefix pass on a library-owned
                                    side stream (same priority) concurrently with the suffix
@@ -138,7 +141,9 @@ typedef struct pkv_tuning {
     int32_t min_prefix_split_tokens;  /* prefix pass: smallest prefix range per workgroup
                                          (rounded up to a multiple of 64) */
     int32_t max_heads_per_item; /* paged pass: at most this many KV heads per work item
-                                   (0: as many as one wave-wide load covers) */
+                                   (0: as many as one wave-wide load covers, or half of that
+                                   for an fp8 pass on its own whose non-empty requests
+                                   average at least 1,024 attended positions) */
     int32_t prefix_placement;   /* 1: a shared prefix whose slots are one run of consecutive
                                    slots is read by the prefix pass as base + offset, without
                                    per-token slot indices ([P2] s.1); 0: always by slot index */

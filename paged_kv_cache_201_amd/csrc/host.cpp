@@ -182,6 +182,40 @@ int64_t fused_prefix_target(const pkv_tuning& tu) {
     return std::max<int64_t>(1, std::min<int64_t>(tu.prefix_target_workgroups, tu.target_workgroups / 4));
 }
 
+// Workgroups the paged pass over `total` positions aims at: a bf16 or fp32
+// pass on its own is bound by HBM and runs best with one workgroup per CU
+// (half the tuning's target: measured 2.1 % faster on the Llama layer, 1.4 %
+// on the short-prefix step's suffix, neutral on short requests), as long as
+// its chunks stay within what one workgroup stages (else the chunk cap would
+// leave a few workgroups over one per CU: 27 % slower on long requests); an
+// fp8 pass (bound by the vector ALU) keeps two per CU to hide its loads; a
+// pass that shares its launch with the prefix items takes what they leave.
+int64_t paged_target(const pkv_plan* pl, const pkv_tuning& tu, int64_t total, bool fused, int64_t fused_target) {
+    if (fused) return fused_target;
+    if (pl->kv_dtype == PKV_FP8_E4M3) return tu.target_workgroups;
+    const int64_t half = std::max<int64_t>(1, tu.target_workgroups / 2);
+    const int64_t chunk = align_up(std::max<int64_t>(tu.min_split_tokens, ceil_div(total * pl->head_blocks, half)),
+                                   pkv::kSplitQuantum);
+    const int64_t cap = pkv::max_chunk_tokens(pl->geo.rs, pl->geo.nhl, pl->geo.tpi, pl->G, pl->D);
+    return chunk <= cap ? half : tu.target_workgroups;
+}
+
+// Lane geometry of the fp8 paged pass when the tuning leaves it open: with
+// long requests (at least 1,024 attended positions per non-empty request on
+// average) a work item takes half the KV heads a wave-wide load covers,
+// two tokens per load, which measured 4.2 % faster on the long-context step
+// (G = 8) and 2.7 % at 2,048 tokens (G = 4), and 2.6 % slower on
+// short requests.
+void fp8_long_geometry(pkv_plan* pl, const pkv_tuning& tu, int64_t tokens, int64_t nonempty) {
+    if (pl->kv_dtype != PKV_FP8_E4M3 || tu.max_heads_per_item != 0 || nonempty == 0) return;
+    if (tokens < 1024 * nonempty) return;
+    pkv::PagedGeometry geo;
+    if (pkv::paged_geometry(pl->kv_dtype, pl->D, pl->G, pl->H_kv, pl->geo.rs / 2, &geo)) {
+        pl->geo = geo;
+        pl->head_blocks = pl->H_kv / geo.hb;
+    }
+}
+
 // Paged-pass chunking over `total` positions, n_of(b) of them request b's:
 // chunk size from the workgroup target, partial states per request.
 template <class LenFn>
@@ -433,8 +467,10 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
             prefix_ranges(tu, prefix_tokens, tiles, tu.prefix_target_workgroups, &pl->prefix_split_tokens,
                           &pl->prefix_splits);
     }
-    int64_t target = tu.target_workgroups;
-    if (pl->fuse_cascade) target -= prefix_wgs;
+    int64_t nonempty = 0;
+    for (int32_t b = 0; b < B; ++b) nonempty += n_of(b) > 0;
+    if (!pl->fuse_cascade) fp8_long_geometry(pl, tu, total, nonempty);
+    const int64_t target = paged_target(pl, tu, total, pl->fuse_cascade, tu.target_workgroups - prefix_wgs);
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, total, target, n_of, &spans, &any_empty);
     // A combine kernel follows the paged pass for a cascade step, when a
@@ -767,8 +803,10 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     // combine.
     const int32_t* sptr = m + pl->meta_suffix_indptr;
     const auto n_of = [&](int32_t b) { return (int64_t)sptr[b + 1] - sptr[b]; };
-    int64_t target = tu.target_workgroups;
-    if (fuse) target -= align_up(dense_items, 8);
+    int64_t nonempty = 0;
+    for (int32_t b = 0; b < B; ++b) nonempty += n_of(b) > 0;
+    if (!fuse) fp8_long_geometry(pl, tu, suffix_total, nonempty);
+    const int64_t target = paged_target(pl, tu, suffix_total, fuse, tu.target_workgroups - align_up(dense_items, 8));
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, suffix_total, target, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;

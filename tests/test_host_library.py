@@ -252,8 +252,20 @@ def test_plan_workspace_and_geometry():
     rows = 32 * 32
     if info["num_splits"] > 1:
         assert info["workspace_bytes"] >= rows * info["num_splits"] * 130 * 4
+    # a bf16 pass on its own aims at one workgroup per CU (half the target),
+    # an fp8 pass at two
+    assert info["num_work_items"] == TUNE["target_workgroups"] // 2
+    # ... unless its chunks would exceed what a workgroup stages
+    big = _both(512, 4, 0, 16, L=1152)
+    assert big["split_tokens"] <= 4096 and big["num_work_items"] == 512
+    f8 = _both(32, 4, 0, 128, L=4096, kv="fp8")
+    assert f8["num_work_items"] == TUNE["target_workgroups"]
+    # an fp8 pass over long requests takes half the heads of a wave-wide load
+    # (two tokens per load); over short ones, or with the tuning set, all four
     c5 = _both(16, 8, 0, 16, L=16384, kv="fp8")
-    assert c5["heads_per_item"] == 4
+    assert c5["heads_per_item"] == 2
+    assert _both(256, 4, 0, 16, L=300, kv="fp8")["heads_per_item"] == 4
+    assert _both(16, 8, 0, 16, L=16384, kv="fp8", tune=dict(max_heads_per_item=4))["heads_per_item"] == 4
     # one chunk holds every request whole: outputs written directly, no workspace
     c1 = _both(4, 4, 0, 16, L=[64, 100, 200, 256], H_kv=2, d=64, q="f32", kv="f32", tune=dict(min_split_tokens=2048))
     assert c1["heads_per_item"] == 2 and c1["num_splits"] == 1 and c1["workspace_bytes"] == 0
