@@ -14,8 +14,14 @@ import ctypes
 import os
 
 import numpy as np
+# torch before the library: libpkv.so needs libamdhip64.so.7, and torch ships a
+# HIP runtime of its own under that soname.  Loaded first, the library would
+# map the system runtime and torch a second one, so torch's streams and
+# allocations and this library's kernels would live in different runtimes;
+# loaded second, it binds to the runtime torch already holds.
+import torch  # noqa: F401
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+_LIB_PATH =os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run `python paged_kv_cache_201_amd/build.py`")
 _lib = ctypes.CDLL(_LIB_PATH)

@@ -41,6 +41,20 @@ def test_library_exports_every_declared_function():
         assert text_syms == declared, text_syms
 
 
+def test_one_hip_runtime_whatever_the_import_order():
+    """The package imported before torch must not map a second HIP runtime:
+    torch's streams and allocations and the library's kernels share one."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_201_amd\nimport torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps), sorted(maps))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("1 "), out.stdout
+
+
 def test_status_strings_and_version():
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert pkv.pkv_status_string(st) != "unknown status"
