@@ -16,7 +16,11 @@
 
 namespace pkv {
 
-constexpr int kReduceBatch = 16;  // partials whose loads are issued together
+// Partials whose loads are issued together.  Four keep the kernel at about
+// 50 VGPRs, eight waves per SIMD, so that a grid of 2,048 workgroups (16,384
+// rows at head_dim 128) is resident in one round; a row with more partials
+// takes one more memory round trip per four.
+constexpr int kReduceBatch = 4;
 
 // Thread (row, e4) owns four consecutive outputs of one row.  The row's
 // partials are the pre_splits prefix partials (if any) followed by the chunk
