@@ -87,7 +87,8 @@ typedef enum pkv_path {
 typedef struct pkv_pool {
     const void* k;          /* device, [num_slots][num_kv_heads][head_dim] of kv_dtype */
     const void* v;          /* device, same layout as k */
-    const float* k_scale;   /* device, [num_kv_heads]; required iff kv_dtype is FP8 */
+    const float* k_scale;   /* device, [num_kv_heads]; required iff kv_dtype is FP8;
+                               finite and > 0 (not checked: device memory) */
     const float* v_scale;   /* device, [num_kv_heads]; required iff kv_dtype is FP8 */
     int64_t num_slots;      /* must be a multiple of page_size */
     int32_t page_size;      /* tokens per page, >= 1 */
@@ -318,7 +319,8 @@ PKV_API void pkv_plan_destroy(pkv_plan* plan);
  *   pool        host struct describing device memory; must match the plan
  *   kv_indptr   device, [B+1] int32, same values as the plan's host indptr
  *   kv_indices  device, [kv_indptr[B]] int32 slots
- *   sm_scale    softmax scale (e.g. 1/sqrt(d))
+ *   sm_scale    softmax scale (e.g. 1/sqrt(d)), finite and > 0; else PKV_EINVAL
+ *               (the kernels scale row maxima of unscaled scores)
  *   o           device, [B][H_q][d] of the q dtype, normalised output; nullable
  *   o_f32       device, [B][H_q][d] fp32, normalised output; nullable
  *   lse         device, [B][H_q] fp32; nullable

@@ -30,6 +30,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The kernels take row maxima of unscaled scores and scale them afterwards,
+// which needs a positive scale (a NaN or infinite one has no softmax either).
+bool scale_ok(float sm_scale) { return sm_scale > 0.f && sm_scale < INFINITY; }
+
 pkv_status check_pool(const pkv_plan* pl, const pkv_pool* pool) {
     if (!pool || !pool->k || !pool->v) return PKV_EINVAL;
     if (pool->kv_dtype != pl->kv_dtype || pool->num_kv_heads != pl->H_kv ||
@@ -275,6 +279,7 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* pl, const void* q, const pkv_po
                                  void* stream) {
     if (!pl || pl->grouped) return PKV_EINVAL;
     if (!o && !o_f32) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);
@@ -291,6 +296,7 @@ pkv_status pkv_paged_decode_attn_pages(const pkv_plan* pl, const void* q, const 
                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
     if (!pl || pl->grouped) return PKV_EINVAL;
     if (!o && !o_f32) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);
@@ -308,6 +314,7 @@ pkv_status pkv_cascade_prefix_attn(const pkv_plan* pl, const void* q, const pkv_
                                    const int32_t* prefix_indices, int32_t prefix_len, float sm_scale,
                                    float* o_p, float* lse_p, void* ws, size_t ws_bytes, void* stream) {
     if (!pl || pl->grouped) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     if (pl->path == PKV_PATH_PAGED) return PKV_EINVAL;
     if (prefix_len != pl->prefix_tokens) return PKV_EINVAL;
     if (!q || !prefix_indices || !o_p || !lse_p) return PKV_EINVAL;
@@ -335,6 +342,7 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
                            size_t ws_bytes, void* stream) {
     if (!pl || !o) return PKV_EINVAL;
     if (pl->grouped) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);
@@ -349,6 +357,7 @@ pkv_status pkv_decode_step_noalloc(const pkv_plan* pl, const void* q, const pkv_
                                    const int32_t* kv_indices, float sm_scale, void* o, float* lse, void* stream) {
     if (!pl || !o) return PKV_EINVAL;
     if (pl->grouped) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     if (pl->workspace_bytes > (int64_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_EWORKSPACE;
@@ -364,6 +373,7 @@ pkv_status pkv_decode_step_noalloc(const pkv_plan* pl, const void* q, const pkv_
 pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_pool* pool, const int32_t* meta,
                                    float sm_scale, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
     if (!pl || !o || !pl->grouped) return PKV_EINVAL;
+    if (!scale_ok(sm_scale)) return PKV_EINVAL;
     pkv_status st = check_pool(pl, pool);
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);

@@ -233,7 +233,9 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
             for (int e = 0; e < EPL; ++e) acc[i][u][e] = 0.f;
     }
 
-    const size_t slot_stride = (size_t)H_kv * D * BK;
+    // bytes per slot (H_kv * D * BK, far below 4 GB): a 32-bit factor, so each
+    // row address is one 32 x 32 -> 64-bit multiply-add
+    const uint32_t slot_stride = (uint32_t)H_kv * D * BK;
     const char* kbase = static_cast<const char*>(a.k) + (size_t)hblk * HB * D * BK;
     const char* vbase = static_cast<const char*>(a.v) + (size_t)hblk * HB * D * BK;
     uint32_t loff[NHL];
@@ -272,8 +274,9 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            gbytes_t kr = as_global(kbase) + (size_t)(uint32_t)slots[j] * slot_stride;
-            gbytes_t vr = as_global(vbase) + (size_t)(uint32_t)slots[j] * slot_stride;
+            const uint64_t off = (uint64_t)(uint32_t)slots[j] * slot_stride;
+            gbytes_t kr = as_global(kbase) + off;
+            gbytes_t vr = as_global(vbase) + off;
             if constexpr (TPI == 1) {
                 // The row base is wave-uniform: keep it in scalar registers
                 // and opaque, so that each load is (scalar base + 32-bit lane
@@ -299,7 +302,6 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         float s[U][NHL];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const bool valid = (w0 + it * TU + j * TPI + tau) < w1;  // padded tail tokens
 #pragma unroll
             for (int i = 0; i < NHL; ++i) {
                 float part[G];
@@ -334,12 +336,22 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
                         part[u] = t;
                     }
                 }
-                const float r = row_reduce_scatter<LPH, G>(part) * sc[i];
-                s[j][i] = valid ? r : -INFINITY;
+                s[j][i] = row_reduce_scatter<LPH, G>(part);  // unscaled: sc[i] > 0 joins in the exponent
+            }
+        }
+        // Padded tail tokens get -inf; only the last iteration of a wave's
+        // range holds any, so the other iterations skip the compares.
+        if (w0 + (it + 1) * TU > w1) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const bool valid = (w0 + it * TU + j * TPI + tau) < w1;
+#pragma unroll
+                for (int i = 0; i < NHL; ++i) s[j][i] = valid ? s[j][i] : -INFINITY;
             }
         }
 
-        // Online softmax with a lazily raised maximum.
+        // Online softmax with a lazily raised maximum (in scaled units: the
+        // scale is positive, so the scaled maximum is the maximum's scaling).
         bool need = false;
         float tmax[NHL];
 #pragma unroll
@@ -347,6 +359,7 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
             float t = s[0][i];
 #pragma unroll
             for (int j = 1; j < U; ++j) t = fmaxf(t, s[j][i]);
+            t *= sc[i];
             tmax[i] = t;
             need |= (t > m[i] + kLazyMaxSlack) || (m[i] == -INFINITY && t != -INFINITY);
         }
@@ -369,10 +382,13 @@ __device__ __forceinline__ void paged_segment(const PagedArgs& a, PagedSmem<KV, 
         float p[U][NHL];
 #pragma unroll
         for (int i = 0; i < NHL; ++i) {
+            // 2^(s * sc - m) as one fma; with no finite score yet (m = -inf)
+            // every probability is 2^-inf = 0
+            const float mneg = m[i] == -INFINITY ? -INFINITY : -m[i];
             float sum = 0.f;
 #pragma unroll
             for (int j = 0; j < U; ++j) {
-                p[j][i] = (m[i] == -INFINITY) ? 0.f : fast_exp2(s[j][i] - m[i]);
+                p[j][i] = fast_exp2(fmaf(s[j][i], sc[i], mneg));
                 sum += p[j][i];
             }
             l[i] += sum;

@@ -390,6 +390,38 @@ def test_grouped_plan_errors_match_oracle_and_abi():
     assert pkv._lib.pkv_plan_metadata(plan.handle, None, plan.info["metadata_ints"] - 1) == pkv.PKV_ERANGE
 
 
+def test_non_positive_softmax_scale_is_refused():
+    """The kernels scale row maxima of unscaled scores, which needs sm_scale
+    > 0; zero, negative, NaN and infinite scales return EINVAL before anything
+    is dereferenced or enqueued (so no GPU is needed here)."""
+    single = pkv.pkv_plan_create(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, q_dtype="bf16",
+                                 kv_dtype="bf16", page_size=16, kv_indptr=[0, 32, 64, 80], shared_prefix_len=16,
+                                 force_path=1)
+    reqs = [["A", "a0"], ["A", "a1"], ["B"]]
+    ptr, pages = tables_from_blocks(reqs, 16)
+    grouped = pkv.pkv_plan_create_grouped(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, q_dtype="bf16",
+                                          kv_dtype="bf16", page_size=16, page_indptr=ptr, page_indices=pages,
+                                          seq_lens=[32, 32, 16], force_path=1)
+    d = 16  # never dereferenced
+    # a pool that matches the plans, so that the scale is the only fault
+    pool = ctypes.byref(pkv.pkv_pool(k=d, v=d, k_scale=None, v_scale=None, num_slots=4096, page_size=16,
+                                     num_kv_heads=2, head_dim=64, kv_dtype=pkv.PKV_BF16))
+    ip = (ctypes.c_int32 * 4)()
+    L = pkv._lib
+    calls = {
+        "paged": lambda s: L.pkv_paged_decode_attn(single.handle, d, pool, ip, ip, s, d, None, None, None, 0, None),
+        "pages": lambda s: L.pkv_paged_decode_attn_pages(single.handle, d, pool, ip, ip, ip, s, d, None, None, None,
+                                                         0, None),
+        "prefix": lambda s: L.pkv_cascade_prefix_attn(single.handle, d, pool, ip, 16, s, d, d, None, 0, None),
+        "step": lambda s: L.pkv_decode_step(single.handle, d, pool, ip, ip, s, d, None, None, 0, None),
+        "noalloc": lambda s: L.pkv_decode_step_noalloc(single.handle, d, pool, ip, ip, s, d, None, None),
+        "grouped": lambda s: L.pkv_decode_step_grouped(grouped.handle, d, pool, ip, s, d, None, None, 0, None),
+    }
+    for name, call in calls.items():
+        for s in (0.0, -0.125, float("nan"), float("inf")):
+            assert call(s) == pkv.PKV_EINVAL, (name, s)
+
+
 def test_grouped_plan_reduces_to_the_single_prefix_plan():
     # every request on one prefix: the grouped plan makes the single-prefix
     # plan's decisions and partition
