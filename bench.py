@@ -714,6 +714,80 @@ def summarize_trace(prof_dir):
     return "\n".join(out), agg
 
 
+PLANNED_TRACE_CONFIGS = "c2,c2p128,c5,c1,c3,c4,c3_fp8,groups4,tree4"
+PLANNED_TRACE_STEPS, PLANNED_TRACE_WARMUP = 60, 200
+
+
+def trace_planned(name, steps, warmup):
+    """The planner's step of one workload, nothing else (for a kernel trace):
+    warmup steps, then steps steps.  c2p128 is the Llama layer at page size
+    128 (c2 itself at page size 1, as in the headline)."""
+    import torch
+    from paged_kv_cache_201_amd.step import DeviceBatch
+    from workloads import make_config
+    if name in ("groups4", "tree4"):
+        from workloads import make_group_config, make_tree_config
+        b = (make_tree_config if name.startswith("tree") else make_group_config)(name, device="cuda")
+        db = DeviceBatch.from_batch(b)
+        plan = db.plan_grouped()
+        meta, ws = db.metadata(plan), db.workspace(plan)
+        run = lambda: db.step_grouped(plan, meta, o, lse, ws)
+    else:
+        over = dict(page_size=1) if name == "c2" else {}
+        b = make_config("c2" if name == "c2p128" else name, device="cuda", **over)
+        db = DeviceBatch.from_batch(b)
+        plan = db.plan(shared_prefix_len=b.prefix_len)
+        ws = db.workspace(plan)
+        run = lambda: db.step(plan, o, lse, ws)
+    o, lse = db.new_out(), db.new_lse()
+    for _ in range(warmup + steps):
+        run()
+    torch.cuda.synchronize()
+    return dict(workload=name, path=plan.info["path_name"], steps=steps, warmup=warmup)
+
+
+def write_planned_traces(parent, configs, command):
+    """profiles/kernels.planned_steps.trace.md: for each workload, the
+    library's kernels in its planned step (one kernel-trace run per workload
+    under parent/<workload>), medians over the second half of each kernel's
+    calls (the steady state after the warm-up)."""
+    import csv
+    import glob
+    import statistics
+    out = [f"# Kernel durations of each workload's planned step\n",
+           "One `rocprofv3 --kernel-trace` run per workload, each running only the planner's step "
+           f"({PLANNED_TRACE_WARMUP} warm-up steps, then {PLANNED_TRACE_STEPS}); library kernels only; "
+           "median, mean and minimum over the second half of each kernel's calls.\n",
+           "Command (per workload W):\n", f"```\n{command}\n```\n"]
+    for name in configs.split(","):
+        agg = {}
+        for f in glob.glob(os.path.join(parent, name, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if "pkv::" not in r["Kernel_Name"]:
+                    continue
+                wg = int(r["Workgroup_Size_X"])
+                key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // wg, int(r["Grid_Size_Y"]), wg)
+                agg.setdefault(key, []).append((int(r["Start_Timestamp"]),
+                                                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        out.append(f"## {name}\n")
+        if not agg:
+            out.append("(no trace)\n")
+            continue
+        out.append("| kernel | workgroups (x,y) | threads | calls | median us | mean us | min us |")
+        out.append("|---|---|---|---|---|---|---|")
+        total = 0.0
+        for k, v in sorted(agg.items(), key=lambda kv: kv[1][0][0]):
+            d = [x for _, x in sorted(v)][len(v) // 2:]
+            total += statistics.median(d)
+            out.append(f"| `{k[0]}` | {k[1]},{k[2]} | {k[3]} | {len(v)} | {statistics.median(d):.1f} | "
+                       f"{statistics.mean(d):.1f} | {min(d):.1f} |")
+        out.append(f"\nSum of kernel medians: {total:.1f} us per step.\n")
+    path = os.path.join(ROOT, "profiles", "kernels.planned_steps.trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    return path
+
+
 def write_trace_summary(trace_dir, name, title, command):
     """profiles/kernels.<name>.trace.md from one rocprofv3 --kernel-trace run."""
     table, _ = summarize_trace(trace_dir)
@@ -1039,6 +1113,12 @@ def main():
                     help="write the prefix-traffic summary from two FETCH_SIZE runs (see --only) and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CONFIGS"),
                     help="write profiles/kernels.<configs>.trace.md from a kernel-trace run of --configs CONFIGS")
+    ap.add_argument("--trace-planned", metavar="CONFIG",
+                    help="run only the planned step of one workload (warm-up, then steps) and exit; for a "
+                         "kernel-trace run per workload")
+    ap.add_argument("--summarize-planned-traces", nargs=2, metavar=("PARENT_DIR", "CONFIGS"),
+                    help="write profiles/kernels.planned_steps.trace.md from PARENT_DIR/<config> kernel traces "
+                         "of --trace-planned runs and exit")
     ap.add_argument("--dispatch-sweep", metavar="OUT_JSON",
                     help="run the dispatcher's forced-path refit grid, write it to OUT_JSON and exit")
     ap.add_argument("--replay-sweep", metavar="SWEEP_JSON",
@@ -1116,6 +1196,13 @@ def main():
         rec = write_prefix_traffic(name, u, c, cmds)
         print(json.dumps({k: v for k, v in rec.items() if k != "runs"}, indent=1))
         return
+    if args.summarize_planned_traces:
+        d, configs = args.summarize_planned_traces
+        cmd = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && timeout -k 10 180 rocprofv3 --kernel-trace "
+               f"--output-format csv -d {d}/W -o run -- python bench.py --trace-planned W\n"
+               f"python bench.py --summarize-planned-traces {d} {configs}")
+        print(write_planned_traces(d, configs, cmd))
+        return
     if args.summarize_trace:
         d, configs = args.summarize_trace
         cmd = ("cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --kernel-trace --stats "
@@ -1154,6 +1241,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.trace_planned:
+        rec = trace_planned(args.trace_planned, PLANNED_TRACE_STEPS, PLANNED_TRACE_WARMUP)
+        rec["source_sha256"] = kernel_source_hash()
+        print(json.dumps(rec), flush=True)
+        return
     if args.clock_probe:
         rec = clock_probe(args.clock_probe, args.steps)
         rec["source_sha256"] = kernel_source_hash()
