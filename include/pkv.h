@@ -148,6 +148,13 @@ typedef struct pkv_tuning {
     int32_t prefix_placement;   /* 1: a shared prefix whose slots are one run of consecutive
                                    slots is read by the prefix pass as base + offset, without
                                    per-token slot indices ([P2] s.1); 0: always by slot index */
+    int32_t segment_tokens;     /* paged pass: the cost of one request segment in a work item,
+                                   in positions.  When every request of the pass is non-empty
+                                   and fits one chunk, the planner also packs whole requests
+                                   into as many bins as chunks (largest first, each to the
+                                   least loaded bin) and takes the bins when their most costly
+                                   one (positions + segment_tokens per request) costs less than
+                                   the most costly chunk; 0: always chunks */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */
@@ -172,6 +179,10 @@ typedef struct pkv_plan_info {
                                    prefix pass reads it as one run of consecutive slots, else -1 */
     int32_t contiguous_prefixes; /* prefix runs the prefix pass reads as base + offset (single
                                     plan: 0 or 1; grouped plan: kept groups) */
+    int32_t request_bins;       /* paged pass: 0 when its work items are chunks of the flat
+                                   sequence; else the number of bins of whole requests (one
+                                   work item per bin and head block; no request is cut, so
+                                   num_splits is 1) */
 } pkv_plan_info;
 
 /* Human-readable name of a status code (static storage). */
@@ -301,6 +312,15 @@ PKV_API pkv_status pkv_plan_create_grouped(const pkv_problem* problem, const pkv
  * with a non-empty block), ERANGE (capacity too small).
  */
 PKV_API pkv_status pkv_plan_metadata(const pkv_plan* plan, int32_t* out, int64_t capacity);
+
+/* Host inspection of a plan whose paged pass runs on bins of whole requests
+ * (pkv_plan_info.request_bins = W > 0; see pkv_tuning.segment_tokens): out
+ * receives bin_start [W+1] (bin w holds entries bin_start[w] ..
+ * bin_start[w+1] - 1 of the list) followed by the list of request indices
+ * [B], each bin's in increasing order.  The bins travel to the kernels with
+ * the plan itself; nothing needs uploading.  Errors: EINVAL (null plan, a
+ * plan without bins, null out), ERANGE (capacity < W + 1 + B). */
+PKV_API pkv_status pkv_plan_request_bins(const pkv_plan* plan, int32_t* out, int64_t capacity);
 
 /* Copy a plan's decisions and sizes into *info.  EINVAL on null pointers. */
 PKV_API pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);

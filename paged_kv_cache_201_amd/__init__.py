@@ -63,7 +63,8 @@ class pkv_tuning(ctypes.Structure):
                 ("target_workgroups", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
                 ("concurrent_prefix", ctypes.c_int32), ("fuse_cascade", ctypes.c_int32),
                 ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32),
-                ("max_heads_per_item", ctypes.c_int32), ("prefix_placement", ctypes.c_int32)]
+                ("max_heads_per_item", ctypes.c_int32), ("prefix_placement", ctypes.c_int32),
+                ("segment_tokens", ctypes.c_int32)]
 
 
 class pkv_plan_info(ctypes.Structure):
@@ -72,7 +73,8 @@ class pkv_plan_info(ctypes.Structure):
                 ("heads_per_item", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
                 ("num_work_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("num_groups", ctypes.c_int32), ("metadata_ints", ctypes.c_int64),
-                ("prefix_base", ctypes.c_int32), ("contiguous_prefixes", ctypes.c_int32)]
+                ("prefix_base", ctypes.c_int32), ("contiguous_prefixes", ctypes.c_int32),
+                ("request_bins", ctypes.c_int32)]
 
 
 _SIGS = {
@@ -87,6 +89,7 @@ _SIGS = {
     "pkv_plan_create_grouped": (ctypes.c_int32, [ctypes.POINTER(pkv_problem), ctypes.POINTER(pkv_tuning),
                                                  _i32p, _i32p, _i32p, ctypes.POINTER(_vp)]),
     "pkv_plan_metadata": (ctypes.c_int32, [_vp, _i32p, ctypes.c_int64]),
+    "pkv_plan_request_bins": (ctypes.c_int32, [_vp, _i32p, ctypes.c_int64]),
     "pkv_plan_get_info": (ctypes.c_int32, [_vp, ctypes.POINTER(pkv_plan_info)]),
     "pkv_plan_destroy": (None, [_vp]),
     "pkv_paged_decode_attn": (ctypes.c_int32, [_vp, _vp, ctypes.POINTER(pkv_pool), _vp, _vp, ctypes.c_float, _vp,
@@ -287,6 +290,15 @@ def pkv_plan_metadata(plan: Plan):
     out = np.zeros(max(n, 1), np.int32)
     _check(_lib.pkv_plan_metadata(plan.handle, out.ctypes.data_as(_i32p), n), "pkv_plan_metadata")
     return out[:n]
+
+
+def pkv_plan_request_bins(plan: Plan):
+    """(bin_start [W+1], requests [B]) of a plan whose paged pass runs on bins
+    of whole requests (plan.info["request_bins"] = W > 0)."""
+    W, B = plan.info["request_bins"], plan.problem["batch"]
+    out = np.zeros(W + 1 + B, np.int32)
+    _check(_lib.pkv_plan_request_bins(plan.handle, out.ctypes.data_as(_i32p), len(out)), "pkv_plan_request_bins")
+    return out[:W + 1], out[W + 1:]
 
 
 def split_metadata(block, batch, num_groups):

@@ -3,6 +3,7 @@
 // synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <unordered_map>
@@ -102,6 +103,11 @@ pkv::PagedArgs paged_args(const pkv_plan* pl, const void* q, const pkv_pool* poo
     a.max_parts = pl->num_splits;
     a.scale_log2 = sm_scale * kLog2e;
     a.out_dtype = pl->q_dtype;
+    a.request_bins = pl->request_bins;
+    if (pl->request_bins > 0) {
+        std::copy(pl->bin_start.begin(), pl->bin_start.end(), a.bin_start);
+        std::copy(pl->bin_req.begin(), pl->bin_req.end(), a.bin_req);
+    }
     return a;
 }
 
@@ -118,6 +124,7 @@ pkv::SplitReduceArgs chunk_reduce_args(const pkv_plan* pl, const pkv::PagedArgs&
     r.kv_indptr = a.kv_indptr;
     r.token_offset = a.token_offset;
     r.chunk_tokens = a.chunk_tokens;
+    r.whole_requests = pl->request_bins > 0;
     r.out_dtype = pl->q_dtype;
     return r;
 }

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <memory>
 #include <new>
+#include <queue>
 #include <unordered_map>
 #include <vector>
 
@@ -90,7 +91,8 @@ pkv_status check_problem(const pkv_problem* pr, const pkv_tuning* tuning, pkv_tu
     if (tu->t_dense < 1 || tu->gate_ratio < 0 || tu->launch_bytes < 0 || tu->target_workgroups < 1 ||
         tu->min_split_tokens < 1 || tu->concurrent_prefix < 0 || tu->concurrent_prefix > 1 ||
         tu->fuse_cascade < 0 || tu->prefix_target_workgroups < 1 || tu->min_prefix_split_tokens < 1 ||
-        tu->max_heads_per_item < 0 || tu->prefix_placement < 0 || tu->prefix_placement > 1)
+        tu->max_heads_per_item < 0 || tu->prefix_placement < 0 || tu->prefix_placement > 1 ||
+        tu->segment_tokens < 0)
         return PKV_EINVAL;
     const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
     if (B < 0 || H_kv < 1 || H_q < 1 || pr->page_size < 1 || pr->head_dim < 1) return PKV_EINVAL;
@@ -216,6 +218,65 @@ void fp8_long_geometry(pkv_plan* pl, const pkv_tuning& tu, int64_t tokens, int64
     }
 }
 
+// Bins of whole requests for the paged pass: when every request of the pass
+// is non-empty and no longer than a chunk, requests are packed, largest
+// first (ties by index), each into the least loaded of num_chunks bins (ties
+// by bin), with a request's load its positions plus tu.segment_tokens.  The
+// bins replace the chunks when their most loaded bin is below the most
+// loaded chunk under the same cost (a chunk counts one segment per request
+// it touches).  The bin's requests are listed in index order.
+template <class LenFn>
+bool bin_requests(pkv_plan* pl, const pkv_tuning& tu, LenFn n_of, int64_t chunk) {
+    const int64_t W = pl->num_chunks, B = pl->B, seg = tu.segment_tokens;
+    if (seg == 0 || W < 2 || W > pkv::kMaxRequestBins || B > pkv::kMaxBinnedRequests) return false;
+    std::vector<int64_t> n(B);
+    int64_t total = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        n[b] = n_of((int32_t)b);
+        if (n[b] == 0 || n[b] > chunk) return false;
+        total += n[b];
+    }
+    // most loaded chunk of the flat partition
+    std::vector<int64_t> chunk_cost(W, 0);
+    int64_t pos = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t c0 = pos / chunk, c1 = (pos + n[b] - 1) / chunk;
+        for (int64_t c = c0; c <= c1; ++c) chunk_cost[c] += seg;
+        pos += n[b];
+    }
+    int64_t chunk_max = 0;
+    for (int64_t c = 0; c < W; ++c) {
+        const int64_t toks = std::min<int64_t>((c + 1) * chunk, total) - c * chunk;
+        chunk_max = std::max(chunk_max, chunk_cost[c] + toks);
+    }
+    // largest first into the least loaded bin
+    std::vector<int32_t> order(B);
+    for (int64_t b = 0; b < B; ++b) order[b] = (int32_t)b;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return n[x] > n[y]; });
+    using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
+    std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> heap;
+    for (int32_t w = 0; w < (int32_t)W; ++w) heap.push({0, w});
+    std::vector<int32_t> bin_of(B);
+    int64_t bin_max = 0;
+    for (int32_t b : order) {
+        Bin top = heap.top();
+        heap.pop();
+        top.first += n[b] + seg;
+        bin_max = std::max(bin_max, top.first);
+        bin_of[b] = top.second;
+        heap.push(top);
+    }
+    if (bin_max >= chunk_max) return false;
+    pl->bin_start.assign(W + 1, 0);
+    for (int64_t b = 0; b < B; ++b) ++pl->bin_start[bin_of[b] + 1];
+    for (int64_t w = 0; w < W; ++w) pl->bin_start[w + 1] = (uint16_t)(pl->bin_start[w + 1] + pl->bin_start[w]);
+    pl->bin_req.assign(B, 0);
+    std::vector<int32_t> fill(pl->bin_start.begin(), pl->bin_start.end() - 1);
+    for (int64_t b = 0; b < B; ++b) pl->bin_req[fill[bin_of[b]]++] = (uint16_t)b;
+    pl->request_bins = (int32_t)W;
+    return true;
+}
+
 // Paged-pass chunking over `total` positions, n_of(b) of them request b's:
 // chunk size from the workgroup target, partial states per request.
 template <class LenFn>
@@ -243,6 +304,13 @@ void plan_chunks(pkv_plan* pl, const pkv_tuning& tu, int64_t total, int64_t targ
         pos += n;
     }
     pl->num_splits = (int32_t)max_parts;
+    pl->request_bins = 0;
+    pl->bin_start.clear();
+    pl->bin_req.clear();
+    if (bin_requests(pl, tu, n_of, chunk)) {
+        pl->num_splits = 1;
+        *spans = false;
+    }
 }
 
 // Workspace: chunk partials of the paged pass (if kept) and prefix_splits
@@ -303,12 +371,18 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     out->launch_bytes = 5LL * 1000 * 1000;
     out->target_workgroups = 512;   // two workgroups per CU
     out->min_split_tokens = 64;
-    out->concurrent_prefix = 0;  // measured: overlap with the suffix pass does not shorten the step
+    // measured: the prefix pass on a side stream shortens the short-prefix step by 1-2 % and
+    // lengthens others by 2-12 % (a small long-context step most)
+    out->concurrent_prefix = 0;
     out->fuse_cascade = 12;  // MFMA flops per suffix byte: fused on c3 (57), separate on c4 (3)
     out->prefix_target_workgroups = 256;
     out->min_prefix_split_tokens = 64;
     out->max_heads_per_item = 0;
     out->prefix_placement = 1;
+    // a request segment costs about 2.5 us on the workgroup that sets the end of a
+    // 2,560-position chunk, 30 positions' worth; as many segments per workgroup
+    // measured the same whatever their lengths
+    out->segment_tokens = 32;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -825,6 +899,15 @@ pkv_status pkv_plan_metadata(const pkv_plan* pl, int32_t* out, int64_t capacity)
     return PKV_OK;
 }
 
+pkv_status pkv_plan_request_bins(const pkv_plan* pl, int32_t* out, int64_t capacity) {
+    if (!pl || pl->request_bins == 0 || !out) return PKV_EINVAL;
+    const int64_t n = (int64_t)pl->bin_start.size() + (int64_t)pl->bin_req.size();
+    if (capacity < n) return PKV_ERANGE;
+    std::copy(pl->bin_start.begin(), pl->bin_start.end(), out);
+    std::copy(pl->bin_req.begin(), pl->bin_req.end(), out + pl->bin_start.size());
+    return PKV_OK;
+}
+
 pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     if (!pl || !info) return PKV_EINVAL;
     info->path = pl->path;
@@ -841,6 +924,7 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
     info->metadata_ints = (int64_t)pl->meta.size();
     info->prefix_base = pl->grouped ? -1 : pl->prefix_base;
     info->contiguous_prefixes = pl->contiguous_prefixes;
+    info->request_bins = pl->request_bins;
     return PKV_OK;
 }
 

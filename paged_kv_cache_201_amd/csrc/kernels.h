@@ -41,6 +41,12 @@ struct PagedArgs {
     float* part_ml;           // [B][max_parts][H_q][2]: (M, L), M in log2 units
     int32_t out_dtype;        // dtype of o (q dtype)
     int32_t force_partial;    // every segment writes a partial (cascade suffix)
+    // > 0: work items are bins of whole requests instead of chunks: item w
+    // takes requests bin_req[bin_start[w] .. bin_start[w + 1]), each as one
+    // segment (no request is cut; a partial state, if any, is slot 0)
+    int32_t request_bins;
+    uint16_t bin_start[kMaxRequestBins + 1];
+    uint16_t bin_req[kMaxBinnedRequests];
 };
 
 // Launch the paged split kernel for the plan's geometry.
@@ -67,6 +73,7 @@ struct SplitReduceArgs {
     const int32_t* kv_indptr; // [B+1]; nullable: no chunk partials, skip nothing
     int32_t token_offset;
     int32_t chunk_tokens;
+    int32_t whole_requests;   // the paged pass ran on bins of whole requests: one partial each
     int32_t skip_whole;
     void* o;                  // nullable; out_dtype
     int32_t out_dtype;

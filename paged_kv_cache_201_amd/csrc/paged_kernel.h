@@ -593,12 +593,29 @@ __device__ __forceinline__ int64_t flat_offset(const PagedArgs& a, int i) {
 }
 
 // One (chunk, head block) work item: positions [w * chunk, (w + 1) * chunk)
-// of the flat sequence, segment by segment.
+// of the flat sequence, segment by segment; or, when the plan packed whole
+// requests into bins, bin w's requests.
 template <int KV, int D, int G, int NHL, int TPI>
 __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D, G, NHL, TPI>& sm, const int w,
                                             const int hblk) {
     constexpr int NT = kPagedWaves * 64;
     const int64_t C = a.chunk_tokens;
+    if (a.request_bins > 0) {
+        // a bin of whole requests, one segment each (direct output, or the
+        // request's one partial state)
+        const int r0 = a.bin_start[w], r1 = a.bin_start[w + 1];
+        for (int k = r0; k < r1; ++k) {
+            const int b = a.bin_req[k];
+            const int64_t ob = flat_offset(a, b), on = flat_offset(a, b + 1);
+            // kv_indptr does not describe the planned batch: no request of
+            // the plan is empty or longer than a chunk (the index stage)
+            if (on <= ob || on - ob > C) return;
+            if (k > r0) __syncthreads();  // the previous segment is done with LDS
+            paged_segment<KV, D, G, NHL, TPI>(a, sm, b, hblk, a.kv_indptr[b] + a.token_offset, (int)(on - ob),
+                                              a.force_partial ? 0 : -1, false);
+        }
+        return;
+    }
     const int64_t c0 = (int64_t)w * C;
     const int64_t c1 = c0 + C < a.total_tokens ? c0 + C : a.total_tokens;
     // Without a skipped prefix the flat sequence is kv_indices itself, so

@@ -49,6 +49,10 @@ constexpr int32_t kMaxPrefixSplitTokens = 1024;
 // wave and token lane group: 4 bytes x slots x heads per item x G x d), and
 // the index stage is sized so that two workgroups still fit in a CU's 160 KB.
 constexpr int32_t kSplitQuantum = 16;
+// Bins of whole requests travel in the paged kernels' arguments (16-bit
+// request ids and bin starts): at most this many bins and requests.
+constexpr int32_t kMaxRequestBins = 256;
+constexpr int32_t kMaxBinnedRequests = 1024;
 constexpr int32_t kMaxSplitTokens = 4096;
 constexpr int32_t max_chunk_tokens(int32_t rs, int32_t nhl, int32_t tpi, int32_t group, int32_t head_dim) {
     return 4 * (tpi == 1 ? 2 : 4 * tpi) * (rs * nhl / tpi) * group * head_dim > 40 * 1024 ? 2048
@@ -80,6 +84,10 @@ struct pkv_plan {
     // prefix pass
     int32_t prefix_rows_per_wg;
     int32_t prefix_split_tokens, prefix_splits;
+    // bins of whole requests (request_bins > 0): bin w holds requests
+    // bin_req[bin_start[w] .. bin_start[w + 1])
+    int32_t request_bins = 0;
+    std::vector<uint16_t> bin_start, bin_req;
     // workspace layout (byte offsets; -1 = unused)
     int64_t ws_paged_acc, ws_paged_ml;
     int64_t ws_prefix_acc, ws_prefix_ml;

@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
         const int64_t ob = a.kv_indptr[b] - base - (int64_t)b * a.token_offset;
         const int64_t on = a.kv_indptr[b + 1] - base - (int64_t)(b + 1) * a.token_offset;
         if (on > ob) {
-            nparts = (int)((on - 1) / a.chunk_tokens - ob / a.chunk_tokens + 1);
+            nparts = a.whole_requests ? 1 : (int)((on - 1) / a.chunk_tokens - ob / a.chunk_tokens + 1);
             if (a.skip_whole && nparts == 1) return;  // written by the paged kernel
             nparts = a.part_acc ? min(nparts, a.max_parts) : 0;
         }

@@ -117,6 +117,27 @@ void check_lowering(const Table& t) {
     }
 }
 
+// Bins of whole requests: exact-size copy, every request once, short buffer refused.
+void check_bins(const pkv_plan* plan, const pkv_plan_info& info, int32_t B) {
+    if (info.request_bins == 0) {
+        int32_t dummy = 0;
+        REQUIRE(pkv_plan_request_bins(plan, &dummy, 1) == PKV_EINVAL);
+        return;
+    }
+    const int64_t n = (int64_t)info.request_bins + 1 + B;
+    std::vector<int32_t> bins(n);
+    REQUIRE(pkv_plan_request_bins(plan, bins.data(), n) == PKV_OK);
+    std::vector<int32_t> short_bins(n - 1);
+    REQUIRE(pkv_plan_request_bins(plan, short_bins.data(), n - 1) == PKV_ERANGE);
+    REQUIRE(bins[0] == 0 && bins[info.request_bins] == B && info.num_splits == 1);
+    std::vector<int> seen(B, 0);
+    for (int64_t k = info.request_bins + 1; k < n; ++k) {
+        REQUIRE(bins[k] >= 0 && bins[k] < B);
+        ++seen[bins[k]];
+    }
+    for (int32_t b = 0; b < B; ++b) REQUIRE(seen[b] == 1);
+}
+
 pkv_tuning random_tuning() {
     pkv_tuning tu;
     pkv_tuning_defaults(&tu);
@@ -131,6 +152,7 @@ pkv_tuning random_tuning() {
         tu.min_prefix_split_tokens = uni(1, 2048);
         tu.max_heads_per_item = uni(0, 8);
         tu.prefix_placement = uni(0, 1);
+        tu.segment_tokens = uni(0, 1) ? uni(0, 300) : 32;
     }
     return tu;
 }
@@ -175,6 +197,7 @@ void check_plan(const Table& t, int* planned) {
             REQUIRE(info.metadata_ints == 0);
             int32_t dummy = 0;
             REQUIRE(pkv_plan_metadata(plan, &dummy, 1) == PKV_EINVAL);  // not a grouped plan
+            check_bins(plan, info, t.B);
             pkv_plan_destroy(plan);
             ++*planned;
         }
@@ -204,6 +227,7 @@ void check_grouped(const Table& t, int* planned, int64_t* meta_ints) {
         if (!plan) continue;
         pkv_plan_info info;
         REQUIRE(pkv_plan_get_info(plan, &info) == PKV_OK);
+        check_bins(plan, info, t.B);
         std::vector<int32_t> meta(info.metadata_ints);
         REQUIRE(pkv_plan_metadata(plan, ptr(meta), info.metadata_ints) == PKV_OK);
         if (info.metadata_ints > 0) {

@@ -291,6 +291,47 @@ def test_chunkings_agree_with_oracle_and_repeat_bitwise(chunk):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_request_bins_and_chunks_agree_with_oracle(kv):
+    """The same batches on bins of whole requests and on chunks of the flat
+    sequence (segment_tokens 0), a plain paged step and a cascade step, both
+    against the oracle; the binned step repeats bitwise, also with a workspace
+    of garbage, and does not depend on the page size."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    for P, force in ((0, 0), (256, 2), (256, 1)):
+        # 400 requests of up to 300 positions: every one fits a chunk, so the planner may bin
+        b = make_decode_batch(seed=31 + P + force, B=400, H_q=32, H_kv=8, d=128,
+                              own_len=(1, 300) if kv == "bf16" else (100, 300), prefix_len=P, kv_dtype=kv,
+                              page_size=16)
+        o_ref, lse_ref = ob.batch_reference(b)
+        db = DeviceBatch.from_batch(b)
+        binned = db.plan(shared_prefix_len=P, force_path=force)
+        chunked = db.plan(shared_prefix_len=P, force_path=force, tuning=dict(segment_tokens=0))
+        assert binned.info["request_bins"] > 0 and chunked.info["request_bins"] == 0, (P, force)
+        say(f"bins {kv} P={P} force={force}: {binned.info['request_bins']} bins")
+        ws = db.workspace(binned)
+        if ws is not None:
+            ws.fill_(0xFF)
+        o1, l1 = db.step(binned, ws=ws)
+        o2, l2 = db.step(binned, ws=ws)
+        oc, lc = db.step(chunked)
+        torch.cuda.synchronize()
+        check_close(kv, o1, l1, o_ref, lse_ref, f"bins {kv} P={P} force={force}")
+        check_close(kv, oc, lc, o_ref, lse_ref, f"chunks {kv} P={P} force={force}")
+        assert same_bits(o1, o2) and same_bits(l1, l2)
+        # the bins depend on the lengths only: a page size of 1 gives the same bits
+        b1 = relayout(b, page_size=1, seed=4001)
+        d1 = DeviceBatch.from_batch(b1)
+        p1 = d1.plan(shared_prefix_len=P, force_path=force)
+        assert p1.info["request_bins"] == binned.info["request_bins"]
+        o3, l3 = d1.step(p1)
+        torch.cuda.synchronize()
+        if P == 0:
+            assert same_bits(o1, o3) and same_bits(l1, l3), f"bins {kv}: page size changed the bits"
+        else:
+            check_close(kv, o3, l3, o_ref, lse_ref, f"bins p=1 {kv} P={P} force={force}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_narrow_head_blocks_and_long_chunks(kv):
     """Work items of 1 and 2 KV heads (several tokens per wave-wide load) and
     whole-request chunks of 4096 positions with no combine step."""

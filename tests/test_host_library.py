@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 20, declared
     lib = ctypes.CDLL(pkv.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -67,7 +67,8 @@ def test_status_strings_and_version():
     assert d["prefix_target_workgroups"] >= 1 and 1 <= d["min_prefix_split_tokens"] <= 1024
     assert d["max_heads_per_item"] >= 0
     assert d["prefix_placement"] in (0, 1)
-    assert len(d) == 11
+    assert 0 <= d["segment_tokens"] <= 4096
+    assert len(d) == 12
 
 
 # ---------------------------------------------------------------- lowering --
@@ -253,10 +254,97 @@ def test_chunk_partition_is_balanced_and_counted():
         chunks, parts = _chunking(lens, info["prefix_tokens"], C)
         head_blocks = 8 // info["heads_per_item"]
         assert info["num_work_items"] == chunks * head_blocks
-        assert info["num_splits"] == parts
+        # bins of whole requests cut no request; chunks count their partial states
+        assert info["num_splits"] == (1 if info["request_bins"] else parts)
         # every chunk but the last holds exactly C positions: equal work per workgroup
         total = int(sum(int(L) - info["prefix_tokens"] for L in lens))
         assert chunks == 0 or (chunks - 1) * C < total <= chunks * C
+
+
+def _expected_bins(lens, chunk, W, seg):
+    """The packing rule, stated again: whole requests, largest first (ties
+    by index), each into the least loaded of W bins (ties by bin), load =
+    positions + seg per request; taken when the most loaded bin costs less
+    than the most loaded chunk of the flat partition (positions + seg per
+    request the chunk touches).  None: chunks."""
+    B = len(lens)
+    if seg == 0 or W < 2 or W > 256 or B > 1024 or any(n == 0 or n > chunk for n in lens):
+        return None
+    total = sum(lens)
+    cost, pos = [0] * W, 0
+    for n in lens:
+        for c in range(pos // chunk, (pos + n - 1) // chunk + 1):
+            cost[c] += seg
+        pos += n
+    chunk_max = max(cost[c] + min((c + 1) * chunk, total) - c * chunk for c in range(W))
+    loads, bin_of = [0] * W, [0] * B
+    for b in sorted(range(B), key=lambda b: (-lens[b], b)):
+        w = min(range(W), key=lambda w: (loads[w], w))
+        loads[w] += lens[b] + seg
+        bin_of[b] = w
+    if max(loads) >= chunk_max:
+        return None
+    start = np.concatenate([[0], np.cumsum(np.bincount(bin_of, minlength=W))])
+    req = np.array(sorted(range(B), key=lambda b: (bin_of[b], b)))
+    return start, req
+
+
+def test_request_bins_follow_the_packing_rule():
+    """The library's bins of whole requests, bit for bit against the rule
+    restated in Python, over random batches (PAGED and cascade plans, bf16 and
+    fp8, several segment costs); and what every binned plan guarantees."""
+    rng = np.random.default_rng(23)
+    n_binned = 0
+    for it in range(400):
+        B = int(rng.integers(2, 400))
+        hi = int(rng.choice([64, 700, 3000, 9000]))
+        lens = rng.integers(1, hi + 1, size=B)
+        if it % 7 == 0:
+            lens[rng.integers(0, B)] = 0
+        if it % 5 == 0:
+            lens = np.sort(lens)
+        P = 0 if it % 2 else int(rng.integers(0, int(lens.min()) + 1)) // 16 * 16
+        seg = int(rng.choice([0, 8, 32, 200]))
+        kv = "fp8" if it % 3 == 0 else "bf16"
+        t = dict(segment_tokens=seg, target_workgroups=int(rng.choice([128, 256, 512, 1024])))
+        info = _both(B, 4, P, 16, L=lens, kv=kv, force=(2 if P else -1), tune=t)
+        if info is None:
+            continue
+        n = [int(L) - info["prefix_tokens"] for L in lens]
+        W = info["num_work_items"] // (8 // info["heads_per_item"])
+        exp = _expected_bins(n, info["split_tokens"], W, seg)
+        plan = pkv.pkv_plan_create(batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                                   kv_dtype=kv, page_size=16,
+                                   kv_indptr=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                                   shared_prefix_len=P, force_path=(2 if P else -1),
+                                   tuning=dict(TUNE, **t))
+        if exp is None:
+            assert info["request_bins"] == 0, (it, B, seg)
+            with pytest.raises(pkv.PkvError):
+                pkv.pkv_plan_request_bins(plan)
+            continue
+        n_binned += 1
+        assert info["request_bins"] == W and info["num_splits"] == 1
+        start, req = pkv.pkv_plan_request_bins(plan)
+        assert np.array_equal(start, exp[0]) and np.array_equal(req, exp[1]), it
+        # every request exactly once, each bin's in increasing order
+        assert sorted(req.tolist()) == list(range(B))
+        assert all((np.diff(req[start[w]:start[w + 1]]) > 0).all() for w in range(W))
+        # a PAGED plan on bins needs no combine: no partial-state workspace
+        if not P:
+            assert info["workspace_bytes"] == 0
+    assert n_binned >= 40, n_binned
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_short_suffix_workloads_run_on_request_bins(name):
+    """The cascade workloads with many short suffixes are planned on bins:
+    no suffix is cut, and the most loaded bin beats the most loaded chunk."""
+    from workloads import make_config
+    b = make_config(name)
+    lens = [int(x) for x in b.seq_lens]
+    info = _both(b.B, b.H_q // b.H_kv, b.prefix_len, b.page_size, L=lens)
+    assert info["path_name"] == "DENSE" and info["request_bins"] > 0 and info["num_splits"] == 1
 
 
 def test_plan_workspace_and_geometry():
