@@ -150,7 +150,8 @@ typedef struct pkv_tuning {
                                    per-token slot indices ([P2] s.1); 0: always by slot index */
     int32_t segment_tokens;     /* paged pass: the cost of one request segment in a work item,
                                    in positions.  When every request of the pass is non-empty
-                                   and fits one chunk, the planner also packs whole requests
+                                   and fits a workgroup's index stage (2,048 or 4,096
+                                   positions by geometry), the planner also packs whole requests
                                    into as many bins as chunks (largest first, each to the
                                    least loaded bin) and takes the bins when their most costly
                                    one (positions + segment_tokens per request) costs less than

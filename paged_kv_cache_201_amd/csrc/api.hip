@@ -104,6 +104,7 @@ pkv::PagedArgs paged_args(const pkv_plan* pl, const void* q, const pkv_pool* poo
     a.scale_log2 = sm_scale * kLog2e;
     a.out_dtype = pl->q_dtype;
     a.request_bins = pl->request_bins;
+    a.bin_max_tokens = pl->bin_max_tokens;
     if (pl->request_bins > 0) {
         std::copy(pl->bin_start.begin(), pl->bin_start.end(), a.bin_start);
         std::copy(pl->bin_req.begin(), pl->bin_req.end(), a.bin_req);

@@ -219,7 +219,7 @@ void fp8_long_geometry(pkv_plan* pl, const pkv_tuning& tu, int64_t tokens, int64
 }
 
 // Bins of whole requests for the paged pass: when every request of the pass
-// is non-empty and no longer than a chunk, requests are packed, largest
+// is non-empty and fits a workgroup's index stage, requests are packed, largest
 // first (ties by index), each into the least loaded of num_chunks bins (ties
 // by bin), with a request's load its positions plus tu.segment_tokens.  The
 // bins replace the chunks when their most loaded bin is below the most
@@ -229,12 +229,14 @@ template <class LenFn>
 bool bin_requests(pkv_plan* pl, const pkv_tuning& tu, LenFn n_of, int64_t chunk) {
     const int64_t W = pl->num_chunks, B = pl->B, seg = tu.segment_tokens;
     if (seg == 0 || W < 2 || W > pkv::kMaxRequestBins || B > pkv::kMaxBinnedRequests) return false;
+    const int64_t stage = pkv::max_chunk_tokens(pl->geo.rs, pl->geo.nhl, pl->geo.tpi, pl->G, pl->D);
     std::vector<int64_t> n(B);
-    int64_t total = 0;
+    int64_t total = 0, longest = 0;
     for (int64_t b = 0; b < B; ++b) {
         n[b] = n_of((int32_t)b);
-        if (n[b] == 0 || n[b] > chunk) return false;
+        if (n[b] == 0 || n[b] > stage) return false;
         total += n[b];
+        longest = std::max(longest, n[b]);
     }
     // most loaded chunk of the flat partition
     std::vector<int64_t> chunk_cost(W, 0);
@@ -274,6 +276,7 @@ bool bin_requests(pkv_plan* pl, const pkv_tuning& tu, LenFn n_of, int64_t chunk)
     std::vector<int32_t> fill(pl->bin_start.begin(), pl->bin_start.end() - 1);
     for (int64_t b = 0; b < B; ++b) pl->bin_req[fill[bin_of[b]]++] = (uint16_t)b;
     pl->request_bins = (int32_t)W;
+    pl->bin_max_tokens = (int32_t)longest;
     return true;
 }
 

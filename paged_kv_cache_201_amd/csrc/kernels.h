@@ -45,6 +45,7 @@ struct PagedArgs {
     // takes requests bin_req[bin_start[w] .. bin_start[w + 1]), each as one
     // segment (no request is cut; a partial state, if any, is slot 0)
     int32_t request_bins;
+    int32_t bin_max_tokens;   // the longest request of the bins (fits the LDS index stage)
     uint16_t bin_start[kMaxRequestBins + 1];
     uint16_t bin_req[kMaxBinnedRequests];
 };

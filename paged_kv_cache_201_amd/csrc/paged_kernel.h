@@ -608,8 +608,9 @@ __device__ __forceinline__ void paged_chunk(const PagedArgs& a, PagedSmem<KV, D,
             const int b = a.bin_req[k];
             const int64_t ob = flat_offset(a, b), on = flat_offset(a, b + 1);
             // kv_indptr does not describe the planned batch: no request of
-            // the plan is empty or longer than a chunk (the index stage)
-            if (on <= ob || on - ob > C) return;
+            // the plan is empty or longer than its longest (which fits the
+            // LDS index stage)
+            if (on <= ob || on - ob > a.bin_max_tokens) return;
             if (k > r0) __syncthreads();  // the previous segment is done with LDS
             paged_segment<KV, D, G, NHL, TPI>(a, sm, b, hblk, a.kv_indptr[b] + a.token_offset, (int)(on - ob),
                                               a.force_partial ? 0 : -1, false);

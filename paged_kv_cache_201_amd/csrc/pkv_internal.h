@@ -87,6 +87,7 @@ struct pkv_plan {
     // bins of whole requests (request_bins > 0): bin w holds requests
     // bin_req[bin_start[w] .. bin_start[w + 1])
     int32_t request_bins = 0;
+    int32_t bin_max_tokens = 0;  // the longest request of a binned pass
     std::vector<uint16_t> bin_start, bin_req;
     // workspace layout (byte offsets; -1 = unused)
     int64_t ws_paged_acc, ws_paged_ml;

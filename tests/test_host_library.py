@@ -261,14 +261,24 @@ def test_chunk_partition_is_balanced_and_counted():
         assert chunks == 0 or (chunks - 1) * C < total <= chunks * C
 
 
-def _expected_bins(lens, chunk, W, seg):
+def _index_stage(kv, hpi):
+    """Positions one paged workgroup stages in LDS (G = 4, d = 128): 4,096
+    unless its merge buffer is large (the library's sizing rule, restated)."""
+    lph = 16  # 8 values per lane at d = 128: 16 bytes of bf16, 8 of fp8
+    rs = 64 // lph
+    tpi = rs // hpi
+    merge = 4 * (2 if tpi == 1 else 4 * tpi) * hpi * 4 * 128
+    return 2048 if merge > 40 * 1024 else 4096
+
+
+def _expected_bins(lens, chunk, W, seg, stage=4096):
     """The packing rule, stated again: whole requests, largest first (ties
     by index), each into the least loaded of W bins (ties by bin), load =
     positions + seg per request; taken when the most loaded bin costs less
     than the most loaded chunk of the flat partition (positions + seg per
     request the chunk touches).  None: chunks."""
     B = len(lens)
-    if seg == 0 or W < 2 or W > 256 or B > 1024 or any(n == 0 or n > chunk for n in lens):
+    if seg == 0 or W < 2 or W > 256 or B > 1024 or any(n == 0 or n > stage for n in lens):
         return None
     total = sum(lens)
     cost, pos = [0] * W, 0
@@ -312,7 +322,7 @@ def test_request_bins_follow_the_packing_rule():
             continue
         n = [int(L) - info["prefix_tokens"] for L in lens]
         W = info["num_work_items"] // (8 // info["heads_per_item"])
-        exp = _expected_bins(n, info["split_tokens"], W, seg)
+        exp = _expected_bins(n, info["split_tokens"], W, seg, _index_stage(kv, info["heads_per_item"]))
         plan = pkv.pkv_plan_create(batch=B, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
                                    kv_dtype=kv, page_size=16,
                                    kv_indptr=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
