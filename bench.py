@@ -571,7 +571,8 @@ def page_control(steps, warmup):
         for p in (16, 64, 128):
             b = base if p == 16 else relayout(base, page_size=p, seed=2007, layout="shared", device="cuda")
             db = DeviceBatch.from_batch(b)
-            plan = db.plan(force_path=0)
+            # the shared case declares its prefix (the pass re-reads it from L2)
+            plan = db.plan(shared_prefix_len=b.prefix_len, force_path=0)
             o, lse, ws = db.new_out(), db.new_lse(), db.workspace(plan)
             for mode in ("page_table", "token_flat"):
                 fn = ((lambda: db.paged_pages(plan, o=o, lse=lse, ws=ws)) if mode == "page_table"
@@ -935,8 +936,9 @@ def write_prefix_counters(name, mfma_dir, lds_dir, commands):
 PAGED_VALU_COUNTERS = ("SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_THREAD_CYCLES_VALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
                        "SQ_WAIT_ANY SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE")
 # the paged kernel of each workload in a `--configs c2,c5` run (kernel name, grid size)
-PAGED_COUNTER_KERNELS = {"c2": ("pkv::paged_split_kernel<1, 128, 4, 1, 1>", 131072),
-                         "c5": ("pkv::paged_split_kernel<2, 128, 8, 1, 1>", 131072)}
+# the paged kernel of each workload in the counter run: the bf16 and the fp8
+# instantiation (KV template argument 1 and 2) with the most dispatches
+PAGED_COUNTER_KERNELS = {"c2": "pkv::paged_split_kernel<1,", "c5": "pkv::paged_split_kernel<2,"}
 
 
 def write_paged_counters(valu_dir, fetch_dir, commands):
@@ -947,12 +949,15 @@ def write_paged_counters(valu_dir, fetch_dir, commands):
     import statistics
     from workloads import make_config
     out = {}
-    for name, key in PAGED_COUNTER_KERNELS.items():
+    per_counter = {c: pmc_per_dispatch(valu_dir, c) for c in PAGED_VALU_COUNTERS.split()}
+    for name, prefix in PAGED_COUNTER_KERNELS.items():
         b = make_config(name)
         tokens = int(sum(int(x) for x in b.seq_lens))
+        cands = {k: len(v) for k, v in per_counter["SQ_INSTS_VALU"].items() if k[0].startswith(prefix)}
+        key = max(cands, key=cands.get) if cands else (prefix, 0)
         med = {}
         for c in PAGED_VALU_COUNTERS.split():
-            vals = pmc_per_dispatch(valu_dir, c).get(key, [])
+            vals = per_counter[c].get(key, [])
             med[c] = statistics.median(vals) if vals else None
         ratio = lambda x, y: (x / y) if (x is not None and y) else None  # noqa: E731
         out[name] = dict(kernel=f"{key[0]} grid={key[1]}", tokens=tokens, kv_heads=b.H_kv, group=b.G,
@@ -1228,9 +1233,9 @@ def main():
         run = "-- python bench.py --page-control --steps 5 --warmup 2"
         cmds = dict(time=f"python bench.py --page-control > {r}",
                     vmem=f"{prof}timeout -s KILL 120 rocprofv3 --pmc SQ_INSTS_VMEM_RD --output-format csv -d {v} "
-                         f"-o run {run}",
+                         f"-o run {run} > {v}.json",
                     tcc=f"{prof}timeout -s KILL 120 rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv "
-                        f"-d {t} -o run {run}",
+                        f"-d {t} -o run {run} > {t}.json",
                     summary=f"python bench.py --summarize-page-control {r} {v} {t}")
         print(write_page_control(r, v, t, cmds))
         return

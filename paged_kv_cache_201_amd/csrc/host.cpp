@@ -192,9 +192,14 @@ int64_t fused_prefix_target(const pkv_tuning& tu) {
 // leave a few workgroups over one per CU: 27 % slower on long requests); an
 // fp8 pass (bound by the vector ALU) keeps two per CU to hide its loads; a
 // pass that shares its launch with the prefix items takes what they leave.
-int64_t paged_target(const pkv_plan* pl, const pkv_tuning& tu, int64_t total, bool fused, int64_t fused_target) {
+// A pass whose positions are mostly re-reads of declared shared pages
+// (`reread` of `total`: a shared prefix the gate left on PAGED) is served
+// from L2 and keeps two workgroups per CU (one per CU measured 26-34 %
+// slower on 8-64 requests over a shared prefix).
+int64_t paged_target(const pkv_plan* pl, const pkv_tuning& tu, int64_t total, bool fused, int64_t fused_target,
+                     int64_t reread) {
     if (fused) return fused_target;
-    if (pl->kv_dtype == PKV_FP8_E4M3) return tu.target_workgroups;
+    if (pl->kv_dtype == PKV_FP8_E4M3 || 2 * reread >= total) return tu.target_workgroups;
     const int64_t half = std::max<int64_t>(1, tu.target_workgroups / 2);
     const int64_t chunk = align_up(std::max<int64_t>(tu.min_split_tokens, ceil_div(total * pl->head_blocks, half)),
                                    pkv::kSplitQuantum);
@@ -289,7 +294,17 @@ void plan_chunks(pkv_plan* pl, const pkv_tuning& tu, int64_t total, int64_t targ
     const int64_t per_item = ceil_div(total * pl->head_blocks, target);
     int64_t chunk = std::max<int64_t>(tu.min_split_tokens, per_item);
     chunk = align_up(chunk, pkv::kSplitQuantum);
-    chunk = std::min<int64_t>(chunk, pkv::max_chunk_tokens(pl->geo.rs, pl->geo.nhl, pl->geo.tpi, pl->G, pl->D));
+    const int64_t cap = pkv::max_chunk_tokens(pl->geo.rs, pl->geo.nhl, pl->geo.tpi, pl->G, pl->D);
+    if (chunk > cap) {
+        // Capped chunks give more work items than the target: take whole
+        // multiples of the target instead, so that no wave runs a remnant
+        // (the PAGED leg of a 256 x 4,382-position step: 548 items 777 us,
+        // 1,024 items 544 us)
+        const int64_t items = ceil_div(total, cap) * pl->head_blocks;
+        const int64_t waves = ceil_div(items, target);
+        chunk = align_up(ceil_div(total * pl->head_blocks, waves * target), pkv::kSplitQuantum);
+        chunk = std::min(std::max<int64_t>(chunk, tu.min_split_tokens), cap);
+    }
     pl->split_tokens = (int32_t)chunk;
     pl->num_chunks = ceil_div(total, chunk);
     pl->num_work_items = pl->num_chunks * pl->head_blocks;
@@ -547,7 +562,9 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     int64_t nonempty = 0;
     for (int32_t b = 0; b < B; ++b) nonempty += n_of(b) > 0;
     if (!pl->fuse_cascade) fp8_long_geometry(pl, tu, total, nonempty);
-    const int64_t target = paged_target(pl, tu, total, pl->fuse_cascade, tu.target_workgroups - prefix_wgs);
+    // positions a PAGED pass re-reads from a declared shared prefix
+    const int64_t reread = path == PKV_PATH_PAGED && n_shared >= 2 ? (n_shared - 1) * shared_pages * p : 0;
+    const int64_t target = paged_target(pl, tu, total, pl->fuse_cascade, tu.target_workgroups - prefix_wgs, reread);
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, total, target, n_of, &spans, &any_empty);
     // A combine kernel follows the paged pass for a cascade step, when a
@@ -883,7 +900,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     int64_t nonempty = 0;
     for (int32_t b = 0; b < B; ++b) nonempty += n_of(b) > 0;
     if (!fuse) fp8_long_geometry(pl, tu, suffix_total, nonempty);
-    const int64_t target = paged_target(pl, tu, suffix_total, fuse, tu.target_workgroups - align_up(dense_items, 8));
+    const int64_t target = paged_target(pl, tu, suffix_total, fuse, tu.target_workgroups - align_up(dense_items, 8), 0);
     bool spans = false, any_empty = false;
     plan_chunks(pl, tu, suffix_total, target, n_of, &spans, &any_empty);
     pl->needs_reduce = NG > 0 || spans || any_empty;

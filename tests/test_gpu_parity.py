@@ -199,10 +199,13 @@ def test_cascade_small_all_paths_and_layouts():
         torch.cuda.synchronize()
         op_ref, lp_ref = ob.prefix_reference(shared, n)
         check_close("bf16", o_p, lse_p, op_ref, lp_ref, f"prefix B={B}")
-        # paged over unique copies of the prefix: same bits as over shared pages
+        # paged over unique copies of the prefix, planned alike (the same
+        # declared prefix length): same bits as over shared pages
         unique = relayout(shared, page_size=16, seed=77, layout="unique")
         say(f"paged unique B={B}")
-        ou, lu, _ = run_paged(DeviceBatch, unique)
+        du = DeviceBatch.from_batch(unique)
+        ou, lu = du.paged(du.plan(shared_prefix_len=P, force_path=0))
+        torch.cuda.synchronize()
         assert same_bits(ou, res[0][0]) and same_bits(lu, res[0][1]), "layout changed the bits"
 
 
