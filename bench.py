@@ -422,7 +422,7 @@ def dispatch_sweep(out_path, steps=10, warmup=3):
              "to the fastest path on the shared-page layout; paged_unique = PAGED over per-request prefix copies",
         grid=dict(B=SWEEP_B, G=SWEEP_G, P=SWEEP_P, kv_dtype=SWEEP_DTYPES, H_kv=8, d=128, own_tokens="U{64..512}",
                   page_size=16, steps=steps, windows=3),
-        defaults_when_measured={k: defaults[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")},
+        defaults_when_measured={k: defaults[k] for k in DISPATCH_CONSTANTS},
         planned_mean_ratio=float(np.mean(planned)), planned_worst_ratio=float(np.max(planned)),
         planned_mean_ratio_b_ge_2=float(np.mean(planned_multi)),
         planned_worst_ratio_b_ge_2=float(np.max(planned_multi)),
@@ -435,6 +435,12 @@ def dispatch_sweep(out_path, steps=10, warmup=3):
 REPLAY_T_DENSE = (1, 64, 256, 1024)
 REPLAY_RATIO = (1, 2, 3, 4, 5, 6, 8)
 REPLAY_LAUNCH_MB = (0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 15, 20, 30)
+REPLAY_CACHED_MIB = (0, 64, 96, 128, 192)  # cached_reread_bytes in MiB (0: no allowance)
+
+
+# the planner constants a dispatcher sweep depends on
+DISPATCH_CONSTANTS = ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade", "cached_prefix_bytes",
+                      "cached_reread_bytes")
 
 
 def write_sweep_json(path, rec):
@@ -466,8 +472,9 @@ def replay_sweep(cells):
         return pl.info["path_name"]
 
     replay = []
-    for t_dense, ratio, launch in itertools.product(REPLAY_T_DENSE, REPLAY_RATIO, REPLAY_LAUNCH_MB):
-        tune = dict(t_dense=t_dense, gate_ratio=ratio, launch_bytes=launch * 10**6)
+    for t_dense, ratio, launch, cached in itertools.product(REPLAY_T_DENSE, REPLAY_RATIO, REPLAY_LAUNCH_MB,
+                                                            REPLAY_CACHED_MIB):
+        tune = dict(t_dense=t_dense, gate_ratio=ratio, launch_bytes=launch * 10**6, cached_reread_bytes=cached << 20)
         ratios = []
         for cell in cells:
             path = decide(cell, tune)
@@ -1152,13 +1159,14 @@ def main():
         rec = json.load(open(args.replay_sweep))
         replay = replay_sweep(rec["cells"])
         rec["replay_best"] = replay[:12]
-        rec["replay_grid"] = dict(t_dense=REPLAY_T_DENSE, gate_ratio=REPLAY_RATIO, launch_mb=REPLAY_LAUNCH_MB)
+        rec["replay_grid"] = dict(t_dense=REPLAY_T_DENSE, gate_ratio=REPLAY_RATIO, launch_mb=REPLAY_LAUNCH_MB,
+                                   cached_reread_mib=REPLAY_CACHED_MIB)
         rec["replay_command"] = f"python bench.py --replay-sweep {args.replay_sweep}"
         import paged_kv_cache_201_amd as pkv
         if "defaults" in rec:
             rec["defaults_when_measured"] = rec.pop("defaults")
         cur = pkv.pkv_tuning_defaults()
-        rec["defaults_now"] = {k: cur[k] for k in ("t_dense", "gate_ratio", "launch_bytes", "fuse_cascade")}
+        rec["defaults_now"] = {k: cur[k] for k in DISPATCH_CONSTANTS}
         write_sweep_json(args.replay_sweep, rec)
         print(json.dumps(replay[:5], indent=1))
         return

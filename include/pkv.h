@@ -121,7 +121,8 @@ typedef struct pkv_problem {
 /* Constants of the planner.  pkv_tuning_defaults() returns the gfx950 values. */
 typedef struct pkv_tuning {
     int32_t t_dense;            /* DENSE when M_eff >= t_dense ([P2] s.3 threshold, refitted) */
-    int32_t gate_ratio;         /* PAGED when saved_bytes < gate_ratio * overhead_bytes */
+    int32_t gate_ratio;         /* PAGED when saved_bytes < gate_ratio * overhead_bytes (0: the
+                                   gate is off, including the cached-prefix allowance below) */
     int64_t launch_bytes;       /* byte-equivalent of the two extra launches of a cascade */
     int32_t target_workgroups;  /* paged pass: workgroups to aim for across the GPU when it is
                                    an fp8 pass or shares its launch with prefix items; a bf16
@@ -156,6 +157,14 @@ typedef struct pkv_tuning {
                                    least loaded bin) and takes the bins when their most costly
                                    one (positions + segment_tokens per request) costs less than
                                    the most costly chunk; 0: always chunks */
+    int64_t cached_prefix_bytes; /* a shared prefix whose stored K and V take at most this many
+                                    bytes stays in the L2 of each XCD while every request of a
+                                    PAGED pass re-reads it: for such a prefix (and gate_ratio
+                                    > 0) pkv_plan_create also takes PAGED while saved_bytes <
+                                    cached_reread_bytes (the grouped planner does not: a
+                                    dissolved group's re-reads would join the suffix pass that
+                                    the kept groups' prefix items overlap); 0: off */
+    int64_t cached_reread_bytes; /* see cached_prefix_bytes */
 } pkv_tuning;
 
 typedef struct pkv_plan pkv_plan;   /* opaque, immutable, host-only */

@@ -89,7 +89,8 @@ def detect_prefix_groups(page_size, page_indptr, page_indices, seq_lens):
 
 def plan_groups(*, H_q, H_kv, d, q_dtype, kv_dtype, page_size, page_indptr, page_indices, seq_lens,
                 force_path, t_dense, gate_ratio, launch_bytes, prefix_placement=1):
-    """The kept groups, each planned on its own run.
+    """The kept groups, each planned on its own run (the single-prefix rule
+    without its cached-prefix allowance: this library's reading, measured).
 
     Returns ``(groups, path_of)``: ``groups`` lists the kept groups in
     depth-first order as dicts with ``members``, ``start_tokens``,

@@ -19,9 +19,18 @@ Rule, in order (all arithmetic in Python integers):
    dtype pair the prefix kernels do not handle -> PAGED;
 3. saved    = (n_shared - 1) * prefix_tokens * H_kv * d * (b_k + b_v)
    overhead = 4 * rows * (d + 1) * 4 + launch_bytes
-   saved < gate_ratio * overhead -> PAGED;  (b_k, b_v: an fp8 value counts
-   as 2 bytes, the bf16 width: the library's fp8 paged pass is bound by the
-   vector ALU, so its tokens cost about the time of bf16 tokens; measured)
+   allowed  = gate_ratio * overhead, raised to cached_reread_bytes when
+              gate_ratio > 0 and the prefix's stored K and V (prefix_tokens *
+              H_kv * d * 2 * the stored value's bytes) take at most
+              cached_prefix_bytes > 0
+   (the allowance only where the DENSE step would not take the fused launch:
+   fuse_cascade = 0, or 4 * M_eff * prefix_tokens * d * H_kv <
+   fuse_cascade * (sum of L_b - prefix_tokens) * H_kv * d * (b_k + b_v))
+   saved < allowed -> PAGED;  (b_k, b_v: an fp8 value counts as 2 bytes, the
+   bf16 width: the library's fp8 paged pass is bound by the vector ALU, so its
+   tokens cost about the time of bf16 tokens; measured.  A small prefix stays
+   cached while every request re-reads it, so its re-reads cost little; also
+   measured)
 4. M_eff >= t_dense -> DENSE, else CASCADE.
 
 Prefix placement ("GraniKV", section 1, asymmetric paging: the shared prefix
@@ -58,7 +67,7 @@ class PlanError(ValueError):
 
 def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
          shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes, prefix_slots=None,
-         prefix_placement=1):
+         prefix_placement=1, cached_prefix_bytes=0, cached_reread_bytes=0, fuse_cascade=0):
     """Returns dict(path, m_eff, shared_pages, prefix_tokens, prefix_base).
 
     ``prefix_slots`` (optional): the slots of the first request's first
@@ -67,7 +76,9 @@ def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
     """
     out = _plan_path(B=B, H_q=H_q, H_kv=H_kv, d=d, q_dtype=q_dtype, kv_dtype=kv_dtype, page_size=page_size,
                      seq_lens=seq_lens, shared_prefix_len=shared_prefix_len, force_path=force_path,
-                     t_dense=t_dense, gate_ratio=gate_ratio, launch_bytes=launch_bytes)
+                     t_dense=t_dense, gate_ratio=gate_ratio, launch_bytes=launch_bytes,
+                     cached_prefix_bytes=cached_prefix_bytes, cached_reread_bytes=cached_reread_bytes,
+                     fuse_cascade=fuse_cascade)
     out["prefix_base"] = -1
     n = out["prefix_tokens"]
     if out["path"] != PAGED and prefix_placement and prefix_slots is not None and n > 0:
@@ -78,7 +89,8 @@ def plan(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
 
 
 def _plan_path(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
-               shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes):
+               shared_prefix_len, force_path, t_dense, gate_ratio, launch_bytes,
+               cached_prefix_bytes=0, cached_reread_bytes=0, fuse_cascade=0):
     """Returns dict(path, m_eff, shared_pages, prefix_tokens).
 
     ``shared_pages`` is floor(P / p) whenever a prefix is declared;
@@ -123,7 +135,13 @@ def _plan_path(*, B, H_q, H_kv, d, q_dtype, kv_dtype, page_size, seq_lens,
     gate_bytes = 2 if kv_dtype == "fp8" else BYTES[kv_dtype]
     saved = (n_shared - 1) * prefix_tokens * H_kv * d * (gate_bytes * 2)
     overhead = 4 * rows * (d + 1) * 4 + launch_bytes
-    if saved < gate_ratio * overhead:
+    allowed = gate_ratio * overhead
+    stored = prefix_tokens * H_kv * d * 2 * BYTES[kv_dtype]
+    suffix = sum(int(x) - prefix_tokens for x in seq_lens)
+    fuses = fuse_cascade > 0 and 4 * m_eff * prefix_tokens * d * H_kv >= fuse_cascade * suffix * H_kv * d * gate_bytes * 2
+    if gate_ratio > 0 and cached_prefix_bytes > 0 and stored <= cached_prefix_bytes and not fuses:
+        allowed = max(allowed, cached_reread_bytes)
+    if saved < allowed:
         out.update(path=PAGED, prefix_tokens=0)
     elif m_eff >= t_dense:
         out["path"] = DENSE

@@ -64,7 +64,8 @@ class pkv_tuning(ctypes.Structure):
                 ("concurrent_prefix", ctypes.c_int32), ("fuse_cascade", ctypes.c_int32),
                 ("prefix_target_workgroups", ctypes.c_int32), ("min_prefix_split_tokens", ctypes.c_int32),
                 ("max_heads_per_item", ctypes.c_int32), ("prefix_placement", ctypes.c_int32),
-                ("segment_tokens", ctypes.c_int32)]
+                ("segment_tokens", ctypes.c_int32), ("cached_prefix_bytes", ctypes.c_int64),
+                ("cached_reread_bytes", ctypes.c_int64)]
 
 
 class pkv_plan_info(ctypes.Structure):

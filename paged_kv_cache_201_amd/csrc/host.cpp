@@ -92,7 +92,7 @@ pkv_status check_problem(const pkv_problem* pr, const pkv_tuning* tuning, pkv_tu
         tu->min_split_tokens < 1 || tu->concurrent_prefix < 0 || tu->concurrent_prefix > 1 ||
         tu->fuse_cascade < 0 || tu->prefix_target_workgroups < 1 || tu->min_prefix_split_tokens < 1 ||
         tu->max_heads_per_item < 0 || tu->prefix_placement < 0 || tu->prefix_placement > 1 ||
-        tu->segment_tokens < 0)
+        tu->segment_tokens < 0 || tu->cached_prefix_bytes < 0 || tu->cached_reread_bytes < 0)
         return PKV_EINVAL;
     const int32_t B = pr->batch, H_q = pr->num_q_heads, H_kv = pr->num_kv_heads;
     if (B < 0 || H_kv < 1 || H_q < 1 || pr->page_size < 1 || pr->head_dim < 1) return PKV_EINVAL;
@@ -120,7 +120,9 @@ int64_t rule_bytes(int32_t kv_dtype) { return kv_dtype == PKV_FP8_E4M3 ? 2 : dty
 // (whole pages), rows query rows and M_eff = m_eff, in order: a forced path;
 // PAGED without two sharers, a shared page or a prefix kernel for the dtype
 // pair; PAGED when the bytes saved are under gate_ratio x the combine's
-// state traffic plus the launch term; DENSE at M_eff >= t_dense; CASCADE.
+// state traffic plus the launch term, or, for a prefix whose stored K/V fit
+// cached_prefix_bytes, under cached_reread_bytes if that is more (gate_ratio
+// 0 turns the whole gate off); DENSE at M_eff >= t_dense; CASCADE.
 pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_shared, int64_t prefix_tokens,
                        int64_t rows, int64_t m_eff, int32_t* path) {
     const bool capable = prefix_pair_supported(pr->q_dtype, pr->kv_dtype, pr->head_dim);
@@ -140,7 +142,12 @@ pkv_status choose_path(const pkv_problem* pr, const pkv_tuning& tu, int64_t n_sh
     const int64_t kv_bytes = 2LL * rule_bytes(pr->kv_dtype);
     const int64_t saved = (n_shared - 1) * prefix_tokens * pr->num_kv_heads * D * kv_bytes;
     const int64_t overhead = 4 * rows * (D + 1) * 4 + tu.launch_bytes;
-    if (saved < (int64_t)tu.gate_ratio * overhead)
+    // a prefix small enough to stay in L2 costs its re-readers little
+    const int64_t stored = prefix_tokens * pr->num_kv_heads * D * 2 * dtype_bytes(pr->kv_dtype);
+    int64_t allowed = (int64_t)tu.gate_ratio * overhead;
+    if (tu.gate_ratio > 0 && tu.cached_prefix_bytes > 0 && stored <= tu.cached_prefix_bytes)
+        allowed = std::max<int64_t>(allowed, tu.cached_reread_bytes);
+    if (saved < allowed)
         *path = PKV_PATH_PAGED;
     else if (m_eff >= tu.t_dense)
         *path = PKV_PATH_DENSE;
@@ -401,6 +408,14 @@ void pkv_tuning_defaults(pkv_tuning* out) {
     // 2,560-position chunk, 30 positions' worth; as many segments per workgroup
     // measured the same whatever their lengths
     out->segment_tokens = 32;
+    // forced-path sweep (B x G x P, bf16 and fp8): PAGED over shared pages beat
+    // the prefix paths with 64 requests over a 256-token prefix (1 MB bf16,
+    // 0.84-0.92 of the best prefix path) and with 16 requests over a 1,024-token
+    // fp8 prefix (2 MB, 0.77-1.01), and lost at four times those re-reads
+    // (1.05-1.59): re-reads of a prefix within half of one XCD's 4 MB L2 come
+    // from L2; the re-read allowance sits between the two (66 MB and 264 MB)
+    out->cached_prefix_bytes = 2 << 20;
+    out->cached_reread_bytes = 128 << 20;
 }
 
 pkv_status pkv_lower_page_table(int32_t batch, int32_t page_size, const int32_t* page_indptr,
@@ -493,8 +508,20 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     const int64_t shared_pages = n_shared ? P / p : 0;
     int64_t prefix_tokens = shared_pages * p;
     const int64_t m_eff = (int64_t)B * G;
+    // The cached-prefix allowance applies where the DENSE step would not
+    // fuse (the fuse rule's flops-per-byte test below): a fused launch hides
+    // the prefix pass under the suffix streaming, which PAGED re-reads would
+    // lengthen instead.
+    pkv_tuning path_tu = tu;
+    if (tu.fuse_cascade > 0 && prefix_tokens > 0) {
+        int64_t suffix = 0;
+        for (int32_t b = 0; b < B; ++b) suffix += (int64_t)pr->kv_indptr[b + 1] - pr->kv_indptr[b] - prefix_tokens;
+        const int64_t prefix_flops = 4 * m_eff * prefix_tokens * D * H_kv;
+        const int64_t suffix_bytes = suffix * H_kv * D * 2 * rule_bytes(pr->kv_dtype);
+        if (prefix_flops >= (int64_t)tu.fuse_cascade * suffix_bytes) path_tu.cached_prefix_bytes = 0;
+    }
     int32_t path;
-    st = choose_path(pr, tu, n_shared, prefix_tokens, (int64_t)B * H_q, m_eff, &path);
+    st = choose_path(pr, path_tu, n_shared, prefix_tokens, (int64_t)B * H_q, m_eff, &path);
     if (st != PKV_OK) return st;
     if (path == PKV_PATH_PAGED) prefix_tokens = 0;
     if (m_eff > INT32_MAX) return PKV_EUNSUPPORTED;
@@ -689,6 +716,12 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
     }
     // Each group is planned as the step it would be on its own over its own
     // run; a group planned PAGED is dissolved (its children still planned).
+    // The cached-prefix allowance is left out: a dissolved group's re-reads
+    // join the suffix pass that every kept group's prefix items overlap
+    // (four prompts of 48 requests: the 512-token prompt dissolved by the
+    // allowance took the step from 72.8 to 96.3 us).
+    pkv_tuning group_tu = tu;
+    group_tu.cached_prefix_bytes = 0;
     struct Group {
         std::vector<int32_t> members;
         int32_t start_tokens, prefix_tokens, parent, path, m_eff, rows_per_wg, row_tiles, split_tokens, splits;
@@ -703,7 +736,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         const Node& nd = nodes[i];
         const int64_t n = (int64_t)nd.members.size();
         int32_t path;
-        st = choose_path(pr, tu, n, (int64_t)(nd.end - nd.start) * p, n * H_q, n * G, &path);
+        st = choose_path(pr, group_tu, n, (int64_t)(nd.end - nd.start) * p, n * H_q, n * G, &path);
         if (st != PKV_OK) return st;
         if (path == PKV_PATH_PAGED) continue;
         int32_t a = nd.parent;  // nearest kept ancestor

@@ -68,7 +68,19 @@ def test_status_strings_and_version():
     assert d["max_heads_per_item"] >= 0
     assert d["prefix_placement"] in (0, 1)
     assert 0 <= d["segment_tokens"] <= 4096
-    assert len(d) == 12
+    assert 0 < d["cached_prefix_bytes"] <= 1 << 30 and d["cached_prefix_bytes"] < d["cached_reread_bytes"] <= 1 << 34
+    assert len(d) == 14
+
+
+def test_negative_tuning_fields_are_refused():
+    """Every tuning constant has a lower bound of 0 or 1: -1 in any field is
+    refused with EINVAL before a plan exists."""
+    for name in pkv.pkv_tuning_defaults():
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_plan_create(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, q_dtype="bf16",
+                                kv_dtype="bf16", page_size=16, kv_indptr=[0, 32, 64], shared_prefix_len=16,
+                                tuning={name: -1})
+        assert e.value.name == "EINVAL", name
 
 
 # ---------------------------------------------------------------- lowering --
@@ -138,7 +150,8 @@ def _both(B, G, P, p, L, H_kv=8, d=128, q="bf16", kv="bf16", force=-1, tune=None
         ref = op.plan(B=B, H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype=q, kv_dtype=kv, page_size=p, seq_lens=lens,
                       shared_prefix_len=P, force_path=force, t_dense=t["t_dense"], gate_ratio=t["gate_ratio"],
                       launch_bytes=t["launch_bytes"], prefix_slots=kv_indices,
-                      prefix_placement=t["prefix_placement"])
+                      prefix_placement=t["prefix_placement"], cached_prefix_bytes=t["cached_prefix_bytes"],
+                      cached_reread_bytes=t["cached_reread_bytes"], fuse_cascade=t["fuse_cascade"])
     except op.PlanError as e:
         err_ref = e.code
     got = err_got = None
@@ -178,6 +191,7 @@ def test_prefix_placement_matches_oracle():
             if it % 3 == 1 and P > 1:
                 idx[int(rng.integers(1, P))] += 1  # ... with one slot out of line
         tune = dict(gate_ratio=int(rng.integers(0, 2)), launch_bytes=0, t_dense=int(rng.integers(1, 300)),
+                    cached_prefix_bytes=0,
                     prefix_placement=int(rng.integers(0, 2)) if it % 5 == 0 else 1)
         got = _both(B, int(rng.choice([1, 2, 4, 8])), P, p, lens, force=int(rng.choice([-1, -1, 0, 1, 2])),
                     tune=tune, kv_indices=idx) if P >= p or it % 4 else None
@@ -196,7 +210,9 @@ def test_planner_tuning_variants_match_oracle():
     rng = np.random.default_rng(0)
     for _ in range(300):
         tune = dict(t_dense=int(rng.integers(1, 4096)), gate_ratio=int(rng.integers(0, 5)),
-                    launch_bytes=int(rng.integers(0, 10**9)))
+                    launch_bytes=int(rng.integers(0, 10**9)),
+                    cached_prefix_bytes=int(rng.choice([0, 1 << 20, 2 << 20, 8 << 20, 64 << 20])),
+                    cached_reread_bytes=int(rng.integers(0, 2 * 10**9)), fuse_cascade=int(rng.choice([0, 1, 12, 200])))
         _both(int(rng.integers(0, 600)), int(rng.choice([1, 2, 4, 8])), int(rng.integers(0, 5000)),
               int(rng.choice([1, 16, 32, 128])), L=5000 + int(rng.integers(0, 100)), tune=tune)
 
@@ -448,7 +464,8 @@ def test_grouped_plan_matches_oracle_on_random_tables():
         reqs, lens = random_group_tables(rng, p, max_batch=12)
         ptr, pages = tables_from_blocks(reqs, p, it, scramble=bool(it % 3))
         tune = dict(t_dense=int(rng.integers(1, 40)), gate_ratio=int(rng.integers(0, 2)),
-                    launch_bytes=int(rng.integers(0, 3)) * 1000, prefix_placement=int(it % 7 != 0))
+                    launch_bytes=int(rng.integers(0, 3)) * 1000, prefix_placement=int(it % 7 != 0),
+                    cached_prefix_bytes=int(rng.choice([0, 1 << 20])), cached_reread_bytes=int(rng.integers(0, 3)) * 1000)
         plan = _grouped_both(p, ptr, pages, lens, force=int(rng.choice([-1, -1, 0, 1, 2])), tune=tune)
         if plan is not None:
             n_kept += plan.info["num_groups"]

@@ -406,6 +406,79 @@ def _plan(B, G, P, p=16, H_kv=8, d=128, L=None, **kw):
     return op.plan(**args)
 
 
+def check_cached_gate(plan_fn):
+    """Pins of the cached-prefix allowance, worked out by hand."""
+    def pl(B, G, P, p=16, H_kv=8, d=128, L=None, **kw):
+        args = dict(B=B, H_q=H_kv * G, H_kv=H_kv, d=d, q_dtype="bf16", kv_dtype="bf16",
+                    page_size=p, seq_lens=[L if L is not None else P + 100] * B,
+                    shared_prefix_len=P, force_path=-1, **TUNE)
+        args.update(kw)
+        return plan_fn(**args)
+
+    # the cached-prefix allowance (constants as the gfx950 defaults: R = 3,
+    # launch term 5,000,000 B, prefixes of at most 2 MiB stored re-read from
+    # L2 below 128 MiB of saved reads), values worked out by hand:
+    cached = dict(t_dense=1, gate_ratio=3, launch_bytes=5_000_000, cached_prefix_bytes=2 << 20,
+                  cached_reread_bytes=128 << 20)
+    # 64 requests, G = 1, P = 256 bf16: stores 256*8*128*2*2 = 1,048,576 B;
+    # saves 63*256*8*128*4 = 66,060,288 B against 3*(4*512*129*4 + 5e6) =
+    # 18,170,304 -> DENSE by the byte rule, PAGED with the allowance
+    assert pl(64, 1, 256, **cached)["path"] == "PAGED"
+    assert pl(64, 1, 256, **dict(cached, cached_prefix_bytes=0))["path"] == "DENSE"
+    assert pl(64, 1, 256, **dict(cached, cached_prefix_bytes=(1 << 20) - 1))["path"] == "DENSE"
+    # 256 requests: saves 267,386,880 B, above the allowance -> DENSE
+    assert pl(256, 1, 256, **cached)["path"] == "DENSE"
+    # 16 requests over 1,024 tokens: fp8 stores exactly 2 MiB (PAGED: saves
+    # 62,914,560 B, counted at 2 bytes a value), bf16 stores 4 MiB (the byte
+    # rule: 62,914,560 >= 3*(4*128*129*4 + 5e6) = 15,792,384 -> DENSE)
+    assert pl(16, 1, 1024, kv_dtype="fp8", **cached)["path"] == "PAGED"
+    assert pl(16, 1, 1024, kv_dtype="bf16", **cached)["path"] == "DENSE"
+    # gate_ratio 0 turns the whole gate off, the allowance included
+    assert pl(64, 1, 256, **dict(cached, gate_ratio=0))["path"] == "DENSE"
+    # ... and a step whose DENSE form would fuse keeps the byte rule: 32
+    # requests, G = 4, P = 512 (2 MiB stored), 8 own tokens each: saves
+    # 31*512*8*128*4 = 65,011,712 B (under the allowance, over 3*(4*1024*129*4
+    # + 5e6) = 21,340,608); prefix flops 4*128*512*128*8 = 268,435,456 >= 12 *
+    # 256*8*128*4 = 12,582,912 -> fuses -> DENSE; 2,000 own tokens each
+    # (suffix 262,144,000 B) or fuse_cascade = 0 -> PAGED
+    fused = dict(cached, fuse_cascade=12)
+    assert pl(32, 4, 512, L=520, **fused)["path"] == "DENSE"
+    assert pl(32, 4, 512, L=2512, **fused)["path"] == "PAGED"
+    assert pl(32, 4, 512, L=520, **dict(fused, fuse_cascade=0))["path"] == "PAGED"
+
+
+def test_planner_cached_prefix_allowance():
+    check_cached_gate(op.plan)
+
+
+# Plausible mistakes in the allowance, each emulated through the oracle's
+# own arguments: the stored bytes counted at the gate's 2 bytes per fp8
+# value, a strict bound, and the fused-step guard left out.
+def _mut_cached_rule_bytes(**kw):
+    kw = dict(kw)
+    if kw.get("kv_dtype") == "fp8":
+        kw["cached_prefix_bytes"] = kw.get("cached_prefix_bytes", 0) // 2
+    return op.plan(**kw)
+
+
+def _mut_cached_strict(**kw):
+    kw = dict(kw)
+    kw["cached_prefix_bytes"] = max(0, kw.get("cached_prefix_bytes", 0) - 1)
+    return op.plan(**kw)
+
+
+def _mut_cached_no_fuse_guard(**kw):
+    kw = dict(kw)
+    kw["fuse_cascade"] = 0
+    return op.plan(**kw)
+
+
+@pytest.mark.parametrize("mutant", [_mut_cached_rule_bytes, _mut_cached_strict, _mut_cached_no_fuse_guard])
+def test_mutant_cached_allowance_caught(mutant):
+    with pytest.raises(AssertionError):
+        check_cached_gate(mutant)
+
+
 def test_dispatcher_golden(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "dispatcher.json")))
     for c in g["cases"]:
