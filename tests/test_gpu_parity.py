@@ -958,3 +958,87 @@ def test_grouped_contiguous_runs_read_as_base_plus_offset(kv_dtype):
         o2, l2 = _grouped_run(db, off)
         check_close(kv_dtype, o1, l1, o_ref, lse_ref, f"grouped contiguous {kv_dtype} t_dense={t_dense}")
         assert same_bits(o1, o2) and same_bits(l1, l2), f"placement changed the bits ({kv_dtype}, {t_dense})"
+
+
+def _capture(fn):
+    """fn captured into a graph on a side stream of default priority, after
+    one warm-up call there (the library allocates nothing and sets no
+    memory: its launches are the whole graph)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _replays_match(g, o, lse, o_ref, lse_ref, what, replays=4):
+    for r in range(replays):
+        # eager work and a synchronisation between replays: the outputs are
+        # overwritten, so each replay has to write all of them again
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(o, o_ref) and same_bits(lse, lse_ref), f"{what}: replay {r} differs from the eager step"
+
+
+@pytest.mark.parametrize("case", ["paged_split", "paged_fp8_bins", "cascade_fused", "cascade_separate"])
+def test_graph_replays_match_the_eager_step(case):
+    """A decode step captured into a HIP graph (as a serving loop would)
+    replays to the eager step's bits, replay after replay."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    if case == "paged_split":
+        b = make_decode_batch(seed=91, B=6, H_q=32, H_kv=8, d=128, own_len=(1500, 3000), q_dtype="bf16",
+                              kv_dtype="bf16", page_size=16)
+        P, tune = 0, dict(target_workgroups=64)
+    elif case == "paged_fp8_bins":
+        b = make_decode_batch(seed=92, B=300, H_q=64, H_kv=8, d=128, own_len=(50, 400), q_dtype="bf16",
+                              kv_dtype="fp8", page_size=16)
+        P, tune = 0, {}
+    else:
+        b = make_decode_batch(seed=93, B=64, H_q=32, H_kv=8, d=128, own_len=(1, 64), prefix_len=1024,
+                              q_dtype="bf16", kv_dtype="bf16", page_size=16)
+        P, tune = 1024, dict(gate_ratio=0, fuse_cascade=12 if case == "cascade_fused" else 0)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan(shared_prefix_len=P, tuning=tune)
+    if case == "paged_split":
+        assert plan.info["num_splits"] > 1
+    if case == "paged_fp8_bins":
+        assert plan.info["request_bins"] > 0
+    if P:
+        assert plan.info["path_name"] == "DENSE"
+    say(f"graph {case}: path={plan.info['path_name']} splits={plan.info['num_splits']}")
+    ws = db.workspace(plan)
+    o, lse = db.new_out(), db.new_lse()
+    db.step(plan, o, lse, ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    reqs = list(range(0, b.B, max(1, b.B // 6)))
+    o64, lse64 = ob.batch_reference(b, requests=reqs)
+    check_close(b.kv_dtype, o_ref[reqs], lse_ref[reqs], o64, lse64, f"graph {case} eager")
+    g = _capture(lambda: db.step(plan, o, lse, ws))
+    _replays_match(g, o, lse, o_ref, lse_ref, f"graph {case}")
+
+
+def test_graph_replays_match_the_eager_grouped_step():
+    pkv, DeviceBatch, ob, make_grouped_batch = _grouped_imports()
+    b = make_grouped_batch(seed=94, B=40, H_q=32, H_kv=8, d=128, groups=[(16, 1024), (12, 512)], own_len=(0, 96),
+                           page_size=16)
+    db = DeviceBatch.from_batch(b)
+    plan = db.plan_grouped(tuning=dict(gate_ratio=0))
+    assert plan.info["num_groups"] == 2
+    meta = db.metadata(plan)
+    ws = db.workspace(plan)
+    o, lse = db.new_out(), db.new_lse()
+    db.step_grouped(plan, meta, o, lse, ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    g = _capture(lambda: db.step_grouped(plan, meta, o, lse, ws))
+    _replays_match(g, o, lse, o_ref, lse_ref, "graph grouped")
