@@ -83,7 +83,7 @@ struct SplitReduceArgs {
 };
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t stream);
 
-// Shared-prefix pass (bf16 MFMA; fp8 K/V widened to bf16 in LDS).  Rows
+// Shared-prefix pass (bf16 MFMA; fp8 K/V widened to bf16 operands in registers).  Rows
 // r = b * G + j of KV head g attend
 // over prefix tokens [split * split_tokens, ...) listed by prefix_indices.
 struct PrefixArgs {

@@ -22,7 +22,10 @@
 // transposing LDS read, ds_read_b64_tr_b16: within a group of 16 lanes, lane
 // 4c+d receives element d of the 64-bit values read by lanes c, c+4, c+8,
 // c+12, so lanes reading four tokens x four column chunks hand each lane
-// four tokens of one column.
+// four tokens of one column.  With e4m3 K/V the tiles stay as codes and
+// each operand is widened in registers as it is read, V^T with the 8-bit
+// form ds_read_b64_tr_b8 (lane 8c+d receives byte d of lanes c, c+2, ..,
+// c+14), which hands each lane eight tokens of one column in one read.
 //
 // Softmax state per row is (m, l) in exp2 units with the same lazily raised
 // maximum as the paged kernel; the partial or final result is written in the
@@ -64,17 +67,15 @@ struct PrefixSmem {
 
 // LDS of one fp8 (e4m3) prefix workgroup ("Track C · Document 10", fp8
 // cache section: the cache stored at one byte per value): the ring holds the
-// stored codes, row-major, half the bytes of a bf16 tile; each landed tile
-// is widened once per workgroup, exactly, into one of two bf16 tiles in the
-// swizzled layout above, which the same MFMA products then read.
+// stored codes, half the bytes of a bf16 tile, with the 16-byte chunks of
+// row t swizzled by chunk_swizzle8(t).  The products read the codes straight
+// from the ring and widen each operand in registers, exactly.
 template <int D, int KT>
 struct PrefixSmem8 {
     static constexpr int STAGES = PKV_PREFIX_STAGES;
-    static constexpr int BUFS = 2;
+    static constexpr int BUFS = STAGES;
     uint8_t k8[STAGES][KT * D];
     uint8_t v8[STAGES][KT * D];
-    uint16_t k[BUFS][KT * D];
-    uint16_t v[BUFS][KT * D];
     int idx[kMaxPrefixSplitTokens];
 };
 
@@ -115,6 +116,21 @@ __host__ __device__ constexpr int chunk_swizzle(int t) {
     return CPR == 16 ? (((t << 1) | ((t >> 3) & 1)) & 15) : (t & (CPR - 1));
 }
 
+// Swizzle of an e4m3 tile row t (128 codes: eight 16-byte chunks; chunk c
+// of row t at position c ^ chunk_swizzle8(t)).  With u = (t >> 1) mod 8 the
+// swizzle is u's bits reordered (bit 1, bit 0, bit 2 become bits 0, 1, 2).
+// K operand reads take one whole chunk of 16 consecutive rows per cycle
+// group: two row parities times eight distinct positions, since the swizzle
+// is a bijection of u.  The transposed V reads take one 8-byte half of two
+// adjacent chunks of rows {0..3, 8..11} (or {4..7, 12..15}) of a 16-row
+// block: per row parity those rows' u differ in bits 0 and 2, which the
+// swizzle moves to bits 1 and 2, so with the chunk pair's bit 0 and the half
+// every lane of a half-wave lands on its own bank pair.
+__host__ __device__ constexpr int chunk_swizzle8(int t) {
+    const int u = (t >> 1) & 7;
+    return ((u >> 1) & 1) | ((u & 1) << 1) | (u & 4);
+}
+
 // This lane's value and that of lane l ^ 32, exchanged between the two
 // halves of the wave in registers (gfx950 v_permlane32_swap swaps the upper
 // half of its first operand with the lower half of its second; with both
@@ -147,8 +163,6 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     constexpr int BLOCKS = KT * D * (F8 ? 1 : 2) / 1024;   // 1 KB wave-wide LDS copies per K (or V) tile
     static_assert(BLOCKS % NW == 0, "each wave copies whole 1 KB blocks of a tile");
     constexpr int PER_WAVE = BLOCKS / NW;
-    auto& s_k = sm.k;
-    auto& s_v = sm.v;
     int* const s_idx = sm.idx;
 
     // XCD-aware placement: workgroups are handed to the 8 XCDs round robin,
@@ -213,12 +227,18 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     const int rb = row_ok ? (members ? members[r / G] : r / G) : 0;
     const int rq = row_ok ? g * G + r % G : 0;
     const size_t qrow = (size_t)rb * H_q + rq;
+    // k-step ks of the first product covers, for this lane's half h, head-dim
+    // columns ks * 16 + h * 8 .. + 8 (bf16 tiles: one 16-byte chunk of a
+    // row); with e4m3 tiles, where one 16-byte chunk holds 16 columns, k-steps
+    // 2j and 2j + 1 cover the two halves of chunk 2j + h, columns
+    // (2j + h) * 16 + (ks % 2) * 8 .. + 8.  K rows and Q^T take the same order.
     bf16x8_t qreg[NKS];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D + h * 8;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            u32x4_t x = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0, 0, 0, 0};
+            const int col = F8 ? (2 * (ks >> 1) + h) * 16 + (ks & 1) * 8 : ks * 16 + h * 8;
+            u32x4_t x = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + col) : u32x4_t{0, 0, 0, 0};
             qreg[ks] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
@@ -248,8 +268,8 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8_t*)&sm.k8[0][0]);
         v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8_t*)&sm.v8[0][0]);
     } else {
-        k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_k[0][0]);
-        v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&s_v[0][0]);
+        k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&sm.k[0][0]);
+        v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16_t*)&sm.v[0][0]);
     }
     auto lds_copy16 = [](const void* src, uint32_t m0) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
@@ -276,8 +296,10 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
             const int blk = wave * PER_WAVE + j;
             const int p = blk * 64 + lane;
             if constexpr (F8) {
-                // plain rows of D codes: chunk p is row p / (D/16), codes 16 (p mod D/16) ..
-                const size_t off = (size_t)next_slot[j] * slot_stride + head_off + (p % (D / 16)) * 16;
+                // rows of D codes: position p holds chunk (p mod D/16) ^ swizzle of row p / (D/16)
+                const int t = p / (D / 16);
+                const int c = (p % (D / 16)) ^ chunk_swizzle8(t);
+                const size_t off = (size_t)next_slot[j] * slot_stride + head_off + c * 16;
                 const uint32_t dst = (uint32_t)(stage * KT * D + blk * 1024);
                 lds_copy16(static_cast<const uint8_t*>(a.k) + off, k_lds + dst);
                 lds_copy16(static_cast<const uint8_t*>(a.v) + off, v_lds + dst);
@@ -288,32 +310,6 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
                 const uint32_t dst = (uint32_t)(stage * KT * D + blk * 512) * 2;
                 lds_copy16(static_cast<const uint16_t*>(a.k) + off, k_lds + dst);
                 lds_copy16(static_cast<const uint16_t*>(a.v) + off, v_lds + dst);
-            }
-        }
-    };
-    // fp8: widen the codes of tile n (ring stage n % S) into bf16 buffer
-    // n % 2, 16 codes of one row per thread and pass, into the swizzled
-    // chunks 2c and 2c + 1 of that row.
-    auto widen_tile = [&](int n) {
-        if constexpr (F8) {
-            const int st = n % S, cb = n % NBUF;
-            for (int i = threadIdx.x; i < KT * D / 16; i += NT) {
-                const int t = i / (D / 16), c = 2 * (i % (D / 16));
-                const int sw = chunk_swizzle<CPR>(t);
-                const u32x4_t xk = *reinterpret_cast<const u32x4_t*>(&sm.k8[st][i * 16]);
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&sm.v8[st][i * 16]);
-                const u32x4_t k0 = {fp8x2_to_bf16x2<false>(xk[0]), fp8x2_to_bf16x2<true>(xk[0]),
-                                    fp8x2_to_bf16x2<false>(xk[1]), fp8x2_to_bf16x2<true>(xk[1])};
-                const u32x4_t k1 = {fp8x2_to_bf16x2<false>(xk[2]), fp8x2_to_bf16x2<true>(xk[2]),
-                                    fp8x2_to_bf16x2<false>(xk[3]), fp8x2_to_bf16x2<true>(xk[3])};
-                const u32x4_t v0 = {fp8x2_to_bf16x2<false>(xv[0]), fp8x2_to_bf16x2<true>(xv[0]),
-                                    fp8x2_to_bf16x2<false>(xv[1]), fp8x2_to_bf16x2<true>(xv[1])};
-                const u32x4_t v1 = {fp8x2_to_bf16x2<false>(xv[2]), fp8x2_to_bf16x2<true>(xv[2]),
-                                    fp8x2_to_bf16x2<false>(xv[3]), fp8x2_to_bf16x2<true>(xv[3])};
-                *reinterpret_cast<u32x4_t*>(&s_k[cb][t * D + ((c ^ sw) << 3)]) = k0;
-                *reinterpret_cast<u32x4_t*>(&s_k[cb][t * D + (((c + 1) ^ sw) << 3)]) = k1;
-                *reinterpret_cast<u32x4_t*>(&s_v[cb][t * D + ((c ^ sw) << 3)]) = v0;
-                *reinterpret_cast<u32x4_t*>(&s_v[cb][t * D + (((c + 1) ^ sw) << 3)]) = v1;
             }
         }
     };
@@ -331,6 +327,18 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         return row * D + (((db * 4 + tr_chunk) ^ chunk_swizzle<CPR>(row)) << 3) + tr_elem;
     };
     const int kr_swz = chunk_swizzle<CPR>(lr);  // swizzle of the K rows this lane reads (rows tb*32 + lr)
+    // e4m3 tiles: transposed 8-bit reads (ds_read_b64_tr_b8: within a group
+    // of 16 lanes, lane 8c + d receives byte d of the 8-byte values read by
+    // lanes c, c + 2, .., c + 14, in that order).  Lane s of a group reads
+    // 8 columns, half s % 2 of the group's 16, of token (i & 3) + 4h +
+    // 8 (i >> 2) of the 16-token chunk, i = s / 2: lane 8c + d then holds
+    // column 16 (group % 2) + 8c + d = lane mod 32 of the 32-column block, for
+    // the 8 tokens of its half in the k-slot order of P^T.
+    const int tr8_i = (lane & 15) >> 1;
+    const int tr8_row = (tr8_i & 3) + h * 4 + (tr8_i >> 2) * 8;
+    const int tr8_g1 = (lane >> 4) & 1;
+    const int tr8_base = tr8_row * D + (lane & 1) * 8;
+    const int tr8_sw = chunk_swizzle8(tr8_row);  // rows c*16 + r keep the swizzle of row r
 
     f32x16_t acc[NDB];
 #pragma unroll
@@ -349,14 +357,29 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
             so[tb] = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ks += 2) {
+                if constexpr (F8) {
+                    // one 16-byte chunk of codes: the A operands of k-steps ks and ks + 1
+                    const int row = tb * 32 + lr;
+                    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(
+                        &sm.k8[buf][row * D + (((ks + h) ^ chunk_swizzle8(row)) << 4)]);
+                    const u32x4_t w0 = {fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
+                                        fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+                    const u32x4_t w1 = {fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
+                                        fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
+                    se[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w0), qreg[ks],
+                                                                     se[tb], 0, 0, 0);
+                    so[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w1), qreg[ks + 1],
+                                                                     so[tb], 0, 0, 0);
+                } else {
                 const bf16x8_t ka0 = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                  &s_k[buf][(tb * 32 + lr) * D + (((ks * 2 + h) ^ kr_swz) << 3)]));
+                                  &sm.k[buf][(tb * 32 + lr) * D + (((ks * 2 + h) ^ kr_swz) << 3)]));
                 const bf16x8_t ka1 = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                  &s_k[buf][(tb * 32 + lr) * D + (((ks * 2 + 2 + h) ^ kr_swz) << 3)]));
+                                  &sm.k[buf][(tb * 32 + lr) * D + (((ks * 2 + 2 + h) ^ kr_swz) << 3)]));
                 se[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qreg[ks], se[tb], 0, 0, 0);
                 so[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qreg[ks + 1], so[tb], 0, 0, 0);
+                }
             }
         }
     };
@@ -430,9 +453,20 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
         for (int c = 0; c < 2 * NTB; ++c) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
+                if constexpr (F8) {
+                    typedef int v2i_t __attribute__((ext_vector_type(2)));
+                    typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+                    const uint8_t* vb = &sm.v8[buf][c * 16 * D];
+                    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_v2i_t*)(vb + tr8_base + (((db * 2 + tr8_g1) ^ tr8_sw) << 4)));
+                    const u32x4_t x = {fp8x2_to_bf16x2<false>((uint32_t)r[0]), fp8x2_to_bf16x2<true>((uint32_t)r[0]),
+                                       fp8x2_to_bf16x2<false>((uint32_t)r[1]), fp8x2_to_bf16x2<true>((uint32_t)r[1])};
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pb[c], acc[db],
+                                                                      0, 0, 0);
+                } else {
                 typedef short v4s_t __attribute__((ext_vector_type(4)));
                 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
-                const uint16_t* vb = &s_v[buf][c * 16 * D];
+                const uint16_t* vb = &sm.v[buf][c * 16 * D];
                 const v4s_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vb + tr_off(tr_row, db)));
                 const v4s_t x1 =
                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(vb + tr_off(tr_row + 8, db)));
@@ -441,6 +475,7 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
                 const u32x4_t x = {y0[0], y0[1], y1[0], y1[1]};
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), pb[c],
                                                                   acc[db], 0, 0, 0);
+                }
             }
         }
     };
@@ -464,10 +499,6 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     // are on their way into the ring.  Two score buffers alternate (the loop
     // takes two tiles per trip), so no scores are copied between them.
     f32x16_t sa_e[NTB], sa_o[NTB], sb_e[NTB], sb_o[NTB];
-    // fp8 adds a widening pass and a second barrier per tile: the bf16
-    // buffer of tile n + 1 is rewritten only after every wave has finished
-    // P.V of tile n - 1 (the first barrier), and read only after the
-    // widening (the second).
     auto step = [&](int n, const f32x16_t (&ce)[NTB], const f32x16_t (&co)[NTB], f32x16_t (&ne)[NTB],
                     f32x16_t (&no)[NTB]) {
         if (n + 1 < ntiles) {
@@ -478,10 +509,6 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
                 issue_tile(n + S - 1);  // into the stage of tile n - 1
                 if (n + S < ntiles) read_slots(n + S);
             }
-            if constexpr (F8) {
-                widen_tile(n + 1);
-                __syncthreads();
-            }
             qk((n + 1) % NBUF, ne, no);
         }
         softmax_pv(ce, co, n, n % NBUF);
@@ -489,10 +516,6 @@ __device__ __forceinline__ void prefix_item(const PrefixArgs& a, SM& sm, const i
     if (ntiles > 0) {
         wait_tile(0, S - 2);
         __syncthreads();
-        if constexpr (F8) {
-            widen_tile(0);
-            __syncthreads();
-        }
         qk(0, sa_e, sa_o);
     }
     for (int n = 0; n < ntiles; n += 2) {

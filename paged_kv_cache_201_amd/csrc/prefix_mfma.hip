@@ -9,8 +9,8 @@ __global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_kernel
     prefix_item<PKV_BF16, D, NW, KT>(a, sm, blockIdx.x);
 }
 
-// fp8 e4m3 K/V (head_dim 128): the codes stream into LDS and are widened
-// there once per workgroup (see PrefixSmem8).
+// fp8 e4m3 K/V (head_dim 128): the codes stream into LDS and each MFMA
+// operand is widened in registers as it is read (see PrefixSmem8).
 template <int NW>
 __global__ void __launch_bounds__(NW * 64, (NW >= 4 ? 2 : 1)) prefix_attn_fp8_kernel(const PrefixArgs a) {
     __shared__ PrefixSmem8<128, 32> sm;
