@@ -56,8 +56,10 @@ constexpr float kPrefixLazySlack = 8.0f;
 // padding; the 16-byte chunks of row t are stored XOR-swizzled, chunk c at
 // position c ^ chunk_swizzle(t), so that both operand reads are free of bank
 // conflicts (see chunk_swizzle).
+// (16-byte aligned: the operand reads are 16-byte LDS loads, which the
+// compiler otherwise splits into pairs of 4-byte loads)
 template <int D, int KT>
-struct PrefixSmem {
+struct alignas(16) PrefixSmem {
     static constexpr int STAGES = PKV_PREFIX_STAGES;
     static constexpr int BUFS = STAGES;   // tiles the products read from
     uint16_t k[STAGES][KT * D];
@@ -71,7 +73,7 @@ struct PrefixSmem {
 // row t swizzled by chunk_swizzle8(t).  The products read the codes straight
 // from the ring and widen each operand in registers, exactly.
 template <int D, int KT>
-struct PrefixSmem8 {
+struct alignas(16) PrefixSmem8 {
     static constexpr int STAGES = PKV_PREFIX_STAGES;
     static constexpr int BUFS = STAGES;
     uint8_t k8[STAGES][KT * D];
