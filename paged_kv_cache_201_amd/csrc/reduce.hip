@@ -19,8 +19,10 @@ namespace pkv {
 // Partials whose loads are issued together.  Four keep the kernel at about
 // 50 VGPRs, eight waves per SIMD, so that a grid of 2,048 workgroups (16,384
 // rows at head_dim 128) is resident in one round; a row with more partials
-// takes one more memory round trip per four.
+// takes one more memory round trip per four.  Rows of five to eight
+// partials (a four-range prefix and a suffix) take one batch of eight.
 constexpr int kReduceBatch = 4;
+constexpr int kReduceBatchWide = 8;
 
 // Thread (row, e4) owns four consecutive outputs of one row.  The row's
 // partials are the pre_splits prefix partials (if any) followed by the chunk
@@ -28,7 +30,7 @@ constexpr int kReduceBatch = 4;
 // for an empty state.  They are consumed in batches whose loads are all
 // issued before any is used, so a batch costs one memory round trip;
 // batches are combined in order with the usual rescaling.
-template <int D>
+template <int D, int BATCH>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs a) {
     constexpr int CH = D / 4;
     constexpr int RPB = 256 / CH;
@@ -39,13 +41,19 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
     const int qh = row % a.H_q;
     const int npre = a.pre_acc ? (a.pre_count ? a.pre_count[b] : a.pre_splits) : 0;
     int nparts = 0;
-    if (a.kv_indptr) {
+    if (a.kv_indptr && a.whole_requests) {
+        // bins of whole requests: the plan has no empty request, and each
+        // request's positions are one segment with one partial state, so
+        // the partials are loaded without a round trip to kv_indptr first
+        nparts = a.skip_whole ? 0 : (a.part_acc ? min(1, a.max_parts) : 0);
+        if (a.skip_whole) return;  // written by the paged kernel
+    } else if (a.kv_indptr) {
         // the chunks that request b's positions [ob, on) of the flat sequence touch
         const int64_t base = (int64_t)a.kv_indptr[0];
         const int64_t ob = a.kv_indptr[b] - base - (int64_t)b * a.token_offset;
         const int64_t on = a.kv_indptr[b + 1] - base - (int64_t)(b + 1) * a.token_offset;
         if (on > ob) {
-            nparts = a.whole_requests ? 1 : (int)((on - 1) / a.chunk_tokens - ob / a.chunk_tokens + 1);
+            nparts = (int)((on - 1) / a.chunk_tokens - ob / a.chunk_tokens + 1);
             if (a.skip_whole && nparts == 1) return;  // written by the paged kernel
             nparts = a.part_acc ? min(nparts, a.max_parts) : 0;
         }
@@ -53,11 +61,11 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
     const int total = npre + nparts;
     float L = 0.f, M = -INFINITY;
     f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < total; k0 += kReduceBatch) {
-        f32x2_t ml[kReduceBatch];
-        f32x4_t x[kReduceBatch];
+    for (int k0 = 0; k0 < total; k0 += BATCH) {
+        f32x2_t ml[BATCH];
+        f32x4_t x[BATCH];
 #pragma unroll
-        for (int j = 0; j < kReduceBatch; ++j) {
+        for (int j = 0; j < BATCH; ++j) {
             const int k = k0 + j;
             if (k < total) {
                 const bool pre = k < npre;
@@ -72,14 +80,14 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const SplitReduceArgs
         }
         float Mc = M;
 #pragma unroll
-        for (int j = 0; j < kReduceBatch; ++j) Mc = fmaxf(Mc, ml[j][0]);
+        for (int j = 0; j < BATCH; ++j) Mc = fmaxf(Mc, ml[j][0]);
         if (Mc == -INFINITY) continue;
         const float c = M == -INFINITY ? 0.f : exp2f(M - Mc);  // rescale what is summed so far
         L *= c;
         o *= c;
         M = Mc;
 #pragma unroll
-        for (int j = 0; j < kReduceBatch; ++j) {
+        for (int j = 0; j < BATCH; ++j) {
             const float w = ml[j][0] == -INFINITY ? 0.f : exp2f(ml[j][0] - M);
             L += w * ml[j][1];
             if (w > 0.f) o += w * x[j];  // an empty item's values are never read into the sum
@@ -137,10 +145,15 @@ __global__ void __launch_bounds__(256) merge_states_kernel(int rows, const float
 hipError_t launch_split_reduce(const SplitReduceArgs& a, hipStream_t stream) {
     const int rows = a.B * a.H_q;
     if (rows == 0) return hipSuccess;
+    // most partials a row can have
+    const int most = (a.pre_acc ? a.pre_splits : 0) + (a.part_acc && a.kv_indptr ? a.max_parts : 0);
+    const bool wide = most > kReduceBatch && most <= kReduceBatchWide;
     if (a.D == 128) {
-        split_reduce_kernel<128><<<(rows + 7) / 8, 256, 0, stream>>>(a);
+        if (wide) split_reduce_kernel<128, kReduceBatchWide><<<(rows + 7) / 8, 256, 0, stream>>>(a);
+        else split_reduce_kernel<128, kReduceBatch><<<(rows + 7) / 8, 256, 0, stream>>>(a);
     } else {
-        split_reduce_kernel<64><<<(rows + 15) / 16, 256, 0, stream>>>(a);
+        if (wide) split_reduce_kernel<64, kReduceBatchWide><<<(rows + 15) / 16, 256, 0, stream>>>(a);
+        else split_reduce_kernel<64, kReduceBatch><<<(rows + 15) / 16, 256, 0, stream>>>(a);
     }
     return hipGetLastError();
 }
