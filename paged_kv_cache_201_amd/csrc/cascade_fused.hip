@@ -41,7 +41,7 @@ __device__ __forceinline__ void fused_role(const int i, const int np, bool& is_p
 
 template <int KV, int D, int G, int NHL, int TPI>
 __global__ void __launch_bounds__(kPagedWaves * 64, 2)
-    cascade_fused_kernel(const PrefixArgs pa, const PagedArgs sa, const int np, const int ns, const int hblks) {
+    cascade_fused_kernel(const PrefixArgs pa, const PagedArgs sa, const int np, const int hblks) {
     using PS = typename std::conditional<KV == PKV_FP8_E4M3, PrefixSmem8<D, 32>, PrefixSmem<D, 32>>::type;
     using SS = PagedSmem<KV, D, G, NHL, TPI>;
     constexpr size_t kBytes = sizeof(PS) > sizeof(SS) ? sizeof(PS) : sizeof(SS);
@@ -79,7 +79,7 @@ struct FusedLaunch {
             if (np + ns > INT32_MAX) return hipErrorInvalidValue;
             if (np + ns == 0) return hipSuccess;
             cascade_fused_kernel<KV, D, G, NHL, TPI>
-                <<<(uint32_t)(np + ns), kPagedWaves * 64, 0, s>>>(pa, sa, np, (int)ns, p.head_blocks);
+                <<<(uint32_t)(np + ns), kPagedWaves * 64, 0, s>>>(pa, sa, np, p.head_blocks);
             return hipGetLastError();
         }
     }

@@ -741,7 +741,7 @@ pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const i
         if (path == PKV_PATH_PAGED) continue;
         int32_t a = nd.parent;  // nearest kept ancestor
         while (a >= 0 && kept_at[a] < 0) a = nodes[a].parent;
-        Group g;
+        Group g{};
         g.members = nd.members;
         g.start_tokens = nd.start * p;
         g.prefix_tokens = (nd.end - nd.start) * p;
