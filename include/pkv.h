@@ -498,7 +498,7 @@ PKV_API pkv_status pkv_decode_step_grouped(const pkv_plan* plan, const void* q, 
  * out[num_workgroups] (device).  Its duration gives the
  * streaming-read bandwidth ceiling of the GPU, against which the attention
  * kernels' achieved bandwidth is compared ([P1] "When source beats
- * intuition" and "A backend where pages really do reach the kernel" judge
+ * intuition" and "A backend where pages really do reach the kernel" measure
  * decode kernels by their fraction of peak DRAM throughput).
  * Errors: EINVAL (null pointers, bytes not a multiple of 16, misaligned buf,
  * num_workgroups < 1), EHIP.

@@ -3,7 +3,7 @@
 // bandwidth of the attention kernels can be set against what a plain stream
 // achieves on the same GPU ("The 25% Page-Size Slowdown That Wasn't",
 // sections "When source beats intuition" and "A backend where pages really
-// do reach the kernel": decode kernels judged by their fraction of peak DRAM
+// do reach the kernel": decode kernels measured by their fraction of peak DRAM
 // throughput).
 #include <hip/hip_runtime.h>
 
