@@ -335,6 +335,26 @@ def test_request_bins_and_chunks_agree_with_oracle(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_request_bins_at_their_limits(kv):
+    """1,024 short requests, the most the kernel arguments carry, run on bins;
+    1,025 fall back to chunks (requests cut at chunk edges and combined);
+    both against the oracle on requests spread over the batch."""
+    pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
+    for B, binned in ((1024, True), (1025, False)):
+        b = make_decode_batch(seed=41 + B, B=B, H_q=32, H_kv=8, d=128, own_len=(20, 200), kv_dtype=kv, page_size=16)
+        db = DeviceBatch.from_batch(b)
+        plan = db.plan()
+        assert (plan.info["request_bins"] > 0) == binned, (B, plan.info)
+        reqs, n_cut = spread_requests(b, plan)
+        assert binned or n_cut >= 8, n_cut
+        say(f"bins limit {kv} B={B}: {plan.info['request_bins']} bins, {len(reqs)} requests checked ({n_cut} cut)")
+        o, lse = db.step(plan)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = ob.batch_reference(b, requests=reqs)
+        check_close(kv, o[reqs], lse[reqs], o_ref, lse_ref, f"bins limit {kv} B={B}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_narrow_head_blocks_and_long_chunks(kv):
     """Work items of 1 and 2 KV heads (several tokens per wave-wide load) and
     whole-request chunks of 4096 positions with no combine step."""
