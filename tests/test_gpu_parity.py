@@ -836,11 +836,12 @@ def test_nested_prefix_groups_full_size_sampled():
 
 # ------------------------------------------------------ randomized sweep --
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(64))
 def test_random_shapes_vs_oracle(case):
     """Seeded random mixes of dtype, head_dim, GQA group, KV heads, page size,
     batch and lengths (empty requests included), shared prefix, forced path
-    and tuning, every request checked against the oracle."""
+    and tuning (work-item target and geometry, bins, gate, fused launch, side
+    stream), every request checked against the oracle."""
     pkv, DeviceBatch, ob, oa, make_config, make_decode_batch, relayout = _imports()
     rng = np.random.default_rng(9000 + case)
     kv = str(rng.choice(["f32", "bf16", "fp8"], p=[0.2, 0.5, 0.3]))
@@ -857,7 +858,9 @@ def test_random_shapes_vs_oracle(case):
     force = int(rng.choice([-1, 0, 1, 2])) if prefix_ok else int(rng.choice([-1, 0]))
     tune = dict(target_workgroups=int(rng.choice([64, 256, 512, 1024])),
                 min_split_tokens=int(rng.choice([16, 64, 256])), gate_ratio=int(rng.choice([0, 3])),
-                fuse_cascade=int(rng.choice([0, 1, 12])), t_dense=int(rng.choice([1, 64, 4096])))
+                fuse_cascade=int(rng.choice([0, 1, 12])), t_dense=int(rng.choice([1, 64, 4096])),
+                segment_tokens=int(rng.choice([0, 32, 128])), max_heads_per_item=int(rng.choice([0, 0, 1, 2])),
+                cached_prefix_bytes=int(rng.choice([0, 2 << 20])), concurrent_prefix=int(rng.choice([0, 0, 1])))
     layout = str(rng.choice(["shared", "unique"])) if P else "shared"
     b = make_decode_batch(seed=9000 + case, B=B, H_q=G * H_kv, H_kv=H_kv, d=d, own_len=(lo, hi), prefix_len=P,
                           q_dtype=q, kv_dtype=kv, page_size=p, layout=layout)
@@ -871,7 +874,7 @@ def test_random_shapes_vs_oracle(case):
     check_close(kv, o, lse, o_ref, lse_ref, what + f" path={plan.info['path_name']}")
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_prefix_trees_vs_oracle(case):
     """Seeded random trees of shared runs (roots with nested children, loners,
     runs crossing page boundaries) planned from the page table."""
@@ -900,7 +903,8 @@ def test_random_prefix_trees_vs_oracle(case):
             left -= m
             tree.append((m, int(rng.integers(1, 300)), r))
     tune = dict(gate_ratio=int(rng.choice([0, 0, 0, 3])), t_dense=int(rng.choice([1, 16, 4096])),
-                fuse_cascade=int(rng.choice([0, 1, 12])))
+                fuse_cascade=int(rng.choice([0, 1, 12])), segment_tokens=int(rng.choice([0, 32])),
+                max_heads_per_item=int(rng.choice([0, 1, 2])))
     b = make_tree_batch(seed=9100 + case, B=B, H_q=G * H_kv, H_kv=H_kv, d=d, tree=tree,
                         own_len=(0, int(rng.integers(1, 200))), page_size=p, kv_dtype=kv)
     what = f"tree case {case}: {kv} d={d} G={G} H_kv={H_kv} p={p} B={B} tree={tree} {tune}"
