@@ -41,6 +41,24 @@
  *     anything is enqueued.  Kernels do not bounds-check kv_indices
  *     (pkv_validate_indices does that on the host); a bad index faults on the
  *     device and surfaces at the caller's next synchronisation.
+ *
+ * Checked library.  libpkv_checked.so exports the same functions with the
+ * same kernels; in it every call that takes device index arrays
+ * (pkv_paged_decode_attn, pkv_paged_decode_attn_pages,
+ * pkv_cascade_prefix_attn, pkv_decode_step, pkv_decode_step_noalloc,
+ * pkv_decode_step_grouped) first synchronises the caller's stream, copies
+ * to the host what its kernels would read of those arrays, and returns,
+ * with nothing enqueued:
+ *   - PKV_EINVAL when kv_indptr differs from the host kv_indptr the plan was
+ *     made from, when a grouped step's metadata block differs from
+ *     pkv_plan_metadata's, when page_indptr[0] < 0, or when a prefix the
+ *     plan reads as one run of slots (pkv_plan_info.prefix_base) is not
+ *     that run;
+ *   - PKV_ERANGE when a slot the kernels would read lies outside
+ *     [0, num_slots), a page outside [0, num_slots / page_size), or a
+ *     request's page list holds fewer than ceil(L_b / page_size) pages.
+ * It is for debugging: the synchronisation and copies cost time, and a call
+ * made while the stream is being captured into a graph fails with PKV_EHIP.
  */
 #ifndef PKV_H
 #define PKV_H

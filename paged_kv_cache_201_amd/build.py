@@ -6,7 +6,10 @@
 
 Host-only C++ (the planner and page-table lowering) is compiled with g++;
 the HIP sources with hipcc for gfx950.  Objects go to ``_build/`` at the
-repository root; the shared library lands in this package directory.
+repository root; the shared library lands in this package directory, next
+to libpkv_checked.so: the same objects with the entry points compiled with
+PKV_CHECKED=1 (host-side checks of every step's index arrays before any
+launch; see include/pkv.h).
 """
 import os
 import shutil
@@ -20,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+CHECKED_LIB = os.path.join(PKG, "libpkv_checked.so")
+CHECKED_SOURCE = "api.hip"  # the one source compiled again with PKV_CHECKED=1
 
 HIP_SOURCES = ["api.hip", "reduce.hip", "prefix_mfma.hip", "cascade_fused.hip", "probe.hip", "paged_f32.hip",
                "paged_bf16.hip", "paged_fp8.hip"]
@@ -54,7 +59,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link libpkv.so; returns its path."""
+    """Compile every source and link libpkv.so and libpkv_checked.so; returns
+    the path of libpkv.so."""
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     steps = []
@@ -67,11 +73,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         obj = os.path.join(BUILD, src + ".o")
         steps.append([hipcc, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    checked_obj = os.path.join(BUILD, CHECKED_SOURCE + ".checked.o")
+    steps.append([hipcc, *COMMON, *HIP_FLAGS, "-DPKV_CHECKED=1", "-c", os.path.join(CSRC, CHECKED_SOURCE), "-o",
+                  checked_obj])
+    checked_objs = [checked_obj if o == os.path.join(BUILD, CHECKED_SOURCE + ".o") else o for o in objs]
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(steps)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), steps))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for lib, parts in ((LIB, objs), (CHECKED_LIB, checked_objs)):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -1,12 +1,20 @@
 // C ABI entry points that enqueue device work: argument checks, workspace
 // carving, and kernel launches on the caller's stream.  No allocation, no
 // synchronisation.
+//
+// Built a second time with PKV_CHECKED=1 into libpkv_checked.so (the same
+// kernels and entry points): there, before any launch, a call that takes
+// device index arrays waits for the caller's stream, copies to the host what
+// its kernels would read of those arrays and checks it against the plan and
+// the pool (the checks are in host.cpp).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <mutex>
+#include <new>
 #include <unordered_map>
+#include <vector>
 
 #include "kernels.h"
 #include "pkv.h"
@@ -248,6 +256,88 @@ pkv_status run_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     return hip_status(pkv::launch_split_reduce(r, s));
 }
 
+#ifndef PKV_CHECKED
+#define PKV_CHECKED 0
+#endif
+
+#if PKV_CHECKED
+// Host copy of n ints of device memory (after the stream sync below).
+pkv_status fetch(const int32_t* dev, int64_t n, std::vector<int32_t>* out) {
+    out->assign((size_t)n, 0);
+    if (n == 0) return PKV_OK;
+    if (!dev) return PKV_EINVAL;
+    return hip_status(hipMemcpy(out->data(), dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost));
+}
+
+// The work already queued on the caller's stream may write the arrays.
+pkv_status sync(hipStream_t s) { return hip_status(hipStreamSynchronize(s)); }
+
+// Token-flat steps: kv_indptr as planned, every slot of
+// kv_indices[kv_indptr[0] .. kv_indptr[B]) in the pool, and (with_prefix) the
+// prefix pass's slots, the first prefix_tokens of them.
+pkv_status checked_flat(const pkv_plan* pl, const pkv_pool* pool, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, bool with_prefix, hipStream_t s) try {
+    pkv_status st = sync(s);
+    std::vector<int32_t> ip, ix;
+    if (st == PKV_OK) st = fetch(kv_indptr, pl->B + 1, &ip);
+    if (st == PKV_OK) st = pkv::check_step_indptr(*pl, ip.data());
+    if (st != PKV_OK) return st;
+    const int64_t n = (int64_t)ip[pl->B] - ip[0];
+    if (n > 0 && kv_indices) {
+        if ((st = fetch(kv_indices + ip[0], n, &ix)) != PKV_OK) return st;
+        if ((st = pkv::check_slots(ix.data(), n, pool->num_slots)) != PKV_OK) return st;
+    }
+    if (with_prefix && pl->path != PKV_PATH_PAGED && pl->prefix_tokens > 0) {
+        if ((int64_t)ix.size() < pl->prefix_tokens) return PKV_EINVAL;
+        st = pkv::check_prefix_slots(*pl, ix.data(), pool->num_slots);
+    }
+    return st;
+} catch (const std::bad_alloc&) {
+    return PKV_ENOMEM;
+}
+
+// Page-table steps: kv_indptr as planned, enough pages per request, and
+// every page the kernel reads in the pool.
+pkv_status checked_pages(const pkv_plan* pl, const pkv_pool* pool, const int32_t* kv_indptr,
+                         const int32_t* page_indptr, const int32_t* page_indices, hipStream_t s) try {
+    pkv_status st = sync(s);
+    std::vector<int32_t> ip, pp, pages;
+    if (st == PKV_OK) st = fetch(kv_indptr, pl->B + 1, &ip);
+    if (st == PKV_OK) st = pkv::check_step_indptr(*pl, ip.data());
+    if (st == PKV_OK) st = fetch(page_indptr, pl->B + 1, &pp);
+    int64_t lo = 0, hi = 0;
+    if (st == PKV_OK) st = pkv::check_page_indptr(*pl, pp.data(), &lo, &hi);
+    if (st != PKV_OK || hi <= lo) return st;
+    if ((st = fetch(page_indices + lo, hi - lo, &pages)) != PKV_OK) return st;
+    return pkv::check_slots(pages.data(), hi - lo, pool->num_slots / pl->page_size);
+} catch (const std::bad_alloc&) {
+    return PKV_ENOMEM;
+}
+
+// The prefix pass alone: its prefix_tokens slots.
+pkv_status checked_prefix(const pkv_plan* pl, const pkv_pool* pool, const int32_t* prefix_indices,
+                          hipStream_t s) try {
+    pkv_status st = sync(s);
+    std::vector<int32_t> px;
+    if (st == PKV_OK) st = fetch(prefix_indices, pl->prefix_tokens, &px);
+    if (st == PKV_OK) st = pkv::check_prefix_slots(*pl, px.data(), pool->num_slots);
+    return st;
+} catch (const std::bad_alloc&) {
+    return PKV_ENOMEM;
+}
+
+// Grouped steps: the metadata block as planned, its slots in the pool.
+pkv_status checked_grouped(const pkv_plan* pl, const pkv_pool* pool, const int32_t* meta, hipStream_t s) try {
+    pkv_status st = sync(s);
+    std::vector<int32_t> m;
+    if (st == PKV_OK) st = fetch(meta, (int64_t)pl->meta.size(), &m);
+    if (st == PKV_OK) st = pkv::check_group_metadata(*pl, m.data(), pool->num_slots);
+    return st;
+} catch (const std::bad_alloc&) {
+    return PKV_ENOMEM;
+}
+#endif
+
 // Workspace of pkv_decode_step_noalloc, for callers that cannot allocate:
 // a fixed array in device memory, one copy per GPU the library runs on,
 // held until the process ends.  In host code `scratch` names only a
@@ -294,6 +384,10 @@ pkv_status pkv_paged_decode_attn(const pkv_plan* pl, const void* q, const pkv_po
     if (st != PKV_OK) return st;
     if (pl->B == 0) return PKV_OK;
     if (!q || !kv_indptr || (pl->paged_tokens > 0 && !kv_indices)) return PKV_EINVAL;
+#if PKV_CHECKED
+    st = checked_flat(pl, pool, kv_indptr, kv_indices, false, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     return run_paged(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, o_f32, lse, ws,
                      static_cast<hipStream_t>(stream));
 }
@@ -311,6 +405,10 @@ pkv_status pkv_paged_decode_attn_pages(const pkv_plan* pl, const void* q, const 
     if (st != PKV_OK) return st;
     if (pl->B == 0) return PKV_OK;
     if (!q || !kv_indptr || !page_indptr || (pl->paged_tokens > 0 && !page_indices)) return PKV_EINVAL;
+#if PKV_CHECKED
+    st = checked_pages(pl, pool, kv_indptr, page_indptr, page_indices, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     pkv::PagedArgs a = paged_args(pl, q, pool, kv_indptr, nullptr, sm_scale);
     a.page_indptr = page_indptr;
     a.page_indices = page_indices;
@@ -330,6 +428,10 @@ pkv_status pkv_cascade_prefix_attn(const pkv_plan* pl, const void* q, const pkv_
     if (st != PKV_OK) return st;
     st = check_workspace(pl, ws, ws_bytes);
     if (st != PKV_OK) return st;
+#if PKV_CHECKED
+    st = checked_prefix(pl, pool, prefix_indices, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     return run_prefix(pl, q, pool, prefix_indices, sm_scale, o_p, lse_p, ws,
                       static_cast<hipStream_t>(stream));
 }
@@ -357,6 +459,10 @@ pkv_status pkv_decode_step(const pkv_plan* pl, const void* q, const pkv_pool* po
     if (st != PKV_OK) return st;
     if (pl->B == 0) return PKV_OK;
     if (!q || !kv_indptr || !kv_indices) return PKV_EINVAL;
+#if PKV_CHECKED
+    st = checked_flat(pl, pool, kv_indptr, kv_indices, true, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     return run_decode_step(pl, q, pool, kv_indptr, kv_indices, sm_scale, o, lse, ws, static_cast<hipStream_t>(stream),
                            pl->concurrent_prefix != 0);
 }
@@ -371,6 +477,10 @@ pkv_status pkv_decode_step_noalloc(const pkv_plan* pl, const void* q, const pkv_
     if (pl->workspace_bytes > (int64_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_EWORKSPACE;
     if (pl->B == 0) return PKV_OK;
     if (!q || !kv_indptr || !kv_indices) return PKV_EINVAL;
+#if PKV_CHECKED
+    st = checked_flat(pl, pool, kv_indptr, kv_indices, true, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     void* ws = nullptr;
     if (pl->workspace_bytes > 0 && device_scratch(&ws) != hipSuccess) return PKV_EHIP;
     // one stream: the side stream of concurrent_prefix would be created here
@@ -388,6 +498,10 @@ pkv_status pkv_decode_step_grouped(const pkv_plan* pl, const void* q, const pkv_
     if (st != PKV_OK) return st;
     if (pl->B == 0) return PKV_OK;
     if (!q || !meta) return PKV_EINVAL;
+#if PKV_CHECKED
+    st = checked_grouped(pl, pool, meta, static_cast<hipStream_t>(stream));
+    if (st != PKV_OK) return st;
+#endif
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int32_t* suffix_indptr = meta + pl->meta_suffix_indptr;
     const int32_t* suffix_indices = meta + pl->meta_suffix_indices;

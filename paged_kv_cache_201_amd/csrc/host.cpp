@@ -480,7 +480,21 @@ pkv_status pkv_validate_indices(const int32_t* kv_indptr, const int32_t* kv_indi
     return PKV_OK;
 }
 
+namespace {
+pkv_status plan_single(const pkv_problem* pr, const pkv_tuning* tuning, pkv_plan** out);
+}  // namespace
+
 pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_plan** out) {
+    // host containers may throw; nothing may cross the C boundary
+    try {
+        return plan_single(pr, tuning, out);
+    } catch (const std::bad_alloc&) {
+        return PKV_ENOMEM;
+    }
+}
+
+namespace {
+pkv_status plan_single(const pkv_problem* pr, const pkv_tuning* tuning, pkv_plan** out) {
     if (!pr || !out) return PKV_EINVAL;
     pkv_tuning tu;
     pkv::PagedGeometry geo;
@@ -528,8 +542,10 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
 
     pkv_plan* pl = new (std::nothrow) pkv_plan();
     if (!pl) return PKV_ENOMEM;
+    std::unique_ptr<pkv_plan> owner(pl);
     fill_problem(pl, pr, tu, geo);
     pl->indptr0 = B > 0 ? pr->kv_indptr[0] : 0;
+    pl->indptr.assign(pr->kv_indptr, pr->kv_indptr + (B > 0 ? B + 1 : 0));
     pl->prefix_len = P;
     pl->path = path;
     // Prefix placement ("GraniKV", s.1): a prefix stored as one run of
@@ -602,9 +618,10 @@ pkv_status pkv_plan_create(const pkv_problem* pr, const pkv_tuning* tuning, pkv_
     // (prefix ranges, then suffix chunks) that one kernel combines; a request
     // inside one chunk of a paged pass has its output written directly.
     layout_workspace(pl, spans || path != PKV_PATH_PAGED, path != PKV_PATH_PAGED ? pl->prefix_splits : 0);
-    *out = pl;
+    *out = owner.release();
     return PKV_OK;
 }
+}  // namespace
 
 namespace {
 pkv_status plan_grouped(const pkv_problem* pr, const pkv_tuning* tuning, const int32_t* page_indptr,
@@ -984,3 +1001,61 @@ pkv_status pkv_plan_get_info(const pkv_plan* pl, pkv_plan_info* info) {
 void pkv_plan_destroy(pkv_plan* pl) { delete pl; }
 
 }  // extern "C"
+
+// Checks of the checked library (libpkv_checked.so), on host copies of the
+// arrays a step's kernels read.
+namespace pkv {
+
+pkv_status check_step_indptr(const pkv_plan& pl, const int32_t* kv_indptr) {
+    if ((int64_t)pl.indptr.size() != (pl.B > 0 ? pl.B + 1 : 0)) return PKV_EINVAL;  // a grouped plan
+    for (size_t i = 0; i < pl.indptr.size(); ++i)
+        if (kv_indptr[i] != pl.indptr[i]) return PKV_EINVAL;
+    return PKV_OK;
+}
+
+pkv_status check_slots(const int32_t* slots, int64_t n, int64_t num_slots) {
+    for (int64_t i = 0; i < n; ++i)
+        if (slots[i] < 0 || slots[i] >= num_slots) return PKV_ERANGE;
+    return PKV_OK;
+}
+
+pkv_status check_prefix_slots(const pkv_plan& pl, const int32_t* prefix, int64_t num_slots) {
+    const int64_t n = pl.prefix_tokens;
+    if (pl.prefix_base < 0) return check_slots(prefix, n, num_slots);
+    // the prefix pass reads slots prefix_base + t and not the indices
+    if ((int64_t)pl.prefix_base + n > num_slots) return PKV_ERANGE;
+    for (int64_t t = 0; t < n; ++t)
+        if ((int64_t)prefix[t] != pl.prefix_base + t) return PKV_EINVAL;
+    return PKV_OK;
+}
+
+pkv_status check_page_indptr(const pkv_plan& pl, const int32_t* page_indptr, int64_t* lo, int64_t* hi) {
+    *lo = *hi = 0;
+    if (pl.B == 0) return PKV_OK;
+    if ((int64_t)pl.indptr.size() != pl.B + 1) return PKV_EINVAL;
+    if (page_indptr[0] < 0) return PKV_EINVAL;
+    int64_t end = page_indptr[0];
+    for (int32_t b = 0; b < pl.B; ++b) {
+        const int64_t len = (int64_t)pl.indptr[b + 1] - pl.indptr[b];
+        const int64_t need = (len + pl.page_size - 1) / pl.page_size;
+        // fewer pages than the request's tokens fill (or a decreasing offset)
+        if ((int64_t)page_indptr[b + 1] - page_indptr[b] < need) return PKV_ERANGE;
+        end = std::max<int64_t>(end, (int64_t)page_indptr[b] + need);
+    }
+    *lo = page_indptr[0];
+    *hi = end;
+    return PKV_OK;
+}
+
+pkv_status check_group_metadata(const pkv_plan& pl, const int32_t* meta, int64_t num_slots) {
+    if (!pl.grouped) return PKV_EINVAL;
+    if (!std::equal(pl.meta.begin(), pl.meta.end(), meta)) return PKV_EINVAL;
+    const int32_t* m = pl.meta.data();
+    pkv_status st = check_slots(m + pl.meta_suffix_indices, pl.meta_group_indptr - pl.meta_suffix_indices, num_slots);
+    if (st != PKV_OK) return st;
+    // a run read as base + offset holds exactly those slots (the planner
+    // found it in these lowered indices)
+    return check_slots(m + pl.meta_prefix_indices, pl.meta_group_parent - pl.meta_prefix_indices, num_slots);
+}
+
+}  // namespace pkv

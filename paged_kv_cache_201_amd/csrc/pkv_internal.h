@@ -61,10 +61,39 @@ constexpr int32_t max_chunk_tokens(int32_t rs, int32_t nhl, int32_t tpi, int32_t
 
 }  // namespace pkv
 
+struct pkv_plan;
+
+namespace pkv {
+
+// Checks of a step's index arrays, made by the checked library
+// (libpkv_checked.so) on host copies of what its kernels would read, before
+// any launch.  Each returns PKV_OK, PKV_EINVAL (an array that does not
+// describe the planned batch) or PKV_ERANGE (a slot or page outside the
+// pool).
+//
+// kv_indptr [B + 1] equals the host kv_indptr the plan was made from.
+pkv_status check_step_indptr(const pkv_plan& pl, const int32_t* kv_indptr);
+// Every slot of slots[0 .. n) lies in [0, num_slots).
+pkv_status check_slots(const int32_t* slots, int64_t n, int64_t num_slots);
+// The prefix pass's slots: prefix [plan prefix_tokens] in range, and, when
+// the plan reads the prefix as one run of slots (prefix_base >= 0), exactly
+// that run.
+pkv_status check_prefix_slots(const pkv_plan& pl, const int32_t* prefix, int64_t num_slots);
+// A page table for the plan's kv_indptr: page_indptr [B + 1] starts at
+// offset >= 0 and gives request b at least ceil(L_b / page_size) pages; the
+// page list the kernel reads is then page_indices [*lo, *hi).
+pkv_status check_page_indptr(const pkv_plan& pl, const int32_t* page_indptr, int64_t* lo, int64_t* hi);
+// A grouped step's metadata block equals the plan's, and its lowered
+// suffix and prefix slots lie in the pool.
+pkv_status check_group_metadata(const pkv_plan& pl, const int32_t* meta, int64_t num_slots);
+
+}  // namespace pkv
+
 struct pkv_plan {
     // problem
     int32_t B, H_q, H_kv, D, G, q_dtype, kv_dtype, page_size;
     int32_t indptr0;          // host kv_indptr[0]
+    std::vector<int32_t> indptr;  // the host kv_indptr [B + 1] the plan was made from (single-prefix plans)
     int32_t prefix_len;       // declared shared prefix (tokens)
     int32_t prefix_base;      // prefix read as slots prefix_base + t (-1: by slot index)
     int32_t contiguous_prefixes; // prefix runs read as base + offset

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "pkv.h"
+#include "pkv_internal.h"
 
 namespace {
 
@@ -258,6 +259,107 @@ void check_grouped(const Table& t, int* planned, int64_t* meta_ints) {
             PKV_EINVAL);
 }
 
+// The checked library's checks (host.cpp), on exact-size copies of what a
+// step's kernels would read: the arrays the plan was made from pass, and a
+// changed indptr, a slot or page outside the pool, a short page list or a
+// broken prefix run is refused.
+void check_step_checks(const Table& t, int* checked) {
+    const int64_t n = total_tokens(t);
+    std::vector<int32_t> ip(t.B + 1), idx(n);
+    REQUIRE(pkv_lower_page_table(t.B, t.p, ptr(t.page_indptr), ptr(t.pages), ptr(t.lens), ptr(ip), ptr(idx), n) ==
+            PKV_OK);
+    int32_t max_page = -1, min_len = INT32_MAX;
+    for (int32_t x : t.pages) max_page = std::max(max_page, x);
+    for (int32_t L : t.lens) min_len = std::min(min_len, L);
+    const int64_t num_pages = max_page + 1, num_slots = num_pages * t.p;
+    pkv_problem pr{};
+    pr.batch = t.B;
+    pr.num_q_heads = 8;
+    pr.num_kv_heads = 2;
+    pr.head_dim = 128;
+    pr.q_dtype = pr.kv_dtype = PKV_BF16;
+    pr.page_size = t.p;
+    pr.kv_indptr = ptr(ip);
+    pr.kv_indices = uni(0, 1) ? ptr(idx) : nullptr;
+    pr.shared_prefix_len = t.B > 0 ? uni(0, min_len) : 0;
+    pr.force_path = uni(-1, 2);
+    pkv_plan* plan = nullptr;
+    if (pkv_plan_create(&pr, nullptr, &plan) != PKV_OK) return;
+    const pkv_plan& pl = *plan;
+    std::vector<int32_t> ip2 = ip;
+    REQUIRE(pkv::check_step_indptr(pl, ptr(ip2)) == PKV_OK);
+    if (t.B > 0) {
+        ip2[uni(0, t.B)] += 1;
+        REQUIRE(pkv::check_step_indptr(pl, ptr(ip2)) == PKV_EINVAL);
+    }
+    REQUIRE(pkv::check_slots(ptr(idx), n, num_slots) == PKV_OK);
+    if (n > 0) {
+        std::vector<int32_t> bad = idx;
+        const int64_t at = uni(0, (int)n - 1);
+        bad[at] = (int32_t)num_slots;
+        REQUIRE(pkv::check_slots(ptr(bad), n, num_slots) == PKV_ERANGE);
+        bad[at] = -1;
+        REQUIRE(pkv::check_slots(ptr(bad), n, num_slots) == PKV_ERANGE);
+    }
+    // the prefix pass's slots: request 0's first prefix_tokens
+    if (pl.path != PKV_PATH_PAGED && pl.prefix_tokens > 0) {
+        std::vector<int32_t> pre(idx.begin(), idx.begin() + pl.prefix_tokens);
+        REQUIRE(pkv::check_prefix_slots(pl, ptr(pre), num_slots) == PKV_OK);
+        if (pl.prefix_base >= 0) {
+            REQUIRE(pkv::check_prefix_slots(pl, ptr(pre), pl.prefix_base + pl.prefix_tokens - 1) == PKV_ERANGE);
+            pre[uni(0, pl.prefix_tokens - 1)] += 1;  // no longer the planned run
+            REQUIRE(pkv::check_prefix_slots(pl, ptr(pre), num_slots) == PKV_EINVAL);
+        } else {
+            pre[uni(0, pl.prefix_tokens - 1)] = (int32_t)num_slots;
+            REQUIRE(pkv::check_prefix_slots(pl, ptr(pre), num_slots) == PKV_ERANGE);
+        }
+    }
+    // the page table the pages entry reads
+    int64_t lo = -1, hi = -1;
+    std::vector<int32_t> pip = t.page_indptr;
+    REQUIRE(pkv::check_page_indptr(pl, ptr(pip), &lo, &hi) == PKV_OK);
+    REQUIRE(0 <= lo && lo <= hi && hi <= (int64_t)t.pages.size());
+    REQUIRE(pkv::check_slots(ptr(t.pages) + lo, hi - lo, num_pages) == PKV_OK);
+    if (hi > lo) {
+        std::vector<int32_t> pg(t.pages.begin() + lo, t.pages.begin() + hi);
+        pg[uni(0, (int)(hi - lo) - 1)] = (int32_t)num_pages;
+        REQUIRE(pkv::check_slots(ptr(pg), hi - lo, num_pages) == PKV_ERANGE);
+    }
+    for (int32_t b = 0; b < t.B; ++b) {
+        if (t.lens[b] == 0) continue;
+        pip = t.page_indptr;  // request b one page short
+        for (int32_t c = b + 1; c <= t.B; ++c) pip[c] -= 1;
+        REQUIRE(pkv::check_page_indptr(pl, ptr(pip), &lo, &hi) == PKV_ERANGE);
+        break;
+    }
+    if (t.B > 0) {
+        pip = t.page_indptr;
+        pip[0] = -1;  // a negative first offset
+        REQUIRE(pkv::check_page_indptr(pl, ptr(pip), &lo, &hi) == PKV_EINVAL);
+    }
+    REQUIRE(pkv::check_group_metadata(pl, ptr(idx), num_slots) == PKV_EINVAL);  // not a grouped plan
+    pkv_plan_destroy(plan);
+    // a grouped step's metadata block
+    pr.kv_indptr = nullptr;
+    pr.kv_indices = nullptr;
+    pr.shared_prefix_len = 0;
+    plan = nullptr;
+    if (pkv_plan_create_grouped(&pr, nullptr, ptr(t.page_indptr), ptr(t.pages), ptr(t.lens), &plan) != PKV_OK) return;
+    pkv_plan_info info;
+    REQUIRE(pkv_plan_get_info(plan, &info) == PKV_OK);
+    std::vector<int32_t> meta(info.metadata_ints);
+    REQUIRE(pkv_plan_metadata(plan, ptr(meta), info.metadata_ints) == PKV_OK);
+    REQUIRE(pkv::check_group_metadata(*plan, ptr(meta), num_slots) == PKV_OK);
+    if (n > 0) REQUIRE(pkv::check_group_metadata(*plan, ptr(meta), num_slots - 1) == PKV_ERANGE ||
+                       *std::max_element(idx.begin(), idx.end()) < num_slots - 1);
+    if (info.metadata_ints > 0) {
+        meta[uni(0, (int)info.metadata_ints - 1)] ^= 1;
+        REQUIRE(pkv::check_group_metadata(*plan, ptr(meta), num_slots) == PKV_EINVAL);
+    }
+    pkv_plan_destroy(plan);
+    ++*checked;
+}
+
 void check_malformed() {
     // null pointers, negative sizes, a non-zero first indptr, decreasing indptr
     int32_t ip[3] = {0, 2, 1}, idx[2] = {0, 1}, lens[2] = {2, 0}, out_ip[3];
@@ -300,7 +402,7 @@ void check_malformed() {
 
 int main(int argc, char** argv) {
     const int cases = argc > 1 ? std::atoi(argv[1]) : 400;
-    int planned = 0, grouped = 0;
+    int planned = 0, grouped = 0, checked = 0;
     int64_t meta_ints = 0;
     check_malformed();
     for (int i = 0; i < cases; ++i) {
@@ -308,8 +410,9 @@ int main(int argc, char** argv) {
         check_lowering(t);
         check_plan(t, &planned);
         check_grouped(t, &grouped, &meta_ints);
+        check_step_checks(t, &checked);
     }
-    std::printf("host_sanitize ok: %d tables, %d plans, %d grouped plans, %lld metadata ints\n", cases, planned,
-                grouped, (long long)meta_ints);
+    std::printf("host_sanitize ok: %d tables, %d plans, %d grouped plans, %lld metadata ints, %d step checks\n",
+                cases, planned, grouped, (long long)meta_ints, checked);
     return 0;
 }

@@ -25,10 +25,14 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
 
 
-def test_library_exports_every_declared_function():
+@pytest.mark.parametrize("path", ["libpkv.so", "libpkv_checked.so"])
+def test_library_exports_every_declared_function(path):
+    """libpkv.so and the checked library export exactly the functions
+    include/pkv.h declares."""
+    path = {"libpkv.so": pkv.LIB_PATH, "libpkv_checked.so": pkv.CHECKED_LIB_PATH}[path]
     declared = _declared_functions()
     assert len(declared) == 20, declared
-    lib = ctypes.CDLL(pkv.LIB_PATH)
+    lib = ctypes.CDLL(path)
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(pkv.EXPORTS) == declared
@@ -36,9 +40,26 @@ def test_library_exports_every_declared_function():
     import shutil
     import subprocess
     if shutil.which("nm"):
-        out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True, text=True).stdout
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
         text_syms = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
         assert text_syms == declared, text_syms
+
+
+def test_checked_library_plans_like_the_release_library():
+    """Inside checked_library() the binding's calls (plans included) go to
+    libpkv_checked.so, whose host half is the same: equal plans, and each
+    plan destroyed by the library that made it."""
+    ip = np.array([0, 700, 1500, 1500, 2600], np.int32)
+    kw = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype="bf16",
+              page_size=16, kv_indptr=ip, shared_prefix_len=0)
+    release = pkv.pkv_plan_create(**kw)
+    with pkv.checked_library() as lib:
+        assert pkv._lib is lib and lib._name == pkv.CHECKED_LIB_PATH
+        checked = pkv.pkv_plan_create(**kw)
+    assert pkv._lib._name == pkv.LIB_PATH
+    assert checked._lib._name == pkv.CHECKED_LIB_PATH and release._lib._name == pkv.LIB_PATH
+    assert checked.info == release.info
+    del checked, release
 
 
 def test_one_hip_runtime_whatever_the_import_order():
