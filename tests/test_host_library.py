@@ -60,6 +60,29 @@ def test_checked_library_plans_like_the_release_library():
     assert checked._lib._name == pkv.CHECKED_LIB_PATH and release._lib._name == pkv.LIB_PATH
     assert checked.info == release.info
     del checked, release
+    # and over random problems and tunings (a stale or mismatched checked
+    # build shows up here, on the CPU)
+    rng = np.random.default_rng(77)
+    for _ in range(150):
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(0, 3000, B)
+        P = int(rng.integers(0, int(lens.min()) + 1)) if rng.random() < 0.6 else 0
+        ip = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        G, H_kv = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 8]))
+        kv = str(rng.choice(["bf16", "fp8"]))
+        tune = dict(target_workgroups=int(rng.choice([128, 256, 512, 768])), fuse_cascade=int(rng.choice([0, 1, 12])),
+                    t_dense=int(rng.choice([1, 64, 4096])), prefix_target_workgroups=int(rng.choice([64, 256, 512])),
+                    segment_tokens=int(rng.choice([0, 16, 64])), max_heads_per_item=int(rng.choice([0, 1, 2])))
+        kw = dict(batch=B, num_q_heads=G * H_kv, num_kv_heads=H_kv, head_dim=int(rng.choice([64, 128])),
+                  q_dtype="bf16", kv_dtype=kv, page_size=int(rng.choice([1, 16, 64])), kv_indptr=ip,
+                  shared_prefix_len=P, force_path=int(rng.choice([-1, 0, 1, 2])), tuning=tune)
+        try:
+            release = pkv.pkv_plan_create(**kw)
+        except pkv.PkvError:
+            continue
+        with pkv.checked_library():
+            checked = pkv.pkv_plan_create(**kw)
+        assert checked.info == release.info, kw
 
 
 def test_one_hip_runtime_whatever_the_import_order():
