@@ -790,6 +790,7 @@ def write_planned_traces(parent, configs, command):
             out.append(f"| `{k[0]}` | {k[1]},{k[2]} | {k[3]} | {len(v)} | {statistics.median(d):.1f} | "
                        f"{statistics.mean(d):.1f} | {min(d):.1f} |")
         out.append(f"\nSum of kernel medians: {total:.1f} us per step.\n")
+    out.append(f"Source sha256 of the profiled library: `{kernel_source_hash()}`\n")
     path = os.path.join(ROOT, "profiles", "kernels.planned_steps.trace.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
@@ -824,6 +825,11 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
     """Turn the rocprofv3 output of the three profiling runs of the headline
     workload into the committed summaries under profiles/."""
     table, agg = summarize_trace(trace_dir)
+    # the sources the profiled run was built from (its bench line), else these
+    try:
+        sha = json.loads(open(trace_dir.rstrip("/") + ".json").read().strip().splitlines()[-1])["source_sha256"]
+    except (OSError, ValueError, KeyError, IndexError):
+        sha = kernel_source_hash()
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "kernels.llama_layer.trace.md"), "w") as f:
         f.write("# Kernel durations, Llama-3.1-8B decode layer (B=32, 4096 tokens, bf16), page size 1 and 128\n\n")
@@ -831,6 +837,7 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
         f.write("Every dispatch of the run, grouped by kernel and grid (the streaming-read probe is the "
                 "read-ceiling measurement; `paged_split_kernel` + `split_reduce_kernel` are one decode step).\n\n")
         f.write(table + "\n")
+        f.write(f"\nSource sha256 of the profiled library: `{sha}`\n")
     fetch = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = pmc_per_dispatch(write_dir, "WRITE_SIZE")
     med = lambda v: sorted(v)[len(v) // 2]
@@ -849,11 +856,6 @@ def write_profile_summaries(trace_dir, fetch_dir, write_dir, commands):
             kernels[f"{k} grid={grid}"] = dict(dispatches=len(vs), fetch_kib_median=med(vs),
                                                write_kib_median=med(w),
                                                bytes=med(vs) * 1024 * fetch_scale + med(w) * 1024 * write_scale)
-    # the sources the profiled run was built from (its bench line), else these
-    try:
-        sha = json.loads(open(trace_dir.rstrip("/") + ".json").read().strip().splitlines()[-1])["source_sha256"]
-    except (OSError, ValueError, KeyError, IndexError):
-        sha = kernel_source_hash()
     rec = dict(workload="Llama-3.1-8B decode layer, B=32, 4096 tokens, bf16, page size 1 and 128 (same plan)",
                commands=commands, source_sha256=sha, fetch_scale=fetch_scale,
                write_scale=write_scale,
