@@ -51,14 +51,17 @@ def algorithmic_bytes(batch, path, prefix_tokens=0):
 
 WINDOWS = 7             # timed windows of --steps steps per leg
 STABLE_TOL = 0.01       # warm until two consecutive windows agree this closely
+MIN_WARM_S = 0.25       # ... after at least this much warming (a leg on a freshly laid out pool drifts
+                        # slowly: consecutive short windows can agree while it is still 3-5 % slow)
 MAX_WARM_S = 3.0        # ... or until this much warming has passed
 
 
 def time_windows(fn, steps, warmup, windows=WINDOWS):
     """`warmup` untimed calls; then windows of `steps` back-to-back calls, each
-    between two events on the launch stream, until two consecutive windows
-    agree within STABLE_TOL (a steady clock and warm caches; at most
-    MAX_WARM_S of such warming); then `windows` timed windows.  Returns the
+    between two events on the launch stream, for at least MIN_WARM_S and until
+    two consecutive windows agree within STABLE_TOL (a steady clock and warm
+    caches; at most MAX_WARM_S of such warming); then `windows` timed
+    windows.  Returns the
     median, min and max ms per step over the timed windows, the warm-up
     windows it took and the total number of calls."""
     import statistics
@@ -86,7 +89,7 @@ def time_windows(fn, steps, warmup, windows=WINDOWS):
     while True:
         warm.append(window())
         a, b = warm[-2], warm[-1]
-        if abs(a - b) <= STABLE_TOL * min(a, b):
+        if abs(a - b) <= STABLE_TOL * min(a, b) and time.perf_counter() - t0 >= MIN_WARM_S:
             stable = True
             break
         if time.perf_counter() - t0 > MAX_WARM_S:
@@ -1363,8 +1366,8 @@ def main():
         "us_min": rec1["us_min"],
         "us_max": rec1["us_max"],
         "timing": f"median of {rec1['windows']} windows of {args.steps} steps each, after {args.warmup} warm-up "
-                  f"steps and {rec1['warm_windows']} warm-up windows (until two windows agree within "
-                  f"{100 * STABLE_TOL:g} %)",
+                  f"steps and {rec1['warm_windows']} warm-up windows (at least {MIN_WARM_S:g} s, until two "
+                  f"windows agree within {100 * STABLE_TOL:g} %)",
         "pct_peak": rec1["pct_peak"],
         "pct_read_ceiling": rec1["pct_read_ceiling"],
         "higher_is_better": True,
